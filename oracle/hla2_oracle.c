@@ -1,0 +1,411 @@
+/*
+ * hla2_oracle.c -- plain, slow fp64 CPU oracle for strictly causal second-order
+ * Higher-order Linear Attention (HLA2).  TEST INFRASTRUCTURE ONLY: nothing on the
+ * product path may link, load or call this file; only the tests, the smoke check
+ * and the benchmark's CPU-baseline leg do.  It shares no code, header or table
+ * with the GPU library.
+ *
+ * Sources (web pages about arXiv 2510.27258):
+ *   [SUM] "Technische Samenvatting: Hogere-orde Lineaire Aandacht (HLA)",
+ *         gist.science -- the technical summary; primary authority.
+ *   [ABS] "Высокоуровневое линейное внимание", chatpaper.ai -- the abstract.
+ *
+ * Everything works on ONE head: q, k are n x d row-major, v is n x dv row-major,
+ * tokens t = 0..n-1.  All arithmetic is IEEE double.
+ *
+ * What is computed (readings of the pages, stated once here):
+ *  - Prefix summaries [SUM §1 "Onderhoud van de toestand"]: key moment
+ *    S_t = sum_{i<=t} k_i k_i^T (d x d), query-value accumulator
+ *    C_t = sum_{i<=t} q_i v_i^T (d x dv), query mass m_t = sum_{i<=t} q_i (d).
+ *  - Cross summaries G_t (d x dv), h_t (d) [SUM §1 "Strenge causaliteit"] remove
+ *    from the naive product S_t C_t the pairs (i, j) where the query index j
+ *    comes BEFORE the key index i.  The pages name G and h but print no update;
+ *    the update used here, G_t = G_{t-1} + k_t (k_t^T C_{t-1}), is the unique one
+ *    that collects exactly those pairs, because at step t the new key k_t pairs
+ *    with every earlier query j <= t-1.  h likewise with m_{t-1}.
+ *  - Output [SUM §1 "Outputformulering"]: num_t = q_t^T (S_t C_t - G_t).
+ *    Expanding, num_t = sum_{j<=t} sum_{i<=j} (q_t.k_i)(q_j.k_i) v_j, i.e. row t
+ *    of L o (A A^T) V with A = L o (Q K^T) and L the lower triangle including
+ *    the diagonal; so the output at t depends on tokens j <= t only
+ *    [SUM "Resultaten en claims", causality bullet].
+ *  - Ratio normalisation [SUM §1 "Normalisatie"]: the masked denominator built
+ *    from the same kind of summaries, den_t = q_t^T (S_t m_t - h_t) = the row sum
+ *    of the same masked matrix; o_t = num_t / den_t with plain IEEE division
+ *    (the pages give no epsilon).
+ *  - Exponential decay [SUM "Belangrijkste bijdragen" 2 names decayed variants
+ *    but prints no formula].  Reading: every first-order summary decays by
+ *    gamma per token, S <- gamma S + k k^T, C <- gamma C + q v^T,
+ *    m <- gamma m + q.  Keeping o_t = q_t^T (S_t C_t - G_t) exact then forces
+ *    G <- gamma^2 G + gamma k (k^T C_{t-1}) (and h likewise), and the pair
+ *    (i <= j <= t) carries weight gamma^{(t-i)+(t-j)}.  gamma = 1 is no decay.
+ *  - Chunk-parallel form [SUM §4 "Associatieve operatoren", "Scan-equivalentie"]:
+ *    a segment of tokens is summarised by (Gamma, S, C, m, G, h), Gamma =
+ *    gamma^{len}; two consecutive segments A then B concatenate by the
+ *    semidirect-product rule
+ *      S = Gamma_B S_A + S_B,  C = Gamma_B C_A + C_B,  m = Gamma_B m_A + m_B,
+ *      G = Gamma_B^2 G_A + G_B + Gamma_B S_B C_A,
+ *      h = Gamma_B^2 h_A + h_B + Gamma_B S_B m_A,   Gamma = Gamma_A Gamma_B,
+ *    whose cross term S_B C_A is the one [SUM §4] names.  An exclusive Blelloch
+ *    scan over chunk summaries gives every chunk its incoming state, from which
+ *    the chunk's outputs follow; the result equals the serial recurrence.
+ *
+ * State block layout (one head), shared by decode and the final-state outputs:
+ *   S[d*d] | C[d*dv] | m[d] | G[d*dv] | h[d], all row-major.
+ */
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define HLA2_ORACLE_ABI_VERSION 1
+
+int hla2_oracle_abi_version(void) { return HLA2_ORACLE_ABI_VERSION; }
+
+long hla2_oracle_state_len(int d, int dv) { return (long)d * d + 2L * d * dv + 2L * d; }
+
+/* Summary block layout used by the chunked path and the combine:
+ *   Gamma[1] | S[d*d] | C[d*dv] | m[d] | G[d*dv] | h[d]. */
+long hla2_oracle_summary_len(int d, int dv) { return 1 + hla2_oracle_state_len(d, dv); }
+
+/* ---------------------------------------------------------------------------
+ * One streaming step [SUM §1; ABS: constant-size state, per-token update].
+ * state (in/out) is the layout above; q[d], k[d], v[dv] are token t.
+ * Writes num[dv] and *den for token t.
+ * Order: the cross summaries use C_{t-1}, m_{t-1}; then S, C, m take token t;
+ * then the readout uses the updated state.
+ * ------------------------------------------------------------------------- */
+void hla2_oracle_step(int d, int dv, double gamma, double *state,
+                      const double *q, const double *k, const double *v,
+                      double *num, double *den) {
+  double *S = state;
+  double *C = S + (long)d * d;
+  double *m = C + (long)d * dv;
+  double *G = m + d;
+  double *h = G + (long)d * dv;
+  double g2 = gamma * gamma;
+  int a, b, c;
+
+  /* kC = k^T C_{t-1} (dv), km = k^T m_{t-1} */
+  double *kC = (double *)calloc((size_t)dv, sizeof(double));
+  double km = 0.0;
+  for (a = 0; a < d; ++a) {
+    for (c = 0; c < dv; ++c) kC[c] += k[a] * C[(long)a * dv + c];
+    km += k[a] * m[a];
+  }
+  /* cross summaries */
+  for (a = 0; a < d; ++a) {
+    for (c = 0; c < dv; ++c)
+      G[(long)a * dv + c] = g2 * G[(long)a * dv + c] + gamma * k[a] * kC[c];
+    h[a] = g2 * h[a] + gamma * k[a] * km;
+  }
+  /* first-order summaries */
+  for (a = 0; a < d; ++a) {
+    for (b = 0; b < d; ++b) S[(long)a * d + b] = gamma * S[(long)a * d + b] + k[a] * k[b];
+    for (c = 0; c < dv; ++c) C[(long)a * dv + c] = gamma * C[(long)a * dv + c] + q[a] * v[c];
+    m[a] = gamma * m[a] + q[a];
+  }
+  /* readout: p = S^T q (S is symmetric), num = p^T C - q^T G, den = p.m - q.h */
+  double *p = (double *)calloc((size_t)d, sizeof(double));
+  for (a = 0; a < d; ++a)
+    for (b = 0; b < d; ++b) p[b] += q[a] * S[(long)a * d + b];
+  for (c = 0; c < dv; ++c) {
+    double s = 0.0;
+    for (a = 0; a < d; ++a) s += p[a] * C[(long)a * dv + c] - q[a] * G[(long)a * dv + c];
+    num[c] = s;
+  }
+  double sd = 0.0;
+  for (a = 0; a < d; ++a) sd += p[a] * m[a] - q[a] * h[a];
+  *den = sd;
+  free(p);
+  free(kC);
+}
+
+/* ---------------------------------------------------------------------------
+ * Serial recurrence over a whole sequence (one head).
+ * state: nullable.  If given, it is the state before token 0 and receives the
+ * state after token n-1; if NULL the run starts from the all-zero state.
+ * num: n*dv, den: n (nullable).
+ * ------------------------------------------------------------------------- */
+int hla2_oracle_serial(int n, int d, int dv, double gamma,
+                       const double *q, const double *k, const double *v,
+                       double *num, double *den, double *state) {
+  if (n < 0 || d <= 0 || dv <= 0) return -1;
+  long L = hla2_oracle_state_len(d, dv);
+  double *st = state ? state : (double *)calloc((size_t)L, sizeof(double));
+  double dummy;
+  int t;
+  for (t = 0; t < n; ++t)
+    hla2_oracle_step(d, dv, gamma, st, q + (long)t * d, k + (long)t * d, v + (long)t * dv,
+                     num + (long)t * dv, den ? den + t : &dummy);
+  if (!state) free(st);
+  return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Brute force straight from the definition (small n only):
+ *   num_t = sum_{j<=t} sum_{i<=j} gamma^{(t-i)+(t-j)} (q_t.k_i)(q_j.k_i) v_j
+ *   den_t = the same sum without v_j.
+ * Cost O(n^2 (n + d) + n^2 dv).
+ * ------------------------------------------------------------------------- */
+int hla2_oracle_bruteforce(int n, int d, int dv, double gamma,
+                           const double *q, const double *k, const double *v,
+                           double *num, double *den) {
+  if (n < 0 || d <= 0 || dv <= 0) return -1;
+  double *dot = (double *)malloc(sizeof(double) * (size_t)n * (size_t)(n > 0 ? n : 1));
+  int t, i, j, a, c;
+  /* dot[t*n + i] = q_t . k_i */
+  for (t = 0; t < n; ++t)
+    for (i = 0; i < n; ++i) {
+      double s = 0.0;
+      for (a = 0; a < d; ++a) s += q[(long)t * d + a] * k[(long)i * d + a];
+      dot[(long)t * n + i] = s;
+    }
+  for (t = 0; t < n; ++t) {
+    for (c = 0; c < dv; ++c) num[(long)t * dv + c] = 0.0;
+    double dsum = 0.0;
+    for (j = 0; j <= t; ++j) {
+      double w = 0.0;
+      for (i = 0; i <= j; ++i)
+        w += pow(gamma, (double)((t - i) + (t - j))) * dot[(long)t * n + i] * dot[(long)j * n + i];
+      for (c = 0; c < dv; ++c) num[(long)t * dv + c] += w * v[(long)j * dv + c];
+      dsum += w;
+    }
+    if (den) den[t] = dsum;
+  }
+  free(dot);
+  return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Summary of one segment of `len` tokens, built by definition (pairs inside
+ * the segment, weights measured from the segment's last token T = len-1):
+ *   S = sum_i g^{T-i} k_i k_i^T,  C = sum_j g^{T-j} q_j v_j^T,  m = sum_j g^{T-j} q_j,
+ *   G = sum_{j<i} g^{(T-i)+(T-j)} k_i (k_i.q_j) v_j^T,   h likewise without v,
+ *   Gamma = g^{len}.
+ * ------------------------------------------------------------------------- */
+void hla2_oracle_segment_summary(int len, int d, int dv, double gamma,
+                                 const double *q, const double *k, const double *v,
+                                 double *sum) {
+  long L = hla2_oracle_summary_len(d, dv);
+  double *Gam = sum, *S = sum + 1;
+  double *C = S + (long)d * d, *m = C + (long)d * dv, *G = m + d, *h = G + (long)d * dv;
+  int i, j, a, b, c;
+  memset(sum, 0, sizeof(double) * (size_t)L);
+  *Gam = pow(gamma, (double)len);
+  int T = len - 1;
+  for (i = 0; i < len; ++i) {
+    double wi = pow(gamma, (double)(T - i));
+    const double *ki = k + (long)i * d, *qi = q + (long)i * d, *vi = v + (long)i * dv;
+    for (a = 0; a < d; ++a) {
+      for (b = 0; b < d; ++b) S[(long)a * d + b] += wi * ki[a] * ki[b];
+      for (c = 0; c < dv; ++c) C[(long)a * dv + c] += wi * qi[a] * vi[c];
+      m[a] += wi * qi[a];
+    }
+    for (j = 0; j < i; ++j) {
+      double wj = pow(gamma, (double)(T - j));
+      const double *qj = q + (long)j * d, *vj = v + (long)j * dv;
+      double kq = 0.0;
+      for (a = 0; a < d; ++a) kq += ki[a] * qj[a];
+      for (a = 0; a < d; ++a) {
+        double f = wi * wj * ki[a] * kq;
+        for (c = 0; c < dv; ++c) G[(long)a * dv + c] += f * vj[c];
+        h[a] += f;
+      }
+    }
+  }
+}
+
+/* Identity element of the combine: Gamma = 1, everything else zero. */
+void hla2_oracle_identity(int d, int dv, double *sum) {
+  memset(sum, 0, sizeof(double) * (size_t)hla2_oracle_summary_len(d, dv));
+  sum[0] = 1.0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Semidirect-product combine: out = A then B (A earlier in the sequence).
+ * [SUM §4 "Associatieve operatoren"]; out may alias neither input.
+ * ------------------------------------------------------------------------- */
+void hla2_oracle_combine(int d, int dv, const double *A, const double *B, double *out) {
+  const double GA = A[0], GB = B[0];
+  const double *SA = A + 1, *CA = SA + (long)d * d, *mA = CA + (long)d * dv,
+               *GgA = mA + d, *hA = GgA + (long)d * dv;
+  const double *SB = B + 1, *CB = SB + (long)d * d, *mB = CB + (long)d * dv,
+               *GgB = mB + d, *hB = GgB + (long)d * dv;
+  double *So = out + 1, *Co = So + (long)d * d, *mo = Co + (long)d * dv,
+         *Go = mo + d, *ho = Go + (long)d * dv;
+  int a, b, c;
+  out[0] = GA * GB;
+  for (a = 0; a < d; ++a) {
+    for (b = 0; b < d; ++b) So[(long)a * d + b] = GB * SA[(long)a * d + b] + SB[(long)a * d + b];
+    for (c = 0; c < dv; ++c) Co[(long)a * dv + c] = GB * CA[(long)a * dv + c] + CB[(long)a * dv + c];
+    mo[a] = GB * mA[a] + mB[a];
+  }
+  /* G = GB^2 G_A + G_B + GB * S_B C_A ;  h = GB^2 h_A + h_B + GB * S_B m_A */
+  for (a = 0; a < d; ++a) {
+    for (c = 0; c < dv; ++c) {
+      double s = 0.0;
+      for (b = 0; b < d; ++b) s += SB[(long)a * d + b] * CA[(long)b * dv + c];
+      Go[(long)a * dv + c] = GB * GB * GgA[(long)a * dv + c] + GgB[(long)a * dv + c] + GB * s;
+    }
+    double s = 0.0;
+    for (b = 0; b < d; ++b) s += SB[(long)a * d + b] * mA[b];
+    ho[a] = GB * GB * hA[a] + hB[a] + GB * s;
+  }
+}
+
+/* ---------------------------------------------------------------------------
+ * Exclusive Blelloch scan, in place, over `count` summaries laid out back to
+ * back (stride = summary length).  The array is padded to a power of two with
+ * identity elements; the up-sweep builds partial products in a balanced tree,
+ * the root is replaced by the identity, and the down-sweep hands every node
+ * the product of everything to its left.  Afterwards element c holds the
+ * combination of elements 0..c-1 (the identity for c = 0).
+ * ------------------------------------------------------------------------- */
+int hla2_oracle_exclusive_scan(int d, int dv, int count, double *sums) {
+  long L = hla2_oracle_summary_len(d, dv);
+  int P = 1, i;
+  if (count <= 0) return 0;
+  while (P < count) P <<= 1;
+  double *x = (double *)malloc(sizeof(double) * (size_t)L * (size_t)P);
+  double *tmp = (double *)malloc(sizeof(double) * (size_t)L);
+  double *left = (double *)malloc(sizeof(double) * (size_t)L);
+  if (!x || !tmp || !left) { free(x); free(tmp); free(left); return -2; }
+  memcpy(x, sums, sizeof(double) * (size_t)L * (size_t)count);
+  for (i = count; i < P; ++i) hla2_oracle_identity(d, dv, x + (long)i * L);
+  /* up-sweep: x[r] <- x[l] then x[r], r = right child of each pair */
+  int stride;
+  for (stride = 1; stride < P; stride <<= 1) {
+    for (i = 2 * stride - 1; i < P; i += 2 * stride) {
+      double *xl = x + (long)(i - stride) * L, *xr = x + (long)i * L;
+      hla2_oracle_combine(d, dv, xl, xr, tmp);
+      memcpy(xr, tmp, sizeof(double) * (size_t)L);
+    }
+  }
+  /* root gets the identity */
+  hla2_oracle_identity(d, dv, x + (long)(P - 1) * L);
+  /* down-sweep: (left, right) <- (right, right then left-subtree total) */
+  for (stride = P >> 1; stride >= 1; stride >>= 1) {
+    for (i = 2 * stride - 1; i < P; i += 2 * stride) {
+      double *xl = x + (long)(i - stride) * L, *xr = x + (long)i * L;
+      memcpy(left, xl, sizeof(double) * (size_t)L);  /* total of left subtree */
+      memcpy(xl, xr, sizeof(double) * (size_t)L);    /* prefix before this node */
+      hla2_oracle_combine(d, dv, xr, left, tmp);     /* prefix, then left subtree */
+      memcpy(xr, tmp, sizeof(double) * (size_t)L);
+    }
+  }
+  memcpy(sums, x, sizeof(double) * (size_t)L * (size_t)count);
+  free(x); free(tmp); free(left);
+  return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Outputs of one chunk of `len` tokens from its incoming state (S0, C0, m0,
+ * G0, h0), written out in the chunk-local matrix form.  With tau the local
+ * index, D[tau][i] = gamma^{tau-i} for i <= tau (else 0), A = L o (Q K^T):
+ *   U0 = S0 C0 - G0,  u0 = S0 m0 - h0,
+ *   W[tau][j] = D[tau][j] * ( gamma^{tau+1} q_tau^T S0 q_j
+ *                            + sum_{i<=j} D[tau][i] A[tau][i] A[j][i] ),  j <= tau
+ *   num_tau = gamma^{2(tau+1)} q_tau^T U0 + sum_{j<=tau} W[tau][j] v_j
+ *   den_tau = gamma^{2(tau+1)} q_tau^T u0 + sum_{j<=tau} W[tau][j].
+ * The first term carries every pair with both indices before the chunk, the
+ * q^T S0 q term the pairs whose key index lies before the chunk and whose query
+ * index lies inside, the last sum the pairs inside the chunk.
+ * ------------------------------------------------------------------------- */
+static void chunk_outputs(int len, int d, int dv, double gamma, const double *state_in,
+                          const double *q, const double *k, const double *v,
+                          double *num, double *den) {
+  const double *S0 = state_in + 1, *C0 = S0 + (long)d * d, *m0 = C0 + (long)d * dv,
+               *G0 = m0 + d, *h0 = G0 + (long)d * dv;
+  double *U0 = (double *)malloc(sizeof(double) * (size_t)d * dv);
+  double *u0 = (double *)malloc(sizeof(double) * (size_t)d);
+  double *A = (double *)malloc(sizeof(double) * (size_t)len * len);
+  double *QS = (double *)malloc(sizeof(double) * (size_t)len * d);
+  int a, b, c, tau, i, j;
+  for (a = 0; a < d; ++a) {
+    for (c = 0; c < dv; ++c) {
+      double s = 0.0;
+      for (b = 0; b < d; ++b) s += S0[(long)a * d + b] * C0[(long)b * dv + c];
+      U0[(long)a * dv + c] = s - G0[(long)a * dv + c];
+    }
+    double s = 0.0;
+    for (b = 0; b < d; ++b) s += S0[(long)a * d + b] * m0[b];
+    u0[a] = s - h0[a];
+  }
+  for (tau = 0; tau < len; ++tau) {
+    for (i = 0; i < len; ++i) {
+      double s = 0.0;
+      if (i <= tau)
+        for (a = 0; a < d; ++a) s += q[(long)tau * d + a] * k[(long)i * d + a];
+      A[(long)tau * len + i] = s;
+    }
+    for (b = 0; b < d; ++b) {
+      double s = 0.0;
+      for (a = 0; a < d; ++a) s += q[(long)tau * d + a] * S0[(long)a * d + b];
+      QS[(long)tau * d + b] = s;
+    }
+  }
+  for (tau = 0; tau < len; ++tau) {
+    double carry = pow(gamma, 2.0 * (tau + 1));
+    double *o = num + (long)tau * dv;
+    for (c = 0; c < dv; ++c) {
+      double s = 0.0;
+      for (a = 0; a < d; ++a) s += q[(long)tau * d + a] * U0[(long)a * dv + c];
+      o[c] = carry * s;
+    }
+    double dn = 0.0;
+    for (a = 0; a < d; ++a) dn += q[(long)tau * d + a] * u0[a];
+    dn *= carry;
+    for (j = 0; j <= tau; ++j) {
+      double qsq = 0.0;
+      for (b = 0; b < d; ++b) qsq += QS[(long)tau * d + b] * q[(long)j * d + b];
+      double inner = 0.0;
+      for (i = 0; i <= j; ++i)
+        inner += pow(gamma, (double)(tau - i)) * A[(long)tau * len + i] * A[(long)j * len + i];
+      double w = pow(gamma, (double)(tau - j)) * (pow(gamma, (double)(tau + 1)) * qsq + inner);
+      for (c = 0; c < dv; ++c) o[c] += w * v[(long)j * dv + c];
+      dn += w;
+    }
+    if (den) den[tau] = dn;
+  }
+  free(U0); free(u0); free(A); free(QS);
+}
+
+/* ---------------------------------------------------------------------------
+ * Chunk-parallel path (one head): summaries of every chunk of `chunk` tokens
+ * (the last may be shorter), exclusive Blelloch scan, then chunk outputs from
+ * each chunk's incoming state.  If `state_out` is non-NULL it receives the
+ * state after the last token (the inclusive total, Gamma dropped).
+ * ------------------------------------------------------------------------- */
+int hla2_oracle_chunked(int n, int d, int dv, double gamma, int chunk,
+                        const double *q, const double *k, const double *v,
+                        double *num, double *den, double *state_out) {
+  if (n < 0 || d <= 0 || dv <= 0 || chunk <= 0) return -1;
+  if (n == 0) {
+    if (state_out) memset(state_out, 0, sizeof(double) * (size_t)hla2_oracle_state_len(d, dv));
+    return 0;
+  }
+  int nc = (n + chunk - 1) / chunk, c;
+  long L = hla2_oracle_summary_len(d, dv);
+  double *sums = (double *)malloc(sizeof(double) * (size_t)L * (size_t)nc);
+  double *incl = (double *)malloc(sizeof(double) * (size_t)L);
+  if (!sums || !incl) { free(sums); free(incl); return -2; }
+  for (c = 0; c < nc; ++c) {
+    int t0 = c * chunk, len = (n - t0 < chunk) ? n - t0 : chunk;
+    hla2_oracle_segment_summary(len, d, dv, gamma, q + (long)t0 * d, k + (long)t0 * d,
+                                v + (long)t0 * dv, sums + (long)c * L);
+  }
+  double *last = (double *)malloc(sizeof(double) * (size_t)L);
+  memcpy(last, sums + (long)(nc - 1) * L, sizeof(double) * (size_t)L);
+  int rc = hla2_oracle_exclusive_scan(d, dv, nc, sums);
+  if (rc) { free(sums); free(incl); free(last); return rc; }
+  for (c = 0; c < nc; ++c) {
+    int t0 = c * chunk, len = (n - t0 < chunk) ? n - t0 : chunk;
+    chunk_outputs(len, d, dv, gamma, sums + (long)c * L, q + (long)t0 * d, k + (long)t0 * d,
+                  v + (long)t0 * dv, num + (long)t0 * dv, den ? den + t0 : NULL);
+  }
+  if (state_out) {
+    hla2_oracle_combine(d, dv, sums + (long)(nc - 1) * L, last, incl);
+    memcpy(state_out, incl + 1, sizeof(double) * (size_t)(L - 1));
+  }
+  free(sums); free(incl); free(last);
+  return 0;
+}

@@ -1,0 +1,254 @@
+"""ctypes front end of the fp64 HLA2 oracle (``hla2_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY.  The tests, ``__graft_entry__.smoke()`` and the
+benchmark's ``cpu_baseline`` leg may import this module; the GPU library and its
+Python binding never do, and this module imports nothing from them.
+
+Every function takes numpy arrays (any float dtype; they are converted to
+float64 C-contiguous copies) and returns float64 arrays.  Leading dimensions
+before (n, d) are independent heads; they are spread over a thread pool (the C
+calls release the GIL), one head per task, each head computed serially.
+
+What the C code computes, and the page passages it follows, is written out in
+the header of ``hla2_oracle.c``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "hla2_oracle.c")
+_LIB = os.path.join(_HERE, "libhla2_oracle.so")
+_lock = threading.Lock()
+_libs: dict = {}
+
+_dp = ctypes.POINTER(ctypes.c_double)
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (strict IEEE double, no contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-std=c99", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+               _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load(path: str | None = None):
+    """The oracle library (built on first use), or another build of the same
+    source at `path` (the tests load deliberately broken builds this way)."""
+    key = path or _LIB
+    with _lock:
+        lib = _libs.get(key)
+        if lib is None:
+            if path is None:
+                build()
+            lib = ctypes.CDLL(key)
+            i, d_ = ctypes.c_int, ctypes.c_double
+            lib.hla2_oracle_state_len.restype = ctypes.c_long
+            lib.hla2_oracle_state_len.argtypes = [i, i]
+            lib.hla2_oracle_summary_len.restype = ctypes.c_long
+            lib.hla2_oracle_summary_len.argtypes = [i, i]
+            lib.hla2_oracle_step.restype = None
+            lib.hla2_oracle_step.argtypes = [i, i, d_, _dp, _dp, _dp, _dp, _dp, _dp]
+            lib.hla2_oracle_serial.restype = i
+            lib.hla2_oracle_serial.argtypes = [i, i, i, d_, _dp, _dp, _dp, _dp, _dp, _dp]
+            lib.hla2_oracle_bruteforce.restype = i
+            lib.hla2_oracle_bruteforce.argtypes = [i, i, i, d_, _dp, _dp, _dp, _dp, _dp]
+            lib.hla2_oracle_segment_summary.restype = None
+            lib.hla2_oracle_segment_summary.argtypes = [i, i, i, d_, _dp, _dp, _dp, _dp]
+            lib.hla2_oracle_identity.restype = None
+            lib.hla2_oracle_identity.argtypes = [i, i, _dp]
+            lib.hla2_oracle_combine.restype = None
+            lib.hla2_oracle_combine.argtypes = [i, i, _dp, _dp, _dp]
+            lib.hla2_oracle_exclusive_scan.restype = i
+            lib.hla2_oracle_exclusive_scan.argtypes = [i, i, i, _dp]
+            lib.hla2_oracle_chunked.restype = i
+            lib.hla2_oracle_chunked.argtypes = [i, i, i, d_, i, _dp, _dp, _dp, _dp, _dp, _dp]
+            _libs[key] = lib
+    return lib
+
+
+def _f64(x) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(_dp)
+
+
+def state_len(d: int, dv: int, lib=None) -> int:
+    return int((lib or _load()).hla2_oracle_state_len(d, dv))
+
+
+def summary_len(d: int, dv: int, lib=None) -> int:
+    return int((lib or _load()).hla2_oracle_summary_len(d, dv))
+
+
+def split_state(state: np.ndarray, d: int, dv: int) -> dict:
+    """Views of S, C, m, G, h inside a state block (last axis = state_len)."""
+    o = 0
+    out = {}
+    for name, shape in (("S", (d, d)), ("C", (d, dv)), ("m", (d,)), ("G", (d, dv)), ("h", (d,))):
+        size = int(np.prod(shape))
+        out[name] = state[..., o:o + size].reshape(state.shape[:-1] + shape)
+        o += size
+    return out
+
+
+def default_threads() -> int:
+    env = os.environ.get("HLA2_ORACLE_THREADS")
+    if env:
+        return max(1, int(env))
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def _run_heads(fn, count: int, threads: int | None):
+    threads = default_threads() if threads is None else max(1, threads)
+    if threads == 1 or count <= 1:
+        for h in range(count):
+            fn(h)
+        return
+    with ThreadPoolExecutor(max_workers=min(threads, count)) as ex:
+        list(ex.map(fn, range(count)))
+
+
+def serial(q, k, v, gamma: float = 1.0, state=None, threads: int | None = None, lib=None):
+    """Serial recurrence over every head.
+
+    q, k: [..., n, d]; v: [..., n, dv]; state: optional [..., state_len] initial
+    state.  Returns (num [..., n, dv], den [..., n], final_state [..., state_len]).
+    """
+    lib = lib or _load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    *lead, n, d = q.shape
+    dv = v.shape[-1]
+    assert k.shape == q.shape and tuple(v.shape[:-1]) == tuple(q.shape[:-1])
+    H = int(np.prod(lead)) if lead else 1
+    qh, kh, vh = q.reshape(H, n, d), k.reshape(H, n, d), v.reshape(H, n, dv)
+    L = state_len(d, dv, lib)
+    st = np.zeros((H, L)) if state is None else _f64(state).reshape(H, L).copy()
+    num = np.empty((H, n, dv))
+    den = np.empty((H, n))
+
+    def one(h):
+        rc = lib.hla2_oracle_serial(n, d, dv, float(gamma), _p(qh[h]), _p(kh[h]), _p(vh[h]),
+                                    _p(num[h]), _p(den[h]), _p(st[h]))
+        assert rc == 0
+
+    _run_heads(one, H, threads)
+    return (num.reshape(*lead, n, dv), den.reshape(*lead, n), st.reshape(*lead, L))
+
+
+def step(state, q, k, v, gamma: float = 1.0, lib=None):
+    """One decode step for every head.  state: [..., state_len] (copied);
+    q, k: [..., d]; v: [..., dv].  Returns (num, den, new_state)."""
+    lib = lib or _load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    *lead, d = q.shape
+    dv = v.shape[-1]
+    H = int(np.prod(lead)) if lead else 1
+    L = state_len(d, dv, lib)
+    st = _f64(state).reshape(H, L).copy()
+    qh, kh, vh = q.reshape(H, d), k.reshape(H, d), v.reshape(H, dv)
+    num = np.empty((H, dv))
+    den = np.empty((H,))
+    for h in range(H):
+        dd = ctypes.c_double(0.0)
+        lib.hla2_oracle_step(d, dv, float(gamma), _p(st[h]), _p(qh[h]), _p(kh[h]), _p(vh[h]),
+                             _p(num[h]), ctypes.byref(dd))
+        den[h] = dd.value
+    return num.reshape(tuple(lead) + (dv,)), den.reshape(tuple(lead)), st.reshape(tuple(lead) + (L,))
+
+
+def bruteforce(q, k, v, gamma: float = 1.0, threads: int | None = None, lib=None):
+    """Definition-level triple sum (small n).  Returns (num, den)."""
+    lib = lib or _load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    *lead, n, d = q.shape
+    dv = v.shape[-1]
+    H = int(np.prod(lead)) if lead else 1
+    qh, kh, vh = q.reshape(H, n, d), k.reshape(H, n, d), v.reshape(H, n, dv)
+    num = np.empty((H, n, dv))
+    den = np.empty((H, n))
+
+    def one(h):
+        assert lib.hla2_oracle_bruteforce(n, d, dv, float(gamma), _p(qh[h]), _p(kh[h]), _p(vh[h]),
+                                          _p(num[h]), _p(den[h])) == 0
+
+    _run_heads(one, H, threads)
+    return num.reshape(*lead, n, dv), den.reshape(*lead, n)
+
+
+def chunked(q, k, v, gamma: float = 1.0, chunk: int = 16, threads: int | None = None, lib=None):
+    """Chunk summaries + exclusive Blelloch scan + chunk outputs.
+    Returns (num, den, final_state)."""
+    lib = lib or _load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    *lead, n, d = q.shape
+    dv = v.shape[-1]
+    H = int(np.prod(lead)) if lead else 1
+    qh, kh, vh = q.reshape(H, n, d), k.reshape(H, n, d), v.reshape(H, n, dv)
+    L = state_len(d, dv, lib)
+    num = np.empty((H, n, dv))
+    den = np.empty((H, n))
+    st = np.empty((H, L))
+
+    def one(h):
+        assert lib.hla2_oracle_chunked(n, d, dv, float(gamma), int(chunk), _p(qh[h]), _p(kh[h]),
+                                       _p(vh[h]), _p(num[h]), _p(den[h]), _p(st[h])) == 0
+
+    _run_heads(one, H, threads)
+    return num.reshape(*lead, n, dv), den.reshape(*lead, n), st.reshape(*lead, L)
+
+
+def segment_summary(q, k, v, gamma: float = 1.0, lib=None):
+    """Summary (Gamma, S, C, m, G, h) of one segment; q,k: [len, d], v: [len, dv]."""
+    lib = lib or _load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    n, d = q.shape
+    dv = v.shape[-1]
+    out = np.empty(summary_len(d, dv, lib))
+    lib.hla2_oracle_segment_summary(n, d, dv, float(gamma), _p(q), _p(k), _p(v), _p(out))
+    return out
+
+
+def identity(d: int, dv: int, lib=None):
+    lib = lib or _load()
+    out = np.empty(summary_len(d, dv, lib))
+    lib.hla2_oracle_identity(d, dv, _p(out))
+    return out
+
+
+def combine(a, b, d: int, dv: int, lib=None):
+    """a then b (a is the earlier segment)."""
+    lib = lib or _load()
+    a, b = _f64(a), _f64(b)
+    out = np.empty(summary_len(d, dv, lib))
+    lib.hla2_oracle_combine(d, dv, _p(a), _p(b), _p(out))
+    return out
+
+
+def exclusive_scan(sums, d: int, dv: int, lib=None):
+    """Exclusive Blelloch scan of a [count, summary_len] array (copied)."""
+    lib = lib or _load()
+    s = _f64(sums).copy()
+    assert lib.hla2_oracle_exclusive_scan(d, dv, s.shape[0], _p(s)) == 0
+    return s
+
+
+def ratio(num, den):
+    """o = num / den with IEEE semantics (no epsilon)."""
+    with np.errstate(divide="ignore", invalid="ignore"):
+        return np.asarray(num) / np.asarray(den)[..., None]
