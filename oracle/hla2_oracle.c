@@ -141,6 +141,38 @@ int hla2_oracle_serial(int n, int d, int dv, double gamma,
 }
 
 /* ---------------------------------------------------------------------------
+ * Serial recurrence that also reports, per token, the Euclidean norm of the
+ * denominator state u_t = S_t m_t - h_t (so den_t = q_t . u_t).  The ratio
+ * q_t . u_t / (|q_t| |u_t|) measures how well-conditioned the ratio-normalised
+ * output is at t [SUM §1 "Normalisatie"]: where it is tiny, den_t is a
+ * cancellation of large terms and num_t / den_t amplifies any rounding.
+ * Arguments as hla2_oracle_serial plus unorm (n).
+ * ------------------------------------------------------------------------- */
+int hla2_oracle_serial_unorm(int n, int d, int dv, double gamma,
+                             const double *q, const double *k, const double *v,
+                             double *num, double *den, double *unorm, double *state) {
+  if (n < 0 || d <= 0 || dv <= 0) return -1;
+  long L = hla2_oracle_state_len(d, dv);
+  double *st = state ? state : (double *)calloc((size_t)L, sizeof(double));
+  const double *S = st, *m = st + (long)d * d + (long)d * dv, *h = m + d + (long)d * dv;
+  double dummy;
+  int t, a, b;
+  for (t = 0; t < n; ++t) {
+    hla2_oracle_step(d, dv, gamma, st, q + (long)t * d, k + (long)t * d, v + (long)t * dv,
+                     num + (long)t * dv, den ? den + t : &dummy);
+    double ss = 0.0;
+    for (a = 0; a < d; ++a) {
+      double u = -h[a];
+      for (b = 0; b < d; ++b) u += S[(long)a * d + b] * m[b];
+      ss += u * u;
+    }
+    unorm[t] = sqrt(ss);
+  }
+  if (!state) free(st);
+  return 0;
+}
+
+/* ---------------------------------------------------------------------------
  * Brute force straight from the definition (small n only):
  *   num_t = sum_{j<=t} sum_{i<=j} gamma^{(t-i)+(t-j)} (q_t.k_i)(q_j.k_i) v_j
  *   den_t = the same sum without v_j.

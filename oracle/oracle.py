@@ -61,6 +61,8 @@ def _load(path: str | None = None):
             lib.hla2_oracle_step.argtypes = [i, i, d_, _dp, _dp, _dp, _dp, _dp, _dp]
             lib.hla2_oracle_serial.restype = i
             lib.hla2_oracle_serial.argtypes = [i, i, i, d_, _dp, _dp, _dp, _dp, _dp, _dp]
+            lib.hla2_oracle_serial_unorm.restype = i
+            lib.hla2_oracle_serial_unorm.argtypes = [i, i, i, d_, _dp, _dp, _dp, _dp, _dp, _dp, _dp]
             lib.hla2_oracle_bruteforce.restype = i
             lib.hla2_oracle_bruteforce.argtypes = [i, i, i, d_, _dp, _dp, _dp, _dp, _dp]
             lib.hla2_oracle_segment_summary.restype = None
@@ -149,6 +151,31 @@ def serial(q, k, v, gamma: float = 1.0, state=None, threads: int | None = None, 
 
     _run_heads(one, H, threads)
     return (num.reshape(*lead, n, dv), den.reshape(*lead, n), st.reshape(*lead, L))
+
+
+def serial_unorm(q, k, v, gamma: float = 1.0, state=None, threads: int | None = None, lib=None):
+    """Like serial(), plus |S_t m_t - h_t| per token.
+
+    Returns (num, den, unorm [..., n], final_state)."""
+    lib = lib or _load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    *lead, n, d = q.shape
+    dv = v.shape[-1]
+    H = int(np.prod(lead)) if lead else 1
+    qh, kh, vh = q.reshape(H, n, d), k.reshape(H, n, d), v.reshape(H, n, dv)
+    L = state_len(d, dv, lib)
+    st = np.zeros((H, L)) if state is None else _f64(state).reshape(H, L).copy()
+    num = np.empty((H, n, dv))
+    den = np.empty((H, n))
+    un = np.empty((H, n))
+
+    def one(h):
+        assert lib.hla2_oracle_serial_unorm(n, d, dv, float(gamma), _p(qh[h]), _p(kh[h]), _p(vh[h]),
+                                            _p(num[h]), _p(den[h]), _p(un[h]), _p(st[h])) == 0
+
+    _run_heads(one, H, threads)
+    lt = tuple(lead)
+    return num.reshape(lt + (n, dv)), den.reshape(lt + (n,)), un.reshape(lt + (n,)), st.reshape(lt + (L,))
 
 
 def step(state, q, k, v, gamma: float = 1.0, lib=None):

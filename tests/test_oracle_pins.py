@@ -250,3 +250,20 @@ def test_multihead_threads_match_single():
         for g in range(2):
             one = O.serial(q[h, g], k[h, g], v[h, g], 0.9)
             np.testing.assert_array_equal(one[0], a[0][h, g])
+
+
+def test_unorm_matches_state_and_serial():
+    # |S_t m_t - h_t| from the recurrence's own state, and num/den identical to serial()
+    r = _rng(37)
+    n, d, dv = 15, 4, 3
+    q, k, v = r.standard_normal((n, d)), r.standard_normal((n, d)), r.standard_normal((n, dv))
+    num, den, st = O.serial(q, k, v, 0.9)
+    n2, d2, un, st2 = O.serial_unorm(q, k, v, 0.9)
+    np.testing.assert_array_equal(num, n2)
+    np.testing.assert_array_equal(den, d2)
+    np.testing.assert_array_equal(st, st2)
+    parts = O.split_state(st, d, dv)
+    u = parts["S"] @ parts["m"] - parts["h"]
+    assert un[-1] == pytest.approx(np.linalg.norm(u), rel=1e-13)
+    # den_t = q_t . u_t, so |den_t| <= |q_t| |u_t|
+    assert np.all(np.abs(den) <= np.linalg.norm(q, axis=1) * un * (1 + 1e-12))
