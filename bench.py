@@ -1,0 +1,249 @@
+#!/usr/bin/env python3
+"""Benchmark of the HLA2 hot path on one MI355X.
+
+A step is one hla2_forward over the headline forward workload (decay_8k:
+B=8, H=16, n=8192, d=64, dv=128, bf16, decay 0.99, chunk 64) with inputs
+resident in HBM.  The same JSON line also carries the decode workload
+(decode_256x32: 256 sequences x 32 heads, d = dv = 64, one hla2_decode_step
+per step, fp32 state) because the metric names both.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Prints ONE JSON line.  Timing uses HIP events on the stream the kernels are
+launched on (torch's current stream), bracketed by device synchronisation.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import glob
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_MFMA = 2.5e15      # dense bf16 MFMA, MI355X, FLOP/s
+PEAK_HBM = 8.0e12            # HBM3E, B/s
+METRIC = "masked HLA2 fwd tokens/s + % bf16 MFMA peak (d=64); decode tokens/s + % HBM BW"
+
+
+def canonical_flops_per_head_token(d, dv, C, normalize):
+    """Algorithmic work of the chunked forward per head-token: chunk summaries
+    + scan combines + masked chunk outputs, every product counted as 2mnk at
+    full chunk tiles of the requested chunk C (dv' = dv + 1 when normalised)."""
+    dvp = dv + (1 if normalize else 0)
+    return 4 * d * d + 6 * d * dvp + 6 * C * d + 4 * C * dvp + 2 * C * C + 6 * d * d * dvp / C
+
+
+def min_bytes_forward(w, esize):
+    """q, k, v read once and out written once."""
+    return w.B * w.H * w.n * (2 * w.d + 2 * w.dv) * esize
+
+
+def decode_bytes_per_step(N, H, d, dv, esize=2):
+    state = N * H * (d * d + 2 * d * dv + 2 * d) * 4
+    return 2 * state + N * H * (2 * d + dv) * esize + N * H * dv * esize
+
+
+def sources_digest():
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "causal_prefix_scan_hla2_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(key):
+    """HBM traffic per call measured with rocprofv3 counters (profiles/traffic.json),
+    or None when the kernels changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = data.get(key)
+    if not ent or ent.get("sources") != sources_digest():
+        return None
+    return ent.get("bytes_per_call")
+
+
+def time_calls(fn, steps, warmup, torch):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(steps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(end) / 1e3 / steps, wall
+
+
+def bench_forward(w, steps, warmup, torch, H, I):
+    dev = torch.device("cuda:0")
+    q, k, v = (x.to(dev) for x in I.make_qkv(w))
+    out = torch.empty_like(v)
+    need = H.hla2_forward_workspace_bytes(w.B, w.H, w.n, w.d, w.dv, w.chunk)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+
+    def fn():
+        H.hla2_forward(q, k, v, out, decay=w.decay, normalize=w.normalize, chunk=w.chunk, workspace=ws)
+
+    t, wall = time_calls(fn, steps, warmup, torch)
+    esize = 4 if w.dtype == "f32" else 2
+    flops = canonical_flops_per_head_token(w.d, w.dv, w.chunk, w.normalize) * w.head_tokens
+    return {
+        "seconds": t,
+        "wall": wall,
+        "tokens_per_s": w.B * w.n / t,
+        "head_tokens_per_s": w.head_tokens / t,
+        "tflops": flops / t / 1e12,
+        "mfma_frac": flops / t / PEAK_BF16_MFMA,
+        "flops_per_call": flops,
+        "min_bytes": min_bytes_forward(w, esize),
+        "segments": H.hla2_forward_segments(w.B, w.H, w.n, w.d, w.dv, w.chunk),
+    }
+
+
+def bench_decode(dw, steps, warmup, torch, H, prefill_tokens):
+    """Prefill every head's state by running the recurrence (the decode step
+    itself) over a random prefix, then time single-token steps."""
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(dw.seed)
+    L = H.hla2_state_floats(dw.d, dw.dv)
+    state = torch.zeros(dw.N, dw.H, L, dtype=torch.float32, device=dev)
+    s = 1.0 / math.sqrt(dw.d)
+    out = torch.empty(dw.N, dw.H, dw.dv, dtype=torch.bfloat16, device=dev)
+    for _ in range(prefill_tokens):
+        q = (torch.randn(dw.N, dw.H, dw.d, generator=g, device=dev) * s).to(torch.bfloat16)
+        k = (torch.randn(dw.N, dw.H, dw.d, generator=g, device=dev) * s).to(torch.bfloat16)
+        v = (torch.randn(dw.N, dw.H, dw.dv, generator=g, device=dev) * s).to(torch.bfloat16)
+        H.hla2_decode_step(state, q, k, v, out, decay=dw.decay, normalize=dw.normalize)
+    nsteps = dw.steps
+    qs = (torch.randn(nsteps, dw.N, dw.H, dw.d, generator=g, device=dev) * s).to(torch.bfloat16)
+    ks = (torch.randn(nsteps, dw.N, dw.H, dw.d, generator=g, device=dev) * s).to(torch.bfloat16)
+    vs = (torch.randn(nsteps, dw.N, dw.H, dw.dv, generator=g, device=dev) * s).to(torch.bfloat16)
+    torch.cuda.synchronize()
+    it = [0]
+
+    def fn():
+        i = it[0] % nsteps
+        it[0] += 1
+        H.hla2_decode_step(state, qs[i], ks[i], vs[i], out, decay=dw.decay, normalize=dw.normalize)
+
+    t, wall = time_calls(fn, steps, warmup, torch)
+    byts = decode_bytes_per_step(dw.N, dw.H, dw.d, dw.dv)
+    return {
+        "seconds": t,
+        "wall": wall,
+        "tokens_per_s": dw.N / t,
+        "head_tokens_per_s": dw.N * dw.H / t,
+        "gbps": byts / t / 1e9,
+        "hbm_frac": byts / t / PEAK_HBM,
+        "bytes_per_call": byts,
+    }
+
+
+def cpu_baseline(w, heads_sample, I):
+    """The fp64 oracle (as it stands) on a bounded sample of the workload's heads."""
+    from oracle import oracle as O
+    q, k, v = I.make_qkv(w, B=1, H=heads_sample)
+    threads = O.default_threads()
+    t0 = time.perf_counter()
+    O.serial(q.double().numpy(), k.double().numpy(), v.double().numpy(), w.decay, threads=threads)
+    dt = time.perf_counter() - t0
+    head_tokens = heads_sample * w.n
+    return {
+        "value": head_tokens / dt / w.H,   # sequence tokens/s: H head-tokens make one token
+        "unit": "tokens/s",
+        "cores": min(threads, heads_sample),
+        "kind": "oracle",
+        "sample": "%d heads x %d tokens drawn with the workload's recipe (of %d heads per step), fp64 serial "
+                  "recurrence, %.1f s wall" % (heads_sample, w.n, w.B * w.H, dt),
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="decay_8k")
+    ap.add_argument("--decode-prefill", type=int, default=None, help="prefix tokens (default: the workload's)")
+    ap.add_argument("--cpu-heads", type=int, default=64, help="heads in the oracle's timed sample (0: skip)")
+    ap.add_argument("--skip-decode", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the forward shards over (b, h) with no communication; see the design notes).", file=sys.stderr)
+        return 2
+
+    import torch
+    from causal_prefix_scan_hla2_amd import build as Bld
+    if not os.path.exists(os.path.join(ROOT, "causal_prefix_scan_hla2_amd", "libhla2.so")):
+        Bld.build()
+    from causal_prefix_scan_hla2_amd import hla2 as H
+    from causal_prefix_scan_hla2_amd import inputs as I
+
+    w = I.WORKLOADS[args.workload]
+    fw = bench_forward(w, args.steps, args.warmup, torch, H, I)
+    line = {
+        "metric": METRIC,
+        "value": fw["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": fw["seconds"] * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) draws with the workload's scaling, rounded to the element type)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "n": w.n, "d": w.d, "dv": w.dv, "chunk": w.chunk,
+                   "decay": w.decay, "normalize": w.normalize, "segments": fw["segments"],
+                   "global_batch": w.B, "seq_len": w.n, "parallelism": "single GPU"},
+        "head_tokens_per_s": fw["head_tokens_per_s"],
+        "tflops": fw["tflops"],
+        "mfma_frac": fw["mfma_frac"],
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "hla2_forward (segment summary + segment scan + chunk output kernels)",
+            "achieved": fw["tflops"],
+            "peak": PEAK_BF16_MFMA / 1e12,
+            "unit": "TFLOP/s",
+            "frac": fw["mfma_frac"],
+            "traffic": load_traffic("forward_" + w.name),
+            "hbm_min_bytes_frac": fw["min_bytes"] / fw["seconds"] / PEAK_HBM,
+        },
+    }
+    if not args.skip_decode:
+        dw = I.DECODE
+        pre = dw.prefix if args.decode_prefill is None else args.decode_prefill
+        dc = bench_decode(dw, max(args.steps, 1) * 4, args.warmup, torch, H, pre)
+        line["decode"] = {
+            "workload": dw.name, "N": dw.N, "H": dw.H, "d": dw.d, "dv": dw.dv, "prefix": pre,
+            "tokens_per_s": dc["tokens_per_s"], "head_tokens_per_s": dc["head_tokens_per_s"],
+            "ms_per_step": dc["seconds"] * 1e3,
+            "roofline": {"bound": "hbm", "kernel": "hla2_decode_step", "achieved": dc["gbps"],
+                         "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": dc["hbm_frac"],
+                         "traffic": load_traffic("decode_" + dw.name)},
+        }
+    if args.cpu_heads > 0:
+        line["cpu_baseline"] = cpu_baseline(w, min(args.cpu_heads, w.B * w.H), I)
+    print(json.dumps(line))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

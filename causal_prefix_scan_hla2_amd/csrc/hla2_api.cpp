@@ -1,0 +1,215 @@
+// hla2_api.cpp -- the C ABI of include/hla2.h: argument validation, the
+// segment plan, workspace layout and kernel launches.  Validation runs on the
+// host before any HIP call, so every error path is testable without a GPU.
+#include <math.h>
+#include <stdint.h>
+
+#include "hla2.h"
+#include "hla2_internal.h"
+
+namespace {
+
+struct Plan {
+  int DK, DV, CP;  // padded head dims and chunk tile of the kernel instantiation
+  int cps;         // chunks per segment
+  int nseg;        // segments per (b, h)
+  long BH;
+};
+
+// Workgroups the output pass aims for: two per compute unit on a 256-CU part.
+constexpr long kTargetGroups = 512;
+constexpr int kMaxSegments = 64;
+
+bool is_pow2_chunk(int c) { return c == 16 || c == 32 || c == 64 || c == 128; }
+
+int check_shape(int B, int H, int n, int d, int dv, int chunk, int dtype) {
+  if (B <= 0 || H <= 0 || n <= 0 || d <= 0 || dv <= 0 || chunk <= 0) return HLA2_ERR_INVALID;
+  if (dtype != HLA2_F32 && dtype != HLA2_BF16) return HLA2_ERR_INVALID;
+  if (d % 16 || dv % 16 || d > 128 || dv > 128 || !is_pow2_chunk(chunk)) return HLA2_ERR_UNSUPPORTED;
+  if (dtype == HLA2_F32 && (d > 64 || dv > 64)) return HLA2_ERR_UNSUPPORTED;
+  const long BH = (long)B * H;
+  if (BH > (1L << 24) || (long)n > (1L << 30) || BH * (long)n > (1L << 40)) return HLA2_ERR_UNSUPPORTED;
+  return HLA2_OK;
+}
+
+Plan make_plan(int B, int H, int n, int d, int dv, int chunk, int dtype, int segments = 0) {
+  Plan p;
+  p.BH = (long)B * H;
+  if (dtype == HLA2_BF16) {
+    p.DK = d <= 64 ? 64 : 128;
+    p.DV = dv <= 64 ? 64 : 128;
+    p.CP = chunk <= 64 ? 64 : 128;
+  } else {
+    const int m = d > dv ? d : dv;
+    p.DK = p.DV = m <= 16 ? 16 : 64;
+    p.CP = chunk <= 16 ? 16 : (chunk <= 64 ? 64 : 128);
+  }
+  const long nc = ((long)n + chunk - 1) / chunk;
+  long r = segments > 0 ? segments : (kTargetGroups + p.BH - 1) / p.BH;
+  if (r > nc) r = nc;
+  if (r > kMaxSegments) r = kMaxSegments;
+  if (r < 1) r = 1;
+  p.cps = (int)((nc + r - 1) / r);
+  p.nseg = (int)((nc + p.cps - 1) / p.cps);
+  return p;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t sums_bytes(const Plan &p) {
+  return p.nseg > 1 ? (size_t)p.BH * (p.nseg - 1) * hla2::sum_block_floats(p.DK, p.DV) * sizeof(float) : 0;
+}
+size_t prefix_bytes(const Plan &p) {
+  return p.nseg > 1 ? (size_t)p.BH * p.nseg * hla2::prefix_block_floats(p.DK, p.DV) * sizeof(float) : 0;
+}
+size_t workspace_bytes(const Plan &p) {
+  return p.nseg > 1 ? align256(sums_bytes(p)) + prefix_bytes(p) : 0;
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char *hla2_strerror(int code) {
+  switch (code) {
+    case HLA2_OK: return "ok";
+    case HLA2_ERR_INVALID: return "invalid argument";
+    case HLA2_ERR_UNSUPPORTED: return "unsupported shape, chunk or dtype";
+    case HLA2_ERR_WORKSPACE: return "workspace missing or too small";
+    case HLA2_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown error code";
+  }
+}
+
+int hla2_abi_version(void) { return 1; }
+
+long hla2_state_floats(int d, int dv) {
+  if (d <= 0 || dv <= 0) return HLA2_ERR_INVALID;
+  return (long)d * d + 2L * d * dv + 2L * d;
+}
+
+size_t hla2_forward_ex_workspace_bytes(int B, int H, int n, int d, int dv, int chunk, int segments) {
+  // the plan does not depend on dtype beyond padding; size for the larger padding
+  if (segments < 0 || check_shape(B, H, n, d, dv, chunk, HLA2_BF16) != HLA2_OK) return 0;
+  Plan pb = make_plan(B, H, n, d, dv, chunk, HLA2_BF16, segments);
+  size_t wb = workspace_bytes(pb);
+  if (d <= 64 && dv <= 64) {
+    Plan pf = make_plan(B, H, n, d, dv, chunk, HLA2_F32, segments);
+    size_t wf = workspace_bytes(pf);
+    if (wf > wb) wb = wf;
+  }
+  return wb;
+}
+
+size_t hla2_forward_workspace_bytes(int B, int H, int n, int d, int dv, int chunk) {
+  return hla2_forward_ex_workspace_bytes(B, H, n, d, dv, chunk, 0);
+}
+
+int hla2_forward_ex_segments(int B, int H, int n, int d, int dv, int chunk, int segments) {
+  if (segments < 0) return HLA2_ERR_INVALID;
+  int rc = check_shape(B, H, n, d, dv, chunk, HLA2_BF16);
+  if (rc != HLA2_OK) return rc;
+  return make_plan(B, H, n, d, dv, chunk, HLA2_BF16, segments).nseg;
+}
+
+int hla2_forward_segments(int B, int H, int n, int d, int dv, int chunk) {
+  return hla2_forward_ex_segments(B, H, n, d, dv, chunk, 0);
+}
+
+int hla2_forward(const void *q, const void *k, const void *v, void *out, int B, int H, int n, int d,
+                 int dv, float decay, int normalize, int chunk, hla2_dtype_t dtype, float *den_out,
+                 void *workspace, size_t workspace_bytes_given, hipStream_t stream) {
+  return hla2_forward_ex(q, k, v, out, B, H, n, d, dv, decay, normalize, chunk, dtype, den_out, workspace,
+                         workspace_bytes_given, 0, stream);
+}
+
+int hla2_forward_ex(const void *q, const void *k, const void *v, void *out, int B, int H, int n, int d,
+                    int dv, float decay, int normalize, int chunk, hla2_dtype_t dtype, float *den_out,
+                    void *workspace, size_t workspace_bytes_given, int segments, hipStream_t stream) {
+  if (!q || !k || !v || !out) return HLA2_ERR_INVALID;
+  if (segments < 0) return HLA2_ERR_INVALID;
+  if (!(decay > 0.0f && decay <= 1.0f)) return HLA2_ERR_INVALID;  // also rejects NaN
+  if (normalize != 0 && normalize != 1) return HLA2_ERR_INVALID;
+  int rc = check_shape(B, H, n, d, dv, chunk, (int)dtype);
+  if (rc != HLA2_OK) return rc;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return HLA2_ERR_INVALID;
+  if (den_out && !aligned(den_out, 4)) return HLA2_ERR_INVALID;
+  const Plan p = make_plan(B, H, n, d, dv, chunk, (int)dtype, segments);
+  const size_t need = workspace_bytes(p);
+  if (need > 0) {
+    if (!workspace || workspace_bytes_given < need || !aligned(workspace, 256)) return HLA2_ERR_WORKSPACE;
+  }
+
+  hla2::WalkArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.den_out = den_out;
+  a.n = n;
+  a.d = d;
+  a.dv = dv;
+  a.chunk = chunk;
+  a.cps = p.cps;
+  a.nseg = p.nseg;
+  a.log2g = decay < 1.0f ? log2f(decay) : 0.0f;
+  a.decay_on = decay < 1.0f ? 1 : 0;
+  a.normalize = normalize;
+  float *sums = nullptr, *prefix = nullptr;
+  if (p.nseg > 1) {
+    sums = (float *)workspace;
+    prefix = (float *)((char *)workspace + align256(sums_bytes(p)));
+  }
+  a.sums = sums;
+  a.prefix = prefix;
+  const int dt = dtype == HLA2_F32 ? 0 : 1;
+
+  hipError_t e;
+  if (p.nseg > 1) {
+    e = hla2::launch_walk(dt, p.DK, p.DV, p.CP, false, dim3((unsigned)(p.BH * (p.nseg - 1))), a, stream);
+    if (e != hipSuccess) return HLA2_ERR_LAUNCH;
+    hla2::ScanArgs s;
+    s.sums = sums;
+    s.prefix = prefix;
+    s.nseg = p.nseg;
+    s.gamma_seg = decay < 1.0f ? (float)pow((double)decay, (double)p.cps * chunk) : 1.0f;
+    e = hla2::launch_scan(p.DK, p.DV, (int)p.BH, s, stream);
+    if (e != hipSuccess) return HLA2_ERR_LAUNCH;
+  }
+  e = hla2::launch_walk(dt, p.DK, p.DV, p.CP, true, dim3((unsigned)(p.BH * p.nseg)), a, stream);
+  if (e != hipSuccess) return HLA2_ERR_LAUNCH;
+  return HLA2_OK;
+}
+
+int hla2_decode_step(float *state, const void *q, const void *k, const void *v, void *out, int N, int H,
+                     int d, int dv, float decay, int normalize, hla2_dtype_t dtype, hipStream_t stream) {
+  if (!state || !q || !k || !v || !out) return HLA2_ERR_INVALID;
+  if (N <= 0 || H <= 0 || d <= 0 || dv <= 0) return HLA2_ERR_INVALID;
+  if (!(decay > 0.0f && decay <= 1.0f)) return HLA2_ERR_INVALID;
+  if (normalize != 0 && normalize != 1) return HLA2_ERR_INVALID;
+  if (dtype != HLA2_F32 && dtype != HLA2_BF16) return HLA2_ERR_INVALID;
+  auto ok = [](int x) { return x == 16 || x == 32 || x == 64 || x == 128; };
+  if (!ok(d) || !ok(dv)) return HLA2_ERR_UNSUPPORTED;
+  const long NH = (long)N * H;
+  if (NH > (1L << 30)) return HLA2_ERR_UNSUPPORTED;
+  if (!aligned(state, 16)) return HLA2_ERR_INVALID;
+  const size_t esz = dtype == HLA2_F32 ? 4 : 2;
+  if (!aligned(q, esz) || !aligned(k, esz) || !aligned(v, esz) || !aligned(out, esz)) return HLA2_ERR_INVALID;
+  hla2::DecodeArgs a;
+  a.state = state;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.NH = (int)NH;
+  a.d = d;
+  a.dv = dv;
+  a.gamma = decay;
+  a.normalize = normalize;
+  hipError_t e = hla2::launch_decode(dtype == HLA2_F32 ? 0 : 1, a, stream);
+  return e == hipSuccess ? HLA2_OK : HLA2_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,149 @@
+/*
+ * hla2.h -- C ABI of the MI355X (gfx950) library for strictly causal
+ * second-order Higher-order Linear Attention (HLA2).
+ *
+ * Sources (web pages about arXiv 2510.27258):
+ *   [SUM] "Technische Samenvatting: Hogere-orde Lineaire Aandacht (HLA)",
+ *         gist.science (technical summary).
+ *   [ABS] "Высокоуровневое линейное внимание", chatpaper.ai (abstract).
+ *   [SKL] "higher-order-linear-attention-mechanism", skillsmp.com (only its
+ *         tensor layout [B, n, H*d] -> [B, H, n, d] is used).
+ *
+ * Operation, per batch b and head h, tokens t = 0..n-1 (q_t, k_t in R^d,
+ * v_t in R^dv):
+ *   S_t = sum_{i<=t} g^{t-i} k_i k_i^T        key moment       [SUM §1, state upkeep]
+ *   C_t = sum_{i<=t} g^{t-i} q_i v_i^T        query-value acc. [SUM §1, state upkeep]
+ *   m_t = sum_{i<=t} g^{t-i} q_i              query mass       [SUM §1, state upkeep]
+ *   G_t, h_t: cross summaries holding the pairs (query j < key i) of the
+ *             naive product S_t C_t (resp. S_t m_t)             [SUM §1, strict causality]
+ *   num_t = q_t^T (S_t C_t - G_t)                               [SUM §1, output]
+ *   den_t = q_t^T (S_t m_t - h_t)                               [SUM §1, normalisation]
+ *   out_t = num_t, or num_t / den_t when ratio-normalised (IEEE division,
+ *           no epsilon).
+ * Equivalently num_t = sum_{j<=t} sum_{i<=j} g^{(t-i)+(t-j)} (q_t.k_i)(q_j.k_i) v_j:
+ * row t of L o (A A^T) V with A = L o (Q K^T) when g = 1, so out_t depends on
+ * tokens j <= t only [SUM "Resultaten en claims"].  g = decay in (0, 1]; the
+ * pages name decayed variants without a formula [SUM "Belangrijkste
+ * bijdragen" 2]; the reading used is that every first-order summary decays
+ * by g per token (g = 1: no decay).
+ *
+ * The forward pass is computed chunk-parallel [SUM §4]: the sequence is cut
+ * into chunks of `chunk` tokens, runs of consecutive chunks are reduced to
+ * segment summaries, an exclusive scan with the semidirect-product combine
+ * gives every segment its incoming state, and the chunks are walked again
+ * from that state to produce the outputs.  The activations equal those of
+ * the serial recurrence up to floating-point rounding [SUM §4, scan
+ * equivalence].
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers on the current HIP device,
+ *    contiguous, row-major, owned by the caller.  The library allocates
+ *    nothing on these paths and keeps no state between calls.
+ *  - Work is enqueued asynchronously on `stream` (0 = the null stream).
+ *  - Arguments are validated on the host before any device call; an invalid
+ *    call returns a negative code and enqueues nothing.  Launch failures are
+ *    reported as HLA2_ERR_LAUNCH.  NaN/Inf inputs are not checked; they
+ *    propagate.  den = 0 under ratio normalisation gives IEEE +-Inf/NaN.
+ *  - Nothing is thrown across the ABI.
+ */
+#ifndef HLA2_H_
+#define HLA2_H_
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v and out.  Accumulation is always fp32. */
+typedef enum { HLA2_F32 = 0, HLA2_BF16 = 1 } hla2_dtype_t;
+
+enum {
+  HLA2_OK = 0,
+  HLA2_ERR_INVALID = -1,     /* null pointer, size <= 0, decay outside (0,1], ... */
+  HLA2_ERR_UNSUPPORTED = -2, /* shape or chunk outside the supported set */
+  HLA2_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
+  HLA2_ERR_LAUNCH = -4       /* a kernel launch failed */
+};
+
+/* Human-readable text for a return code (static storage). */
+const char *hla2_strerror(int code);
+
+/* ABI version of this header (incremented on incompatible changes). */
+int hla2_abi_version(void);
+
+/*
+ * Workspace needed by hla2_forward for this shape, in bytes (0 when the
+ * sequence fits one segment).  Depends only on the arguments.  Returns 0 for
+ * an invalid or unsupported shape as well; hla2_forward reports those.
+ */
+size_t hla2_forward_workspace_bytes(int B, int H, int n, int d, int dv, int chunk);
+
+/*
+ * Number of segments per (b, h) that hla2_forward uses for this shape (the
+ * length of the scanned sequence of segment summaries), or a negative code.
+ */
+int hla2_forward_segments(int B, int H, int n, int d, int dv, int chunk);
+
+/*
+ * Masked second-order HLA forward pass.
+ *   q, k : [B, H, n, d]    element type `dtype`
+ *   v    : [B, H, n, dv]   element type `dtype`
+ *   out  : [B, H, n, dv]   element type `dtype` (written)
+ *   decay: g in (0, 1]; 1 = no decay
+ *   normalize: 0 -> out = num;  1 -> out = num / den
+ *   chunk: tokens per chunk, one of 16, 32, 64, 128 (128 needs d, dv <= 128;
+ *          chunk only changes rounding, not the result)
+ *   den_out: nullable [B, H, n] fp32; when given, den_t is written whatever
+ *          `normalize` says
+ *   workspace: device buffer of at least hla2_forward_workspace_bytes(...)
+ *          bytes (may be NULL when that is 0); contents on entry are ignored
+ * Supported: d, dv multiples of 16 in [16, 128]; n >= 1; B, H >= 1; B*H*n*max(d,dv)
+ * below 2^31.
+ */
+int hla2_forward(const void *q, const void *k, const void *v, void *out,
+                 int B, int H, int n, int d, int dv, float decay, int normalize, int chunk,
+                 hla2_dtype_t dtype, float *den_out, void *workspace, size_t workspace_bytes,
+                 hipStream_t stream);
+
+/*
+ * One streaming step for N sequences x H heads, state updated in place
+ * [SUM §1, state upkeep / output / normalisation; ABS: constant-size state].
+ *   state: [N, H] blocks of fp32, each block laid out as
+ *          S[d*d] | C[d*dv] | m[d] | G[d*dv] | h[d]   (row-major; see the
+ *          definitions above), i.e. hla2_state_floats(d, dv) floats per block
+ *   q, k : [N, H, d]   element type `dtype`
+ *   v    : [N, H, dv]  element type `dtype`
+ *   out  : [N, H, dv]  element type `dtype` (written)
+ * Order inside the step: the cross summaries take the new key against the
+ * OLD C and m, then S, C, m absorb the token, then the readout uses the new
+ * state.  Supported: d, dv in {16, 32, 64, 128}.
+ */
+int hla2_decode_step(float *state, const void *q, const void *k, const void *v, void *out,
+                     int N, int H, int d, int dv, float decay, int normalize,
+                     hla2_dtype_t dtype, hipStream_t stream);
+
+/*
+ * hla2_forward with an explicit segment count (a scheduling knob for tuning and
+ * tests; the result does not depend on it beyond rounding).  segments = 0
+ * picks the count hla2_forward uses; otherwise the requested count is clamped
+ * to [1, min(number of chunks, 64)] and the chunks are split as evenly as
+ * whole chunks allow.  The workspace must be sized with
+ * hla2_forward_ex_workspace_bytes for the same `segments`.
+ */
+size_t hla2_forward_ex_workspace_bytes(int B, int H, int n, int d, int dv, int chunk, int segments);
+int hla2_forward_ex_segments(int B, int H, int n, int d, int dv, int chunk, int segments);
+int hla2_forward_ex(const void *q, const void *k, const void *v, void *out,
+                    int B, int H, int n, int d, int dv, float decay, int normalize, int chunk,
+                    hla2_dtype_t dtype, float *den_out, void *workspace, size_t workspace_bytes,
+                    int segments, hipStream_t stream);
+
+/* Floats per (sequence, head) state block: d*d + 2*d*dv + 2*d. */
+long hla2_state_floats(int d, int dv);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HLA2_H_ */

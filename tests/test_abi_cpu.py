@@ -1,0 +1,145 @@
+"""The C ABI library on the CPU: it loads, exports every symbol the header
+declares, and rejects invalid calls on the host before touching a device.
+
+Only error paths are called here (no kernel is launched): every argument check
+in the library runs before its first HIP call.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from causal_prefix_scan_hla2_amd import build as B
+from causal_prefix_scan_hla2_amd import hla2 as H
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hla2.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(H.LIB_PATH):
+        B.build()
+    return H.lib()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hla2_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_expected_functions():
+    assert header_functions() == sorted(H.EXPORTS)
+
+
+def test_library_exports_every_header_symbol(L):
+    for name in header_functions():
+        assert hasattr(L, name), name
+    out = os.popen("nm -D --defined-only %s" % H.LIB_PATH).read()
+    for name in header_functions():
+        assert re.search(r"\bT %s\b" % name, out), name
+
+
+def test_strerror_and_version(L):
+    assert H.strerror(0) == "ok"
+    for c in (-1, -2, -3, -4):
+        assert H.strerror(c) and H.strerror(c) != "ok"
+    assert H.strerror(12345) == "unknown error code"
+    assert L.hla2_abi_version() == 1
+
+
+def test_state_floats(L):
+    assert H.hla2_state_floats(64, 64) == 64 * 64 + 2 * 64 * 64 + 2 * 64
+    assert H.hla2_state_floats(16, 128) == 16 * 16 + 2 * 16 * 128 + 2 * 16
+    assert L.hla2_state_floats(0, 4) == H.HLA2_ERR_INVALID
+
+
+P = ctypes.c_void_p(4096)  # a non-null, aligned pointer that is never dereferenced
+
+
+def fwd(L, q=P, k=P, v=P, out=P, B_=1, H_=1, n=64, d=16, dv=16, decay=1.0, norm=0, chunk=16, dtype=0,
+        den=None, ws=None, wsb=0, segments=0):
+    return L.hla2_forward_ex(q, k, v, out, B_, H_, n, d, dv, decay, norm, chunk, dtype, den, ws, wsb, segments,
+                             None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), H.HLA2_ERR_INVALID),
+    (dict(out=None), H.HLA2_ERR_INVALID),
+    (dict(B_=0), H.HLA2_ERR_INVALID),
+    (dict(n=0), H.HLA2_ERR_INVALID),
+    (dict(n=-5), H.HLA2_ERR_INVALID),
+    (dict(decay=0.0), H.HLA2_ERR_INVALID),
+    (dict(decay=1.5), H.HLA2_ERR_INVALID),
+    (dict(decay=float("nan")), H.HLA2_ERR_INVALID),
+    (dict(norm=2), H.HLA2_ERR_INVALID),
+    (dict(dtype=7), H.HLA2_ERR_INVALID),
+    (dict(segments=-1), H.HLA2_ERR_INVALID),
+    (dict(d=24), H.HLA2_ERR_UNSUPPORTED),
+    (dict(dv=144), H.HLA2_ERR_UNSUPPORTED),
+    (dict(chunk=48), H.HLA2_ERR_UNSUPPORTED),
+    (dict(chunk=256), H.HLA2_ERR_UNSUPPORTED),
+    (dict(d=128, dv=16, dtype=0), H.HLA2_ERR_UNSUPPORTED),  # fp32 is limited to d, dv <= 64
+    (dict(q=ctypes.c_void_p(4098)), H.HLA2_ERR_INVALID),   # misaligned
+    (dict(den=ctypes.c_void_p(4098)), H.HLA2_ERR_INVALID),
+])
+def test_forward_rejects(L, kw, code):
+    assert fwd(L, **kw) == code
+
+
+def test_forward_workspace_checks(L):
+    # 4 x 8 heads x 2048 tokens in chunks of 64 uses several segments -> needs a workspace
+    need = H.hla2_forward_workspace_bytes(4, 8, 2048, 64, 64, 64)
+    assert need > 0
+    assert H.hla2_forward_segments(4, 8, 2048, 64, 64, 64) > 1
+    args = dict(B_=4, H_=8, n=2048, d=64, dv=64, chunk=64, dtype=1)
+    assert fwd(L, **args) == H.HLA2_ERR_WORKSPACE                         # missing
+    assert fwd(L, ws=P, wsb=need - 1, **args) == H.HLA2_ERR_WORKSPACE    # too small
+    assert fwd(L, ws=ctypes.c_void_p(4096 + 16), wsb=need, **args) == H.HLA2_ERR_WORKSPACE  # misaligned
+
+
+def test_workspace_and_segment_plan(L):
+    # one segment -> no workspace
+    assert H.hla2_forward_segments(1, 1, 64, 16, 16, 16, segments=1) == 1
+    assert H.hla2_forward_workspace_bytes(1, 1, 64, 16, 16, 16, segments=1) == 0
+    # explicit segment counts are clamped to the number of chunks and to 64
+    assert H.hla2_forward_segments(1, 1, 100, 64, 64, 64, segments=10) == 2
+    assert H.hla2_forward_segments(1, 1, 1 << 16, 128, 128, 128, segments=1000) == 64
+    # the automatic plan aims at >= 512 workgroups when there are enough chunks
+    for shape in [(4, 8, 2048, 64, 64, 64), (8, 16, 8192, 64, 128, 64), (1, 16, 65536, 128, 128, 128)]:
+        b, h, n, d, dv, c = shape
+        r = H.hla2_forward_segments(*shape)
+        nc = -(-n // c)
+        assert 1 <= r <= min(nc, 64)
+        assert b * h * r >= min(512, b * h * min(nc, 64)) - b * h  # within one segment of the target
+    # invalid shapes report 0 bytes / an error code
+    assert H.hla2_forward_workspace_bytes(1, 1, 64, 24, 16, 16) == 0
+    assert H.hla2_forward_segments(1, 1, 64, 24, 16, 16) == H.HLA2_ERR_UNSUPPORTED
+
+
+def dec(L, state=P, q=P, k=P, v=P, out=P, N=1, H_=1, d=64, dv=64, decay=1.0, norm=1, dtype=1):
+    return L.hla2_decode_step(state, q, k, v, out, N, H_, d, dv, decay, norm, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(state=None), H.HLA2_ERR_INVALID),
+    (dict(v=None), H.HLA2_ERR_INVALID),
+    (dict(N=0), H.HLA2_ERR_INVALID),
+    (dict(decay=-1.0), H.HLA2_ERR_INVALID),
+    (dict(norm=3), H.HLA2_ERR_INVALID),
+    (dict(dtype=2), H.HLA2_ERR_INVALID),
+    (dict(d=48), H.HLA2_ERR_UNSUPPORTED),
+    (dict(dv=256), H.HLA2_ERR_UNSUPPORTED),
+    (dict(state=ctypes.c_void_p(4100)), H.HLA2_ERR_INVALID),  # state must be 16-byte aligned
+])
+def test_decode_rejects(L, kw, code):
+    assert dec(L, **kw) == code
+
+
+def test_binding_refuses_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(H, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(H, "_lib", None)
+    with pytest.raises(RuntimeError):
+        H.lib()
