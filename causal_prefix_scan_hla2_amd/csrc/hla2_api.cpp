@@ -16,8 +16,8 @@ struct Plan {
   long BH;
 };
 
-// Workgroups the output pass aims for: two per compute unit on a 256-CU part.
-constexpr long kTargetGroups = 512;
+// The output pass aims for one full round of workgroups on a 256-CU part.
+constexpr long kComputeUnits = 256;
 constexpr int kMaxSegments = 64;
 
 bool is_pow2_chunk(int c) { return c == 16 || c == 32 || c == 64 || c == 128; }
@@ -45,7 +45,8 @@ Plan make_plan(int B, int H, int n, int d, int dv, int chunk, int dtype, int seg
     p.CP = chunk <= 16 ? 16 : (chunk <= 64 ? 64 : 128);
   }
   const long nc = ((long)n + chunk - 1) / chunk;
-  long r = segments > 0 ? segments : (kTargetGroups + p.BH - 1) / p.BH;
+  const long target = kComputeUnits * hla2::walk_groups_per_cu(dtype == HLA2_BF16 ? 2 : 4, p.DK, p.DV, p.CP, true);
+  long r = segments > 0 ? segments : (target + p.BH - 1) / p.BH;
   if (r > nc) r = nc;
   if (r > kMaxSegments) r = kMaxSegments;
   if (r < 1) r = 1;
@@ -157,6 +158,7 @@ int hla2_forward_ex(const void *q, const void *k, const void *v, void *out, int 
   a.log2g = decay < 1.0f ? log2f(decay) : 0.0f;
   a.decay_on = decay < 1.0f ? 1 : 0;
   a.normalize = normalize;
+  a.need_den = (normalize || den_out) ? 1 : 0;
   float *sums = nullptr, *prefix = nullptr;
   if (p.nseg > 1) {
     sums = (float *)workspace;

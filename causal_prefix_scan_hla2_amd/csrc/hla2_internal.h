@@ -16,6 +16,7 @@ struct WalkArgs {
   float log2g;            // log2(decay)
   int decay_on;           // decay < 1
   int normalize;
+  int need_den;           // normalize || den_out: carry u (and m)
 };
 
 // Arguments of the segment-level exclusive scan.
@@ -31,6 +32,30 @@ struct ScanArgs {
 //   prefix block:  S0[DK*DK] | U0[DK*DV] | u0[DK]
 __host__ __device__ inline long sum_block_floats(int DK, int DV) { return (long)DK * DK + 2L * DK * DV + 2L * DK; }
 __host__ __device__ inline long prefix_block_floats(int DK, int DV) { return (long)DK * DK + (long)DK * DV + DK; }
+
+// LDS bytes of a chunk-walker instantiation (element size esize, padded
+// head dims DK, DV, chunk tile CP; out = output mode).  Shared by the kernel's
+// static layout and the host's occupancy estimate.
+__host__ __device__ constexpr int walk_lds_bytes(int esize, int DK, int DV, int CP, bool out) {
+  const int pade = 16 / esize;
+  const int ldk = DK + pade, ldv = DV + pade, ldz = CP + pade;
+  const int kz = CP * ldk > DK * ldz ? CP * ldk : DK * ldz;
+  const int elems = kz + CP * ldv + DK * ldk + (out ? DV * ldk : 0) + (out ? 0 : CP * ldk);
+  return elems * esize + (2 * CP + 1 + DK) * 4;
+}
+__host__ __device__ constexpr int walk_waves(int CP) { return CP / 16 > 4 ? CP / 16 : 4; }
+// workgroups of the walker that fit one CU: LDS-limited, and at most 8 waves
+__host__ __device__ constexpr int walk_groups_per_cu(int esize, int DK, int DV, int CP, bool out) {
+  const int by_lds = (160 * 1024) / walk_lds_bytes(esize, DK, DV, CP, out);
+  const int by_waves = 8 / walk_waves(CP);
+  const int gmin = by_lds < by_waves ? by_lds : by_waves;
+  return gmin < 1 ? 1 : gmin;
+}
+// waves each SIMD must hold (the register budget the compiler targets)
+__host__ __device__ constexpr int walk_waves_per_eu(int esize, int DK, int DV, int CP, bool out) {
+  const int w = walk_groups_per_cu(esize, DK, DV, CP, out) * walk_waves(CP) / 4;
+  return w < 1 ? 1 : (w > 2 ? 2 : w);
+}
 
 // dtype: 0 = f32, 1 = bf16.  Returns hipErrorInvalidValue when no kernel exists
 // for (dtype, DK, DV, CP).

@@ -42,11 +42,23 @@ template <> struct Ktile<float> {
 __device__ __forceinline__ f32x4 mma(const bf16x8 &a, const bf16x8 &b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+// fp32 MFMA (8 passes) followed by 16 wait states that nothing can be scheduled
+// into.  An 8-pass MFMA reads its accumulator input late, so a VALU write to
+// that register must wait 7 states; with this compiler the f32 form has been
+// seen emitted with a VALU overwrite of its accumulator input right after the
+// MFMA (and wrong results).  The explicit gap makes every such write safe.
+__device__ __forceinline__ f32x4 mfma_f32_guarded(float a, float b, f32x4 c) {
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  return c;
+}
 __device__ __forceinline__ f32x4 mma(const f32x4 &a, const f32x4 &b, f32x4 c) {
-  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], c, 0, 0, 0);
-  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], c, 0, 0, 0);
-  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], c, 0, 0, 0);
-  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], c, 0, 0, 0);
+  c = mfma_f32_guarded(a[0], b[0], c);
+  c = mfma_f32_guarded(a[1], b[1], c);
+  c = mfma_f32_guarded(a[2], b[2], c);
+  c = mfma_f32_guarded(a[3], b[3], c);
   return c;
 }
 
