@@ -39,6 +39,21 @@ def canonical_flops_per_head_token(d, dv, C, normalize):
     return 4 * d * d + 6 * d * dvp + 6 * C * d + 4 * C * dvp + 2 * C * C + 6 * d * d * dvp / C
 
 
+def output_kernel_flops_per_head_token(d, dv, C, normalize):
+    """Algorithmic work of the chunk-output step alone (masked chunk-local
+    block A, W and the carried-state terms Q S0, Q U0) per head-token, at full
+    chunk tiles of the requested chunk C."""
+    dvp = dv + (1 if normalize else 0)
+    return 4 * C * d + 2 * C * C + 2 * d * d + 2 * C * dvp + 2 * d * dvp
+
+
+def summary_kernel_flops_per_head_token(d, dv, C, normalize):
+    """Algorithmic work of forming a chunk's summaries (S, C, m, G, h) per
+    head-token, at full chunk tiles of the requested chunk C."""
+    dvp = dv + (1 if normalize else 0)
+    return 2 * d * d + 4 * d * dvp + 2 * C * d + 2 * C * dvp
+
+
 def min_bytes_forward(w, esize):
     """q, k, v read once and out written once."""
     return w.B * w.H * w.n * (2 * w.d + 2 * w.dv) * esize
@@ -89,28 +104,54 @@ def time_calls(fn, steps, warmup, torch):
 
 
 def bench_forward(w, steps, warmup, torch, H, I):
+    """Time `steps` forward calls back to back.  Each call also records four
+    HIP events between its kernels (on the stream they run on), which give the
+    average duration of every kernel over the same timed region."""
     dev = torch.device("cuda:0")
     q, k, v = (x.to(dev) for x in I.make_qkv(w))
     out = torch.empty_like(v)
     need = H.hla2_forward_workspace_bytes(w.B, w.H, w.n, w.d, w.dv, w.chunk)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(max(steps, 1))]
+    for row in evs:      # create the underlying HIP events
+        for e in row:
+            e.record()
+    it = [0]
 
     def fn():
         H.hla2_forward(q, k, v, out, decay=w.decay, normalize=w.normalize, chunk=w.chunk, workspace=ws)
 
-    t, wall = time_calls(fn, steps, warmup, torch)
+    def fn_timed():
+        row = evs[it[0] % len(evs)]
+        it[0] += 1
+        H.hla2_forward(q, k, v, out, decay=w.decay, normalize=w.normalize, chunk=w.chunk, workspace=ws,
+                       events=row)
+
+    for _ in range(warmup):
+        fn()
+    t, wall = time_calls(fn_timed, steps, 0, torch)
+    phases = {"summary": 0.0, "scan": 0.0, "output": 0.0}
+    for row in evs[:steps]:
+        phases["summary"] += row[0].elapsed_time(row[1]) / 1e3
+        phases["scan"] += row[1].elapsed_time(row[2]) / 1e3
+        phases["output"] += row[2].elapsed_time(row[3]) / 1e3
+    phases = {key: val / max(steps, 1) for key, val in phases.items()}
     esize = 4 if w.dtype == "f32" else 2
     flops = canonical_flops_per_head_token(w.d, w.dv, w.chunk, w.normalize) * w.head_tokens
+    nseg = H.hla2_forward_segments(w.B, w.H, w.n, w.d, w.dv, w.chunk)
     return {
         "seconds": t,
         "wall": wall,
+        "phases": phases,
+        "output_flops_per_call": output_kernel_flops_per_head_token(w.d, w.dv, w.chunk, w.normalize)
+                                 * w.head_tokens,
         "tokens_per_s": w.B * w.n / t,
         "head_tokens_per_s": w.head_tokens / t,
         "tflops": flops / t / 1e12,
         "mfma_frac": flops / t / PEAK_BF16_MFMA,
         "flops_per_call": flops,
         "min_bytes": min_bytes_forward(w, esize),
-        "segments": H.hla2_forward_segments(w.B, w.H, w.n, w.d, w.dv, w.chunk),
+        "segments": nseg,
     }
 
 
@@ -154,12 +195,14 @@ def bench_decode(dw, steps, warmup, torch, H, prefill_tokens):
 
 
 def cpu_baseline(w, heads_sample, I):
-    """The fp64 oracle (as it stands) on a bounded sample of the workload's heads."""
+    """The fp64 oracle (as it stands) on a bounded sample of the workload's
+    heads: the serial recurrence, threaded over heads."""
     from oracle import oracle as O
-    q, k, v = I.make_qkv(w, B=1, H=heads_sample)
+    q, k, v = I.make_qkv(w)
+    q, k, v = (x.reshape(w.B * w.H, w.n, -1)[:heads_sample].double().numpy() for x in (q, k, v))
     threads = O.default_threads()
     t0 = time.perf_counter()
-    O.serial(q.double().numpy(), k.double().numpy(), v.double().numpy(), w.decay, threads=threads)
+    O.serial(q, k, v, w.decay, threads=threads)
     dt = time.perf_counter() - t0
     head_tokens = heads_sample * w.n
     return {
@@ -167,9 +210,22 @@ def cpu_baseline(w, heads_sample, I):
         "unit": "tokens/s",
         "cores": min(threads, heads_sample),
         "kind": "oracle",
-        "sample": "%d heads x %d tokens drawn with the workload's recipe (of %d heads per step), fp64 serial "
-                  "recurrence, %.1f s wall" % (heads_sample, w.n, w.B * w.H, dt),
+        "sample": "%d of the %d heads of one step (%d tokens each, the step's own inputs), fp64 serial "
+                  "recurrence on %d threads, %.1f s wall" % (heads_sample, w.B * w.H, w.n,
+                                                              min(threads, heads_sample), dt),
     }
+
+
+def copy_calibration(torch, gib=1):
+    """Two plain device-to-device copies of `gib` GiB, after the timed work:
+    the reference kernel against which rocprofv3's FETCH_SIZE / WRITE_SIZE
+    counters are scaled (each copy reads and writes gib GiB)."""
+    src = torch.empty(gib << 28, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
 
 
 def main(argv=None):
@@ -179,8 +235,10 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="decay_8k")
     ap.add_argument("--decode-prefill", type=int, default=None, help="prefix tokens (default: the workload's)")
-    ap.add_argument("--cpu-heads", type=int, default=64, help="heads in the oracle's timed sample (0: skip)")
+    ap.add_argument("--cpu-heads", type=int, default=128, help="heads in the oracle's timed sample (0: skip)")
     ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="finish with two 1 GiB device copies (reference for HBM byte counters)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -216,15 +274,19 @@ def main(argv=None):
         "head_tokens_per_s": fw["head_tokens_per_s"],
         "tflops": fw["tflops"],
         "mfma_frac": fw["mfma_frac"],
+        "hbm_min_bytes_frac": fw["min_bytes"] / fw["seconds"] / PEAK_HBM,
+        "kernel_ms": {key: val * 1e3 for key, val in fw["phases"].items()},
         "roofline": {
             "bound": "mfma",
-            "kernel": "hla2_forward (segment summary + segment scan + chunk output kernels)",
-            "achieved": fw["tflops"],
+            "kernel": "walk_kernel<bf16,%d,%d,%d,out> (chunk outputs)" % (
+                64 if w.d <= 64 else 128, 64 if w.dv <= 64 else 128, 64 if w.chunk <= 64 else 128),
+            "achieved": fw["output_flops_per_call"] / fw["phases"]["output"] / 1e12,
             "peak": PEAK_BF16_MFMA / 1e12,
             "unit": "TFLOP/s",
-            "frac": fw["mfma_frac"],
-            "traffic": load_traffic("forward_" + w.name),
-            "hbm_min_bytes_frac": fw["min_bytes"] / fw["seconds"] / PEAK_HBM,
+            "frac": fw["output_flops_per_call"] / fw["phases"]["output"] / PEAK_BF16_MFMA,
+            "traffic": load_traffic("output_" + w.name),
+            "avg_launch_ms": fw["phases"]["output"] * 1e3,
+            "algorithmic_flops_per_launch": fw["output_flops_per_call"],
         },
     }
     if not args.skip_decode:
@@ -241,6 +303,8 @@ def main(argv=None):
         }
     if args.cpu_heads > 0:
         line["cpu_baseline"] = cpu_baseline(w, min(args.cpu_heads, w.B * w.H), I)
+    if args.copy_calibration:
+        copy_calibration(torch)
     print(json.dumps(line))
     return 0
 

@@ -129,6 +129,14 @@ int hla2_forward(const void *q, const void *k, const void *v, void *out, int B, 
 int hla2_forward_ex(const void *q, const void *k, const void *v, void *out, int B, int H, int n, int d,
                     int dv, float decay, int normalize, int chunk, hla2_dtype_t dtype, float *den_out,
                     void *workspace, size_t workspace_bytes_given, int segments, hipStream_t stream) {
+  return hla2_forward_timed(q, k, v, out, B, H, n, d, dv, decay, normalize, chunk, dtype, den_out, workspace,
+                            workspace_bytes_given, segments, nullptr, stream);
+}
+
+int hla2_forward_timed(const void *q, const void *k, const void *v, void *out, int B, int H, int n, int d,
+                       int dv, float decay, int normalize, int chunk, hla2_dtype_t dtype, float *den_out,
+                       void *workspace, size_t workspace_bytes_given, int segments, hipEvent_t const *events,
+                       hipStream_t stream) {
   if (!q || !k || !v || !out) return HLA2_ERR_INVALID;
   if (segments < 0) return HLA2_ERR_INVALID;
   if (!(decay > 0.0f && decay <= 1.0f)) return HLA2_ERR_INVALID;  // also rejects NaN
@@ -168,10 +176,13 @@ int hla2_forward_ex(const void *q, const void *k, const void *v, void *out, int 
   a.prefix = prefix;
   const int dt = dtype == HLA2_F32 ? 0 : 1;
 
-  hipError_t e;
+  auto mark = [&](int i) { return (events && events[i]) ? hipEventRecord(events[i], stream) : hipSuccess; };
+  hipError_t e = mark(0);
+  if (e != hipSuccess) return HLA2_ERR_LAUNCH;
   if (p.nseg > 1) {
     e = hla2::launch_walk(dt, p.DK, p.DV, p.CP, false, dim3((unsigned)(p.BH * (p.nseg - 1))), a, stream);
     if (e != hipSuccess) return HLA2_ERR_LAUNCH;
+    if (mark(1) != hipSuccess) return HLA2_ERR_LAUNCH;
     hla2::ScanArgs s;
     s.sums = sums;
     s.prefix = prefix;
@@ -179,9 +190,13 @@ int hla2_forward_ex(const void *q, const void *k, const void *v, void *out, int 
     s.gamma_seg = decay < 1.0f ? (float)pow((double)decay, (double)p.cps * chunk) : 1.0f;
     e = hla2::launch_scan(p.DK, p.DV, (int)p.BH, s, stream);
     if (e != hipSuccess) return HLA2_ERR_LAUNCH;
+  } else if (mark(1) != hipSuccess) {
+    return HLA2_ERR_LAUNCH;
   }
+  if (mark(2) != hipSuccess) return HLA2_ERR_LAUNCH;
   e = hla2::launch_walk(dt, p.DK, p.DV, p.CP, true, dim3((unsigned)(p.BH * p.nseg)), a, stream);
   if (e != hipSuccess) return HLA2_ERR_LAUNCH;
+  if (mark(3) != hipSuccess) return HLA2_ERR_LAUNCH;
   return HLA2_OK;
 }
 

@@ -19,7 +19,7 @@ HLA2_OK, HLA2_ERR_INVALID, HLA2_ERR_UNSUPPORTED, HLA2_ERR_WORKSPACE, HLA2_ERR_LA
 # every symbol include/hla2.h declares
 EXPORTS = ("hla2_strerror", "hla2_abi_version", "hla2_forward_workspace_bytes", "hla2_forward_segments",
            "hla2_forward", "hla2_forward_ex_workspace_bytes", "hla2_forward_ex_segments", "hla2_forward_ex",
-           "hla2_decode_step", "hla2_state_floats")
+           "hla2_forward_timed", "hla2_decode_step", "hla2_state_floats")
 
 _lock = threading.Lock()
 _lib = None
@@ -56,6 +56,8 @@ def lib():
             L.hla2_forward_ex_segments.argtypes = [i, i, i, i, i, i, i]
             L.hla2_forward_ex.restype = i
             L.hla2_forward_ex.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, vp, sz, i, vp]
+            L.hla2_forward_timed.restype = i
+            L.hla2_forward_timed.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, vp, sz, i, vp, vp]
             L.hla2_decode_step.restype = i
             L.hla2_decode_step.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
             L.hla2_state_floats.restype = ctypes.c_long
@@ -103,13 +105,15 @@ def hla2_state_floats(d, dv) -> int:
 
 
 def hla2_forward(q, k, v, out, decay=1.0, normalize=False, chunk=64, den_out=None, workspace=None,
-                 stream=None, segments=0, check=True) -> int:
+                 stream=None, segments=0, check=True, events=None) -> int:
     """Call the C forward pass on torch tensors q, k: [B,H,n,d]; v, out: [B,H,n,dv].
 
     ``hla2_forward`` when segments == 0, else ``hla2_forward_ex`` with that
-    segment count.  ``workspace``: a uint8 device tensor of at least the
-    required bytes; allocated here (torch caching allocator) when None.
-    Returns the C return code (and raises on error when check=True)."""
+    segment count; ``hla2_forward_timed`` when ``events`` (four created
+    torch.cuda.Event objects, or None entries) is given.  ``workspace``: a
+    uint8 device tensor of at least the required bytes; allocated here (torch
+    caching allocator) when None.  Returns the C return code (and raises on
+    error when check=True)."""
     import torch
     B, H, n, d = q.shape
     dv = v.shape[-1]
@@ -122,7 +126,12 @@ def hla2_forward(q, k, v, out, decay=1.0, normalize=False, chunk=64, den_out=Non
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, n, d, dv, float(decay), int(bool(normalize)), int(chunk),
             _dtype_code(q), _ptr(den_out), _ptr(workspace), wbytes)
-    if segments:
+    if events is not None:
+        if len(events) != 4:
+            raise ValueError("events must hold four entries")
+        arr = (ctypes.c_void_p * 4)(*[None if e is None else e.cuda_event for e in events])
+        rc = lib().hla2_forward_timed(*args, int(segments), arr, _stream(stream))
+    elif segments:
         rc = lib().hla2_forward_ex(*args, int(segments), _stream(stream))
     else:
         rc = lib().hla2_forward(*args, _stream(stream))

@@ -139,6 +139,24 @@ int hla2_forward_ex(const void *q, const void *k, const void *v, void *out,
                     hla2_dtype_t dtype, float *den_out, void *workspace, size_t workspace_bytes,
                     int segments, hipStream_t stream);
 
+/*
+ * hla2_forward_ex that also records HIP events on `stream` between its kernel
+ * launches, so a caller can time each phase of the chunk-parallel pass
+ * [SUM §4] on the stream the kernels run on.  `events` is NULL or an array of
+ * four hipEvent_t (entries may be NULL; the caller creates and owns them):
+ *   events[0] before the segment-summary kernel,
+ *   events[1] after it (before the segment scan),
+ *   events[2] after the scan (before the chunk-output kernel),
+ *   events[3] after the chunk-output kernel.
+ * With one segment only the chunk-output kernel runs and events[0..2] are
+ * recorded back to back.  Results are those of hla2_forward_ex.  A failed
+ * hipEventRecord is reported as HLA2_ERR_LAUNCH.
+ */
+int hla2_forward_timed(const void *q, const void *k, const void *v, void *out,
+                       int B, int H, int n, int d, int dv, float decay, int normalize, int chunk,
+                       hla2_dtype_t dtype, float *den_out, void *workspace, size_t workspace_bytes,
+                       int segments, hipEvent_t const *events, hipStream_t stream);
+
 /* Floats per (sequence, head) state block: d*d + 2*d*dv + 2*d. */
 long hla2_state_floats(int d, int dv);
 

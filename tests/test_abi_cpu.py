@@ -143,3 +143,14 @@ def test_binding_refuses_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(H, "_lib", None)
     with pytest.raises(RuntimeError):
         H.lib()
+
+
+def test_forward_timed_validates_like_forward_ex(L):
+    ev = (ctypes.c_void_p * 4)()
+    args = (P, P, P, P, 1, 1, 64, 16, 16, 1.0, 0, 16, 0, None, None, 0, 0)
+    assert L.hla2_forward_timed(None, *args[1:], ev, None) == H.HLA2_ERR_INVALID
+    bad = list(args)
+    bad[11] = 48  # chunk
+    assert L.hla2_forward_timed(*bad, ev, None) == H.HLA2_ERR_UNSUPPORTED
+    big = (P, P, P, P, 4, 8, 2048, 64, 64, 1.0, 0, 64, 1, None, None, 0, 0)
+    assert L.hla2_forward_timed(*big, ev, None) == H.HLA2_ERR_WORKSPACE

@@ -127,6 +127,25 @@ def test_repeatable_bitwise():
     np.testing.assert_array_equal(da, db)
 
 
+def test_timed_entry_point_matches_and_records_phases():
+    # the phase events change nothing in the results and bracket every kernel
+    q, k, v = draw(2, 4, 1500, 64, 128, "bf16", seed=3)
+    a, da = gpu_forward(q, k, v, 0.99, True, 64, segments=3)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    out = torch.empty_like(vd)
+    den = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in evs:
+        e.record()
+    H.hla2_forward(qd, kd, vd, out, decay=0.99, normalize=True, chunk=64, den_out=den, segments=3, events=evs)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.double().cpu().numpy(), a)
+    np.testing.assert_array_equal(den.double().cpu().numpy(), da)
+    spans = [evs[i].elapsed_time(evs[i + 1]) for i in range(3)]
+    assert all(s >= 0 for s in spans) and spans[0] > 0 and spans[2] > 0
+
+
 def test_heads_independent():
     # one head computed alone equals the same head inside a batch (same plan)
     q, k, v = draw(2, 3, 500, 64, 64, "bf16", seed=9)
