@@ -278,8 +278,8 @@ def main(argv=None):
         "kernel_ms": {key: val * 1e3 for key, val in fw["phases"].items()},
         "roofline": {
             "bound": "mfma",
-            "kernel": "walk_kernel<bf16,%d,%d,%d,out> (chunk outputs)" % (
-                64 if w.d <= 64 else 128, 64 if w.dv <= 64 else 128, 64 if w.chunk <= 64 else 128),
+            "kernel": "walk3_kernel<%d,%d,out,decay=%d,den=%d> (chunk outputs)" % (
+                64 if w.d <= 64 else 128, 64 if w.dv <= 64 else 128, int(w.decay < 1), int(w.normalize)),
             "achieved": fw["output_flops_per_call"] / fw["phases"]["output"] / 1e12,
             "peak": PEAK_BF16_MFMA / 1e12,
             "unit": "TFLOP/s",

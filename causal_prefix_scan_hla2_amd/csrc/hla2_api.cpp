@@ -11,6 +11,7 @@ namespace {
 
 struct Plan {
   int DK, DV, CP;  // padded head dims and chunk tile of the kernel instantiation
+  int kc;          // tokens per chunk the walker steps by
   int cps;         // chunks per segment
   int nseg;        // segments per (b, h)
   long BH;
@@ -29,23 +30,30 @@ int check_shape(int B, int H, int n, int d, int dv, int chunk, int dtype) {
   if (dtype == HLA2_F32 && (d > 64 || dv > 64)) return HLA2_ERR_UNSUPPORTED;
   const long BH = (long)B * H;
   if (BH > (1L << 24) || (long)n > (1L << 30) || BH * (long)n > (1L << 40)) return HLA2_ERR_UNSUPPORTED;
+  // one head's rows are addressed with 32-bit byte offsets
+  if ((long)n * (d > dv ? d : dv) * 4 > 0x7fffffffL) return HLA2_ERR_UNSUPPORTED;
   return HLA2_OK;
 }
 
 Plan make_plan(int B, int H, int n, int d, int dv, int chunk, int dtype, int segments = 0) {
   Plan p;
   p.BH = (long)B * H;
+  long gpc;  // workgroups of the output walker per CU
   if (dtype == HLA2_BF16) {
+    // the bf16 walker always steps by 64-token chunks; `chunk` only changes rounding
     p.DK = d <= 64 ? 64 : 128;
     p.DV = dv <= 64 ? 64 : 128;
-    p.CP = chunk <= 64 ? 64 : 128;
+    p.CP = p.kc = 64;
+    gpc = hla2::walk3_groups_per_cu(p.DK, p.DV, true);
   } else {
     const int m = d > dv ? d : dv;
     p.DK = p.DV = m <= 16 ? 16 : 64;
     p.CP = chunk <= 16 ? 16 : (chunk <= 64 ? 64 : 128);
+    p.kc = chunk;
+    gpc = hla2::walk_groups_per_cu(4, p.DK, p.DV, p.CP, true);
   }
-  const long nc = ((long)n + chunk - 1) / chunk;
-  const long target = kComputeUnits * hla2::walk_groups_per_cu(dtype == HLA2_BF16 ? 2 : 4, p.DK, p.DV, p.CP, true);
+  const long nc = ((long)n + p.kc - 1) / p.kc;
+  const long target = kComputeUnits * gpc;
   long r = segments > 0 ? segments : (target + p.BH - 1) / p.BH;
   if (r > nc) r = nc;
   if (r > kMaxSegments) r = kMaxSegments;
@@ -160,7 +168,7 @@ int hla2_forward_timed(const void *q, const void *k, const void *v, void *out, i
   a.n = n;
   a.d = d;
   a.dv = dv;
-  a.chunk = chunk;
+  a.chunk = p.kc;
   a.cps = p.cps;
   a.nseg = p.nseg;
   a.log2g = decay < 1.0f ? log2f(decay) : 0.0f;
@@ -187,7 +195,7 @@ int hla2_forward_timed(const void *q, const void *k, const void *v, void *out, i
     s.sums = sums;
     s.prefix = prefix;
     s.nseg = p.nseg;
-    s.gamma_seg = decay < 1.0f ? (float)pow((double)decay, (double)p.cps * chunk) : 1.0f;
+    s.gamma_seg = decay < 1.0f ? (float)pow((double)decay, (double)p.cps * p.kc) : 1.0f;
     e = hla2::launch_scan(p.DK, p.DV, (int)p.BH, s, stream);
     if (e != hipSuccess) return HLA2_ERR_LAUNCH;
   } else if (mark(1) != hipSuccess) {

@@ -57,16 +57,33 @@ __host__ __device__ constexpr int walk_waves_per_eu(int esize, int DK, int DV, i
   return w < 1 ? 1 : (w > 2 ? 2 : w);
 }
 
+// The bf16 walker (hla2_walk3.h): 64-token chunks, 4 waves.  LDS bytes of an
+// instantiation: Q, K, V, Z~ and bf16 S0 rows, plus Z and W rows in output
+// mode, each row padded by 16 bytes; then the decay table, den and u0.
+__host__ __device__ constexpr int walk3_lds_bytes(int DK, int DV, bool out) {
+  const int CP = 64, ldk = DK + 8, ldv = DV + 8, ldw = CP + 8;
+  const int elems = 3 * CP * ldk + CP * ldv + DK * ldk + (out ? CP * ldk + CP * ldw : 0);
+  return elems * 2 + (2 * CP + 1 + CP + 2 * DK) * 4;
+}
+__host__ __device__ constexpr int walk3_groups_per_cu(int DK, int DV, bool out) {
+  const int by_lds = (160 * 1024) / walk3_lds_bytes(DK, DV, out);
+  return by_lds < 1 ? 1 : (by_lds > 2 ? 2 : by_lds);
+}
+// each 4-wave group puts one wave on every SIMD
+__host__ __device__ constexpr int walk3_waves_per_eu(int DK, int DV, bool out) {
+  return walk3_groups_per_cu(DK, DV, out);
+}
+
 // dtype: 0 = f32, 1 = bf16.  Returns hipErrorInvalidValue when no kernel exists
 // for (dtype, DK, DV, CP).
 hipError_t launch_walk(int dtype, int DK, int DV, int CP, bool output_mode, dim3 grid,
                        const WalkArgs &a, hipStream_t s);
 hipError_t launch_walk_f32(int DK, int DV, int CP, bool output_mode, dim3 grid, const WalkArgs &a,
                            hipStream_t s);
-hipError_t launch_walk_bf16_dk64(int DV, int CP, bool output_mode, dim3 grid, const WalkArgs &a,
-                                 hipStream_t s);
-hipError_t launch_walk_bf16_dk128(int DV, int CP, bool output_mode, dim3 grid, const WalkArgs &a,
-                                  hipStream_t s);
+hipError_t launch_walk3_dk64(int DV, bool output_mode, bool decay, bool den, dim3 grid, const WalkArgs &a,
+                             hipStream_t s);
+hipError_t launch_walk3_dk128(int DV, bool output_mode, bool decay, bool den, dim3 grid, const WalkArgs &a,
+                              hipStream_t s);
 hipError_t launch_scan(int DK, int DV, int BH, const ScanArgs &a, hipStream_t s);
 
 struct DecodeArgs {

@@ -111,8 +111,10 @@ hipError_t launch_scan(int DK, int DV, int BH, const ScanArgs &a, hipStream_t s)
 hipError_t launch_walk(int dtype, int DK, int DV, int CP, bool output_mode, dim3 grid,
                        const WalkArgs &a, hipStream_t s) {
   if (dtype == 0) return launch_walk_f32(DK, DV, CP, output_mode, grid, a, s);
-  if (DK == 64) return launch_walk_bf16_dk64(DV, CP, output_mode, grid, a, s);
-  if (DK == 128) return launch_walk_bf16_dk128(DV, CP, output_mode, grid, a, s);
+  if (CP != 64) return hipErrorInvalidValue;
+  const bool dec = a.decay_on != 0, den = a.need_den != 0;
+  if (DK == 64) return launch_walk3_dk64(DV, output_mode, dec, den, grid, a, s);
+  if (DK == 128) return launch_walk3_dk128(DV, output_mode, dec, den, grid, a, s);
   return hipErrorInvalidValue;
 }
 

@@ -1,0 +1,13 @@
+// bf16 chunk-walker instantiations with d padded to 128.
+#include "hla2_walk3.h"
+
+namespace hla2 {
+
+hipError_t launch_walk3_dk128(int DV, bool output_mode, bool decay, bool den, dim3 grid, const WalkArgs &a,
+                             hipStream_t s) {
+  if (DV == 64) return launch_walk3_t<128, 64>(output_mode, decay, den, grid, a, s);
+  if (DV == 128) return launch_walk3_t<128, 128>(output_mode, decay, den, grid, a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace hla2
