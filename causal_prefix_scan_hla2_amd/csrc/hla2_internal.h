@@ -59,10 +59,11 @@ __host__ __device__ constexpr int walk_waves_per_eu(int esize, int DK, int DV, i
 
 // The bf16 walker (hla2_walk3.h): 64-token chunks, 4 waves.  LDS bytes of an
 // instantiation: Q, K, V, Z~ and bf16 S0 rows, plus Z and W rows in output
-// mode, each row padded by 16 bytes; then the decay table, den and u0.
+// mode, each row padded (16 or 32 bytes); then the decay table, den and u0.
 __host__ __device__ constexpr int walk3_lds_bytes(int DK, int DV, bool out) {
-  const int CP = 64, ldk = DK + 8, ldv = DV + 8, ldw = CP + 8;
-  const int elems = 3 * CP * ldk + CP * ldv + DK * ldk + (out ? CP * ldk + CP * ldw : 0);
+  const int CP = 64, ldk = DK + 16, ldq = out ? DK + 8 : DK + 16, ldt = DK + 16, lds0 = DK + 16, ldz = DK + 16;
+  const int ldv = DV + 16, ldw = CP + 16;
+  const int elems = CP * ldq + CP * ldk + CP * ldt + CP * ldv + DK * lds0 + (out ? CP * ldz + CP * ldw : 0);
   return elems * 2 + (2 * CP + 1 + CP + 2 * DK) * 4;
 }
 __host__ __device__ constexpr int walk3_groups_per_cu(int DK, int DV, bool out) {

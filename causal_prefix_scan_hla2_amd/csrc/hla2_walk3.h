@@ -24,9 +24,11 @@
 // [DV/4 w, DV/4 (w+1)) of U, C, V and the output.  Each wave therefore keeps
 // its V columns, its U columns (and their bf16 copy U0) and all of Q as MFMA
 // operands in registers; only K, Q, V, Z, Z~ (the decayed Z), W and a bf16
-// copy of S0 pass through LDS.  Every product feeds the next from registers in
-// one k-order (hla2_mfma.h), and the output is produced transposed (out^T =
-// U0^T Q^T + V^T W^T) so that each lane stores four consecutive values.
+// copy of S0 pass through LDS.  Products whose operand comes from an accumulator
+// use the accumulator k-order of hla2_mfma.h (the other operand is read in that
+// order too); products of two LDS operands read both as contiguous 16-byte
+// vectors.  The output is produced transposed (out^T = U0^T Q^T + V^T W^T) so that
+// each lane stores four consecutive values.
 //
 // Per chunk there are two workgroup barriers:
 //   [A, Z, Z~ -> LDS; S update; C, m updates; operand fragments to registers]
@@ -53,6 +55,31 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, int
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
 }
 
+// Operand fragment in the contiguous k-order: lane (g, n) gets X[row0 + n][k0 + 8g + 0..7]
+// with one 16-byte read.  Used for products whose two operands both come from LDS (both
+// are read in this order).
+__device__ __forceinline__ bf16x8 ld_rows_c(const bf16 *X, int ld, int row0, int k0, int lane) {
+  return *(const bf16x8 *)(X + (row0 + (lane & 15)) * ld + k0 + 8 * (lane >> 4));
+}
+
+// LDS byte address of an element, passed through an empty asm: reads made from different
+// laundered addresses are never paired by the compiler into one (slower) paired read.
+__device__ __forceinline__ unsigned lds_addr_opaque(const bf16 *p) {
+  unsigned a = (unsigned)(size_t)(__attribute__((address_space(3))) const bf16 *)p;
+  asm("" : "+v"(a));
+  return a;
+}
+__device__ __forceinline__ bf16x4 lds_ld4(unsigned a) {
+  return *(__attribute__((address_space(3))) const bf16x4 *)(size_t)a;
+}
+
+// Column position of logical token j in a W row: within every 32 columns, the four
+// 4-element groups a lane reads in the accumulator k-order (4g and 16 + 4g) sit side by
+// side, so a fragment of W^T is one 16-byte read.
+__device__ __forceinline__ int wpos(int j) {
+  return (j & ~31) | (((j >> 2) & 3) << 3) | (((j >> 4) & 1) << 2) | (j & 3);
+}
+
 template <int DK, int DV, bool OUT>
 struct W3Cfg {
   static constexpr int CP = 64;            // tokens per chunk
@@ -65,18 +92,29 @@ struct W3Cfg {
   static constexpr int SCT = RT / NW;      // S column tiles per wave
   static constexpr int UCT = DV / 16 / NW; // U / output column tiles per wave
   static constexpr int URT = RT / NW;      // row tiles of u (and m) per wave
-  static constexpr int LDK = DK + 8;       // row pitch (elements) of Q, K, Z, Z~, S0 in LDS
-  static constexpr int LDV = DV + 8;
-  static constexpr int LDW = CP + 8;
+  // Row pitches (elements) in LDS, chosen for how each buffer is read (gfx950 LDS:
+  // 64 banks of 4 bytes).  Measured on the device: 16-byte reads of 16 rows at one
+  // column and transpose reads of 8 rows x 32 bytes are conflict-free when rows start
+  // 160 (or 288) bytes apart; 8-byte reads of 16 rows at one column are conflict-free
+  // 144 bytes apart.  Two 8-byte reads that the compiler merges into one paired read
+  // 32 bytes apart cost four times a plain read, so operands are read either as one
+  // 16-byte vector per lane or as two separate 8-byte reads.
+  static constexpr int LDK = DK + 16;      // K: 16-byte row reads and transpose reads
+  static constexpr int LDQ = OUT ? DK + 8 : DK + 16;  // Q: 8-byte row reads (summary mode: transpose)
+  static constexpr int LDT = DK + 16;      // Z~: transpose reads
+  static constexpr int LDS0 = DK + 16;     // S0: 16-byte row reads
+  static constexpr int LDZ = DK + 16;      // Z: 16-byte row reads
+  static constexpr int LDV = DV + 16;      // V: transpose reads
+  static constexpr int LDW = CP + 16;      // W: 16-byte row reads (columns permuted, see wpos)
   static constexpr int NVK = CP * DK / 8 / NT;  // 16-byte vectors per thread, Q and K
   static constexpr int NVV = CP * DV / 8 / NT;  // 16-byte vectors per thread, V
   static constexpr int Q_OFF = 0;
-  static constexpr int K_OFF = Q_OFF + CP * LDK;
+  static constexpr int K_OFF = Q_OFF + CP * LDQ;
   static constexpr int V_OFF = K_OFF + CP * LDK;
   static constexpr int ZT_OFF = V_OFF + CP * LDV;   // Z~ rows
-  static constexpr int SB_OFF = ZT_OFF + CP * LDK;  // bf16 S0 rows
-  static constexpr int Z_OFF = SB_OFF + DK * LDK;   // Z rows   (output mode)
-  static constexpr int W_OFF = Z_OFF + (OUT ? CP * LDK : 0);  // W rows (output mode)
+  static constexpr int SB_OFF = ZT_OFF + CP * LDT;  // bf16 S0 rows
+  static constexpr int Z_OFF = SB_OFF + DK * LDS0;  // Z rows   (output mode)
+  static constexpr int W_OFF = Z_OFF + (OUT ? CP * LDZ : 0);  // W rows (output mode)
   static constexpr int ELEMS = W_OFF + (OUT ? CP * LDW : 0);
   static constexpr int LDS_BYTES = walk3_lds_bytes(DK, DV, OUT);
   static_assert(SCT >= 1 && UCT >= 1 && URT >= 1, "shape not supported by the 4-wave split");
@@ -90,7 +128,8 @@ walk3_kernel(WalkArgs a) {
   using Cfg = W3Cfg<DK, DV, OUT>;
   constexpr int CP = Cfg::CP, NB = Cfg::NB, NT = Cfg::NT, RT = Cfg::RT, KD = Cfg::KD, KC = Cfg::KC;
   constexpr int SCT = Cfg::SCT, UCT = Cfg::UCT, URT = Cfg::URT;
-  constexpr int LDK = Cfg::LDK, LDV = Cfg::LDV, LDW = Cfg::LDW, NVK = Cfg::NVK, NVV = Cfg::NVV;
+  constexpr int LDK = Cfg::LDK, LDQ = Cfg::LDQ, LDT = Cfg::LDT, LDS0 = Cfg::LDS0, LDZ = Cfg::LDZ;
+  constexpr int LDV = Cfg::LDV, LDW = Cfg::LDW, NVK = Cfg::NVK, NVV = Cfg::NVV;
 
   __shared__ __attribute__((aligned(16))) bf16 smem[Cfg::ELEMS];
   __shared__ float pw[2 * CP + 1];            // decay^x, x = 0 .. 2 CP
@@ -153,7 +192,7 @@ walk3_kernel(WalkArgs a) {
 #pragma unroll
     for (int i = 0; i < NVK; ++i) {
       const int vi = tid + i * NT, t = vi / (DK / 8), e0 = 8 * (vi % (DK / 8));
-      *(u32x4 *)(Qs + t * LDK + e0) = rgq[i];
+      *(u32x4 *)(Qs + t * LDQ + e0) = rgq[i];
       *(u32x4 *)(Ks + t * LDK + e0) = rgk[i];
     }
 #pragma unroll
@@ -208,7 +247,7 @@ walk3_kernel(WalkArgs a) {
 #pragma unroll
     for (int i = 0; i < RT; ++i)
 #pragma unroll
-      for (int j = 0; j < SCT; ++j) st4(Sb + (16 * (w * SCT + j) + n) * LDK + 16 * i + 4 * g, Sacc[i][j]);
+      for (int j = 0; j < SCT; ++j) st4(Sb + (16 * (w * SCT + j) + n) * LDS0 + 16 * i + 4 * g, Sacc[i][j]);
   };
   auto write_u0 = [&](int buf) __attribute__((always_inline)) {
     if constexpr (DEN) {
@@ -272,7 +311,7 @@ walk3_kernel(WalkArgs a) {
     // ======== phase 1: chunk-local products of the wave's token block ========
     bf16x8 qw[KD];
 #pragma unroll
-    for (int s = 0; s < KD; ++s) qw[s] = ld_rows(Qs, LDK, 16 * w, 32 * s, lane);
+    for (int s = 0; s < KD; ++s) qw[s] = ld_rows_c(Qs, LDQ, 16 * w, 32 * s, lane);
 
     // A^T tiles (rows i, column tau of the block) -> masked, decayed -> Ad^T fragments.
     // Every wave computes all tiles and zeroes those above its block: the products
@@ -284,7 +323,7 @@ walk3_kernel(WalkArgs a) {
       for (int I = 0; I < NB; ++I) {
         at[I] = zero4();
 #pragma unroll
-        for (int s = 0; s < KD; ++s) at[I] = mma(ld_rows(Ks, LDK, 16 * I, 32 * s, lane), qw[s], at[I]);
+        for (int s = 0; s < KD; ++s) at[I] = mma(ld_rows_c(Ks, LDK, 16 * I, 32 * s, lane), qw[s], at[I]);
         const float sc = DEC ? pw[16 * max(w - I - 1, 0)] : 1.f;  // uniform
 #pragma unroll
         for (int r = 0; r < 4; ++r) at[I][r] *= I < w ? sc * fa_off[r] : (I == w ? fa_dg[r] : 0.f);
@@ -306,13 +345,13 @@ walk3_kernel(WalkArgs a) {
       for (int i = 0; i < RT; ++i) {
         f32x4 z = zero4();
 #pragma unroll
-        for (int s = 0; s < KD; ++s) z = mma(ld_rows(Sb, LDK, 16 * i, 32 * s, lane), qw[s], z);
+        for (int s = 0; s < KD; ++s) z = mma(ld_rows_c(Sb, LDS0, 16 * i, 32 * s, lane), qw[s], z);
         if (DEC) z *= zf;
 #pragma unroll
         for (int s = 0; s < KC; ++s) z = mma(kt[i][s], adf[s], z);
         // Z[tau][16 i + 4 g + r] and its decayed copy, as rows
-        if constexpr (OUT) st4(Zs + tau_w * LDK + 16 * i + 4 * g, z);
-        st4(Zts + tau_w * LDK + 16 * i + 4 * g, DEC ? z * ztf : z);
+        if constexpr (OUT) st4(Zs + tau_w * LDZ + 16 * i + 4 * g, z);
+        st4(Zts + tau_w * LDT + 16 * i + 4 * g, DEC ? z * ztf : z);
       }
     }
 
@@ -344,13 +383,18 @@ walk3_kernel(WalkArgs a) {
 #pragma unroll
       for (int s = 0; s < KC; ++s) vf[j][s] = ld_cols(Vs, LDV, 32 * s, 16 * (w * UCT + j), lane);
 
-    // Q fragments of every row tile (B operand of out^T)
+    // Q fragments of every row tile (B operand of out^T), in the accumulator k-order of U0:
+    // two separate 8-byte reads per fragment, from one opaque base per (k-step, half)
     bf16x8 qall[OUT ? NB : 1][KD];
     if constexpr (OUT) {
 #pragma unroll
-      for (int r = 0; r < NB; ++r)
+      for (int s = 0; s < KD; ++s) {
+        const unsigned a0 = lds_addr_opaque(Qs + n * LDQ + 32 * s + 4 * g);
+        const unsigned a1 = lds_addr_opaque(Qs + n * LDQ + 32 * s + 16 + 4 * g);
 #pragma unroll
-        for (int s = 0; s < KD; ++s) qall[r][s] = ld_rows(Qs, LDK, 16 * r, 32 * s, lane);
+        for (int r = 0; r < NB; ++r)
+          qall[r][s] = cat8(lds_ld4(a0 + 2 * 16 * r * LDQ), lds_ld4(a1 + 2 * 16 * r * LDQ));
+      }
     }
 
     if constexpr (!OUT) {
@@ -359,7 +403,7 @@ walk3_kernel(WalkArgs a) {
 #pragma unroll
       for (int i = 0; i < RT; ++i)
 #pragma unroll
-        for (int s = 0; s < KC; ++s) qt[i][s] = ld_cols(Qs, LDK, 32 * s, 16 * i, lane);
+        for (int s = 0; s < KC; ++s) qt[i][s] = ld_cols(Qs, LDQ, 32 * s, 16 * i, lane);
 #pragma unroll
       for (int j = 0; j < UCT; ++j) {
         bf16x8 vb[KC];
@@ -384,7 +428,7 @@ walk3_kernel(WalkArgs a) {
         for (int ur = 0; ur < URT; ++ur) {
           f32x4 acc = DEC ? macc[ur] * g64 : macc[ur];
 #pragma unroll
-          for (int s = 0; s < KC; ++s) acc = mma(ld_cols(Qs, LDK, 32 * s, 16 * (w * URT + ur), lane), onesw[s], acc);
+          for (int s = 0; s < KC; ++s) acc = mma(ld_cols(Qs, LDQ, 32 * s, 16 * (w * URT + ur), lane), onesw[s], acc);
           macc[ur] = acc;
         }
       }
@@ -412,21 +456,21 @@ walk3_kernel(WalkArgs a) {
       for (int J = 0; J < NB; ++J) {
         f32x4 wt = zero4();
 #pragma unroll
-        for (int s = 0; s < KD; ++s) wt = mma(ld_rows(Zs, LDK, 16 * J, 32 * s, lane), qw[s], wt);
+        for (int s = 0; s < KD; ++s) wt = mma(ld_rows_c(Zs, LDZ, 16 * J, 32 * s, lane), qw[s], wt);
         const float sc = DEC ? pw[32 * max(w - J - 1, 0)] : 1.f;  // uniform
 #pragma unroll
         for (int r = 0; r < 4; ++r) wt[r] *= J < w ? sc * fw_off[r] : (J == w ? fw_dg[r] : 0.f);
         if constexpr (DEN) rs += (wt[0] + wt[1]) + (wt[2] + wt[3]);
-        st4(Ws + tau_w * LDW + 16 * J + 4 * g, wt);
+        st4(Ws + tau_w * LDW + wpos(16 * J + 4 * g), wt);
       }
       if constexpr (DEN) {
         // den_tau = g^{2(tau+1)} q_tau . u0 + sum_j W[tau][j]
         const float *u0 = u0s[c & 1];
         float qu = 0.f;
 #pragma unroll
-        for (int s = 0; s < KD; ++s) {
-          const f32x4 ua = *(const f32x4 *)(u0 + 32 * s + 4 * g);
-          const f32x4 ub = *(const f32x4 *)(u0 + 32 * s + 16 + 4 * g);
+        for (int s = 0; s < KD; ++s) {  // qw holds k = 32 s + 8 g + 0..7
+          const f32x4 ua = *(const f32x4 *)(u0 + 32 * s + 8 * g);
+          const f32x4 ub = *(const f32x4 *)(u0 + 32 * s + 8 * g + 4);
 #pragma unroll
           for (int e = 0; e < 4; ++e) qu += (float)qw[s][e] * ua[e] + (float)qw[s][4 + e] * ub[e];
         }
@@ -447,7 +491,7 @@ walk3_kernel(WalkArgs a) {
 #pragma unroll
       for (int i = 0; i < RT; ++i)
 #pragma unroll
-        for (int s = 0; s < KC; ++s) zt[i][s] = ld_cols(Zts, LDK, 32 * s, 16 * i, lane);
+        for (int s = 0; s < KC; ++s) zt[i][s] = ld_cols(Zts, LDT, 32 * s, 16 * i, lane);
 #pragma unroll
       for (int i = 0; i < RT; ++i)
 #pragma unroll
@@ -462,7 +506,7 @@ walk3_kernel(WalkArgs a) {
         for (int ur = 0; ur < URT; ++ur) {
           f32x4 acc = DEC ? uacc[ur] * g128 : uacc[ur];
 #pragma unroll
-          for (int s = 0; s < KC; ++s) acc = mma(ld_cols(Zts, LDK, 32 * s, 16 * (w * URT + ur), lane), ones, acc);
+          for (int s = 0; s < KC; ++s) acc = mma(ld_cols(Zts, LDT, 32 * s, 16 * (w * URT + ur), lane), ones, acc);
           uacc[ur] = acc;
         }
         if constexpr (OUT) write_u0((c + 1) & 1);
@@ -484,7 +528,7 @@ walk3_kernel(WalkArgs a) {
         bf16x8 wb[KC];
 #pragma unroll
         for (int s = 0; s < KC; ++s)
-          if (32 * s <= 16 * r + 15) wb[s] = ld_rows(Ws, LDW, 16 * r, 32 * s, lane);
+          if (32 * s <= 16 * r + 15) wb[s] = ld_rows_c(Ws, LDW, 16 * r, 32 * s, lane);
 #pragma unroll
         for (int j = 0; j < UCT; ++j) {
           f32x4 o = zero4();
