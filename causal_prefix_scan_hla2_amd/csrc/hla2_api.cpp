@@ -20,6 +20,7 @@ struct Plan {
 // The output pass aims for one full round of workgroups on a 256-CU part.
 constexpr long kComputeUnits = 256;
 constexpr int kMaxSegments = 64;
+constexpr long kMinChunksPerSegment = 4;
 
 bool is_pow2_chunk(int c) { return c == 16 || c == 32 || c == 64 || c == 128; }
 
@@ -55,6 +56,9 @@ Plan make_plan(int B, int H, int n, int d, int dv, int chunk, int dtype, int seg
   const long nc = ((long)n + p.kc - 1) / p.kc;
   const long target = kComputeUnits * gpc;
   long r = segments > 0 ? segments : (target + p.BH - 1) / p.BH;
+  // automatic plans keep at least kMinChunksPerSegment chunks per segment: shorter
+  // segments add scan steps faster than they shorten the walks
+  if (segments == 0 && r > nc / kMinChunksPerSegment) r = nc / kMinChunksPerSegment;
   if (r > nc) r = nc;
   if (r > kMaxSegments) r = kMaxSegments;
   if (r < 1) r = 1;
@@ -196,7 +200,7 @@ int hla2_forward_timed(const void *q, const void *k, const void *v, void *out, i
     s.prefix = prefix;
     s.nseg = p.nseg;
     s.gamma_seg = decay < 1.0f ? (float)pow((double)decay, (double)p.cps * p.kc) : 1.0f;
-    e = hla2::launch_scan(p.DK, p.DV, (int)p.BH, s, stream);
+    e = hla2::launch_scan(dt, p.DK, p.DV, (int)p.BH, s, stream);
     if (e != hipSuccess) return HLA2_ERR_LAUNCH;
   } else if (mark(1) != hipSuccess) {
     return HLA2_ERR_LAUNCH;

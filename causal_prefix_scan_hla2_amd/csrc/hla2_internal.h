@@ -85,7 +85,7 @@ hipError_t launch_walk3_dk64(int DV, bool output_mode, bool decay, bool den, dim
                              hipStream_t s);
 hipError_t launch_walk3_dk128(int DV, bool output_mode, bool decay, bool den, dim3 grid, const WalkArgs &a,
                               hipStream_t s);
-hipError_t launch_scan(int DK, int DV, int BH, const ScanArgs &a, hipStream_t s);
+hipError_t launch_scan(int dtype, int DK, int DV, int BH, const ScanArgs &a, hipStream_t s);
 
 struct DecodeArgs {
   float *state;

@@ -14,19 +14,23 @@
 //   S0_{r+1} = g S0_r + S_r,   U0_{r+1} = g^2 U0_r + U_r + g S0_r C_r,
 // every full segment having the same length.  One wave owns a 16x16 tile of U0
 // (or the 16-row slice of u0) and the matching 16-row slice of S0, and walks r;
-// tiles and heads run in parallel.  The S0 C_r product runs on fp32 MFMA, and
-// the loads of step r+1 are issued before step r is computed.
+// tiles and heads run in parallel.  The S0 C_r product runs on fp32 MFMA.  Steps
+// have no loads that depend on earlier steps, so the loads of PF consecutive steps
+// are issued together and the walk pays one memory latency per PF steps.
 #include "hla2_internal.h"
 #include "hla2_mfma.h"
 
 namespace hla2 {
 
+// fp32 path (fp32 inputs, d <= 64): one wave per (head, 16-row tile, column tile),
+// fp32 MFMA for the cross term.
 template <int DK, int DV>
 __global__ void __launch_bounds__(64) scan_kernel(ScanArgs a) {
   // MFMA k-order: for step (jj, e) lane group g holds k = 16 jj + 4 g + e, so a
   // lane's share of an S0 row is DK/16 contiguous float4s.
   constexpr int NJ = DK / 16;
-  constexpr int CU = DV / 16;  // column tile index of the u column
+  constexpr int CU = DV / 16;         // column tile index of the u column
+  constexpr int PF = DK == 64 ? 4 : 2;  // steps whose loads are in flight together
   const long SB = sum_block_floats(DK, DV), PB = prefix_block_floats(DK, DV);
   const int bh = blockIdx.x, rt = blockIdx.y, ct = blockIdx.z;
   const int lane = threadIdx.x, g = lane >> 4, n = lane & 15;
@@ -56,10 +60,8 @@ __global__ void __launch_bounds__(64) scan_kernel(ScanArgs a) {
     for (int q = 0; q < 4; ++q)
       loc[q] = (ct < CU) ? sU[(16 * rt + 4 * g + q) * DV + 16 * ct + n] : (n == 0 ? su[16 * rt + 4 * g + q] : 0.f);
   };
-
-  f32x4 sr[NJ], cr[NJ], loc;
-  if (a.nseg > 1) load(0, sr, cr, loc);
-  for (int r = 0; r < a.nseg; ++r) {
+  // write the exclusive prefix of segment r (the state before it)
+  auto store = [&](int r) __attribute__((always_inline)) {
     float *pb = prefix + ((long)bh * a.nseg + r) * PB;
     if (ct == 0) {
 #pragma unroll
@@ -71,40 +73,159 @@ __global__ void __launch_bounds__(64) scan_kernel(ScanArgs a) {
     } else if (n == 0) {
       *(f32x4 *)(pb + DK * DK + DK * DV + 16 * rt + 4 * g) = acc;
     }
-    if (r == a.nseg - 1) break;
-    f32x4 srn[NJ], crn[NJ], locn;
-    if (r + 1 < a.nseg - 1) load(r + 1, srn, crn, locn);  // prefetch the next step
-    f32x4 mm = zero4();
+  };
+
+  const int steps = a.nseg - 1;  // segment summaries to fold in
+  for (int r0 = 0; r0 < steps; r0 += PF) {
+    f32x4 sr[PF][NJ], cr[PF][NJ], loc[PF];
 #pragma unroll
-    for (int jj = 0; jj < NJ; ++jj)
+    for (int j = 0; j < PF; ++j)
+      if (r0 + j < steps) load(r0 + j, sr[j], cr[j], loc[j]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) mm = mfma_f32_guarded(s0[jj][e], cr[jj][e], mm);
-    acc = G2 * acc + loc + G1 * mm;
+    for (int j = 0; j < PF; ++j) {
+      if (r0 + j < steps) {
+        store(r0 + j);
+        f32x4 mm = zero4();
 #pragma unroll
-    for (int jj = 0; jj < NJ; ++jj) s0[jj] = G1 * s0[jj] + sr[jj];
-    if (r + 1 < a.nseg - 1) {
+        for (int jj = 0; jj < NJ; ++jj)
 #pragma unroll
-      for (int jj = 0; jj < NJ; ++jj) {
-        sr[jj] = srn[jj];
-        cr[jj] = crn[jj];
+          for (int e = 0; e < 4; ++e) mm = mfma_f32_guarded(s0[jj][e], cr[j][jj][e], mm);
+        acc = G2 * acc + loc[j] + G1 * mm;
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj) s0[jj] = G1 * s0[jj] + sr[j][jj];
       }
-      loc = locn;
     }
   }
+  store(steps);
+}
+
+// bf16 path: two workgroups per head, each owning half of the value columns (the second
+// also the u column) for all rows, with one wave per 16-row tile.  The cross term S0 C_r
+// runs on bf16 MFMA, like every other state product of the bf16 walkers: each step the
+// group's columns of C_r (and m_r) are converted to bf16 into LDS once and read by every
+// wave, while the next step's C_r is already being fetched.
+template <int DK, int DV>
+__global__ void __launch_bounds__(64 * (DK / 16)) scan_bf16_kernel(ScanArgs a) {
+  constexpr int NWV = DK / 16;        // waves = row tiles
+  constexpr int NT = 64 * NWV;
+  constexpr int NJ = DK / 16;         // f32x4 per lane of an S0 row
+  constexpr int HC = DV / 2;          // value columns per workgroup
+  constexpr int CT = HC / 16;         // value column tiles per workgroup
+  constexpr int LDC = HC + 16;        // bf16 C_r rows: HC values, then m_r (second group), zeros
+  constexpr int NC4 = DK * HC / 4 / NT;  // f32x4 of C_r per thread
+  static_assert(NC4 * 4 * NT == DK * HC, "C staging split");
+  const long SB = sum_block_floats(DK, DV), PB = prefix_block_floats(DK, DV);
+  const int bh = blockIdx.x, half = blockIdx.y, c0 = half * HC;  // first value column
+  const bool has_u = half == 1;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const float G1 = a.gamma_seg, G2 = a.gamma_seg * a.gamma_seg;
+  __shared__ __attribute__((aligned(16))) bf16 Cb[2][DK * LDC];
+
+  // columns HC .. HC+15 hold m_r (column HC, second group) and zeros; zero them once
+  for (int x = tid; x < 2 * DK * 16; x += NT) {
+    const int b = x / (DK * 16), r = (x / 16) % DK, c = HC + x % 16;
+    Cb[b][r * LDC + c] = (bf16)0.f;
+  }
+
+  f32x4 s0[NJ];       // S0[16 w + n][16 jj + 4 g + e]
+  f32x4 acc[CT + 1];  // U0[16 w + 4 g + q][c0 + 16 ct + n]; tile CT holds u0 in column 0
+#pragma unroll
+  for (int jj = 0; jj < NJ; ++jj) s0[jj] = zero4();
+#pragma unroll
+  for (int ct = 0; ct <= CT; ++ct) acc[ct] = zero4();
+
+  // loads of one step: the group's C_r columns and m_r (staged into LDS at the top of the
+  // step, so they are fetched one step ahead) and the wave's rows of S_r and U_r
+  f32x4 cr[NC4], sr[NJ], lr[CT + 1];
+  float mr = 0.f;
+  auto block = [&](int r) __attribute__((always_inline)) {
+    return a.sums + ((long)bh * (a.nseg - 1) + r) * SB;
+  };
+  auto load_c = [&](int r) __attribute__((always_inline)) {
+    const float *sC = block(r) + DK * DK, *sm = sC + 2 * DK * DV;
+#pragma unroll
+    for (int i = 0; i < NC4; ++i) {
+      const int e = 4 * (tid + i * NT), row = e / HC, col = e % HC;
+      cr[i] = *(const f32x4 *)(sC + row * DV + c0 + col);
+    }
+    if (has_u && tid < DK) mr = sm[tid];
+  };
+  auto load_su = [&](int r) __attribute__((always_inline)) {
+    const float *sS = block(r), *sU = sS + DK * DK + DK * DV, *su = sU + DK * DV + DK;
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) sr[jj] = *(const f32x4 *)(sS + (16 * w + n) * DK + 16 * jj + 4 * g);
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) lr[ct][q] = sU[(16 * w + 4 * g + q) * DV + c0 + 16 * ct + n];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) lr[CT][q] = (has_u && n == 0) ? su[16 * w + 4 * g + q] : 0.f;
+  };
+  // the exclusive prefix of segment r (S0 rows written by the first group only)
+  auto store = [&](int r) __attribute__((always_inline)) {
+    float *pb = a.prefix + ((long)bh * a.nseg + r) * PB;
+    if (!has_u) {
+#pragma unroll
+      for (int jj = 0; jj < NJ; ++jj) *(f32x4 *)(pb + (16 * w + n) * DK + 16 * jj + 4 * g) = s0[jj];
+    }
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) pb[DK * DK + (16 * w + 4 * g + q) * DV + c0 + 16 * ct + n] = acc[ct][q];
+    if (has_u && n == 0) *(f32x4 *)(pb + DK * DK + DK * DV + 16 * w + 4 * g) = acc[CT];
+  };
+
+  const int steps = a.nseg - 1;
+  load_c(0);
+  for (int r = 0; r < steps; ++r) {
+    load_su(r);
+    bf16 *cb = Cb[r & 1];
+#pragma unroll
+    for (int i = 0; i < NC4; ++i) {
+      const int e = 4 * (tid + i * NT), row = e / HC, col = e % HC;
+      st4(cb + row * LDC + col, cr[i]);
+    }
+    if (has_u && tid < DK) cb[tid * LDC + HC] = (bf16)mr;
+    __syncthreads();  // C_r visible; the other buffer is free again
+    if (r + 1 < steps) load_c(r + 1);
+
+    store(r);
+    bf16x8 af[DK / 32];
+#pragma unroll
+    for (int s = 0; s < DK / 32; ++s) af[s] = frag_from_acc(s0[2 * s], s0[2 * s + 1]);
+#pragma unroll
+    for (int ct = 0; ct <= CT; ++ct) {
+      f32x4 mm = zero4();
+#pragma unroll
+      for (int s = 0; s < DK / 32; ++s) mm = mma(af[s], ld_cols(cb, LDC, 32 * s, 16 * ct, lane), mm);
+      acc[ct] = G2 * acc[ct] + lr[ct] + G1 * mm;
+    }
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) s0[jj] = G1 * s0[jj] + sr[jj];
+  }
+  store(steps);
 }
 
 template <int DK, int DV>
-static hipError_t launch_scan_t(int BH, const ScanArgs &a, hipStream_t s) {
+static hipError_t launch_scan_t(int BH, bool bf, const ScanArgs &a, hipStream_t s) {
+  if constexpr (DK >= 64) {
+    if (bf) {
+      hipLaunchKernelGGL((scan_bf16_kernel<DK, DV>), dim3(BH, 2), dim3(64 * (DK / 16)), 0, s, a);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((scan_kernel<DK, DV>), dim3(BH, DK / 16, DV / 16 + 1), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_scan(int DK, int DV, int BH, const ScanArgs &a, hipStream_t s) {
-  if (DK == 16 && DV == 16) return launch_scan_t<16, 16>(BH, a, s);
-  if (DK == 64 && DV == 64) return launch_scan_t<64, 64>(BH, a, s);
-  if (DK == 64 && DV == 128) return launch_scan_t<64, 128>(BH, a, s);
-  if (DK == 128 && DV == 64) return launch_scan_t<128, 64>(BH, a, s);
-  if (DK == 128 && DV == 128) return launch_scan_t<128, 128>(BH, a, s);
+hipError_t launch_scan(int dtype, int DK, int DV, int BH, const ScanArgs &a, hipStream_t s) {
+  const bool bf = dtype != 0;
+  if (DK == 16 && DV == 16) return launch_scan_t<16, 16>(BH, false, a, s);
+  if (DK == 64 && DV == 64) return launch_scan_t<64, 64>(BH, bf, a, s);
+  if (DK == 64 && DV == 128) return launch_scan_t<64, 128>(BH, bf, a, s);
+  if (DK == 128 && DV == 64) return launch_scan_t<128, 64>(BH, bf, a, s);
+  if (DK == 128 && DV == 128) return launch_scan_t<128, 128>(BH, bf, a, s);
   return hipErrorInvalidValue;
 }
 

@@ -107,13 +107,15 @@ def test_workspace_and_segment_plan(L):
     # explicit segment counts are clamped to the number of chunks and to 64
     assert H.hla2_forward_segments(1, 1, 100, 64, 64, 64, segments=10) == 2
     assert H.hla2_forward_segments(1, 1, 1 << 16, 128, 128, 128, segments=1000) == 64
-    # the automatic plan fills at least one round of workgroups on 256 CUs when there are enough chunks
+    # the automatic plan fills at least one round of workgroups on 256 CUs when there are enough
+    # chunks, keeping at least 4 chunks of 64 tokens (the bf16 walker's step) per segment
     for shape in [(4, 8, 2048, 64, 64, 64), (8, 16, 8192, 64, 128, 64), (1, 16, 65536, 128, 128, 128)]:
         b, h, n, d, dv, c = shape
         r = H.hla2_forward_segments(*shape)
-        nc = -(-n // c)
-        assert 1 <= r <= min(nc, 64)
-        assert b * h * r >= min(256, b * h * min(nc, 64)) - b * h  # within one segment of the target
+        nc = -(-n // 64)
+        assert 1 <= r <= min(max(nc // 4, 1), 64)
+        assert b * h * r >= min(256, b * h * min(nc // 4, 64)) - b * h  # within one segment of the target
+    assert H.hla2_forward_segments(4, 8, 2048, 64, 64, 64) == 8
     # invalid shapes report 0 bytes / an error code
     assert H.hla2_forward_workspace_bytes(1, 1, 64, 24, 16, 16) == 0
     assert H.hla2_forward_segments(1, 1, 64, 24, 16, 16) == H.HLA2_ERR_UNSUPPORTED
