@@ -69,15 +69,25 @@ Plan make_plan(int B, int H, int n, int d, int dv, int chunk, int dtype, int seg
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t sums_bytes(const Plan &p) {
-  return p.nseg > 1 ? (size_t)p.BH * (p.nseg - 1) * hla2::sum_block_floats(p.DK, p.DV) * sizeof(float) : 0;
+// summary blocks per (b, h): segments 0 .. nseg-2 for the scan; every segment when the final
+// state is exported
+int nsum(const Plan &p, bool state) { return state ? p.nseg : p.nseg - 1; }
+size_t sums_bytes(const Plan &p, bool state) {
+  return (size_t)p.BH * nsum(p, state) * hla2::sum_block_floats(p.DK, p.DV) * sizeof(float);
 }
 size_t prefix_bytes(const Plan &p) {
   return p.nseg > 1 ? (size_t)p.BH * p.nseg * hla2::prefix_block_floats(p.DK, p.DV) * sizeof(float) : 0;
 }
-size_t workspace_bytes(const Plan &p) {
-  return p.nseg > 1 ? align256(sums_bytes(p)) + prefix_bytes(p) : 0;
+size_t workspace_bytes(const Plan &p, bool state = false) {
+  if (p.nseg == 1 && !state) return 0;
+  return align256(sums_bytes(p, state)) + prefix_bytes(p);
 }
+
+// Shared body of every forward entry point (arguments already validated).
+int run_forward(const void *q, const void *k, const void *v, void *out, int B, int H, int n, int d, int dv,
+                float decay, int normalize, int chunk, hla2_dtype_t dtype, float *den_out, float *state_out,
+                void *workspace, size_t workspace_bytes_given, int segments, hipEvent_t const *events,
+                hipStream_t stream);
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -103,17 +113,25 @@ long hla2_state_floats(int d, int dv) {
   return (long)d * d + 2L * d * dv + 2L * d;
 }
 
-size_t hla2_forward_ex_workspace_bytes(int B, int H, int n, int d, int dv, int chunk, int segments) {
+static size_t forward_workspace(int B, int H, int n, int d, int dv, int chunk, int segments, bool state) {
   // the plan does not depend on dtype beyond padding; size for the larger padding
   if (segments < 0 || check_shape(B, H, n, d, dv, chunk, HLA2_BF16) != HLA2_OK) return 0;
   Plan pb = make_plan(B, H, n, d, dv, chunk, HLA2_BF16, segments);
-  size_t wb = workspace_bytes(pb);
+  size_t wb = workspace_bytes(pb, state);
   if (d <= 64 && dv <= 64) {
     Plan pf = make_plan(B, H, n, d, dv, chunk, HLA2_F32, segments);
-    size_t wf = workspace_bytes(pf);
+    size_t wf = workspace_bytes(pf, state);
     if (wf > wb) wb = wf;
   }
   return wb;
+}
+
+size_t hla2_forward_ex_workspace_bytes(int B, int H, int n, int d, int dv, int chunk, int segments) {
+  return forward_workspace(B, H, n, d, dv, chunk, segments, false);
+}
+
+size_t hla2_forward_state_workspace_bytes(int B, int H, int n, int d, int dv, int chunk, int segments) {
+  return forward_workspace(B, H, n, d, dv, chunk, segments, true);
 }
 
 size_t hla2_forward_workspace_bytes(int B, int H, int n, int d, int dv, int chunk) {
@@ -149,67 +167,17 @@ int hla2_forward_timed(const void *q, const void *k, const void *v, void *out, i
                        int dv, float decay, int normalize, int chunk, hla2_dtype_t dtype, float *den_out,
                        void *workspace, size_t workspace_bytes_given, int segments, hipEvent_t const *events,
                        hipStream_t stream) {
-  if (!q || !k || !v || !out) return HLA2_ERR_INVALID;
-  if (segments < 0) return HLA2_ERR_INVALID;
-  if (!(decay > 0.0f && decay <= 1.0f)) return HLA2_ERR_INVALID;  // also rejects NaN
-  if (normalize != 0 && normalize != 1) return HLA2_ERR_INVALID;
-  int rc = check_shape(B, H, n, d, dv, chunk, (int)dtype);
-  if (rc != HLA2_OK) return rc;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return HLA2_ERR_INVALID;
-  if (den_out && !aligned(den_out, 4)) return HLA2_ERR_INVALID;
-  const Plan p = make_plan(B, H, n, d, dv, chunk, (int)dtype, segments);
-  const size_t need = workspace_bytes(p);
-  if (need > 0) {
-    if (!workspace || workspace_bytes_given < need || !aligned(workspace, 256)) return HLA2_ERR_WORKSPACE;
-  }
+  return run_forward(q, k, v, out, B, H, n, d, dv, decay, normalize, chunk, dtype, den_out, nullptr, workspace,
+                     workspace_bytes_given, segments, events, stream);
+}
 
-  hla2::WalkArgs a;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.out = out;
-  a.den_out = den_out;
-  a.n = n;
-  a.d = d;
-  a.dv = dv;
-  a.chunk = p.kc;
-  a.cps = p.cps;
-  a.nseg = p.nseg;
-  a.log2g = decay < 1.0f ? log2f(decay) : 0.0f;
-  a.decay_on = decay < 1.0f ? 1 : 0;
-  a.normalize = normalize;
-  a.need_den = (normalize || den_out) ? 1 : 0;
-  float *sums = nullptr, *prefix = nullptr;
-  if (p.nseg > 1) {
-    sums = (float *)workspace;
-    prefix = (float *)((char *)workspace + align256(sums_bytes(p)));
-  }
-  a.sums = sums;
-  a.prefix = prefix;
-  const int dt = dtype == HLA2_F32 ? 0 : 1;
-
-  auto mark = [&](int i) { return (events && events[i]) ? hipEventRecord(events[i], stream) : hipSuccess; };
-  hipError_t e = mark(0);
-  if (e != hipSuccess) return HLA2_ERR_LAUNCH;
-  if (p.nseg > 1) {
-    e = hla2::launch_walk(dt, p.DK, p.DV, p.CP, false, dim3((unsigned)(p.BH * (p.nseg - 1))), a, stream);
-    if (e != hipSuccess) return HLA2_ERR_LAUNCH;
-    if (mark(1) != hipSuccess) return HLA2_ERR_LAUNCH;
-    hla2::ScanArgs s;
-    s.sums = sums;
-    s.prefix = prefix;
-    s.nseg = p.nseg;
-    s.gamma_seg = decay < 1.0f ? (float)pow((double)decay, (double)p.cps * p.kc) : 1.0f;
-    e = hla2::launch_scan(dt, p.DK, p.DV, (int)p.BH, s, stream);
-    if (e != hipSuccess) return HLA2_ERR_LAUNCH;
-  } else if (mark(1) != hipSuccess) {
-    return HLA2_ERR_LAUNCH;
-  }
-  if (mark(2) != hipSuccess) return HLA2_ERR_LAUNCH;
-  e = hla2::launch_walk(dt, p.DK, p.DV, p.CP, true, dim3((unsigned)(p.BH * p.nseg)), a, stream);
-  if (e != hipSuccess) return HLA2_ERR_LAUNCH;
-  if (mark(3) != hipSuccess) return HLA2_ERR_LAUNCH;
-  return HLA2_OK;
+int hla2_forward_state(const void *q, const void *k, const void *v, void *out, int B, int H, int n, int d,
+                       int dv, float decay, int normalize, int chunk, hla2_dtype_t dtype, float *den_out,
+                       float *state_out, void *workspace, size_t workspace_bytes_given, int segments,
+                       hipStream_t stream) {
+  if (!state_out) return HLA2_ERR_INVALID;
+  return run_forward(q, k, v, out, B, H, n, d, dv, decay, normalize, chunk, dtype, den_out, state_out, workspace,
+                     workspace_bytes_given, segments, nullptr, stream);
 }
 
 int hla2_decode_step(float *state, const void *q, const void *k, const void *v, void *out, int N, int H,
@@ -242,3 +210,98 @@ int hla2_decode_step(float *state, const void *q, const void *k, const void *v, 
 }
 
 }  // extern "C"
+
+namespace {
+
+int run_forward(const void *q, const void *k, const void *v, void *out, int B, int H, int n, int d, int dv,
+                float decay, int normalize, int chunk, hla2_dtype_t dtype, float *den_out, float *state_out,
+                void *workspace, size_t workspace_bytes_given, int segments, hipEvent_t const *events,
+                hipStream_t stream) {
+  if (!q || !k || !v || !out) return HLA2_ERR_INVALID;
+  if (segments < 0) return HLA2_ERR_INVALID;
+  if (!(decay > 0.0f && decay <= 1.0f)) return HLA2_ERR_INVALID;  // also rejects NaN
+  if (normalize != 0 && normalize != 1) return HLA2_ERR_INVALID;
+  int rc = check_shape(B, H, n, d, dv, chunk, (int)dtype);
+  if (rc != HLA2_OK) return rc;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return HLA2_ERR_INVALID;
+  if (den_out && !aligned(den_out, 4)) return HLA2_ERR_INVALID;
+  if (state_out && !aligned(state_out, 4)) return HLA2_ERR_INVALID;
+  const bool state = state_out != nullptr;
+  const Plan p = make_plan(B, H, n, d, dv, chunk, (int)dtype, segments);
+  const size_t need = workspace_bytes(p, state);
+  if (need > 0) {
+    if (!workspace || workspace_bytes_given < need || !aligned(workspace, 256)) return HLA2_ERR_WORKSPACE;
+  }
+
+  hla2::WalkArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.den_out = den_out;
+  a.n = n;
+  a.d = d;
+  a.dv = dv;
+  a.chunk = p.kc;
+  a.cps = p.cps;
+  a.nseg = p.nseg;
+  a.log2g = decay < 1.0f ? log2f(decay) : 0.0f;
+  a.decay_on = decay < 1.0f ? 1 : 0;
+  a.normalize = normalize;
+  a.need_den = (normalize || den_out || state) ? 1 : 0;
+  a.sum_all = state ? 1 : 0;
+  float *sums = nullptr, *prefix = nullptr;
+  if (need > 0) {
+    sums = (float *)workspace;
+    prefix = p.nseg > 1 ? (float *)((char *)workspace + align256(sums_bytes(p, state))) : nullptr;
+  }
+  a.sums = sums;
+  a.prefix = prefix;
+  const int dt = dtype == HLA2_F32 ? 0 : 1;
+  const int ns = nsum(p, state);
+
+  auto mark = [&](int i) { return (events && events[i]) ? hipEventRecord(events[i], stream) : hipSuccess; };
+  hipError_t e = mark(0);
+  if (e != hipSuccess) return HLA2_ERR_LAUNCH;
+  if (ns > 0) {
+    e = hla2::launch_walk(dt, p.DK, p.DV, p.CP, false, dim3((unsigned)(p.BH * ns)), a, stream);
+    if (e != hipSuccess) return HLA2_ERR_LAUNCH;
+  }
+  if (mark(1) != hipSuccess) return HLA2_ERR_LAUNCH;
+  if (p.nseg > 1) {
+    hla2::ScanArgs s;
+    s.sums = sums;
+    s.nsum = ns;
+    s.prefix = prefix;
+    s.nseg = p.nseg;
+    s.gamma_seg = decay < 1.0f ? (float)pow((double)decay, (double)p.cps * p.kc) : 1.0f;
+    e = hla2::launch_scan(dt, p.DK, p.DV, (int)p.BH, s, stream);
+    if (e != hipSuccess) return HLA2_ERR_LAUNCH;
+  }
+  if (mark(2) != hipSuccess) return HLA2_ERR_LAUNCH;
+  e = hla2::launch_walk(dt, p.DK, p.DV, p.CP, true, dim3((unsigned)(p.BH * p.nseg)), a, stream);
+  if (e != hipSuccess) return HLA2_ERR_LAUNCH;
+  if (mark(3) != hipSuccess) return HLA2_ERR_LAUNCH;
+  if (state) {
+    hla2::StateArgs st;
+    st.sums = sums;
+    st.prefix = prefix;
+    st.q = q;
+    st.k = k;
+    st.v = v;
+    st.state_out = state_out;
+    st.n = n;
+    st.d = d;
+    st.dv = dv;
+    st.nseg = p.nseg;
+    st.cps = p.cps;
+    st.kc = p.kc;
+    st.log2g = a.log2g;
+    st.decay_on = a.decay_on;
+    e = hla2::launch_state(dt, p.DK, p.DV, (int)p.BH, st, stream);
+    if (e != hipSuccess) return HLA2_ERR_LAUNCH;
+  }
+  return HLA2_OK;
+}
+
+}  // namespace

@@ -17,11 +17,16 @@ struct WalkArgs {
   int decay_on;           // decay < 1
   int normalize;
   int need_den;           // normalize || den_out: carry u (and m)
+  int sum_all;            // summary mode: summarise every segment, the last one over its full
+                          // chunks only (for the final state); else segments 0 .. nseg-2
 };
+// summary blocks per (b, h) in the workspace
+__host__ __device__ inline int walk_nsum(const WalkArgs &a) { return a.sum_all ? a.nseg : a.nseg - 1; }
 
 // Arguments of the segment-level exclusive scan.
 struct ScanArgs {
-  const float *sums;  // [BH, nseg-1] summary blocks
+  const float *sums;  // [BH, nsum] summary blocks (the first nseg-1 are scanned)
+  int nsum;
   float *prefix;      // [BH, nseg] prefix blocks
   int nseg;
   float gamma_seg;    // decay^(tokens per full segment)
@@ -86,6 +91,19 @@ hipError_t launch_walk3_dk64(int DV, bool output_mode, bool decay, bool den, dim
 hipError_t launch_walk3_dk128(int DV, bool output_mode, bool decay, bool den, dim3 grid, const WalkArgs &a,
                               hipStream_t s);
 hipError_t launch_scan(int dtype, int DK, int DV, int BH, const ScanArgs &a, hipStream_t s);
+
+// Final state of a forward pass: fold every segment summary, then the tokens after the
+// last full chunk, into S, C, U, m, u and write the decode-layout block S | C | m | G | h.
+struct StateArgs {
+  const float *sums;       // [BH, nseg] summary blocks (padded DK, DV)
+  const float *prefix;     // [BH, nseg] exclusive prefix blocks (null when nseg == 1)
+  const void *q, *k, *v;   // [BH, n, d|dv], for the tail tokens
+  float *state_out;        // [BH, d*d + 2*d*dv + 2*d]
+  int n, d, dv, nseg, cps, kc;  // kc: tokens per chunk of the walker
+  float log2g;
+  int decay_on;
+};
+hipError_t launch_state(int dtype, int DK, int DV, int BH, const StateArgs &a, hipStream_t s);
 
 struct DecodeArgs {
   float *state;

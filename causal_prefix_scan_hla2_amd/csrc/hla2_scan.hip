@@ -45,7 +45,7 @@ __global__ void __launch_bounds__(64) scan_kernel(ScanArgs a) {
 
   // the loads of one step: rows of S_r, a column tile of C_r (or m_r), a tile of U_r (or u_r)
   auto load = [&](int r, f32x4 (&sr)[NJ], f32x4 (&cr)[NJ], f32x4 &loc) __attribute__((always_inline)) {
-    const float *sb = sums + ((long)bh * (a.nseg - 1) + r) * SB;
+    const float *sb = sums + ((long)bh * a.nsum + r) * SB;
     const float *sS = sb, *sC = sS + DK * DK, *sU = sC + DK * DV, *sm = sU + DK * DV, *su = sm + DK;
 #pragma unroll
     for (int jj = 0; jj < NJ; ++jj) {
@@ -140,7 +140,7 @@ __global__ void __launch_bounds__(64 * (DK / 16)) scan_bf16_kernel(ScanArgs a) {
   f32x4 cr[NC4], sr[NJ], lr[CT + 1];
   float mr = 0.f;
   auto block = [&](int r) __attribute__((always_inline)) {
-    return a.sums + ((long)bh * (a.nseg - 1) + r) * SB;
+    return a.sums + ((long)bh * a.nsum + r) * SB;
   };
   auto load_c = [&](int r) __attribute__((always_inline)) {
     const float *sC = block(r) + DK * DK, *sm = sC + 2 * DK * DV;

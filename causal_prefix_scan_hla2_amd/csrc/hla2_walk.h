@@ -111,11 +111,13 @@ walk_kernel(WalkArgs a) {
   // the wave index is uniform across the wave: keep it in a scalar register so that every
   // branch on it (token block, state tiles) is a scalar branch around whole-wave MFMA code
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nseg_here = OUT ? a.nseg : a.nseg - 1;
+  const int nseg_here = OUT ? a.nseg : walk_nsum(a);
   const int bh = blockIdx.x / nseg_here, seg = blockIdx.x % nseg_here;
   const long tok0 = (long)seg * a.cps * a.chunk;
   const long tokE = ((long)a.n < tok0 + (long)a.cps * a.chunk) ? (long)a.n : tok0 + (long)a.cps * a.chunk;
-  const int nch = (int)((tokE - tok0 + a.chunk - 1) / a.chunk);
+  // a summary of the last segment (final state) stops at its last full chunk
+  const int nch = (!OUT && seg == a.nseg - 1) ? (int)((tokE - tok0) / a.chunk)
+                                              : (int)((tokE - tok0 + a.chunk - 1) / a.chunk);
   const T *qg = (const T *)a.q + (long)bh * a.n * a.d;
   const T *kg = (const T *)a.k + (long)bh * a.n * a.d;
   const T *vg = (const T *)a.v + (long)bh * a.n * a.dv;
@@ -517,7 +519,7 @@ walk_kernel(WalkArgs a) {
 
   if constexpr (!OUT) {
     // segment summary: S | C | U | m | u
-    float *sb = a.sums + ((long)bh * (a.nseg - 1) + seg) * sum_block_floats(DK, DV);
+    float *sb = a.sums + ((long)bh * walk_nsum(a) + seg) * sum_block_floats(DK, DV);
     float *sS = sb, *sC = sS + DK * DK, *sU = sC + DK * DV, *sm = sU + DK * DV, *su = sm + DK;
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {

@@ -145,12 +145,13 @@ walk3_kernel(WalkArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nseg_here = OUT ? a.nseg : a.nseg - 1;
+  const int nseg_here = OUT ? a.nseg : walk_nsum(a);
   const int bh = blockIdx.x / nseg_here, seg = blockIdx.x % nseg_here;
   const int d = a.d, dv = a.dv;
   const int tok0 = seg * a.cps * CP;  // first token of the segment
   const int tokE = min(a.n, tok0 + a.cps * CP);
-  const int nch = (tokE - tok0 + CP - 1) / CP;
+  // a summary of the last segment (final state) stops at its last full chunk
+  const int nch = (!OUT && seg == a.nseg - 1) ? (tokE - tok0) / CP : (tokE - tok0 + CP - 1) / CP;
 
   // buffer resources over this head's rows; reads past the end return zero
   const long hq = (long)bh * a.n * d, hv = (long)bh * a.n * dv;
@@ -551,7 +552,7 @@ walk3_kernel(WalkArgs a) {
 
   // ---------------- segment summary: S | C | U | m | u ----------------
   if constexpr (!OUT) {
-    float *sb = a.sums + ((long)bh * (a.nseg - 1) + seg) * sum_block_floats(DK, DV);
+    float *sb = a.sums + ((long)bh * walk_nsum(a) + seg) * sum_block_floats(DK, DV);
     float *sS = sb, *sC = sS + DK * DK, *sU = sC + DK * DV, *sm = sU + DK * DV, *su = sm + DK;
 #pragma unroll
     for (int i = 0; i < RT; ++i) {

@@ -19,7 +19,8 @@ HLA2_OK, HLA2_ERR_INVALID, HLA2_ERR_UNSUPPORTED, HLA2_ERR_WORKSPACE, HLA2_ERR_LA
 # every symbol include/hla2.h declares
 EXPORTS = ("hla2_strerror", "hla2_abi_version", "hla2_forward_workspace_bytes", "hla2_forward_segments",
            "hla2_forward", "hla2_forward_ex_workspace_bytes", "hla2_forward_ex_segments", "hla2_forward_ex",
-           "hla2_forward_timed", "hla2_decode_step", "hla2_state_floats")
+           "hla2_forward_timed", "hla2_decode_step", "hla2_state_floats", "hla2_forward_state_workspace_bytes",
+           "hla2_forward_state")
 
 _lock = threading.Lock()
 _lib = None
@@ -62,6 +63,10 @@ def lib():
             L.hla2_decode_step.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
             L.hla2_state_floats.restype = ctypes.c_long
             L.hla2_state_floats.argtypes = [i, i]
+            L.hla2_forward_state_workspace_bytes.restype = sz
+            L.hla2_forward_state_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+            L.hla2_forward_state.restype = i
+            L.hla2_forward_state.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, vp, vp, sz, i, vp]
             _lib = L
     return _lib
 
@@ -137,6 +142,35 @@ def hla2_forward(q, k, v, out, decay=1.0, normalize=False, chunk=64, den_out=Non
         rc = lib().hla2_forward(*args, _stream(stream))
     if check and rc != HLA2_OK:
         raise HLA2Error(rc, "hla2_forward")
+    return rc
+
+
+def hla2_forward_state_workspace_bytes(B, H, n, d, dv, chunk, segments=0) -> int:
+    return int(lib().hla2_forward_state_workspace_bytes(B, H, n, d, dv, chunk, segments))
+
+
+def hla2_forward_state(q, k, v, out, state_out, decay=1.0, normalize=False, chunk=64, den_out=None,
+                       workspace=None, stream=None, segments=0, check=True) -> int:
+    """Call ``hla2_forward_state``: the forward pass of ``hla2_forward`` plus the
+    final state, written to ``state_out`` (fp32 [B,H,state_floats], the layout
+    ``hla2_decode_step`` reads).  ``workspace`` as for ``hla2_forward``."""
+    import torch
+    B, H, n, d = q.shape
+    dv = v.shape[-1]
+    for t in (q, k, v, out, state_out):
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    if state_out.dtype != torch.float32 or state_out.numel() != B * H * hla2_state_floats(d, dv):
+        raise ValueError("state_out must be fp32 [B, H, state_floats]")
+    need = hla2_forward_state_workspace_bytes(B, H, n, d, dv, chunk, segments)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().hla2_forward_state(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, n, d, dv, float(decay),
+                                  int(bool(normalize)), int(chunk), _dtype_code(q), _ptr(den_out),
+                                  _ptr(state_out), _ptr(workspace), wbytes, int(segments), _stream(stream))
+    if check and rc != HLA2_OK:
+        raise HLA2Error(rc, "hla2_forward_state")
     return rc
 
 

@@ -160,6 +160,30 @@ int hla2_forward_timed(const void *q, const void *k, const void *v, void *out,
 /* Floats per (sequence, head) state block: d*d + 2*d*dv + 2*d. */
 long hla2_state_floats(int d, int dv);
 
+/*
+ * hla2_forward that also exports the state after the last token, in the
+ * layout hla2_decode_step reads, so streaming decode continues where the
+ * forward pass stopped [SUM §1, state upkeep; SUM §4: the inclusive total of
+ * the scan is the state after the whole sequence].
+ *   state_out: [B, H] blocks of hla2_state_floats(d, dv) fp32 (written),
+ *          S[d*d] | C[d*dv] | m[d] | G[d*dv] | h[d] as for hla2_decode_step,
+ *          equal (up to rounding) to the state the serial recurrence holds
+ *          after token n-1.  Must not be NULL (HLA2_ERR_INVALID).
+ *   workspace: at least hla2_forward_state_workspace_bytes(...) bytes for the
+ *          same `segments`, 256-byte aligned; never 0 bytes, since every
+ *          segment keeps its summary for the export.
+ *   segments: as for hla2_forward_ex (0 = the automatic count).
+ * All other arguments, outputs and errors are those of hla2_forward_ex.
+ * Internally the summaries of every segment are
+ * folded with the incoming prefix of the last one, and the tokens after the
+ * last full chunk are absorbed one by one, in fp32.
+ */
+size_t hla2_forward_state_workspace_bytes(int B, int H, int n, int d, int dv, int chunk, int segments);
+int hla2_forward_state(const void *q, const void *k, const void *v, void *out,
+                       int B, int H, int n, int d, int dv, float decay, int normalize, int chunk,
+                       hla2_dtype_t dtype, float *den_out, float *state_out, void *workspace,
+                       size_t workspace_bytes, int segments, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -156,3 +156,34 @@ def test_forward_timed_validates_like_forward_ex(L):
     assert L.hla2_forward_timed(*bad, ev, None) == H.HLA2_ERR_UNSUPPORTED
     big = (P, P, P, P, 4, 8, 2048, 64, 64, 1.0, 0, 64, 1, None, None, 0, 0)
     assert L.hla2_forward_timed(*big, ev, None) == H.HLA2_ERR_WORKSPACE
+
+
+def fst(L, state=P, ws=None, wsb=0, segments=0, B_=1, H_=1, n=64, d=16, dv=16, chunk=16, dtype=0, decay=1.0):
+    return L.hla2_forward_state(P, P, P, P, B_, H_, n, d, dv, decay, 0, chunk, dtype, None, state, ws, wsb,
+                                segments, None)
+
+
+def test_forward_state_validates(L):
+    # every segment keeps a summary for the export, so even one segment needs a workspace
+    # (bf16 at d = dv = 64: the size reported is exactly what that call checks)
+    need1 = H.hla2_forward_state_workspace_bytes(1, 1, 64, 64, 64, 64, segments=1)
+    assert need1 > 0 and H.hla2_forward_workspace_bytes(1, 1, 64, 64, 64, 64, segments=1) == 0
+    bf = dict(d=64, dv=64, chunk=64, dtype=1, segments=1)
+    assert fst(L, state=None, ws=P, wsb=1 << 30, **bf) == H.HLA2_ERR_INVALID
+    assert fst(L, state=ctypes.c_void_p(4098), ws=P, wsb=1 << 30, **bf) == H.HLA2_ERR_INVALID  # misaligned
+    assert fst(L, **bf) == H.HLA2_ERR_WORKSPACE                                         # missing
+    assert fst(L, ws=P, wsb=need1 - 1, **bf) == H.HLA2_ERR_WORKSPACE                    # too small
+    assert fst(L, ws=ctypes.c_void_p(4096 + 64), wsb=need1, **bf) == H.HLA2_ERR_WORKSPACE  # misaligned
+    assert fst(L, ws=P, wsb=1 << 30, chunk=48) == H.HLA2_ERR_UNSUPPORTED
+    assert fst(L, ws=P, wsb=1 << 30, decay=0.0) == H.HLA2_ERR_INVALID
+    assert fst(L, ws=P, wsb=1 << 30, segments=-2) == H.HLA2_ERR_INVALID
+    # the export adds one summary block per (b, h) to the plain forward's workspace
+    for shape in [(4, 8, 2048, 64, 64, 64), (1, 2, 1000, 128, 128, 64), (2, 3, 200, 32, 48, 16)]:
+        b, h, n, d, dv, c = shape
+        for seg in (0, 1, 3):
+            plain = H.hla2_forward_workspace_bytes(*shape, segments=seg)
+            st = H.hla2_forward_state_workspace_bytes(*shape, segments=seg)
+            dk = 16 if max(d, dv) <= 16 and d <= 64 and dv <= 64 else (64 if d <= 64 else 128)
+            assert st > plain
+            assert st >= b * h * H.hla2_forward_segments(*shape, segments=seg) * dk * dk * 4
+    assert H.hla2_forward_state_workspace_bytes(1, 1, 64, 24, 16, 16, 0) == 0

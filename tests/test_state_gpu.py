@@ -1,0 +1,137 @@
+"""GPU parity of hla2_forward_state (through the C ABI) against the fp64 oracle.
+
+The exported state after the last token is compared with the state the
+oracle's serial recurrence holds after the same tokens (S, C, m, G, h each by
+relative L2), the activations with the oracle's outputs, and decoding resumed
+from the exported state with the oracle's serial pass over prefix + the new
+tokens.  Cases cover one and many segments, a last segment with and without
+full chunks, a sequence shorter than one chunk, every padded head size and
+both element types.
+"""
+import numpy as np
+import pytest
+import torch
+
+from causal_prefix_scan_hla2_amd import hla2 as H
+from causal_prefix_scan_hla2_amd import inputs as I
+from oracle import oracle as O
+from tests.parity import ratio_ok, ratio_report, rel_l2, tol_for
+
+pytestmark = pytest.mark.gpu
+
+
+def draw(B, H_, n, d, dv, dtype, seed):
+    w = I.Workload("state", B, H_, n, d, dv, dtype, 1.0, False, 64, seed=seed)
+    return I.make_qkv(w)
+
+
+def gpu_forward_state(q, k, v, decay, normalize, chunk, segments):
+    dev = torch.device("cuda:0")
+    B, H_, n, d = q.shape
+    dv = v.shape[-1]
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    out = torch.empty_like(vd)
+    st = torch.full((B, H_, H.hla2_state_floats(d, dv)), float("nan"), dtype=torch.float32, device=dev)
+    H.hla2_forward_state(qd, kd, vd, out, st, decay=decay, normalize=normalize, chunk=chunk, segments=segments)
+    torch.cuda.synchronize()
+    return out, st
+
+
+def state_errors(st_gpu, st_ref, d, dv):
+    g, r = O.split_state(st_gpu, d, dv), O.split_state(st_ref, d, dv)
+    return {key: rel_l2(g[key], r[key]) for key in ("S", "C", "m", "G", "h")}
+
+
+CASES = [
+    # B, H, n, d, dv, dtype, decay, normalize, chunk, segments
+    (1, 2, 64, 16, 16, "f32", 1.0, False, 16, 0),      # one segment, no tail
+    (2, 3, 200, 32, 48, "f32", 0.9, True, 16, 3),      # tail of 8 tokens after 3 segments
+    (1, 2, 333, 64, 64, "f32", 0.97, False, 32, 0),
+    (1, 1, 130, 16, 64, "f32", 0.95, False, 128, 0),
+    (1, 1, 40, 64, 64, "f32", 0.9, False, 64, 0),      # shorter than a chunk: all tail
+    (2, 3, 300, 64, 128, "bf16", 0.99, False, 64, 0),
+    (1, 2, 1000, 128, 128, "bf16", 1.0, True, 64, 16),  # last segment has no full chunk
+    (1, 1, 1000, 64, 128, "bf16", 0.99, False, 64, 7),
+    (1, 2, 2048, 64, 64, "bf16", 0.999, False, 64, 0),  # several automatic segments, no tail
+    (1, 2, 700, 128, 64, "bf16", 0.98, True, 64, 4),
+    (1, 1, 40, 64, 64, "bf16", 0.9, False, 64, 0),     # shorter than a chunk: all tail
+    (1, 1, 100, 16, 16, "bf16", 1.0, False, 16, 1),
+]
+
+
+@pytest.mark.parametrize("B,H_,n,d,dv,dtype,decay,normalize,chunk,segments", CASES)
+def test_final_state_matches_oracle(B, H_, n, d, dv, dtype, decay, normalize, chunk, segments):
+    print("case", B, H_, n, d, dv, dtype, decay, normalize, chunk, segments, flush=True)
+    q, k, v = draw(B, H_, n, d, dv, dtype, seed=1000 + n + d)
+    out, st = gpu_forward_state(q, k, v, decay, normalize, chunk, segments)
+    num, den, un, st_ref = O.serial_unorm(q.double().numpy(), k.double().numpy(), v.double().numpy(), decay)
+    tol = tol_for(dtype)
+    errs = state_errors(st.double().cpu().numpy(), st_ref, d, dv)
+    msg = " ".join("%s %.3g" % kv for kv in errs.items())
+    o = out.double().cpu().numpy()
+    if normalize:
+        rep = ratio_report(o, np.zeros_like(den), num, den, un, q.double().numpy())
+        msg += " | ratio(well) %.3g excluded %.3f" % (rep["ratio_well"], rep["excluded"])
+        ok_out = ratio_ok(rep, tol, subset=True)
+    else:
+        r_o = rel_l2(o, num)
+        msg += " | out %.3g" % r_o
+        ok_out = r_o <= tol
+    print(msg)
+    assert all(e <= tol for e in errs.values()), msg
+    assert ok_out, msg
+
+
+def test_state_export_leaves_outputs_unchanged():
+    """The activations of hla2_forward_state are those of hla2_forward (same plan)."""
+    q, k, v = draw(2, 2, 777, 64, 64, "bf16", seed=5)
+    dev = torch.device("cuda:0")
+    out_s, _ = gpu_forward_state(q, k, v, 0.99, True, 64, 0)
+    out = torch.empty_like(out_s)
+    H.hla2_forward(q.to(dev), k.to(dev), v.to(dev), out, decay=0.99, normalize=True, chunk=64)
+    torch.cuda.synchronize()
+    r = rel_l2(out_s.double().cpu().numpy(), out.double().cpu().numpy())
+    assert r <= 1e-3, r
+
+
+@pytest.mark.parametrize("d,dv,dtype,decay,normalize,prefix", [
+    (64, 64, "bf16", 0.99, False, 1000),
+    (128, 128, "bf16", 1.0, True, 777),
+    (64, 128, "bf16", 0.95, False, 64),
+    (32, 32, "f32", 0.9, True, 150),
+])
+def test_decode_resumes_from_exported_state(d, dv, dtype, decay, normalize, prefix):
+    """Forward over a prefix, export the state, decode more tokens; compare with the
+    oracle's serial pass over prefix + decoded tokens."""
+    print("case", d, dv, dtype, decay, normalize, prefix, flush=True)
+    B, H_, steps = 2, 3, 6
+    q, k, v = draw(B, H_, prefix + steps, d, dv, dtype, seed=77 + prefix)
+    _, st = gpu_forward_state(q[:, :, :prefix].contiguous(), k[:, :, :prefix].contiguous(),
+                              v[:, :, :prefix].contiguous(), decay, normalize, 64 if dtype == "bf16" else 16, 0)
+    dev = torch.device("cuda:0")
+    outs = []
+    for s in range(steps):
+        t = prefix + s
+        o = torch.empty(B, H_, dv, dtype=q.dtype, device=dev)
+        H.hla2_decode_step(st, q[:, :, t].contiguous().to(dev), k[:, :, t].contiguous().to(dev),
+                           v[:, :, t].contiguous().to(dev), o, decay=decay, normalize=normalize)
+        outs.append(o)
+    torch.cuda.synchronize()
+    o_gpu = torch.stack(outs, 2).double().cpu().numpy()
+    num, den, un, st_ref = O.serial_unorm(q.double().numpy(), k.double().numpy(), v.double().numpy(), decay)
+    tol = tol_for(dtype)
+    tail = slice(prefix, prefix + steps)
+    if normalize:
+        rep = ratio_report(o_gpu, np.zeros_like(den[..., tail]), num[..., tail, :], den[..., tail],
+                           un[..., tail], q[:, :, tail].double().numpy())
+        msg = "ratio(well) %.3g excluded %.3f" % (rep["ratio_well"], rep["excluded"])
+        ok = ratio_ok(rep, tol, subset=True)
+    else:
+        r = rel_l2(o_gpu, num[..., tail, :])
+        msg = "out %.3g" % r
+        ok = r <= tol
+    errs = state_errors(st.double().cpu().numpy(), st_ref, d, dv)
+    msg += " | " + " ".join("%s %.3g" % kv for kv in errs.items())
+    print(msg)
+    assert ok, msg
+    assert all(e <= tol for e in errs.values()), msg
