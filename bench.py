@@ -156,19 +156,22 @@ def bench_forward(w, steps, warmup, torch, H, I):
 
 
 def bench_decode(dw, steps, warmup, torch, H, prefill_tokens):
-    """Prefill every head's state by running the recurrence (the decode step
-    itself) over a random prefix, then time single-token steps."""
+    """Build every head's state from a random prefix with the chunk-parallel
+    forward pass and its final-state export, then time single-token steps."""
     dev = torch.device("cuda:0")
     g = torch.Generator(device=dev).manual_seed(dw.seed)
     L = H.hla2_state_floats(dw.d, dw.dv)
     state = torch.zeros(dw.N, dw.H, L, dtype=torch.float32, device=dev)
     s = 1.0 / math.sqrt(dw.d)
     out = torch.empty(dw.N, dw.H, dw.dv, dtype=torch.bfloat16, device=dev)
-    for _ in range(prefill_tokens):
-        q = (torch.randn(dw.N, dw.H, dw.d, generator=g, device=dev) * s).to(torch.bfloat16)
-        k = (torch.randn(dw.N, dw.H, dw.d, generator=g, device=dev) * s).to(torch.bfloat16)
-        v = (torch.randn(dw.N, dw.H, dw.dv, generator=g, device=dev) * s).to(torch.bfloat16)
-        H.hla2_decode_step(state, q, k, v, out, decay=dw.decay, normalize=dw.normalize)
+    if prefill_tokens > 0:
+        shp = (dw.N, dw.H, prefill_tokens)
+        pq = (torch.randn(*shp, dw.d, generator=g, device=dev) * s).to(torch.bfloat16)
+        pk = (torch.randn(*shp, dw.d, generator=g, device=dev) * s).to(torch.bfloat16)
+        pv = (torch.randn(*shp, dw.dv, generator=g, device=dev) * s).to(torch.bfloat16)
+        po = torch.empty_like(pv)
+        H.hla2_forward_state(pq, pk, pv, po, state, decay=dw.decay, normalize=dw.normalize, chunk=64)
+        del pq, pk, pv, po
     nsteps = dw.steps
     qs = (torch.randn(nsteps, dw.N, dw.H, dw.d, generator=g, device=dev) * s).to(torch.bfloat16)
     ks = (torch.randn(nsteps, dw.N, dw.H, dw.d, generator=g, device=dev) * s).to(torch.bfloat16)

@@ -135,3 +135,23 @@ def test_decode_resumes_from_exported_state(d, dv, dtype, decay, normalize, pref
     print(msg)
     assert ok, msg
     assert all(e <= tol for e in errs.values()), msg
+
+
+def test_decode_workload_prefix_state_sampled():
+    """The state after the decode workload's 4096-token prefix (d = dv = 64, normalised), built by the
+    forward pass with its export for two sequences x all 32 heads, matches the oracle's serial state on
+    sampled heads; the same per-head shape the benchmark prefills."""
+    w = I.DECODE
+    N = 2
+    toks = [[I.decode_prefix_tokens(w, s, h) for h in range(w.H)] for s in range(N)]
+    q = torch.stack([torch.stack([t[0] for t in row]) for row in toks])
+    k = torch.stack([torch.stack([t[1] for t in row]) for row in toks])
+    v = torch.stack([torch.stack([t[2] for t in row]) for row in toks])
+    _, st = gpu_forward_state(q, k, v, w.decay, w.normalize, 64, 0)
+    st = st.double().cpu().numpy()
+    for (s, h) in I.sample_heads(N, w.H, 4):
+        _, _, ref = O.serial(q[s, h].double().numpy(), k[s, h].double().numpy(), v[s, h].double().numpy(), w.decay)
+        errs = state_errors(st[s, h], ref, w.d, w.dv)
+        msg = "head (%d, %d): " % (s, h) + " ".join("%s %.3g" % kv for kv in errs.items())
+        print(msg)
+        assert all(e <= tol_for(w.dtype) for e in errs.values()), msg
