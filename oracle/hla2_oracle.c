@@ -441,3 +441,121 @@ int hla2_oracle_chunked(int n, int d, int dv, double gamma, int chunk,
   free(sums); free(incl); free(last);
   return 0;
 }
+
+/* ---------------------------------------------------------------------------
+ * Gradients of the forward pass (one head): the adjoint of the serial
+ * recurrence, run backwards in time.  The pages train through the scan but
+ * print no backward formulas [SUM §4]; this is the chain rule applied to the
+ * recurrence above, for the loss L = sum_t dout_t . o_t.
+ *
+ * Change of variables: U_t = S_t C_t - G_t and u_t = S_t m_t - h_t.  Expanding
+ * S_t C_t with S_t = gamma S_{t-1} + k k^T and C_t = gamma C_{t-1} + q v^T, the
+ * part gamma k (k^T C_{t-1}) is exactly G's new term, so
+ *     U_t = gamma^2 U_{t-1} + (S_t q_t) v_t^T   (and u_t with v_t -> 1).
+ * With z_t = S_t q_t and the augmented value v'_t = [v_t, 1] (dv + 1 columns),
+ *     U'_t = gamma^2 U'_{t-1} + z_t v'_t^T,   [num_t, den_t] = U'_t^T q_t.
+ * Upstream gradient of [num_t, den_t]: g'_t = [dout_t, 0] unnormalised, or
+ * [dout_t / den_t, -(dout_t . out_t) / den_t] for the ratio, where out and den
+ * are the forward's outputs (passed in, so both sides of a comparison use the
+ * same values).
+ * Adjoint states (gradients w.r.t. U'_t and S_t, including every later use):
+ *     Ubar_t = q_t g'_t^T + gamma^2 Ubar_{t+1},   zbar_t = Ubar_t v'_t,
+ *     Sbar_t = zbar_t q_t^T + gamma Sbar_{t+1},
+ *     dq_t = U'_t g'_t + S_t zbar_t   (S_t symmetric),
+ *     dv_t = (Ubar_t^T z_t)[0 .. dv-1],
+ *     dk_t = (Sbar_t + Sbar_t^T) k_t.
+ * Three passes: forward for z_t; backward for the adjoints, dk and dv; forward
+ * again (S_t, U'_t rebuilt) for dq.
+ * out, den: n*dv and n, read only when normalize = 1.
+ * ------------------------------------------------------------------------- */
+int hla2_oracle_backward_serial(int n, int d, int dv, double gamma, int normalize,
+                                const double *q, const double *k, const double *v,
+                                const double *dout, const double *out, const double *den,
+                                double *dq, double *dk, double *dvv) {
+  const int dvp = dv + 1;
+  const double g2 = gamma * gamma;
+  int t, a, b, c;
+  if (n <= 0) return 0;
+  if (normalize && (!out || !den)) return -1;
+  double *gp = (double *)calloc((size_t)n * dvp, sizeof(double));
+  double *z = (double *)calloc((size_t)n * d, sizeof(double));
+  double *zb = (double *)calloc((size_t)n * d, sizeof(double));
+  double *S = (double *)calloc((size_t)d * d, sizeof(double));
+  double *U = (double *)calloc((size_t)d * dvp, sizeof(double));
+  double *Ub = (double *)calloc((size_t)d * dvp, sizeof(double));
+  double *Sb = (double *)calloc((size_t)d * d, sizeof(double));
+  if (!gp || !z || !zb || !S || !U || !Ub || !Sb) {
+    free(gp); free(z); free(zb); free(S); free(U); free(Ub); free(Sb);
+    return -2;
+  }
+  /* upstream gradient of [num, den] */
+  for (t = 0; t < n; ++t) {
+    const double *g = dout + (long)t * dv;
+    double *gt = gp + (long)t * dvp;
+    if (normalize) {
+      double dot = 0.0;
+      for (c = 0; c < dv; ++c) dot += g[c] * out[(long)t * dv + c];
+      for (c = 0; c < dv; ++c) gt[c] = g[c] / den[t];
+      gt[dv] = -dot / den[t];
+    } else {
+      for (c = 0; c < dv; ++c) gt[c] = g[c];
+      gt[dv] = 0.0;
+    }
+  }
+  /* pass 1: z_t = S_t q_t */
+  for (t = 0; t < n; ++t) {
+    const double *qt = q + (long)t * d, *kt = k + (long)t * d;
+    for (a = 0; a < d; ++a)
+      for (b = 0; b < d; ++b) S[(long)a * d + b] = gamma * S[(long)a * d + b] + kt[a] * kt[b];
+    for (a = 0; a < d; ++a) {
+      double s = 0.0;
+      for (b = 0; b < d; ++b) s += S[(long)a * d + b] * qt[b];
+      z[(long)t * d + a] = s;
+    }
+  }
+  /* pass 2: adjoints backwards in time; dk, dv */
+  for (t = n - 1; t >= 0; --t) {
+    const double *qt = q + (long)t * d, *kt = k + (long)t * d, *vt = v + (long)t * dv;
+    const double *gt = gp + (long)t * dvp;
+    double *zbt = zb + (long)t * d;
+    for (a = 0; a < d; ++a)
+      for (c = 0; c < dvp; ++c) Ub[(long)a * dvp + c] = g2 * Ub[(long)a * dvp + c] + qt[a] * gt[c];
+    for (a = 0; a < d; ++a) {
+      double s = Ub[(long)a * dvp + dv];  /* the ones column of v' */
+      for (c = 0; c < dv; ++c) s += Ub[(long)a * dvp + c] * vt[c];
+      zbt[a] = s;
+    }
+    for (a = 0; a < d; ++a)
+      for (b = 0; b < d; ++b) Sb[(long)a * d + b] = gamma * Sb[(long)a * d + b] + zbt[a] * qt[b];
+    for (a = 0; a < d; ++a) {
+      double s = 0.0;
+      for (b = 0; b < d; ++b) s += (Sb[(long)a * d + b] + Sb[(long)b * d + a]) * kt[b];
+      dk[(long)t * d + a] = s;
+    }
+    for (c = 0; c < dv; ++c) {
+      double s = 0.0;
+      for (a = 0; a < d; ++a) s += Ub[(long)a * dvp + c] * z[(long)t * d + a];
+      dvv[(long)t * dv + c] = s;
+    }
+  }
+  /* pass 3: forward again; dq */
+  memset(S, 0, sizeof(double) * (size_t)d * d);
+  for (t = 0; t < n; ++t) {
+    const double *kt = k + (long)t * d, *vt = v + (long)t * dv;
+    const double *gt = gp + (long)t * dvp, *zt = z + (long)t * d, *zbt = zb + (long)t * d;
+    for (a = 0; a < d; ++a)
+      for (b = 0; b < d; ++b) S[(long)a * d + b] = gamma * S[(long)a * d + b] + kt[a] * kt[b];
+    for (a = 0; a < d; ++a) {
+      for (c = 0; c < dv; ++c) U[(long)a * dvp + c] = g2 * U[(long)a * dvp + c] + zt[a] * vt[c];
+      U[(long)a * dvp + dv] = g2 * U[(long)a * dvp + dv] + zt[a];
+    }
+    for (a = 0; a < d; ++a) {
+      double s = 0.0;
+      for (c = 0; c < dvp; ++c) s += U[(long)a * dvp + c] * gt[c];
+      for (b = 0; b < d; ++b) s += S[(long)a * d + b] * zbt[b];
+      dq[(long)t * d + a] = s;
+    }
+  }
+  free(gp); free(z); free(zb); free(S); free(U); free(Ub); free(Sb);
+  return 0;
+}

@@ -10,7 +10,9 @@ before (n, d) are independent heads; they are spread over a thread pool (the C
 calls release the GIL), one head per task, each head computed serially.
 
 What the C code computes, and the page passages it follows, is written out in
-the header of ``hla2_oracle.c``.
+the header of ``hla2_oracle.c``.  ``backward`` (numpy, the chain rule through the
+definition in matrix form) and ``backward_serial`` (C, the adjoint of the serial
+recurrence) give the gradients; the pages print none, so both are derived here.
 """
 from __future__ import annotations
 
@@ -75,6 +77,9 @@ def _load(path: str | None = None):
             lib.hla2_oracle_exclusive_scan.argtypes = [i, i, i, _dp]
             lib.hla2_oracle_chunked.restype = i
             lib.hla2_oracle_chunked.argtypes = [i, i, i, d_, i, _dp, _dp, _dp, _dp, _dp, _dp]
+            lib.hla2_oracle_backward_serial.restype = i
+            lib.hla2_oracle_backward_serial.argtypes = [i, i, i, d_, i, _dp, _dp, _dp, _dp, _dp, _dp, _dp,
+                                                        _dp, _dp]
             _libs[key] = lib
     return lib
 
@@ -279,3 +284,97 @@ def ratio(num, den):
     """o = num / den with IEEE semantics (no epsilon)."""
     with np.errstate(divide="ignore", invalid="ignore"):
         return np.asarray(num) / np.asarray(den)[..., None]
+
+
+def _upstream(dout, gamma, normalize, out, den, q, k, v, lib):
+    """out and den for the ratio's upstream gradient: the ones given, else the forward's."""
+    if not normalize:
+        return None, None
+    if out is None or den is None:
+        num, den_, _ = serial(q, k, v, gamma, lib=lib)
+        out = ratio(num, den_) if out is None else out
+        den = den_ if den is None else den
+    return _f64(out), _f64(den)
+
+
+def backward(q, k, v, dout, gamma: float = 1.0, normalize: bool = False, out=None, den=None,
+             threads: int | None = None):
+    """Gradients (dq, dk, dv) of L = sum(dout * o) by the chain rule through the
+    definition, in matrix form, per head (memory and time grow as n^2 and n^3:
+    for small n only).
+
+    Forward, as defined for the oracle (0-based t, lower triangles include the
+    diagonal): A = L o (Q K^T), D[t, i] = gamma^(t - i) for t >= i (else 0),
+    A_g = D o A, M = D o L o (A_g A^T), num = M V, den = M 1, o = num or num / den.
+    Backward of a loss with upstream g_num, g_den (g_num = dout, g_den = 0
+    unnormalised; g_num = dout / den, g_den = -(dout . out) / den for the ratio,
+    with out and den the forward's outputs, given or computed here):
+        dV = M^T g_num,   dM = L o (g_num V^T + g_den 1^T),   P = D o dM,
+        dA_g = P A,       dA = P^T A_g + D o dA_g,            dX = L o dA,
+        dQ = dX K,        dK = dX^T Q            (X = Q K^T, the raw scores).
+    The pages print no backward formulas; this is the definition's chain rule.
+    """
+    lib = _load()
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    out, den = _upstream(dout, gamma, normalize, out, den, q, k, v, lib)
+    *lead, n, d = q.shape
+    dv = v.shape[-1]
+    H = int(np.prod(lead)) if lead else 1
+    qh, kh, vh, gh = q.reshape(H, n, d), k.reshape(H, n, d), v.reshape(H, n, dv), dout.reshape(H, n, dv)
+    oh = out.reshape(H, n, dv) if normalize else None
+    dh = den.reshape(H, n) if normalize else None
+    t = np.arange(n)
+    lower = t[:, None] >= t[None, :]
+    D = np.where(lower, float(gamma) ** np.maximum(t[:, None] - t[None, :], 0), 0.0)
+    dq, dk, dvv = np.empty((H, n, d)), np.empty((H, n, d)), np.empty((H, n, dv))
+
+    def one(h):
+        Q, K, V, G = qh[h], kh[h], vh[h], gh[h]
+        A = np.where(lower, Q @ K.T, 0.0)
+        Ag = D * A
+        M = D * np.where(lower, Ag @ A.T, 0.0)
+        if normalize:
+            gnum = G / dh[h][:, None]
+            gden = -np.sum(G * oh[h], axis=-1) / dh[h]
+        else:
+            gnum, gden = G, np.zeros(n)
+        dvv[h] = M.T @ gnum
+        dM = np.where(lower, gnum @ V.T + gden[:, None], 0.0)
+        P = D * dM
+        dAg = P @ A
+        dA = P.T @ Ag + D * dAg
+        dX = np.where(lower, dA, 0.0)
+        dq[h] = dX @ K
+        dk[h] = dX.T @ Q
+
+    _run_heads(one, H, threads)
+    lt = tuple(lead)
+    return dq.reshape(lt + (n, d)), dk.reshape(lt + (n, d)), dvv.reshape(lt + (n, dv))
+
+
+def backward_serial(q, k, v, dout, gamma: float = 1.0, normalize: bool = False, out=None, den=None,
+                    threads: int | None = None, lib=None):
+    """Gradients (dq, dk, dv) of L = sum(dout * o) by the adjoint of the serial
+    recurrence (``hla2_oracle_backward_serial``): O(n (d^2 + d dv)) per head, for
+    any n.  out and den as for ``backward``."""
+    lib = lib or _load()
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    out, den = _upstream(dout, gamma, normalize, out, den, q, k, v, lib)
+    *lead, n, d = q.shape
+    dv = v.shape[-1]
+    H = int(np.prod(lead)) if lead else 1
+    qh, kh, vh, gh = q.reshape(H, n, d), k.reshape(H, n, d), v.reshape(H, n, dv), dout.reshape(H, n, dv)
+    oh = np.ascontiguousarray(out.reshape(H, n, dv)) if normalize else None
+    dh = np.ascontiguousarray(den.reshape(H, n)) if normalize else None
+    dq, dk, dvv = np.empty((H, n, d)), np.empty((H, n, d)), np.empty((H, n, dv))
+
+    def one(h):
+        rc = lib.hla2_oracle_backward_serial(n, d, dv, float(gamma), int(bool(normalize)), _p(qh[h]), _p(kh[h]),
+                                             _p(vh[h]), _p(gh[h]), _p(oh[h]) if normalize else None,
+                                             _p(dh[h]) if normalize else None, _p(dq[h]), _p(dk[h]), _p(dvv[h]))
+        assert rc == 0
+
+    _run_heads(one, H, threads)
+    lt = tuple(lead)
+    return dq.reshape(lt + (n, d)), dk.reshape(lt + (n, d)), dvv.reshape(lt + (n, dv))
+
