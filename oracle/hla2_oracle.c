@@ -473,7 +473,7 @@ int hla2_oracle_backward_serial(int n, int d, int dv, double gamma, int normaliz
                                 const double *dout, const double *out, const double *den,
                                 double *dq, double *dk, double *dvv) {
   const int dvp = dv + 1;
-  const double g2 = gamma * gamma;
+  const double gsq = gamma * gamma;
   int t, a, b, c;
   if (n <= 0) return 0;
   if (normalize && (!out || !den)) return -1;
@@ -519,7 +519,7 @@ int hla2_oracle_backward_serial(int n, int d, int dv, double gamma, int normaliz
     const double *gt = gp + (long)t * dvp;
     double *zbt = zb + (long)t * d;
     for (a = 0; a < d; ++a)
-      for (c = 0; c < dvp; ++c) Ub[(long)a * dvp + c] = g2 * Ub[(long)a * dvp + c] + qt[a] * gt[c];
+      for (c = 0; c < dvp; ++c) Ub[(long)a * dvp + c] = gsq * Ub[(long)a * dvp + c] + qt[a] * gt[c];
     for (a = 0; a < d; ++a) {
       double s = Ub[(long)a * dvp + dv];  /* the ones column of v' */
       for (c = 0; c < dv; ++c) s += Ub[(long)a * dvp + c] * vt[c];
@@ -546,8 +546,8 @@ int hla2_oracle_backward_serial(int n, int d, int dv, double gamma, int normaliz
     for (a = 0; a < d; ++a)
       for (b = 0; b < d; ++b) S[(long)a * d + b] = gamma * S[(long)a * d + b] + kt[a] * kt[b];
     for (a = 0; a < d; ++a) {
-      for (c = 0; c < dv; ++c) U[(long)a * dvp + c] = g2 * U[(long)a * dvp + c] + zt[a] * vt[c];
-      U[(long)a * dvp + dv] = g2 * U[(long)a * dvp + dv] + zt[a];
+      for (c = 0; c < dv; ++c) U[(long)a * dvp + c] = gsq * U[(long)a * dvp + c] + zt[a] * vt[c];
+      U[(long)a * dvp + dv] = gsq * U[(long)a * dvp + dv] + zt[a];
     }
     for (a = 0; a < d; ++a) {
       double s = 0.0;

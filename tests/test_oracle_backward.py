@@ -157,14 +157,14 @@ def test_given_forward_outputs_are_used():
 
 
 MUTANTS_C = {
-    "Ubar decays by gamma": ("Ub[(long)a * dvp + c] = g2 * Ub[(long)a * dvp + c] + qt[a] * gt[c];",
+    "Ubar decays by gamma": ("Ub[(long)a * dvp + c] = gsq * Ub[(long)a * dvp + c] + qt[a] * gt[c];",
                              "Ub[(long)a * dvp + c] = gamma * Ub[(long)a * dvp + c] + qt[a] * gt[c];"),
     "zbar drops the ones column": ("double s = Ub[(long)a * dvp + dv];  /* the ones column of v' */",
                                    "double s = 0.0;"),
     "dk without the transpose": ("s += (Sb[(long)a * d + b] + Sb[(long)b * d + a]) * kt[b];",
                                  "s += 2.0 * Sb[(long)a * d + b] * kt[b];"),
     "Sbar decays by gamma^2": ("Sb[(long)a * d + b] = gamma * Sb[(long)a * d + b] + zbt[a] * qt[b];",
-                               "Sb[(long)a * d + b] = g2 * Sb[(long)a * d + b] + zbt[a] * qt[b];"),
+                               "Sb[(long)a * d + b] = gsq * Sb[(long)a * d + b] + zbt[a] * qt[b];"),
     "dq drops S zbar": ("for (b = 0; b < d; ++b) s += S[(long)a * d + b] * zbt[b];\n      dq",
                         "for (b = 0; b < 0; ++b) s += S[(long)a * d + b] * zbt[b];\n      dq"),
     "ratio gradient of den squared": ("gt[dv] = -dot / den[t];", "gt[dv] = -dot / (den[t] * den[t]);"),
