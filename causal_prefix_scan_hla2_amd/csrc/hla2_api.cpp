@@ -36,7 +36,7 @@ int check_shape(int B, int H, int n, int d, int dv, int chunk, int dtype) {
   return HLA2_OK;
 }
 
-Plan make_plan(int B, int H, int n, int d, int dv, int chunk, int dtype, int segments = 0) {
+Plan make_plan(int B, int H, int n, int d, int dv, int chunk, int dtype, int segments = 0, long groups_per_cu = 0) {
   Plan p;
   p.BH = (long)B * H;
   long gpc;  // workgroups of the output walker per CU
@@ -53,6 +53,7 @@ Plan make_plan(int B, int H, int n, int d, int dv, int chunk, int dtype, int seg
     p.kc = chunk;
     gpc = hla2::walk_groups_per_cu(4, p.DK, p.DV, p.CP, true);
   }
+  if (groups_per_cu > 0) gpc = groups_per_cu;
   const long nc = ((long)n + p.kc - 1) / p.kc;
   const long target = kComputeUnits * gpc;
   long r = segments > 0 ? segments : (target + p.BH - 1) / p.BH;
@@ -81,6 +82,42 @@ size_t prefix_bytes(const Plan &p) {
 size_t workspace_bytes(const Plan &p, bool state = false) {
   if (p.nseg == 1 && !state) return 0;
   return align256(sums_bytes(p, state)) + prefix_bytes(p);
+}
+
+// Backward pass: the forward's segment plan (its summary walk and scan give each segment's
+// incoming state), walked again in chunks of BC tokens.  The backward walkers hold one
+// workgroup per CU.
+struct BwdPlan {
+  Plan p;
+  int BC, DVP, nbc;
+  bool norm;
+  size_t off_fsum, off_prefix, off_cst, off_rsum, off_suffix, off_gprep, total;
+};
+BwdPlan make_bwd_plan(int B, int H, int n, int d, int dv, int dtype, int normalize, int segments) {
+  BwdPlan b;
+  const int chunk = dtype == HLA2_BF16 ? 64 : 32;
+  b.p = make_plan(B, H, n, d, dv, chunk, dtype, segments, 1);
+  b.norm = normalize != 0;
+  b.BC = hla2::bwd_chunk(dtype == HLA2_F32 ? 0 : 1, b.p.DK);
+  b.DVP = hla2::bwd_dvp(dtype == HLA2_F32 ? 0 : 1, b.p.DV, b.norm);
+  b.nbc = (n + b.BC - 1) / b.BC;
+  const size_t es = dtype == HLA2_F32 ? 4 : 2, BH = (size_t)b.p.BH, R = (size_t)b.p.nseg;
+  const size_t DK = (size_t)b.p.DK, DVP = (size_t)b.DVP, adj = (DK * DVP + DK * DK) * 4;
+  size_t o = 0;
+  b.off_fsum = o;
+  o += align256(BH * (R - 1) * (size_t)hla2::sum_block_floats(b.p.DK, b.p.DV) * 4);
+  b.off_prefix = o;
+  o += R > 1 ? align256(BH * R * (size_t)hla2::prefix_block_floats(b.p.DK, b.p.DV) * 4) : 0;
+  b.off_cst = o;
+  o += align256(BH * (size_t)b.nbc * (DK * DK + DK * DVP) * es);
+  b.off_rsum = o;
+  o += align256(BH * R * adj);
+  b.off_suffix = o;
+  o += align256(BH * R * adj);
+  b.off_gprep = o;
+  o += b.norm ? align256(BH * (size_t)n * DVP * es) : 0;
+  b.total = o;
+  return b;
 }
 
 // Shared body of every forward entry point (arguments already validated).
@@ -178,6 +215,115 @@ int hla2_forward_state(const void *q, const void *k, const void *v, void *out, i
   if (!state_out) return HLA2_ERR_INVALID;
   return run_forward(q, k, v, out, B, H, n, d, dv, decay, normalize, chunk, dtype, den_out, state_out, workspace,
                      workspace_bytes_given, segments, nullptr, stream);
+}
+
+size_t hla2_backward_workspace_bytes(int B, int H, int n, int d, int dv, int normalize, hla2_dtype_t dtype,
+                                     int segments) {
+  if (segments < 0 || (normalize != 0 && normalize != 1)) return 0;
+  const int chunk = dtype == HLA2_BF16 ? 64 : 32;
+  if (check_shape(B, H, n, d, dv, chunk, (int)dtype) != HLA2_OK) return 0;
+  return make_bwd_plan(B, H, n, d, dv, (int)dtype, normalize, segments).total;
+}
+
+int hla2_backward(const void *q, const void *k, const void *v, const void *out, const float *den, const void *dout,
+                  void *grad_q, void *grad_k, void *grad_v, int B, int H, int n, int d, int dv, float decay,
+                  int normalize, hla2_dtype_t dtype, void *workspace, size_t workspace_bytes_given, int segments,
+                  hipStream_t stream) {
+  if (!q || !k || !v || !dout || !grad_q || !grad_k || !grad_v) return HLA2_ERR_INVALID;
+  if (normalize != 0 && normalize != 1) return HLA2_ERR_INVALID;
+  if (normalize && (!out || !den)) return HLA2_ERR_INVALID;
+  if (segments < 0) return HLA2_ERR_INVALID;
+  if (!(decay > 0.0f && decay <= 1.0f)) return HLA2_ERR_INVALID;
+  if (dtype != HLA2_F32 && dtype != HLA2_BF16) return HLA2_ERR_INVALID;
+  const int chunk = dtype == HLA2_BF16 ? 64 : 32;
+  int rc = check_shape(B, H, n, d, dv, chunk, (int)dtype);
+  if (rc != HLA2_OK) return rc;
+  const void *tens[] = {q, k, v, dout, grad_q, grad_k, grad_v};
+  for (const void *t : tens)
+    if (!aligned(t, 16)) return HLA2_ERR_INVALID;
+  if (normalize && (!aligned(out, 16) || !aligned(den, 4))) return HLA2_ERR_INVALID;
+  const BwdPlan b = make_bwd_plan(B, H, n, d, dv, (int)dtype, normalize, segments);
+  if (!workspace || workspace_bytes_given < b.total || !aligned(workspace, 256)) return HLA2_ERR_WORKSPACE;
+  const Plan &p = b.p;
+  const int dt = dtype == HLA2_F32 ? 0 : 1;
+  char *ws = (char *)workspace;
+  float *fsum = (float *)(ws + b.off_fsum), *prefix = p.nseg > 1 ? (float *)(ws + b.off_prefix) : nullptr;
+  const float log2g = decay < 1.0f ? log2f(decay) : 0.0f;
+  hipError_t e;
+
+  hla2::BwdPrepArgs pa;
+  pa.dout = dout;
+  pa.out = out;
+  pa.den = den;
+  pa.gprep = ws + b.off_gprep;
+  pa.rows = p.BH * n;
+  pa.dv = dv;
+  if (b.norm) {
+    e = hla2::launch_bwd(dt, p.DK, p.DV, true, hla2::BWD_PREP, (int)p.BH, hla2::BwdArgs{}, pa, 1.f, stream);
+    if (e != hipSuccess) return HLA2_ERR_LAUNCH;
+  }
+  // incoming forward state of every segment: the forward's summary walk and scan
+  if (p.nseg > 1) {
+    hla2::WalkArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = nullptr;
+    a.den_out = nullptr;
+    a.prefix = nullptr;
+    a.sums = fsum;
+    a.n = n;
+    a.d = d;
+    a.dv = dv;
+    a.chunk = p.kc;
+    a.cps = p.cps;
+    a.nseg = p.nseg;
+    a.log2g = log2g;
+    a.decay_on = decay < 1.0f ? 1 : 0;
+    a.normalize = normalize;
+    a.need_den = normalize;
+    a.sum_all = 0;
+    e = hla2::launch_walk(dt, p.DK, p.DV, p.CP, false, dim3((unsigned)(p.BH * (p.nseg - 1))), a, stream);
+    if (e != hipSuccess) return HLA2_ERR_LAUNCH;
+    hla2::ScanArgs sa;
+    sa.sums = fsum;
+    sa.nsum = p.nseg - 1;
+    sa.prefix = prefix;
+    sa.nseg = p.nseg;
+    sa.gamma_seg = decay < 1.0f ? (float)pow((double)decay, (double)p.cps * p.kc) : 1.0f;
+    e = hla2::launch_scan(dt, p.DK, p.DV, (int)p.BH, sa, stream);
+    if (e != hipSuccess) return HLA2_ERR_LAUNCH;
+  }
+  hla2::BwdArgs ba;
+  ba.q = q;
+  ba.k = k;
+  ba.v = v;
+  ba.g = b.norm ? (const void *)(ws + b.off_gprep) : dout;
+  ba.dq_out = grad_q;
+  ba.dk_out = grad_k;
+  ba.dv_out = grad_v;
+  ba.prefix = prefix;
+  ba.fsum = fsum;
+  ba.cstate = ws + b.off_cst;
+  ba.rsum = (float *)(ws + b.off_rsum);
+  ba.suffix = (float *)(ws + b.off_suffix);
+  ba.n = n;
+  ba.d = d;
+  ba.dv = dv;
+  ba.gld = b.norm ? b.DVP : dv;
+  ba.nseg = p.nseg;
+  ba.cps = p.cps;
+  ba.kc = p.kc;
+  ba.nbc = b.nbc;
+  ba.log2g = log2g;
+  const float gL = decay < 1.0f ? (float)pow((double)decay, (double)p.cps * p.kc) : 1.0f;
+  const int phases[] = {hla2::BWD_STATE, hla2::BWD_RSUM, hla2::BWD_RSCAN, hla2::BWD_WALK};
+  for (int ph : phases) {
+    if (ph == hla2::BWD_RSUM && p.nseg == 1) continue;
+    e = hla2::launch_bwd(dt, p.DK, p.DV, b.norm, ph, (int)p.BH, ba, pa, gL, stream);
+    if (e != hipSuccess) return HLA2_ERR_LAUNCH;
+  }
+  return HLA2_OK;
 }
 
 int hla2_decode_step(float *state, const void *q, const void *k, const void *v, void *out, int N, int H,

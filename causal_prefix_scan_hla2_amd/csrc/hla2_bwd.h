@@ -1,0 +1,480 @@
+// hla2_bwd.h -- chunk walkers of the backward pass: the gradients of the
+// masked second-order HLA forward with respect to q, k and v.
+//
+// The pages train through the scan (technical summary of arXiv 2510.27258 on
+// gist.science, §4) but print no gradient, so these kernels run the adjoint of
+// the chunked forward, derived by the chain rule.  With U' = [SC - G | Sm - h]
+// (the corrected state, one column per value plus one for the denominator),
+// v' = [v | 1] and g' the upstream gradient of [num | den], the forward and its
+// adjoint per token are
+//   S_t = g S_{t-1} + k k^T,   z_t = S_t q_t,   U'_t = g^2 U'_{t-1} + z_t v'^T,
+//   Ubar_t = q_t g'^T + g^2 Ubar_{t+1},  zbar_t = Ubar_t v'_t,
+//   Shat_t = zbar_t q_t^T + q_t zbar_t^T + g Shat_{t+1}          (Shat = Sbar + Sbar^T)
+//   dq_t = U'_t g'_t + S_t zbar_t,  dv_t = Ubar_t^T z_t,  dk_t = Shat_t k_t.
+// Per chunk of BC tokens (local index tau, lower triangles include the
+// diagonal, D1[t][i] = g^(t-i), D2 = D1 o D1), from the forward state (S0, U0')
+// at the chunk start and the adjoint state (Ubar, Shat) at the chunk end:
+//   Ad = L o D1 o (Q K^T),  Bm = L o D2 o (G' V'^T),
+//   Z  = diag(g^(tau+1)) Q S0 + Ad K,
+//   Zb = Bm^T Q + diag(g^(2(BC-tau))) V' Ubar^T,
+//   W  = L o D2 o (Q Z^T),  Ek = L o D1 o (Zb K^T),
+//   dV' = W^T G' + diag(g^(2(BC-tau))) Z Ubar,
+//   dQ  = diag(g^(tau+1)) [diag(g^(tau+1)) G' U0'^T + Zb S0] + Bm Z + Ek K,
+//   dK  = Ad^T Zb + Ek^T Q + diag(g^(BC-tau)) K Shat,
+// and the states move on as
+//   S   <- g^BC S + K^T diag(g^(BC-1-i)) K,   U' <- g^(2BC) U' + Z^T diag(g^(2(BC-1-tau))) V',
+//   Ubar <- g^(2BC) Ubar + Q^T diag(g^(2 tau)) G',
+//   Shat <- g^BC Shat + Zb^T diag(g^tau) Q + Q^T diag(g^tau) Zb.
+// Tokens past the end are zero rows in Q, K, V' (its ones column too) and G',
+// so a ragged last chunk takes the same path.
+//
+// Kernels (one 256-thread workgroup per (b, h, segment), 4 waves):
+//   bwd_state_kernel   walks a segment forwards from its scanned prefix and
+//                      writes every chunk's (S0, U0') in the element type;
+//   bwd_rsum_kernel    walks a segment backwards from a zero adjoint state and
+//                      writes its adjoint summary (Ubar, Shat);
+//   bwd_walk_kernel    walks a segment backwards from its scanned adjoint
+//                      state, reads the stored forward states and writes
+//                      dq, dk, dv.
+// Every product is a set of 16x16 MFMA tiles computed transposed, so that a
+// lane holds four consecutive columns of one row of the result; each wave
+// takes every fourth tile.  MFMAs never sit under a runtime branch: tile
+// loops have compile-time trip counts, and a wave with no tile left repeats
+// the last one without storing it.
+#pragma once
+#include "hla2_internal.h"
+#include "hla2_mfma.h"
+
+namespace hla2 {
+
+// ---------------------------------------------------------------------------
+// Tile products.  mm: acc(m0.., n0..) += sum_k A(m, k) B(k, n) over k < K, with
+// A(m, k) = AT ? A[k*lda + m] : A[m*lda + k] and B(k, n) = BT ? B[n*ldb + k] : B[k*ldb + n].
+// A transposed A or a non-transposed B is read with the LDS transpose read, so
+// those operands must live in LDS; the others may be global.  wk(k) scales the
+// k-th term.
+template <bool AT, bool BT, int K, typename T, typename WF>
+__device__ __forceinline__ f32x4 mmw(f32x4 acc, const T *A, int lda, const T *B, int ldb, int m0, int n0,
+                                     int lane, WF &&wk) {
+  constexpr int KT = Ktile<T>::ROWS;
+  static_assert(K % KT == 0, "contraction length must be a whole number of k-tiles");
+  const int g = lane >> 4;
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += KT) {
+    auto a = AT ? ld_cols(A, lda, k0, m0, lane) : ld_rows(A, lda, m0, k0, lane);
+    auto b = BT ? ld_rows(B, ldb, n0, k0, lane) : ld_cols(B, ldb, k0, n0, lane);
+    a = scale_frag(a, g, [&](int kk) { return wk(k0 + kk); });
+    acc = mma(a, b, acc);
+  }
+  return acc;
+}
+template <bool AT, bool BT, int K, typename T>
+__device__ __forceinline__ f32x4 mm(f32x4 acc, const T *A, int lda, const T *B, int ldb, int m0, int n0,
+                                    int lane) {
+  constexpr int KT = Ktile<T>::ROWS;
+  static_assert(K % KT == 0, "contraction length must be a whole number of k-tiles");
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += KT) {
+    auto a = AT ? ld_cols(A, lda, k0, m0, lane) : ld_rows(A, lda, m0, k0, lane);
+    auto b = BT ? ld_rows(B, ldb, n0, k0, lane) : ld_cols(B, ldb, k0, n0, lane);
+    acc = mma(a, b, acc);
+  }
+  return acc;
+}
+// Tile of P = X Y at P-rows i0.., P-columns j0.., computed as P^T so that lane
+// (g, n) holds P[i0 + n][j0 + 4g + e], e = 0..3.  XT: X(i, k) stored at X[k*ldx + i];
+// YT: Y(k, j) stored at Y[j*ldy + k].
+template <bool XT, bool YT, int K, typename T>
+__device__ __forceinline__ f32x4 pt(f32x4 acc, const T *X, int ldx, const T *Y, int ldy, int i0, int j0, int lane) {
+  return mm<!YT, !XT, K>(acc, Y, ldy, X, ldx, j0, i0, lane);
+}
+// the same with weights w(k) on the contraction index: P = X diag(w) Y
+template <bool XT, bool YT, int K, typename T, typename WF>
+__device__ __forceinline__ f32x4 ptw(f32x4 acc, const T *X, int ldx, const T *Y, int ldy, int i0, int j0, int lane,
+                                     WF &&wk) {
+  return mmw<!YT, !XT, K>(acc, Y, ldy, X, ldx, j0, i0, lane, wk);
+}
+
+// Iterate a wave's share of the 16x16 tiles of an I x J result: f(i0, j0, store_ok).
+template <int I, int J, typename F>
+__device__ __forceinline__ void for_tiles(int w, F &&f) {
+  constexpr int NJ = J / 16, NT = (I / 16) * NJ, PER = (NT + 3) / 4;
+#pragma unroll
+  for (int it = 0; it < PER; ++it) {
+    const int t = w + 4 * it;
+    const int tt = t < NT ? t : NT - 1;
+    f(16 * (tt / NJ), 16 * (tt % NJ), t < NT, it);
+  }
+}
+template <int I, int J> struct TileCount {
+  static constexpr int NT = (I / 16) * (J / 16), PER = (NT + 3) / 4;
+};
+
+// 16-byte vector of the element type
+template <typename T> struct Vec16;
+template <> struct Vec16<bf16> {
+  typedef bf16x8 type;
+  static constexpr int N = 8;
+};
+template <> struct Vec16<float> {
+  typedef f32x4 type;
+  static constexpr int N = 4;
+};
+
+// LDS layout of the backward walkers.  Row pitches carry 16 bytes of padding.
+template <typename T, int DK, int DVP, int BC>
+struct BwdCfg {
+  static constexpr int PAD = 16 / sizeof(T);
+  static constexpr int LDQ = DK + PAD;   // Q, K, Z, Zb rows; S / Shat copy rows
+  static constexpr int LDV = DVP + PAD;  // V', G' rows; Ubar / U' copy rows
+  static constexpr int LDC = BC + PAD;   // BC x BC masks
+  static constexpr int Q_OFF = 0, K_OFF = Q_OFF + BC * LDQ, V_OFF = K_OFF + BC * LDQ,
+                       G_OFF = V_OFF + BC * LDV, U_OFF = G_OFF + BC * LDV, S_OFF = U_OFF + DK * LDV,
+                       AD_OFF = S_OFF + DK * LDQ, BM_OFF = AD_OFF + BC * LDC, W_OFF = BM_OFF + BC * LDC,
+                       EK_OFF = W_OFF + BC * LDC, Z_OFF = EK_OFF + BC * LDC, ZB_OFF = Z_OFF + BC * LDQ,
+                       ELEMS = ZB_OFF + BC * LDQ;
+  static constexpr int BLOCK = DK * DK + DK * DVP;  // stored chunk state S0 | U0' (elements)
+};
+
+// Copy rows [t0, t0+BC) of a [n][gc] global matrix into LDS rows of width W
+// (zero past n and past column gc; with ones >= 0, column `ones` holds 1 for
+// rows before n).
+template <typename T, int BC, int W>
+__device__ __forceinline__ void load_rows(T *dst, int ld, const T *src, int gc, int t0, int n, int ones, int tid) {
+  typedef typename Vec16<T>::type V;
+  constexpr int VN = Vec16<T>::N, PERROW = W / VN, TOT = BC * PERROW;
+#pragma unroll
+  for (int i = tid; i < TOT; i += 256) {
+    const int r = i / PERROW, c = (i % PERROW) * VN, t = t0 + r;
+    V x{};
+    if (t < n && c < gc) x = *(const V *)(src + (long)t * gc + c);
+    if (c == ones && t < n) x[0] = (T)1.f;
+    *(V *)(dst + r * ld + c) = x;
+  }
+}
+
+// Store four consecutive values of row t, columns c .. c+3, of a [n][ncols] matrix.
+__device__ __forceinline__ void st_out(bf16 *dst, int ncols, int t, int c, int n, f32x4 x) {
+  if (t < n && c < ncols) *(bf16x4 *)(dst + (long)t * ncols + c) = bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
+}
+__device__ __forceinline__ void st_out(float *dst, int ncols, int t, int c, int n, f32x4 x) {
+  if (t < n && c < ncols) *(f32x4 *)(dst + (long)t * ncols + c) = x;
+}
+__device__ __forceinline__ void st4g(bf16 *p, f32x4 x) { *(bf16x4 *)p = bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]}; }
+__device__ __forceinline__ void st4g(float *p, f32x4 x) { *(f32x4 *)p = x; }
+
+// ---------------------------------------------------------------------------
+// Forward state of every chunk: S0 and U0' at the chunk start, in the element
+// type (the precision the gradient kernel's products consume).
+template <typename T, int DK, int DV, int DVP, int BC, bool NORM>
+__global__ void __launch_bounds__(256) bwd_state_kernel(BwdArgs a) {
+  using Cfg = BwdCfg<T, DK, DVP, BC>;
+  __shared__ __attribute__((aligned(16))) T smem[Cfg::ELEMS];
+  __shared__ float pw[2 * BC + 3];
+  T *const Qs = smem + Cfg::Q_OFF, *const Ks = smem + Cfg::K_OFF, *const Vs = smem + Cfg::V_OFF;
+  T *const Ss = smem + Cfg::S_OFF, *const Ads = smem + Cfg::AD_OFF, *const Zs = smem + Cfg::Z_OFF;
+  const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 4, nn = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int bh = blockIdx.x / a.nseg, seg = blockIdx.x % a.nseg;
+  const int tok0 = seg * a.cps * a.kc, tokE = min(a.n, tok0 + a.cps * a.kc);
+  const int nch = (tokE - tok0 + BC - 1) / BC, c0 = tok0 / BC;
+  const T *qh = (const T *)a.q + (long)bh * a.n * a.d, *kh = (const T *)a.k + (long)bh * a.n * a.d;
+  const T *vh = (const T *)a.v + (long)bh * a.n * a.dv;
+  T *cst = (T *)a.cstate + ((long)bh * a.nbc + c0) * Cfg::BLOCK;
+  for (int e = tid; e < 2 * BC + 3; e += 256) pw[e] = exp2f((float)e * a.log2g);
+
+  using TS = TileCount<DK, DK>;
+  using TU = TileCount<DK, DVP>;
+  f32x4 S[TS::PER], U[TU::PER];
+  // incoming state from the scanned prefix (zero for the first segment)
+  const float *pref = (a.prefix && seg > 0) ? a.prefix + ((long)bh * a.nseg + seg) * prefix_block_floats(DK, DV) : nullptr;
+  for_tiles<DK, DK>(w, [&](int i0, int j0, bool, int it) {
+    S[it] = pref ? *(const f32x4 *)(pref + (i0 + nn) * DK + j0 + 4 * gq) : zero4();
+  });
+  for_tiles<DK, DVP>(w, [&](int i0, int j0, bool, int it) {
+    f32x4 x = zero4();
+    if (pref) {
+      const int r = i0 + nn, c = j0 + 4 * gq;
+      if (c < DV) x = *(const f32x4 *)(pref + DK * DK + r * DV + c);
+      else if (NORM && c == DV) x[0] = pref[DK * DK + DK * DV + r];
+    }
+    U[it] = x;
+  });
+  __syncthreads();  // pw
+
+  for (int ch = 0; ch < nch; ++ch) {
+    const int t0 = tok0 + ch * BC;
+    // state at the chunk start: bf16/fp32 copy of S into LDS and both into the chunk store
+    T *blk = cst + (long)ch * Cfg::BLOCK;
+    for_tiles<DK, DK>(w, [&](int i0, int j0, bool ok, int it) {
+      if (ok) {
+        st4(Ss + (i0 + nn) * Cfg::LDQ + j0 + 4 * gq, S[it]);
+        st4g(blk + (i0 + nn) * DK + j0 + 4 * gq, S[it]);
+      }
+    });
+    for_tiles<DK, DVP>(w, [&](int i0, int j0, bool ok, int it) {
+      if (ok) st4g(blk + DK * DK + (i0 + nn) * DVP + j0 + 4 * gq, U[it]);
+    });
+    load_rows<T, BC, DK>(Qs, Cfg::LDQ, qh, a.d, t0, a.n, -1, tid);
+    load_rows<T, BC, DK>(Ks, Cfg::LDQ, kh, a.d, t0, a.n, -1, tid);
+    load_rows<T, BC, DVP>(Vs, Cfg::LDV, vh, a.dv, t0, a.n, NORM ? DV : -1, tid);
+    __syncthreads();
+    // Ad = L o D1 o (Q K^T)
+    for_tiles<BC, BC>(w, [&](int i0, int j0, bool ok, int) {
+      f32x4 x = pt<false, true, DK>(zero4(), Qs, Cfg::LDQ, Ks, Cfg::LDQ, i0, j0, lane);
+      const int tr = i0 + nn;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int ti = j0 + 4 * gq + e;
+        x[e] = ti <= tr ? x[e] * pw[tr - ti] : 0.f;
+      }
+      if (ok) st4(Ads + tr * Cfg::LDC + j0 + 4 * gq, x);
+    });
+    __syncthreads();
+    // Z = diag(g^(tau+1)) Q S0 + Ad K
+    for_tiles<BC, DK>(w, [&](int i0, int j0, bool ok, int) {
+      f32x4 x = pt<false, true, DK>(zero4(), Qs, Cfg::LDQ, Ss, Cfg::LDQ, i0, j0, lane);
+      x *= pw[i0 + nn + 1];
+      x = pt<false, false, BC>(x, Ads, Cfg::LDC, Ks, Cfg::LDQ, i0, j0, lane);
+      if (ok) st4(Zs + (i0 + nn) * Cfg::LDQ + j0 + 4 * gq, x);
+    });
+    __syncthreads();
+    // S <- g^BC S + K^T diag(g^(BC-1-i)) K;  U' <- g^(2BC) U' + Z^T diag(g^(2(BC-1-tau))) V'
+    const float gB = pw[BC], gB2 = pw[2 * BC];
+    for_tiles<DK, DK>(w, [&](int i0, int j0, bool, int it) {
+      S[it] = ptw<true, false, BC>(gB * S[it], Ks, Cfg::LDQ, Ks, Cfg::LDQ, i0, j0, lane,
+                                   [&](int i) { return pw[BC - 1 - i]; });
+    });
+    for_tiles<DK, DVP>(w, [&](int i0, int j0, bool, int it) {
+      U[it] = ptw<true, false, BC>(gB2 * U[it], Zs, Cfg::LDQ, Vs, Cfg::LDV, i0, j0, lane,
+                                   [&](int t) { return pw[2 * (BC - 1 - t)]; });
+    });
+    __syncthreads();  // every read of Ss, Qs, Ks, Vs, Zs done before the next chunk overwrites them
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Shared adjoint step: Bm, Zb into LDS (needs Q, V', G' and the Ubar copy).
+template <typename T, int DK, int DVP, int BC>
+__device__ __forceinline__ void bwd_bm_zb(T *smem, const float *pw, int w, int lane) {
+  using Cfg = BwdCfg<T, DK, DVP, BC>;
+  T *const Qs = smem + Cfg::Q_OFF, *const Vs = smem + Cfg::V_OFF, *const Gs = smem + Cfg::G_OFF;
+  T *const Ubs = smem + Cfg::U_OFF, *const Bms = smem + Cfg::BM_OFF, *const Zbs = smem + Cfg::ZB_OFF;
+  const int gq = lane >> 4, nn = lane & 15;
+  // Bm = L o D2 o (G' V'^T)   (rows s, columns tau <= s)
+  for_tiles<BC, BC>(w, [&](int i0, int j0, bool ok, int) {
+    f32x4 x = pt<false, true, DVP>(zero4(), Gs, Cfg::LDV, Vs, Cfg::LDV, i0, j0, lane);
+    const int s = i0 + nn;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int tau = j0 + 4 * gq + e;
+      x[e] = tau <= s ? x[e] * pw[2 * (s - tau)] : 0.f;
+    }
+    if (ok) st4(Bms + s * Cfg::LDC + j0 + 4 * gq, x);
+  });
+  __syncthreads();
+  // Zb = Bm^T Q + diag(g^(2(BC-tau))) V' Ubar^T
+  for_tiles<BC, DK>(w, [&](int i0, int j0, bool ok, int) {
+    f32x4 x = pt<false, true, DVP>(zero4(), Vs, Cfg::LDV, Ubs, Cfg::LDV, i0, j0, lane);
+    x *= pw[2 * (BC - (i0 + nn))];
+    x = pt<true, false, BC>(x, Bms, Cfg::LDC, Qs, Cfg::LDQ, i0, j0, lane);
+    if (ok) st4(Zbs + (i0 + nn) * Cfg::LDQ + j0 + 4 * gq, x);
+  });
+}
+
+// Adjoint state update (registers): Ubar <- g^(2BC) Ubar + Q^T diag(g^(2tau)) G';
+// Shat <- g^BC Shat + Zb^T diag(g^tau) Q + Q^T diag(g^tau) Zb.
+template <typename T, int DK, int DVP, int BC>
+__device__ __forceinline__ void bwd_adjoint_update(T *smem, const float *pw, int w, int lane, f32x4 *Ub, f32x4 *Sh) {
+  using Cfg = BwdCfg<T, DK, DVP, BC>;
+  T *const Qs = smem + Cfg::Q_OFF, *const Gs = smem + Cfg::G_OFF, *const Zbs = smem + Cfg::ZB_OFF;
+  const float gB = pw[BC], gB2 = pw[2 * BC];
+  for_tiles<DK, DVP>(w, [&](int i0, int j0, bool, int it) {
+    Ub[it] = ptw<true, false, BC>(gB2 * Ub[it], Qs, Cfg::LDQ, Gs, Cfg::LDV, i0, j0, lane,
+                                  [&](int s) { return pw[2 * s]; });
+  });
+  for_tiles<DK, DK>(w, [&](int i0, int j0, bool, int it) {
+    f32x4 x = ptw<true, false, BC>(gB * Sh[it], Zbs, Cfg::LDQ, Qs, Cfg::LDQ, i0, j0, lane,
+                                   [&](int s) { return pw[s]; });
+    Sh[it] = ptw<true, false, BC>(x, Qs, Cfg::LDQ, Zbs, Cfg::LDQ, i0, j0, lane, [&](int s) { return pw[s]; });
+  });
+}
+
+// bf16 / fp32 copies of the adjoint state for the next chunk's products
+template <typename T, int DK, int DVP, int BC>
+__device__ __forceinline__ void bwd_adjoint_copy(T *smem, int w, int lane, const f32x4 *Ub, const f32x4 *Sh) {
+  using Cfg = BwdCfg<T, DK, DVP, BC>;
+  T *const Ubs = smem + Cfg::U_OFF, *const Shs = smem + Cfg::S_OFF;
+  const int gq = lane >> 4, nn = lane & 15;
+  for_tiles<DK, DVP>(w, [&](int i0, int j0, bool ok, int it) {
+    if (ok) st4(Ubs + (i0 + nn) * Cfg::LDV + j0 + 4 * gq, Ub[it]);
+  });
+  for_tiles<DK, DK>(w, [&](int i0, int j0, bool ok, int it) {
+    if (ok) st4(Shs + (i0 + nn) * Cfg::LDQ + j0 + 4 * gq, Sh[it]);
+  });
+}
+
+// ---------------------------------------------------------------------------
+// Adjoint summary of a segment (segments 1 .. nseg-1): walked backwards from a
+// zero adjoint state at the segment end.
+template <typename T, int DK, int DV, int DVP, int BC, bool NORM>
+__global__ void __launch_bounds__(256) bwd_rsum_kernel(BwdArgs a) {
+  using Cfg = BwdCfg<T, DK, DVP, BC>;
+  __shared__ __attribute__((aligned(16))) T smem[Cfg::ELEMS];
+  __shared__ float pw[2 * BC + 3];
+  T *const Qs = smem + Cfg::Q_OFF, *const Vs = smem + Cfg::V_OFF, *const Gs = smem + Cfg::G_OFF;
+  const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 4, nn = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int bh = blockIdx.x / (a.nseg - 1), seg = 1 + blockIdx.x % (a.nseg - 1);
+  const int tok0 = seg * a.cps * a.kc, tokE = min(a.n, tok0 + a.cps * a.kc);
+  const int nch = (tokE - tok0 + BC - 1) / BC;
+  const T *qh = (const T *)a.q + (long)bh * a.n * a.d, *vh = (const T *)a.v + (long)bh * a.n * a.dv;
+  const T *gh = (const T *)a.g + (long)bh * a.n * a.gld;
+  for (int e = tid; e < 2 * BC + 3; e += 256) pw[e] = exp2f((float)e * a.log2g);
+  f32x4 Ub[TileCount<DK, DVP>::PER], Sh[TileCount<DK, DK>::PER];
+#pragma unroll
+  for (int i = 0; i < TileCount<DK, DVP>::PER; ++i) Ub[i] = zero4();
+#pragma unroll
+  for (int i = 0; i < TileCount<DK, DK>::PER; ++i) Sh[i] = zero4();
+  bwd_adjoint_copy<T, DK, DVP, BC>(smem, w, lane, Ub, Sh);
+
+  for (int ch = nch - 1; ch >= 0; --ch) {
+    const int t0 = tok0 + ch * BC;
+    load_rows<T, BC, DK>(Qs, Cfg::LDQ, qh, a.d, t0, a.n, -1, tid);
+    load_rows<T, BC, DVP>(Vs, Cfg::LDV, vh, a.dv, t0, a.n, NORM ? DV : -1, tid);
+    load_rows<T, BC, DVP>(Gs, Cfg::LDV, gh, a.gld, t0, a.n, -1, tid);
+    __syncthreads();
+    bwd_bm_zb<T, DK, DVP, BC>(smem, pw, w, lane);
+    __syncthreads();
+    bwd_adjoint_update<T, DK, DVP, BC>(smem, pw, w, lane, Ub, Sh);
+    __syncthreads();  // reads of the old copies and of the chunk done
+    bwd_adjoint_copy<T, DK, DVP, BC>(smem, w, lane, Ub, Sh);
+  }
+  float *out = a.rsum + ((long)bh * a.nseg + seg) * ((long)DK * DVP + DK * DK);
+  for_tiles<DK, DVP>(w, [&](int i0, int j0, bool ok, int it) {
+    if (ok) *(f32x4 *)(out + (i0 + nn) * DVP + j0 + 4 * gq) = Ub[it];
+  });
+  for_tiles<DK, DK>(w, [&](int i0, int j0, bool ok, int it) {
+    if (ok) *(f32x4 *)(out + DK * DVP + (i0 + nn) * DK + j0 + 4 * gq) = Sh[it];
+  });
+}
+
+// ---------------------------------------------------------------------------
+// Gradients: each segment walked backwards from its scanned adjoint state.
+template <typename T, int DK, int DV, int DVP, int BC, bool NORM>
+__global__ void __launch_bounds__(256) bwd_walk_kernel(BwdArgs a) {
+  using Cfg = BwdCfg<T, DK, DVP, BC>;
+  __shared__ __attribute__((aligned(16))) T smem[Cfg::ELEMS];
+  __shared__ float pw[2 * BC + 3];
+  T *const Qs = smem + Cfg::Q_OFF, *const Ks = smem + Cfg::K_OFF, *const Vs = smem + Cfg::V_OFF;
+  T *const Gs = smem + Cfg::G_OFF, *const Ubs = smem + Cfg::U_OFF, *const Shs = smem + Cfg::S_OFF;
+  T *const Ads = smem + Cfg::AD_OFF, *const Bms = smem + Cfg::BM_OFF, *const Ws = smem + Cfg::W_OFF;
+  T *const Eks = smem + Cfg::EK_OFF, *const Zs = smem + Cfg::Z_OFF, *const Zbs = smem + Cfg::ZB_OFF;
+  const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 4, nn = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int bh = blockIdx.x / a.nseg, seg = blockIdx.x % a.nseg;
+  const int tok0 = seg * a.cps * a.kc, tokE = min(a.n, tok0 + a.cps * a.kc);
+  const int nch = (tokE - tok0 + BC - 1) / BC, c0 = tok0 / BC;
+  const long hq = (long)bh * a.n * a.d, hv = (long)bh * a.n * a.dv;
+  const T *qh = (const T *)a.q + hq, *kh = (const T *)a.k + hq, *vh = (const T *)a.v + hv;
+  const T *gh = (const T *)a.g + (long)bh * a.n * a.gld;
+  T *dqh = (T *)a.dq_out + hq, *dkh = (T *)a.dk_out + hq, *dvh = (T *)a.dv_out + hv;
+  const T *cst = (const T *)a.cstate + ((long)bh * a.nbc + c0) * Cfg::BLOCK;
+  for (int e = tid; e < 2 * BC + 3; e += 256) pw[e] = exp2f((float)e * a.log2g);
+
+  f32x4 Ub[TileCount<DK, DVP>::PER], Sh[TileCount<DK, DK>::PER];
+  {
+    const float *suf = a.suffix + ((long)bh * a.nseg + seg) * ((long)DK * DVP + DK * DK);
+    for_tiles<DK, DVP>(w, [&](int i0, int j0, bool, int it) {
+      Ub[it] = *(const f32x4 *)(suf + (i0 + nn) * DVP + j0 + 4 * gq);
+    });
+    for_tiles<DK, DK>(w, [&](int i0, int j0, bool, int it) {
+      Sh[it] = *(const f32x4 *)(suf + DK * DVP + (i0 + nn) * DK + j0 + 4 * gq);
+    });
+  }
+  bwd_adjoint_copy<T, DK, DVP, BC>(smem, w, lane, Ub, Sh);
+
+  for (int ch = nch - 1; ch >= 0; --ch) {
+    const int t0 = tok0 + ch * BC;
+    const T *S0 = cst + (long)ch * Cfg::BLOCK, *U0 = S0 + DK * DK;  // global, row-major
+    load_rows<T, BC, DK>(Qs, Cfg::LDQ, qh, a.d, t0, a.n, -1, tid);
+    load_rows<T, BC, DK>(Ks, Cfg::LDQ, kh, a.d, t0, a.n, -1, tid);
+    load_rows<T, BC, DVP>(Vs, Cfg::LDV, vh, a.dv, t0, a.n, NORM ? DV : -1, tid);
+    load_rows<T, BC, DVP>(Gs, Cfg::LDV, gh, a.gld, t0, a.n, -1, tid);
+    __syncthreads();
+    // Ad = L o D1 o (Q K^T)
+    for_tiles<BC, BC>(w, [&](int i0, int j0, bool ok, int) {
+      f32x4 x = pt<false, true, DK>(zero4(), Qs, Cfg::LDQ, Ks, Cfg::LDQ, i0, j0, lane);
+      const int tr = i0 + nn;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int ti = j0 + 4 * gq + e;
+        x[e] = ti <= tr ? x[e] * pw[tr - ti] : 0.f;
+      }
+      if (ok) st4(Ads + tr * Cfg::LDC + j0 + 4 * gq, x);
+    });
+    // Bm, then Zb (one barrier inside)
+    bwd_bm_zb<T, DK, DVP, BC>(smem, pw, w, lane);
+    // Z = diag(g^(tau+1)) Q S0 + Ad K   (Ad is complete: the barrier inside bwd_bm_zb)
+    for_tiles<BC, DK>(w, [&](int i0, int j0, bool ok, int) {
+      f32x4 x = pt<false, true, DK>(zero4(), Qs, Cfg::LDQ, S0, DK, i0, j0, lane);
+      x *= pw[i0 + nn + 1];
+      x = pt<false, false, BC>(x, Ads, Cfg::LDC, Ks, Cfg::LDQ, i0, j0, lane);
+      if (ok) st4(Zs + (i0 + nn) * Cfg::LDQ + j0 + 4 * gq, x);
+    });
+    __syncthreads();
+    // W = L o D2 o (Q Z^T) (rows s, columns tau <= s);  Ek = L o D1 o (Zb K^T)
+    for_tiles<BC, BC>(w, [&](int i0, int j0, bool ok, int) {
+      f32x4 x = pt<false, true, DK>(zero4(), Qs, Cfg::LDQ, Zs, Cfg::LDQ, i0, j0, lane);
+      const int s = i0 + nn;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int tau = j0 + 4 * gq + e;
+        x[e] = tau <= s ? x[e] * pw[2 * (s - tau)] : 0.f;
+      }
+      if (ok) st4(Ws + s * Cfg::LDC + j0 + 4 * gq, x);
+    });
+    for_tiles<BC, BC>(w, [&](int i0, int j0, bool ok, int) {
+      f32x4 x = pt<false, true, DK>(zero4(), Zbs, Cfg::LDQ, Ks, Cfg::LDQ, i0, j0, lane);
+      const int tr = i0 + nn;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int ti = j0 + 4 * gq + e;
+        x[e] = ti <= tr ? x[e] * pw[tr - ti] : 0.f;
+      }
+      if (ok) st4(Eks + tr * Cfg::LDC + j0 + 4 * gq, x);
+    });
+    __syncthreads();
+    // dV' = W^T G' + diag(g^(2(BC-tau))) Z Ubar
+    for_tiles<BC, DVP>(w, [&](int i0, int j0, bool ok, int) {
+      f32x4 x = pt<false, false, DK>(zero4(), Zs, Cfg::LDQ, Ubs, Cfg::LDV, i0, j0, lane);
+      x *= pw[2 * (BC - (i0 + nn))];
+      x = pt<true, false, BC>(x, Ws, Cfg::LDC, Gs, Cfg::LDV, i0, j0, lane);
+      if (ok) st_out(dvh, a.dv, t0 + i0 + nn, j0 + 4 * gq, a.n, x);
+    });
+    // dQ = diag(g^(tau+1)) [diag(g^(tau+1)) G' U0'^T + Zb S0] + Bm Z + Ek K
+    for_tiles<BC, DK>(w, [&](int i0, int j0, bool ok, int) {
+      const float gt = pw[i0 + nn + 1];
+      f32x4 x = pt<false, true, DVP>(zero4(), Gs, Cfg::LDV, U0, DVP, i0, j0, lane);
+      x *= gt;
+      x = pt<false, true, DK>(x, Zbs, Cfg::LDQ, S0, DK, i0, j0, lane);
+      x *= gt;
+      x = pt<false, false, BC>(x, Bms, Cfg::LDC, Zs, Cfg::LDQ, i0, j0, lane);
+      x = pt<false, false, BC>(x, Eks, Cfg::LDC, Ks, Cfg::LDQ, i0, j0, lane);
+      if (ok) st_out(dqh, a.d, t0 + i0 + nn, j0 + 4 * gq, a.n, x);
+    });
+    // dK = Ad^T Zb + Ek^T Q + diag(g^(BC-tau)) K Shat
+    for_tiles<BC, DK>(w, [&](int i0, int j0, bool ok, int) {
+      f32x4 x = pt<false, true, DK>(zero4(), Ks, Cfg::LDQ, Shs, Cfg::LDQ, i0, j0, lane);
+      x *= pw[BC - (i0 + nn)];
+      x = pt<true, false, BC>(x, Ads, Cfg::LDC, Zbs, Cfg::LDQ, i0, j0, lane);
+      x = pt<true, false, BC>(x, Eks, Cfg::LDC, Qs, Cfg::LDQ, i0, j0, lane);
+      if (ok) st_out(dkh, a.d, t0 + i0 + nn, j0 + 4 * gq, a.n, x);
+    });
+    bwd_adjoint_update<T, DK, DVP, BC>(smem, pw, w, lane, Ub, Sh);
+    __syncthreads();  // every read of this chunk's LDS done
+    bwd_adjoint_copy<T, DK, DVP, BC>(smem, w, lane, Ub, Sh);
+  }
+}
+
+}  // namespace hla2

@@ -1,0 +1,196 @@
+// hla2_bwd.hip -- the backward pass: upstream-gradient preparation for the
+// ratio, the reverse scan over segments, and the instantiations and launchers
+// of the backward walkers (hla2_bwd.h).
+#include "hla2_bwd.h"
+
+namespace hla2 {
+
+// Upstream gradient of [num | den] under the ratio o = num / den:
+//   g'[t][c] = dout[t][c] / den[t]  (c < dv),   g'[t][DV] = -(dout[t] . out[t]) / den[t],
+// zero elsewhere; rows of DVP elements.  One wave per token.
+template <typename T, int DV, int DVP>
+__global__ void __launch_bounds__(256) bwd_prep_kernel(BwdPrepArgs a) {
+  const int lane = threadIdx.x & 63;
+  const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.rows) return;
+  const T *g = (const T *)a.dout + row * a.dv, *o = (const T *)a.out + row * a.dv;
+  T *gp = (T *)a.gprep + row * DVP;
+  const float inv = 1.f / a.den[row];
+  float dot = 0.f;
+  for (int c = lane; c < a.dv; c += 64) dot += (float)g[c] * (float)o[c];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) dot += __shfl_xor(dot, off);
+  for (int c = lane; c < DVP; c += 64) {
+    float x = 0.f;
+    if (c < a.dv) x = (float)g[c] * inv;
+    else if (c == DV) x = -dot * inv;
+    gp[c] = (T)x;
+  }
+}
+
+// Reverse (adjoint) scan over segments, per (b, h): the adjoint state at the end
+// of segment r is the fold of the adjoint summaries of the later segments,
+//   Ubar <- g^(2L) Ubar + Ubar_r,
+//   Shat <- g^L Shat + Shat_r + g^(L+1) (Ubar C'_r^T + C'_r Ubar^T)   (old Ubar),
+// taken from the last segment backwards; L = tokens per full segment and
+// C'_r = [C_r | m_r] the segment's forward summary.  fp32 on VALU.
+template <int DK, int DV, int DVP, bool NORM>
+__global__ void __launch_bounds__(256) bwd_rscan_kernel(BwdArgs a, float gL) {
+  constexpr int CW = DVP / 2;                     // columns staged per pass
+  constexpr long RB = (long)DK * DVP + DK * DK;   // adjoint block
+  constexpr int NU = (DK * DVP + 255) / 256;      // Ubar elements per thread
+  constexpr int NB = DK * DK / 16, NBT = (NB + 255) / 256;  // 4x4 blocks of Shat
+  __shared__ __attribute__((aligned(16))) float Us[DK * CW], Cs[DK * CW];
+  const int tid = threadIdx.x, bh = blockIdx.x;
+  const long SB = sum_block_floats(DK, DV);
+  float *suf = a.suffix + (long)bh * a.nseg * RB;
+  const float *rs = a.rsum + (long)bh * a.nseg * RB;
+  const float gL1 = gL * exp2f(a.log2g), gL2 = gL * gL;
+  float U[NU];
+  f32x4 Sh[NBT][4];
+#pragma unroll
+  for (int i = 0; i < NU; ++i) U[i] = 0.f;
+#pragma unroll
+  for (int b = 0; b < NBT; ++b)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Sh[b][r] = zero4();
+  auto store = [&](int r) {
+    float *o = suf + (long)r * RB;
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+      const int e = tid + 256 * i;
+      if (e < DK * DVP) o[e] = U[i];
+    }
+#pragma unroll
+    for (int b = 0; b < NBT; ++b) {
+      const int blk = tid + 256 * b;
+      if (blk < NB) {
+        const int a0 = 4 * (blk / (DK / 4)), b0 = 4 * (blk % (DK / 4));
+#pragma unroll
+        for (int r2 = 0; r2 < 4; ++r2) *(f32x4 *)(o + DK * DVP + (a0 + r2) * DK + b0) = Sh[b][r2];
+      }
+    }
+  };
+  store(a.nseg - 1);
+  for (int r = a.nseg - 1; r >= 1; --r) {
+    const float *ad = rs + (long)r * RB;
+    // cross term with the old Ubar (zero for the last segment, whose C' is not needed)
+    f32x4 X[NBT][4];
+#pragma unroll
+    for (int b = 0; b < NBT; ++b)
+#pragma unroll
+      for (int r2 = 0; r2 < 4; ++r2) X[b][r2] = zero4();
+    if (r < a.nseg - 1) {
+      const float *fs = a.fsum + ((long)bh * (a.nseg - 1) + r) * SB;
+      const float *Cg = fs + DK * DK, *mg = fs + DK * DK + 2 * DK * DV;
+      for (int h = 0; h < 2; ++h) {
+        __syncthreads();
+        for (int e = tid; e < DK * CW; e += 256) {
+          const int row = e / CW, c = h * CW + e % CW;
+          // the old Ubar is the adjoint state stored for the end of segment r
+          Us[e] = suf[(long)r * RB + row * DVP + c];
+          Cs[e] = c < DV ? Cg[row * DV + c] : ((NORM && c == DV) ? mg[row] : 0.f);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int b = 0; b < NBT; ++b) {
+          const int blk = tid + 256 * b;
+          if (blk < NB) {
+            const int a0 = 4 * (blk / (DK / 4)), b0 = 4 * (blk % (DK / 4));
+            for (int c = 0; c < CW; ++c) {
+              f32x4 ua, ub, ca, cb;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                ua[i] = Us[(a0 + i) * CW + c];
+                ub[i] = Us[(b0 + i) * CW + c];
+                ca[i] = Cs[(a0 + i) * CW + c];
+                cb[i] = Cs[(b0 + i) * CW + c];
+              }
+#pragma unroll
+              for (int i = 0; i < 4; ++i) X[b][i] += ua[i] * cb + ca[i] * ub;
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < NBT; ++b) {
+      const int blk = tid + 256 * b;
+      if (blk < NB) {
+        const int a0 = 4 * (blk / (DK / 4)), b0 = 4 * (blk % (DK / 4));
+#pragma unroll
+        for (int r2 = 0; r2 < 4; ++r2)
+          Sh[b][r2] = gL * Sh[b][r2] + *(const f32x4 *)(ad + DK * DVP + (a0 + r2) * DK + b0) + gL1 * X[b][r2];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+      const int e = tid + 256 * i;
+      if (e < DK * DVP) U[i] = gL2 * U[i] + ad[e];
+    }
+    store(r - 1);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers.  The backward walkers hold one workgroup per CU (their LDS), so
+// each may use every register of its SIMD.
+template <typename T, int DK, int DV, bool NORM>
+struct BwdShape {
+  static constexpr int DVP = DV + (NORM ? Ktile<T>::ROWS : 0);
+  static constexpr int BC = (sizeof(T) == 4 || DK == 128) ? 32 : 64;
+};
+
+template <typename T, int DK, int DV, bool NORM>
+static hipError_t launch_bwd_t(int phase, int BH, const BwdArgs &a, const BwdPrepArgs &pa, float gL, hipStream_t s) {
+  using Sh = BwdShape<T, DK, DV, NORM>;
+  constexpr int DVP = Sh::DVP, BC = Sh::BC;
+  switch (phase) {
+    case BWD_PREP:
+      if constexpr (NORM) {
+        hipLaunchKernelGGL((bwd_prep_kernel<T, DV, DVP>), dim3((unsigned)((pa.rows + 3) / 4)), dim3(256), 0, s, pa);
+        return hipGetLastError();
+      } else {
+        return hipErrorInvalidValue;
+      }
+    case BWD_STATE:
+      hipLaunchKernelGGL((bwd_state_kernel<T, DK, DV, DVP, BC, NORM>), dim3(BH * a.nseg), dim3(256), 0, s, a);
+      return hipGetLastError();
+    case BWD_RSUM:
+      hipLaunchKernelGGL((bwd_rsum_kernel<T, DK, DV, DVP, BC, NORM>), dim3(BH * (a.nseg - 1)), dim3(256), 0, s, a);
+      return hipGetLastError();
+    case BWD_RSCAN:
+      hipLaunchKernelGGL((bwd_rscan_kernel<DK, DV, DVP, NORM>), dim3(BH), dim3(256), 0, s, a, gL);
+      return hipGetLastError();
+    case BWD_WALK:
+      hipLaunchKernelGGL((bwd_walk_kernel<T, DK, DV, DVP, BC, NORM>), dim3(BH * a.nseg), dim3(256), 0, s, a);
+      return hipGetLastError();
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T, int DK, int DV>
+static hipError_t launch_bwd_n(bool norm, int phase, int BH, const BwdArgs &a, const BwdPrepArgs &pa, float gL,
+                               hipStream_t s) {
+  return norm ? launch_bwd_t<T, DK, DV, true>(phase, BH, a, pa, gL, s)
+              : launch_bwd_t<T, DK, DV, false>(phase, BH, a, pa, gL, s);
+}
+
+int bwd_chunk(int dtype, int DK) { return (dtype == 0 || DK == 128) ? 32 : 64; }
+int bwd_dvp(int dtype, int DV, bool norm) { return DV + (norm ? (dtype == 0 ? 16 : 32) : 0); }
+
+hipError_t launch_bwd(int dtype, int DK, int DV, bool norm, int phase, int BH, const BwdArgs &a,
+                      const BwdPrepArgs &pa, float gL, hipStream_t s) {
+  if (dtype == 0) {
+    if (DK == 16 && DV == 16) return launch_bwd_n<float, 16, 16>(norm, phase, BH, a, pa, gL, s);
+    if (DK == 64 && DV == 64) return launch_bwd_n<float, 64, 64>(norm, phase, BH, a, pa, gL, s);
+    return hipErrorInvalidValue;
+  }
+  if (DK == 64 && DV == 64) return launch_bwd_n<bf16, 64, 64>(norm, phase, BH, a, pa, gL, s);
+  if (DK == 64 && DV == 128) return launch_bwd_n<bf16, 64, 128>(norm, phase, BH, a, pa, gL, s);
+  if (DK == 128 && DV == 64) return launch_bwd_n<bf16, 128, 64>(norm, phase, BH, a, pa, gL, s);
+  if (DK == 128 && DV == 128) return launch_bwd_n<bf16, 128, 128>(norm, phase, BH, a, pa, gL, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace hla2

@@ -115,4 +115,36 @@ struct DecodeArgs {
 };
 hipError_t launch_decode(int dtype, const DecodeArgs &a, hipStream_t s);
 
+
+// Arguments of the backward kernels (hla2_bwd.h, hla2_bwd.hip).
+struct BwdArgs {
+  const void *q, *k, *v;   // [BH, n, d], [BH, n, d], [BH, n, dv]
+  const void *g;           // upstream gradient rows: dout [BH, n, dv], or [BH, n, gld] prepared for the ratio
+  void *dq_out, *dk_out, *dv_out;  // [BH, n, d], [BH, n, d], [BH, n, dv]
+  const float *prefix;     // forward prefix blocks [BH, nseg] (null when nseg == 1)
+  const float *fsum;       // forward summary blocks [BH, nseg-1] (C and m of each segment)
+  void *cstate;            // chunk states [BH, nbc] blocks of S0 | U0' (element type)
+  float *rsum;             // adjoint summaries [BH, nseg] blocks of Ubar | Shat (fp32)
+  float *suffix;           // adjoint states at segment ends [BH, nseg] blocks of Ubar | Shat
+  int n, d, dv, gld;       // gld: columns of a row of g
+  int nseg, cps, kc;       // segments of cps chunks of kc tokens (the forward's plan)
+  int nbc;                 // backward chunks per head
+  float log2g;             // log2(decay)
+};
+// Arguments of the ratio's upstream-gradient preparation.
+struct BwdPrepArgs {
+  const void *dout, *out;  // [rows, dv]
+  const float *den;        // [rows]
+  void *gprep;             // [rows, DVP]
+  long rows;
+  int dv;
+};
+enum { BWD_PREP = 0, BWD_STATE = 1, BWD_RSUM = 2, BWD_RSCAN = 3, BWD_WALK = 4 };
+// backward chunk length and padded value width (values, plus the denominator column under the ratio)
+int bwd_chunk(int dtype, int DK);
+int bwd_dvp(int dtype, int DV, bool norm);
+// one phase of the backward pass; gL = decay^(tokens per full segment) (reverse scan)
+hipError_t launch_bwd(int dtype, int DK, int DV, bool norm, int phase, int BH, const BwdArgs &a,
+                      const BwdPrepArgs &pa, float gL, hipStream_t s);
+
 }  // namespace hla2

@@ -20,7 +20,7 @@ HLA2_OK, HLA2_ERR_INVALID, HLA2_ERR_UNSUPPORTED, HLA2_ERR_WORKSPACE, HLA2_ERR_LA
 EXPORTS = ("hla2_strerror", "hla2_abi_version", "hla2_forward_workspace_bytes", "hla2_forward_segments",
            "hla2_forward", "hla2_forward_ex_workspace_bytes", "hla2_forward_ex_segments", "hla2_forward_ex",
            "hla2_forward_timed", "hla2_decode_step", "hla2_state_floats", "hla2_forward_state_workspace_bytes",
-           "hla2_forward_state")
+           "hla2_forward_state", "hla2_backward_workspace_bytes", "hla2_backward")
 
 _lock = threading.Lock()
 _lib = None
@@ -67,6 +67,10 @@ def lib():
             L.hla2_forward_state_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
             L.hla2_forward_state.restype = i
             L.hla2_forward_state.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, vp, vp, sz, i, vp]
+            L.hla2_backward_workspace_bytes.restype = sz
+            L.hla2_backward_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i]
+            L.hla2_backward.restype = i
+            L.hla2_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, i, vp]
             _lib = L
     return _lib
 
@@ -171,6 +175,35 @@ def hla2_forward_state(q, k, v, out, state_out, decay=1.0, normalize=False, chun
                                   _ptr(state_out), _ptr(workspace), wbytes, int(segments), _stream(stream))
     if check and rc != HLA2_OK:
         raise HLA2Error(rc, "hla2_forward_state")
+    return rc
+
+
+def hla2_backward_workspace_bytes(B, H, n, d, dv, normalize, dtype_code, segments=0) -> int:
+    return int(lib().hla2_backward_workspace_bytes(B, H, n, d, dv, int(bool(normalize)), int(dtype_code), segments))
+
+
+def hla2_backward(q, k, v, dout, grad_q, grad_k, grad_v, decay=1.0, normalize=False, out=None, den=None,
+                  workspace=None, stream=None, segments=0, check=True) -> int:
+    """Call ``hla2_backward``: gradients of sum(dout * out) w.r.t. q, k, v written to
+    grad_q, grad_k: [B,H,n,d] and grad_v: [B,H,n,dv] (same dtype as q).  Under
+    ``normalize`` the forward's ``out`` and fp32 ``den`` are required."""
+    import torch
+    B, H, n, d = q.shape
+    dv = v.shape[-1]
+    for t in (q, k, v, dout, grad_q, grad_k, grad_v) + ((out, den) if normalize else ()):
+        if t is None or not t.is_contiguous():
+            raise ValueError("tensors must be given and contiguous")
+    code = _dtype_code(q)
+    need = hla2_backward_workspace_bytes(B, H, n, d, dv, normalize, code, segments)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().hla2_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(out) if normalize else None,
+                             _ptr(den) if normalize else None, _ptr(dout), _ptr(grad_q), _ptr(grad_k), _ptr(grad_v),
+                             B, H, n, d, dv, float(decay), int(bool(normalize)), code, _ptr(workspace), wbytes,
+                             int(segments), _stream(stream))
+    if check and rc != HLA2_OK:
+        raise HLA2Error(rc, "hla2_backward")
     return rc
 
 

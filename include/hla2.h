@@ -184,6 +184,41 @@ int hla2_forward_state(const void *q, const void *k, const void *v, void *out,
                        hla2_dtype_t dtype, float *den_out, float *state_out, void *workspace,
                        size_t workspace_bytes, int segments, hipStream_t stream);
 
+/*
+ * Backward pass: the gradients of L = sum(dout * out) with respect to q, k and
+ * v, for the forward of hla2_forward (same decay and normalisation).  The
+ * pages run the chunk-parallel scan for training [SUM §4] but print no
+ * gradient; it is the chain rule of the operation defined above:
+ *   with M[t][j] = sum_{i<=j} g^{(t-i)+(t-j)} (q_t.k_i)(q_j.k_i) (j <= t),
+ *   num = M V, den = M 1, and the upstream gradients g_num = dout, g_den = 0
+ *   (normalize = 0) or g_num = dout / den, g_den = -(dout . out) / den
+ *   (normalize = 1, using the forward's own out and den),
+ *   dV = M^T g_num;  dq, dk through the scores q_t.k_i of both factors.
+ * It runs as the adjoint of the chunked forward: a forward walk that stores
+ * every chunk's incoming state, a reverse scan of adjoint segment summaries,
+ * and a backward walk that writes the gradients.
+ *   q, k : [B, H, n, d];  v, dout, out : [B, H, n, dv]   element type `dtype`
+ *   den  : [B, H, n] fp32 (the forward's den_out)
+ *   out, den: read only when normalize = 1 (may be NULL otherwise)
+ *   grad_q, grad_k : [B, H, n, d];  grad_v : [B, H, n, dv]  (written, `dtype`)
+ *   decay: g in (0, 1], a constant (no gradient is formed for it)
+ *   workspace: device buffer of at least hla2_backward_workspace_bytes(...)
+ *          bytes for the same arguments, 256-byte aligned; never 0 bytes
+ *   segments: 0 picks the plan; otherwise as for hla2_forward_ex
+ * Supported: as hla2_forward (bf16: d, dv multiples of 16 up to 128; fp32: up
+ * to 64).  The chunking is internal (64 tokens for bf16 at d <= 64, else 32);
+ * the results change only by rounding with it.  All tensor pointers 16-byte
+ * aligned.  Errors as for hla2_forward; workspace problems give
+ * HLA2_ERR_WORKSPACE, a missing out/den under normalize = 1 HLA2_ERR_INVALID.
+ */
+size_t hla2_backward_workspace_bytes(int B, int H, int n, int d, int dv, int normalize,
+                                     hla2_dtype_t dtype, int segments);
+int hla2_backward(const void *q, const void *k, const void *v, const void *out, const float *den,
+                  const void *dout, void *grad_q, void *grad_k, void *grad_v,
+                  int B, int H, int n, int d, int dv, float decay, int normalize,
+                  hla2_dtype_t dtype, void *workspace, size_t workspace_bytes, int segments,
+                  hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -187,3 +187,34 @@ def test_forward_state_validates(L):
             assert st > plain
             assert st >= b * h * H.hla2_forward_segments(*shape, segments=seg) * dk * dk * 4
     assert H.hla2_forward_state_workspace_bytes(1, 1, 64, 24, 16, 16, 0) == 0
+
+
+def bwd(L, q=P, k=P, v=P, out=None, den=None, dout=P, gq=P, gk=P, gv=P, B_=1, H_=1, n=64, d=64, dv=64, decay=1.0,
+        norm=0, dtype=1, ws=None, wsb=0, segments=0):
+    return L.hla2_backward(q, k, v, out, den, dout, gq, gk, gv, B_, H_, n, d, dv, decay, norm, dtype, ws, wsb,
+                           segments, None)
+
+
+def test_backward_validates(L):
+    need = H.hla2_backward_workspace_bytes(1, 1, 64, 64, 64, 0, 1)
+    assert need > 0
+    big = dict(ws=P, wsb=1 << 40)
+    assert bwd(L, q=None, **big) == H.HLA2_ERR_INVALID
+    assert bwd(L, gv=None, **big) == H.HLA2_ERR_INVALID
+    assert bwd(L, norm=1, **big) == H.HLA2_ERR_INVALID               # out and den required
+    assert bwd(L, norm=1, out=P, **big) == H.HLA2_ERR_INVALID
+    assert bwd(L, norm=2, **big) == H.HLA2_ERR_INVALID
+    assert bwd(L, decay=0.0, **big) == H.HLA2_ERR_INVALID
+    assert bwd(L, decay=float("nan"), **big) == H.HLA2_ERR_INVALID
+    assert bwd(L, segments=-1, **big) == H.HLA2_ERR_INVALID
+    assert bwd(L, dtype=3, **big) == H.HLA2_ERR_INVALID
+    assert bwd(L, d=24, **big) == H.HLA2_ERR_UNSUPPORTED
+    assert bwd(L, d=128, dtype=0, **big) == H.HLA2_ERR_UNSUPPORTED
+    assert bwd(L, q=ctypes.c_void_p(4104), **big) == H.HLA2_ERR_INVALID  # misaligned
+    assert bwd(L) == H.HLA2_ERR_WORKSPACE
+    assert bwd(L, ws=P, wsb=need - 1) == H.HLA2_ERR_WORKSPACE
+    assert bwd(L, ws=ctypes.c_void_p(4096 + 128), wsb=need) == H.HLA2_ERR_WORKSPACE
+    # the ratio adds a prepared upstream-gradient buffer; more tokens need more
+    assert H.hla2_backward_workspace_bytes(1, 1, 64, 64, 64, 1, 1) > need
+    assert H.hla2_backward_workspace_bytes(1, 1, 4096, 64, 64, 0, 1) > need
+    assert H.hla2_backward_workspace_bytes(1, 1, 64, 24, 64, 0, 1) == 0
