@@ -197,6 +197,33 @@ def bench_decode(dw, steps, warmup, torch, H, prefill_tokens):
     }
 
 
+def bench_backward(w, steps, warmup, torch, H, I):
+    """Time `steps` backward calls (gradients w.r.t. q, k, v) on the workload,
+    with the forward's out and den (from one forward call) and a random dout."""
+    dev = torch.device("cuda:0")
+    q, k, v = (x.to(dev) for x in I.make_qkv(w))
+    g = torch.Generator(device=dev).manual_seed(w.seed + 7)
+    dout = torch.randn(w.B, w.H, w.n, w.dv, generator=g, device=dev).to(q.dtype)
+    out = den = None
+    if w.normalize:
+        out = torch.empty_like(v)
+        den = torch.empty(w.B, w.H, w.n, dtype=torch.float32, device=dev)
+        H.hla2_forward(q, k, v, out, decay=w.decay, normalize=True, chunk=w.chunk, den_out=den)
+    gq, gk, gv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    code = H.HLA2_BF16 if q.dtype == torch.bfloat16 else H.HLA2_F32
+    ws = torch.empty(H.hla2_backward_workspace_bytes(w.B, w.H, w.n, w.d, w.dv, w.normalize, code),
+                     dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def fn():
+        H.hla2_backward(q, k, v, dout, gq, gk, gv, decay=w.decay, normalize=w.normalize, out=out, den=den,
+                        workspace=ws)
+
+    t, wall = time_calls(fn, steps, warmup, torch)
+    return {"seconds": t, "wall": wall, "tokens_per_s": w.B * w.n / t, "head_tokens_per_s": w.B * w.H * w.n / t,
+            "workspace_bytes": ws.numel()}
+
+
 def cpu_baseline(w, heads_sample, I):
     """The fp64 oracle (as it stands) on a bounded sample of the workload's
     heads: the serial recurrence, threaded over heads."""
@@ -240,6 +267,7 @@ def main(argv=None):
     ap.add_argument("--decode-prefill", type=int, default=None, help="prefix tokens (default: the workload's)")
     ap.add_argument("--cpu-heads", type=int, default=128, help="heads in the oracle's timed sample (0: skip)")
     ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--skip-backward", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="finish with two 1 GiB device copies (reference for HBM byte counters)")
     args = ap.parse_args(argv)
@@ -303,6 +331,13 @@ def main(argv=None):
             "roofline": {"bound": "hbm", "kernel": "hla2_decode_step", "achieved": dc["gbps"],
                          "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": dc["hbm_frac"],
                          "traffic": load_traffic("decode_" + dw.name)},
+        }
+    if not args.skip_backward:
+        bw = bench_backward(w, args.steps, args.warmup, torch, H, I)
+        line["backward"] = {
+            "workload": w.name, "ms_per_step": bw["seconds"] * 1e3, "tokens_per_s": bw["tokens_per_s"],
+            "head_tokens_per_s": bw["head_tokens_per_s"], "vs_forward_time": bw["seconds"] / fw["seconds"],
+            "workspace_bytes": bw["workspace_bytes"],
         }
     if args.cpu_heads > 0:
         line["cpu_baseline"] = cpu_baseline(w, min(args.cpu_heads, w.B * w.H), I)

@@ -28,7 +28,7 @@
 // Tokens past the end are zero rows in Q, K, V' (its ones column too) and G',
 // so a ragged last chunk takes the same path.
 //
-// Kernels (one 256-thread workgroup per (b, h, segment), 4 waves):
+// Kernels (one 512-thread workgroup per (b, h, segment), 8 waves):
 //   bwd_state_kernel   walks a segment forwards from its scanned prefix and
 //                      writes every chunk's (S0, U0') in the element type;
 //   bwd_rsum_kernel    walks a segment backwards from a zero adjoint state and
@@ -38,7 +38,7 @@
 //                      dq, dk, dv.
 // Every product is a set of 16x16 MFMA tiles computed transposed, so that a
 // lane holds four consecutive columns of one row of the result; each wave
-// takes every fourth tile.  MFMAs never sit under a runtime branch: tile
+// takes every eighth tile.  MFMAs never sit under a runtime branch: tile
 // loops have compile-time trip counts, and a wave with no tile left repeats
 // the last one without storing it.
 #pragma once
@@ -95,19 +95,22 @@ __device__ __forceinline__ f32x4 ptw(f32x4 acc, const T *X, int ldx, const T *Y,
   return mmw<!YT, !XT, K>(acc, Y, ldy, X, ldx, j0, i0, lane, wk);
 }
 
-// Iterate a wave's share of the 16x16 tiles of an I x J result: f(i0, j0, store_ok).
+// Waves per workgroup of the backward walkers (two per SIMD).
+constexpr int BWD_WAVES = 8, BWD_THREADS = 64 * BWD_WAVES;
+
+// Iterate a wave's share of the 16x16 tiles of an I x J result: f(i0, j0, store_ok, slot).
 template <int I, int J, typename F>
 __device__ __forceinline__ void for_tiles(int w, F &&f) {
-  constexpr int NJ = J / 16, NT = (I / 16) * NJ, PER = (NT + 3) / 4;
+  constexpr int NJ = J / 16, NT = (I / 16) * NJ, PER = (NT + BWD_WAVES - 1) / BWD_WAVES;
 #pragma unroll
   for (int it = 0; it < PER; ++it) {
-    const int t = w + 4 * it;
+    const int t = w + BWD_WAVES * it;
     const int tt = t < NT ? t : NT - 1;
     f(16 * (tt / NJ), 16 * (tt % NJ), t < NT, it);
   }
 }
 template <int I, int J> struct TileCount {
-  static constexpr int NT = (I / 16) * (J / 16), PER = (NT + 3) / 4;
+  static constexpr int NT = (I / 16) * (J / 16), PER = (NT + BWD_WAVES - 1) / BWD_WAVES;
 };
 
 // 16-byte vector of the element type
@@ -136,22 +139,35 @@ struct BwdCfg {
   static constexpr int BLOCK = DK * DK + DK * DVP;  // stored chunk state S0 | U0' (elements)
 };
 
-// Copy rows [t0, t0+BC) of a [n][gc] global matrix into LDS rows of width W
-// (zero past n and past column gc; with ones >= 0, column `ones` holds 1 for
-// rows before n).
+// Rows [t0, t0+BC) of a [n][gc] global matrix, as LDS rows of width W (zero
+// past n and past column gc; with ones >= 0, column `ones` holds 1 for rows
+// before n).  fetch() reads a thread's share into registers, put() writes them
+// to LDS, so the global reads of the next chunk can fly during this one.
 template <typename T, int BC, int W>
-__device__ __forceinline__ void load_rows(T *dst, int ld, const T *src, int gc, int t0, int n, int ones, int tid) {
+struct RowTile {
   typedef typename Vec16<T>::type V;
-  constexpr int VN = Vec16<T>::N, PERROW = W / VN, TOT = BC * PERROW;
+  static constexpr int VN = Vec16<T>::N, PERROW = W / VN, TOT = BC * PERROW,
+                       PER = (TOT + BWD_THREADS - 1) / BWD_THREADS;
+  V x[PER];
+  __device__ __forceinline__ void fetch(const T *src, int gc, int t0, int n, int ones, int tid) {
 #pragma unroll
-  for (int i = tid; i < TOT; i += 256) {
-    const int r = i / PERROW, c = (i % PERROW) * VN, t = t0 + r;
-    V x{};
-    if (t < n && c < gc) x = *(const V *)(src + (long)t * gc + c);
-    if (c == ones && t < n) x[0] = (T)1.f;
-    *(V *)(dst + r * ld + c) = x;
+    for (int j = 0; j < PER; ++j) {
+      const int i = tid + j * BWD_THREADS;
+      const int r = i / PERROW, c = (i % PERROW) * VN, t = t0 + r;
+      V v{};
+      if (i < TOT && t < n && c < gc) v = *(const V *)(src + (long)t * gc + c);
+      if (i < TOT && c == ones && t < n) v[0] = (T)1.f;
+      x[j] = v;
+    }
   }
-}
+  __device__ __forceinline__ void put(T *dst, int ld, int tid) const {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int i = tid + j * BWD_THREADS;
+      if (i < TOT) *(V *)(dst + (i / PERROW) * ld + (i % PERROW) * VN) = x[j];
+    }
+  }
+};
 
 // Store four consecutive values of row t, columns c .. c+3, of a [n][ncols] matrix.
 __device__ __forceinline__ void st_out(bf16 *dst, int ncols, int t, int c, int n, f32x4 x) {
@@ -167,7 +183,7 @@ __device__ __forceinline__ void st4g(float *p, f32x4 x) { *(f32x4 *)p = x; }
 // Forward state of every chunk: S0 and U0' at the chunk start, in the element
 // type (the precision the gradient kernel's products consume).
 template <typename T, int DK, int DV, int DVP, int BC, bool NORM>
-__global__ void __launch_bounds__(256) bwd_state_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(BWD_THREADS) bwd_state_kernel(BwdArgs a) {
   using Cfg = BwdCfg<T, DK, DVP, BC>;
   __shared__ __attribute__((aligned(16))) T smem[Cfg::ELEMS];
   __shared__ float pw[2 * BC + 3];
@@ -181,7 +197,7 @@ __global__ void __launch_bounds__(256) bwd_state_kernel(BwdArgs a) {
   const T *qh = (const T *)a.q + (long)bh * a.n * a.d, *kh = (const T *)a.k + (long)bh * a.n * a.d;
   const T *vh = (const T *)a.v + (long)bh * a.n * a.dv;
   T *cst = (T *)a.cstate + ((long)bh * a.nbc + c0) * Cfg::BLOCK;
-  for (int e = tid; e < 2 * BC + 3; e += 256) pw[e] = exp2f((float)e * a.log2g);
+  for (int e = tid; e < 2 * BC + 3; e += BWD_THREADS) pw[e] = exp2f((float)e * a.log2g);
 
   using TS = TileCount<DK, DK>;
   using TU = TileCount<DK, DVP>;
@@ -200,10 +216,14 @@ __global__ void __launch_bounds__(256) bwd_state_kernel(BwdArgs a) {
     }
     U[it] = x;
   });
+  RowTile<T, BC, DK> rq, rk;
+  RowTile<T, BC, DVP> rv;
+  rq.fetch(qh, a.d, tok0, a.n, -1, tid);
+  rk.fetch(kh, a.d, tok0, a.n, -1, tid);
+  rv.fetch(vh, a.dv, tok0, a.n, NORM ? DV : -1, tid);
   __syncthreads();  // pw
 
   for (int ch = 0; ch < nch; ++ch) {
-    const int t0 = tok0 + ch * BC;
     // state at the chunk start: bf16/fp32 copy of S into LDS and both into the chunk store
     T *blk = cst + (long)ch * Cfg::BLOCK;
     for_tiles<DK, DK>(w, [&](int i0, int j0, bool ok, int it) {
@@ -215,10 +235,16 @@ __global__ void __launch_bounds__(256) bwd_state_kernel(BwdArgs a) {
     for_tiles<DK, DVP>(w, [&](int i0, int j0, bool ok, int it) {
       if (ok) st4g(blk + DK * DK + (i0 + nn) * DVP + j0 + 4 * gq, U[it]);
     });
-    load_rows<T, BC, DK>(Qs, Cfg::LDQ, qh, a.d, t0, a.n, -1, tid);
-    load_rows<T, BC, DK>(Ks, Cfg::LDQ, kh, a.d, t0, a.n, -1, tid);
-    load_rows<T, BC, DVP>(Vs, Cfg::LDV, vh, a.dv, t0, a.n, NORM ? DV : -1, tid);
+    rq.put(Qs, Cfg::LDQ, tid);
+    rk.put(Ks, Cfg::LDQ, tid);
+    rv.put(Vs, Cfg::LDV, tid);
     __syncthreads();
+    {  // the next chunk's rows fly while this one is processed
+      const int tn = tok0 + min(ch + 1, nch - 1) * BC;
+      rq.fetch(qh, a.d, tn, a.n, -1, tid);
+      rk.fetch(kh, a.d, tn, a.n, -1, tid);
+      rv.fetch(vh, a.dv, tn, a.n, NORM ? DV : -1, tid);
+    }
     // Ad = L o D1 o (Q K^T)
     for_tiles<BC, BC>(w, [&](int i0, int j0, bool ok, int) {
       f32x4 x = pt<false, true, DK>(zero4(), Qs, Cfg::LDQ, Ks, Cfg::LDQ, i0, j0, lane);
@@ -318,7 +344,7 @@ __device__ __forceinline__ void bwd_adjoint_copy(T *smem, int w, int lane, const
 // Adjoint summary of a segment (segments 1 .. nseg-1): walked backwards from a
 // zero adjoint state at the segment end.
 template <typename T, int DK, int DV, int DVP, int BC, bool NORM>
-__global__ void __launch_bounds__(256) bwd_rsum_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(BWD_THREADS) bwd_rsum_kernel(BwdArgs a) {
   using Cfg = BwdCfg<T, DK, DVP, BC>;
   __shared__ __attribute__((aligned(16))) T smem[Cfg::ELEMS];
   __shared__ float pw[2 * BC + 3];
@@ -330,20 +356,33 @@ __global__ void __launch_bounds__(256) bwd_rsum_kernel(BwdArgs a) {
   const int nch = (tokE - tok0 + BC - 1) / BC;
   const T *qh = (const T *)a.q + (long)bh * a.n * a.d, *vh = (const T *)a.v + (long)bh * a.n * a.dv;
   const T *gh = (const T *)a.g + (long)bh * a.n * a.gld;
-  for (int e = tid; e < 2 * BC + 3; e += 256) pw[e] = exp2f((float)e * a.log2g);
+  for (int e = tid; e < 2 * BC + 3; e += BWD_THREADS) pw[e] = exp2f((float)e * a.log2g);
   f32x4 Ub[TileCount<DK, DVP>::PER], Sh[TileCount<DK, DK>::PER];
 #pragma unroll
   for (int i = 0; i < TileCount<DK, DVP>::PER; ++i) Ub[i] = zero4();
 #pragma unroll
   for (int i = 0; i < TileCount<DK, DK>::PER; ++i) Sh[i] = zero4();
   bwd_adjoint_copy<T, DK, DVP, BC>(smem, w, lane, Ub, Sh);
+  RowTile<T, BC, DK> rq;
+  RowTile<T, BC, DVP> rv, rg;
+  {
+    const int t0 = tok0 + (nch - 1) * BC;
+    rq.fetch(qh, a.d, t0, a.n, -1, tid);
+    rv.fetch(vh, a.dv, t0, a.n, NORM ? DV : -1, tid);
+    rg.fetch(gh, a.gld, t0, a.n, -1, tid);
+  }
 
   for (int ch = nch - 1; ch >= 0; --ch) {
-    const int t0 = tok0 + ch * BC;
-    load_rows<T, BC, DK>(Qs, Cfg::LDQ, qh, a.d, t0, a.n, -1, tid);
-    load_rows<T, BC, DVP>(Vs, Cfg::LDV, vh, a.dv, t0, a.n, NORM ? DV : -1, tid);
-    load_rows<T, BC, DVP>(Gs, Cfg::LDV, gh, a.gld, t0, a.n, -1, tid);
+    rq.put(Qs, Cfg::LDQ, tid);
+    rv.put(Vs, Cfg::LDV, tid);
+    rg.put(Gs, Cfg::LDV, tid);
     __syncthreads();
+    {  // the next (earlier) chunk's rows fly while this one is processed
+      const int tn = tok0 + max(ch - 1, 0) * BC;
+      rq.fetch(qh, a.d, tn, a.n, -1, tid);
+      rv.fetch(vh, a.dv, tn, a.n, NORM ? DV : -1, tid);
+      rg.fetch(gh, a.gld, tn, a.n, -1, tid);
+    }
     bwd_bm_zb<T, DK, DVP, BC>(smem, pw, w, lane);
     __syncthreads();
     bwd_adjoint_update<T, DK, DVP, BC>(smem, pw, w, lane, Ub, Sh);
@@ -362,7 +401,7 @@ __global__ void __launch_bounds__(256) bwd_rsum_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // Gradients: each segment walked backwards from its scanned adjoint state.
 template <typename T, int DK, int DV, int DVP, int BC, bool NORM>
-__global__ void __launch_bounds__(256) bwd_walk_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(BWD_THREADS) bwd_walk_kernel(BwdArgs a) {
   using Cfg = BwdCfg<T, DK, DVP, BC>;
   __shared__ __attribute__((aligned(16))) T smem[Cfg::ELEMS];
   __shared__ float pw[2 * BC + 3];
@@ -380,7 +419,7 @@ __global__ void __launch_bounds__(256) bwd_walk_kernel(BwdArgs a) {
   const T *gh = (const T *)a.g + (long)bh * a.n * a.gld;
   T *dqh = (T *)a.dq_out + hq, *dkh = (T *)a.dk_out + hq, *dvh = (T *)a.dv_out + hv;
   const T *cst = (const T *)a.cstate + ((long)bh * a.nbc + c0) * Cfg::BLOCK;
-  for (int e = tid; e < 2 * BC + 3; e += 256) pw[e] = exp2f((float)e * a.log2g);
+  for (int e = tid; e < 2 * BC + 3; e += BWD_THREADS) pw[e] = exp2f((float)e * a.log2g);
 
   f32x4 Ub[TileCount<DK, DVP>::PER], Sh[TileCount<DK, DK>::PER];
   {
@@ -393,15 +432,31 @@ __global__ void __launch_bounds__(256) bwd_walk_kernel(BwdArgs a) {
     });
   }
   bwd_adjoint_copy<T, DK, DVP, BC>(smem, w, lane, Ub, Sh);
+  RowTile<T, BC, DK> rq, rk;
+  RowTile<T, BC, DVP> rv, rg;
+  {
+    const int t0 = tok0 + (nch - 1) * BC;
+    rq.fetch(qh, a.d, t0, a.n, -1, tid);
+    rk.fetch(kh, a.d, t0, a.n, -1, tid);
+    rv.fetch(vh, a.dv, t0, a.n, NORM ? DV : -1, tid);
+    rg.fetch(gh, a.gld, t0, a.n, -1, tid);
+  }
 
   for (int ch = nch - 1; ch >= 0; --ch) {
     const int t0 = tok0 + ch * BC;
     const T *S0 = cst + (long)ch * Cfg::BLOCK, *U0 = S0 + DK * DK;  // global, row-major
-    load_rows<T, BC, DK>(Qs, Cfg::LDQ, qh, a.d, t0, a.n, -1, tid);
-    load_rows<T, BC, DK>(Ks, Cfg::LDQ, kh, a.d, t0, a.n, -1, tid);
-    load_rows<T, BC, DVP>(Vs, Cfg::LDV, vh, a.dv, t0, a.n, NORM ? DV : -1, tid);
-    load_rows<T, BC, DVP>(Gs, Cfg::LDV, gh, a.gld, t0, a.n, -1, tid);
+    rq.put(Qs, Cfg::LDQ, tid);
+    rk.put(Ks, Cfg::LDQ, tid);
+    rv.put(Vs, Cfg::LDV, tid);
+    rg.put(Gs, Cfg::LDV, tid);
     __syncthreads();
+    {  // the next (earlier) chunk's rows fly while this one is processed
+      const int tn = tok0 + max(ch - 1, 0) * BC;
+      rq.fetch(qh, a.d, tn, a.n, -1, tid);
+      rk.fetch(kh, a.d, tn, a.n, -1, tid);
+      rv.fetch(vh, a.dv, tn, a.n, NORM ? DV : -1, tid);
+      rg.fetch(gh, a.gld, tn, a.n, -1, tid);
+    }
     // Ad = L o D1 o (Q K^T)
     for_tiles<BC, BC>(w, [&](int i0, int j0, bool ok, int) {
       f32x4 x = pt<false, true, DK>(zero4(), Qs, Cfg::LDQ, Ks, Cfg::LDQ, i0, j0, lane);
