@@ -559,3 +559,140 @@ int hla2_oracle_backward_serial(int n, int d, int dv, double gamma, int normaliz
   free(gp); free(z); free(zb); free(S); free(U); free(Ub); free(Sb);
   return 0;
 }
+
+/* ===========================================================================
+ * AHLA, the asymmetric variant [SUM §2]: the operator Q (K^T Q)(K^T V), with
+ * the streaming summaries P^KV_t, m^K_t, E_t, n_t the page names.  Masked as
+ * the second-order case (every index at or before t), row t is
+ *     num_t = sum_{j<=t} sum_{i<=j} (q_t.k_j)(q_j.k_i) v_i,
+ * i.e. A A V with A = L o (Q K^T): the value of key i reaches query t through
+ * the intermediate key index j.  Reading of the summaries (the page gives only
+ * their names): P^KV_t = sum_{i<=t} k_i v_i^T and m^K_t = sum_{i<=t} k_i are
+ * the key-value and key-mass prefixes; E_t = sum_{j<=t} k_j (q_j^T P^KV_j) and
+ * n_t = sum_{j<=t} k_j (q_j . m^K_j) carry the inner sums already masked at
+ * their own index j, so num_t = q_t^T E_t and den_t = q_t^T n_t.  With decay
+ * every summary decays by gamma per token (as in the second-order case), so
+ * the term (j, i) carries gamma^{t-i}: num = A_g A_g V with A_g = D o A.
+ * State block: P[d*dv] | m[d] | E[d*dv] | n[d].
+ * ------------------------------------------------------------------------- */
+long hla2_oracle_ahla_state_len(int d, int dv) { return 2L * d * dv + 2L * d; }
+
+/* One token: P, m absorb (k, v); then E, n absorb k (q^T P_t), k (q . m_t); readout. */
+void hla2_oracle_ahla_step(int d, int dv, double gamma, double *state, const double *q, const double *k,
+                           const double *v, double *num, double *den) {
+  double *P = state, *m = P + (long)d * dv, *E = m + d, *nn = E + (long)d * dv;
+  int a, c;
+  double *qP = (double *)calloc((size_t)dv, sizeof(double));
+  double qm = 0.0;
+  for (a = 0; a < d; ++a) {
+    for (c = 0; c < dv; ++c) P[(long)a * dv + c] = gamma * P[(long)a * dv + c] + k[a] * v[c];
+    m[a] = gamma * m[a] + k[a];
+  }
+  for (a = 0; a < d; ++a) {
+    for (c = 0; c < dv; ++c) qP[c] += q[a] * P[(long)a * dv + c];
+    qm += q[a] * m[a];
+  }
+  for (a = 0; a < d; ++a) {
+    for (c = 0; c < dv; ++c) E[(long)a * dv + c] = gamma * E[(long)a * dv + c] + k[a] * qP[c];
+    nn[a] = gamma * nn[a] + k[a] * qm;
+  }
+  for (c = 0; c < dv; ++c) {
+    double s = 0.0;
+    for (a = 0; a < d; ++a) s += q[a] * E[(long)a * dv + c];
+    num[c] = s;
+  }
+  double sd = 0.0;
+  for (a = 0; a < d; ++a) sd += q[a] * nn[a];
+  *den = sd;
+  free(qP);
+}
+
+/* Serial recurrence (state nullable: zero start; else in/out). */
+int hla2_oracle_ahla_serial(int n, int d, int dv, double gamma, const double *q, const double *k,
+                            const double *v, double *num, double *den, double *state) {
+  long L = hla2_oracle_ahla_state_len(d, dv);
+  double *st = state ? state : (double *)calloc((size_t)L, sizeof(double));
+  int t;
+  if (!st) return -2;
+  for (t = 0; t < n; ++t) {
+    double dd;
+    hla2_oracle_ahla_step(d, dv, gamma, st, q + (long)t * d, k + (long)t * d, v + (long)t * dv,
+                          num + (long)t * dv, &dd);
+    if (den) den[t] = dd;
+  }
+  if (!state) free(st);
+  return 0;
+}
+
+/* The definition as a triple sum (small n). */
+int hla2_oracle_ahla_bruteforce(int n, int d, int dv, double gamma, const double *q, const double *k,
+                                const double *v, double *num, double *den) {
+  int t, j, i, a, c;
+  for (t = 0; t < n; ++t) {
+    for (c = 0; c < dv; ++c) num[(long)t * dv + c] = 0.0;
+    double sd = 0.0;
+    for (j = 0; j <= t; ++j) {
+      double qk_tj = 0.0;
+      for (a = 0; a < d; ++a) qk_tj += q[(long)t * d + a] * k[(long)j * d + a];
+      for (i = 0; i <= j; ++i) {
+        double qk_ji = 0.0;
+        for (a = 0; a < d; ++a) qk_ji += q[(long)j * d + a] * k[(long)i * d + a];
+        double w = pow(gamma, (double)(t - i)) * qk_tj * qk_ji;
+        for (c = 0; c < dv; ++c) num[(long)t * dv + c] += w * v[(long)i * dv + c];
+        sd += w;
+      }
+    }
+    if (den) den[t] = sd;
+  }
+  return 0;
+}
+
+/* Segment summary for the chunk-parallel form: (Gamma, P, m, E, n, M) of a run
+ * of len tokens from the zero state, with M = sum_j k_j q_j^T (d x d, no decay:
+ * for a later segment B, the term gamma^{end-1-j} k_j q_j^T (gamma^{j-start+1} P_A)
+ * loses every power of j, so E_{AB} = Gamma_B E_A + E_B + Gamma_B M_B P_A).
+ * Layout: Gamma | P | m | E | n | M. */
+long hla2_oracle_ahla_summary_len(int d, int dv) { return 1 + hla2_oracle_ahla_state_len(d, dv) + (long)d * d; }
+
+void hla2_oracle_ahla_summary(int len, int d, int dv, double gamma, const double *q, const double *k,
+                              const double *v, double *sum) {
+  long L = hla2_oracle_ahla_state_len(d, dv);
+  double *num = (double *)malloc(sizeof(double) * (size_t)(len > 0 ? len : 1) * dv);
+  double *M = sum + 1 + L;
+  int t, a, b;
+  memset(sum, 0, sizeof(double) * (size_t)hla2_oracle_ahla_summary_len(d, dv));
+  sum[0] = pow(gamma, (double)len);
+  hla2_oracle_ahla_serial(len, d, dv, gamma, q, k, v, num, NULL, sum + 1);
+  for (t = 0; t < len; ++t)
+    for (a = 0; a < d; ++a)
+      for (b = 0; b < d; ++b) M[(long)a * d + b] += k[(long)t * d + a] * q[(long)t * d + b];
+  free(num);
+}
+
+/* A then B: P = G_B P_A + P_B, m likewise, E = G_B E_A + E_B + G_B M_B P_A,
+ * n = G_B n_A + n_B + G_B M_B m_A, M = M_A + M_B, Gamma = G_A G_B. */
+void hla2_oracle_ahla_combine(int d, int dv, const double *A, const double *B, double *out) {
+  long L = hla2_oracle_ahla_state_len(d, dv);
+  const double GB = B[0];
+  const double *PA = A + 1, *mA = PA + (long)d * dv, *EA = mA + d, *nA = EA + (long)d * dv, *MA = A + 1 + L;
+  const double *PB = B + 1, *mB = PB + (long)d * dv, *EB = mB + d, *nB = EB + (long)d * dv, *MB = B + 1 + L;
+  double *tmp = (double *)malloc(sizeof(double) * (size_t)hla2_oracle_ahla_summary_len(d, dv));
+  double *Po = tmp + 1, *mo = Po + (long)d * dv, *Eo = mo + d, *no = Eo + (long)d * dv, *Mo = tmp + 1 + L;
+  int a, b, c;
+  tmp[0] = A[0] * GB;
+  for (a = 0; a < d; ++a) {
+    for (c = 0; c < dv; ++c) {
+      double s = 0.0;
+      for (b = 0; b < d; ++b) s += MB[(long)a * d + b] * PA[(long)b * dv + c];
+      Po[(long)a * dv + c] = GB * PA[(long)a * dv + c] + PB[(long)a * dv + c];
+      Eo[(long)a * dv + c] = GB * EA[(long)a * dv + c] + EB[(long)a * dv + c] + GB * s;
+    }
+    double s = 0.0;
+    for (b = 0; b < d; ++b) s += MB[(long)a * d + b] * mA[b];
+    mo[a] = GB * mA[a] + mB[a];
+    no[a] = GB * nA[a] + nB[a] + GB * s;
+    for (b = 0; b < d; ++b) Mo[(long)a * d + b] = MA[(long)a * d + b] + MB[(long)a * d + b];
+  }
+  memcpy(out, tmp, sizeof(double) * (size_t)hla2_oracle_ahla_summary_len(d, dv));
+  free(tmp);
+}

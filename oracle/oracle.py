@@ -77,6 +77,18 @@ def _load(path: str | None = None):
             lib.hla2_oracle_exclusive_scan.argtypes = [i, i, i, _dp]
             lib.hla2_oracle_chunked.restype = i
             lib.hla2_oracle_chunked.argtypes = [i, i, i, d_, i, _dp, _dp, _dp, _dp, _dp, _dp]
+            lib.hla2_oracle_ahla_state_len.restype = ctypes.c_long
+            lib.hla2_oracle_ahla_state_len.argtypes = [i, i]
+            lib.hla2_oracle_ahla_summary_len.restype = ctypes.c_long
+            lib.hla2_oracle_ahla_summary_len.argtypes = [i, i]
+            lib.hla2_oracle_ahla_serial.restype = i
+            lib.hla2_oracle_ahla_serial.argtypes = [i, i, i, d_, _dp, _dp, _dp, _dp, _dp, _dp]
+            lib.hla2_oracle_ahla_bruteforce.restype = i
+            lib.hla2_oracle_ahla_bruteforce.argtypes = [i, i, i, d_, _dp, _dp, _dp, _dp, _dp]
+            lib.hla2_oracle_ahla_summary.restype = None
+            lib.hla2_oracle_ahla_summary.argtypes = [i, i, i, d_, _dp, _dp, _dp, _dp]
+            lib.hla2_oracle_ahla_combine.restype = None
+            lib.hla2_oracle_ahla_combine.argtypes = [i, i, _dp, _dp, _dp]
             lib.hla2_oracle_backward_serial.restype = i
             lib.hla2_oracle_backward_serial.argtypes = [i, i, i, d_, i, _dp, _dp, _dp, _dp, _dp, _dp, _dp,
                                                         _dp, _dp]
@@ -377,4 +389,69 @@ def backward_serial(q, k, v, dout, gamma: float = 1.0, normalize: bool = False, 
     _run_heads(one, H, threads)
     lt = tuple(lead)
     return dq.reshape(lt + (n, d)), dk.reshape(lt + (n, d)), dvv.reshape(lt + (n, dv))
+
+
+# ---------------------------------------------------------------------------
+# AHLA, the asymmetric variant (see the AHLA section of hla2_oracle.c).
+
+def ahla_state_len(d: int, dv: int, lib=None) -> int:
+    return int((lib or _load()).hla2_oracle_ahla_state_len(d, dv))
+
+
+def ahla_summary_len(d: int, dv: int, lib=None) -> int:
+    return int((lib or _load()).hla2_oracle_ahla_summary_len(d, dv))
+
+
+def ahla_serial(q, k, v, gamma: float = 1.0, state=None, threads: int | None = None, lib=None):
+    """AHLA serial recurrence over every head.  Returns (num, den, final_state);
+    state: optional [..., ahla_state_len] initial state (P | m | E | n)."""
+    lib = lib or _load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    *lead, n, d = q.shape
+    dv = v.shape[-1]
+    H = int(np.prod(lead)) if lead else 1
+    qh, kh, vh = q.reshape(H, n, d), k.reshape(H, n, d), v.reshape(H, n, dv)
+    L = ahla_state_len(d, dv, lib)
+    st = np.zeros((H, L)) if state is None else _f64(state).reshape(H, L).copy()
+    num = np.empty((H, n, dv))
+    den = np.empty((H, n))
+
+    def one(h):
+        assert lib.hla2_oracle_ahla_serial(n, d, dv, float(gamma), _p(qh[h]), _p(kh[h]), _p(vh[h]), _p(num[h]),
+                                           _p(den[h]), _p(st[h])) == 0
+
+    _run_heads(one, H, threads)
+    lt = tuple(lead)
+    return num.reshape(lt + (n, dv)), den.reshape(lt + (n,)), st.reshape(lt + (L,))
+
+
+def ahla_bruteforce(q, k, v, gamma: float = 1.0, lib=None):
+    """AHLA definition as a triple sum, one head (small n).  Returns (num, den)."""
+    lib = lib or _load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    n, d = q.shape
+    dv = v.shape[-1]
+    num, den = np.empty((n, dv)), np.empty(n)
+    assert lib.hla2_oracle_ahla_bruteforce(n, d, dv, float(gamma), _p(q), _p(k), _p(v), _p(num), _p(den)) == 0
+    return num, den
+
+
+def ahla_summary(q, k, v, gamma: float = 1.0, lib=None):
+    """(Gamma, P, m, E, n, M) of one run of tokens; q, k: [len, d], v: [len, dv]."""
+    lib = lib or _load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    n, d = q.shape
+    dv = v.shape[-1]
+    out = np.empty(ahla_summary_len(d, dv, lib))
+    lib.hla2_oracle_ahla_summary(n, d, dv, float(gamma), _p(q), _p(k), _p(v), _p(out))
+    return out
+
+
+def ahla_combine(a, b, d: int, dv: int, lib=None):
+    """a then b (a is the earlier segment)."""
+    lib = lib or _load()
+    a, b = _f64(a), _f64(b)
+    out = np.empty(ahla_summary_len(d, dv, lib))
+    lib.hla2_oracle_ahla_combine(d, dv, _p(a), _p(b), _p(out))
+    return out
 
