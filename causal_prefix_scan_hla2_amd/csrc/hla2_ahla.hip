@@ -1,0 +1,234 @@
+// hla2_ahla.hip -- AHLA, the asymmetric variant of the technical summary of
+// arXiv 2510.27258 on gist.science (§2): the operator Q (K^T Q)(K^T V), causally
+// masked, row t
+//     num_t = sum_{j<=t} sum_{i<=j} g^(t-i) (q_t.k_j)(q_j.k_i) v_i,   den_t likewise with v_i -> 1,
+// i.e. A_g A_g V with A_g = L o D o (Q K^T).  Streaming summaries (the page
+// names them P^KV, m^K, E, n): P' = [P^KV | m^K] = sum g^(t-i) k_i v'_i^T with
+// v' = [v | 1], and E' = [E | n] = sum_j g^(t-j) k_j y_j^T with y_j = P'_j^T q_j;
+// then [num | den]_t = E'_t^T q_t.
+//
+// Chunk-parallel form (chunks of BC tokens, local index tau, Ad = L o D1 o (Q K^T)):
+//     Y = diag(g^(tau+1)) Q P0' + Ad V',     O = diag(g^(tau+1)) Q E0' + Ad Y,
+//     P' <- g^BC P' + K^T diag(g^(BC-1-i)) V',   E' <- g^BC E' + K^T diag(g^(BC-1-j)) Y,
+// and two consecutive segments A, B combine as
+//     P' = G_B P'_A + P'_B,   E' = G_B E'_A + E'_B + G_B M_B P'_A,   M = M_A + M_B,
+// with M_B = sum_{j in B} k_j q_j^T (no decay: the powers of j cancel).
+// Three launches, as for the second-order forward: segment summaries, the
+// exclusive scan over segments, and the output walk from each segment's prefix.
+#include "hla2_internal.h"
+#include "hla2_tiles.h"
+
+namespace hla2 {
+
+template <typename T, int DK, int DVP, int BC>
+struct AhlaCfg {
+  static constexpr int PAD = 16 / sizeof(T);
+  static constexpr int LDQ = DK + PAD, LDV = DVP + PAD, LDC = BC + PAD;
+  static constexpr int Q_OFF = 0, K_OFF = BC * LDQ, V_OFF = K_OFF + BC * LDQ, Y_OFF = V_OFF + BC * LDV,
+                       AD_OFF = Y_OFF + BC * LDV, P_OFF = AD_OFF + BC * LDC, E_OFF = P_OFF + DK * LDV,
+                       ELEMS = E_OFF + DK * LDV;
+};
+
+// Summary mode (OUT = false): segments 0 .. nseg-2 from the zero state, writing
+// P' | E' | M.  Output mode: every segment from its scanned prefix P' | E'.
+template <typename T, int DK, int DV, int DVP, int BC, bool OUT, bool NORM>
+__global__ void __launch_bounds__(BWD_THREADS) ahla_walk_kernel(AhlaArgs a) {
+  using Cfg = AhlaCfg<T, DK, DVP, BC>;
+  __shared__ __attribute__((aligned(16))) T smem[Cfg::ELEMS];
+  __shared__ float pw[2 * BC + 3];
+  __shared__ float dens[OUT ? BC : 1];
+  T *const Qs = smem + Cfg::Q_OFF, *const Ks = smem + Cfg::K_OFF, *const Vs = smem + Cfg::V_OFF;
+  T *const Ys = smem + Cfg::Y_OFF, *const Ads = smem + Cfg::AD_OFF, *const Ps = smem + Cfg::P_OFF;
+  T *const Es = smem + Cfg::E_OFF;
+  const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 4, nn = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nseg_here = OUT ? a.nseg : a.nseg - 1;
+  const int bh = blockIdx.x / nseg_here, seg = blockIdx.x % nseg_here;
+  const int tok0 = seg * a.cps * a.kc, tokE = min(a.n, tok0 + a.cps * a.kc);
+  const int nch = (tokE - tok0 + BC - 1) / BC;
+  const long hq = (long)bh * a.n * a.d, hv = (long)bh * a.n * a.dv;
+  const T *qh = (const T *)a.q + hq, *kh = (const T *)a.k + hq, *vh = (const T *)a.v + hv;
+  for (int e = tid; e < 2 * BC + 3; e += BWD_THREADS) pw[e] = exp2f((float)e * a.log2g);
+  constexpr long PB = 2L * DK * DVP, SB = 2L * DK * DVP + (long)DK * DK;
+
+  using TU = TileCount<DK, DVP>;
+  f32x4 P[TU::PER], E[TU::PER];
+  const float *pref = (OUT && seg > 0) ? a.prefix + ((long)bh * a.nseg + seg) * PB : nullptr;
+  for_tiles<DK, DVP>(w, [&](int i0, int j0, bool, int it) {
+    const int o = (i0 + nn) * DVP + j0 + 4 * gq;
+    P[it] = pref ? *(const f32x4 *)(pref + o) : zero4();
+    E[it] = pref ? *(const f32x4 *)(pref + DK * DVP + o) : zero4();
+  });
+  using TM = TileCount<DK, DK>;
+  f32x4 M[OUT ? 1 : TM::PER];
+#pragma unroll
+  for (int i = 0; i < (OUT ? 1 : TM::PER); ++i) M[i] = zero4();
+
+  RowTile<T, BC, DK> rq, rk;
+  RowTile<T, BC, DVP> rv;
+  rq.fetch(qh, a.d, tok0, a.n, -1, tid);
+  rk.fetch(kh, a.d, tok0, a.n, -1, tid);
+  rv.fetch(vh, a.dv, tok0, a.n, NORM ? DV : -1, tid);
+
+  for (int ch = 0; ch < nch; ++ch) {
+    const int t0 = tok0 + ch * BC;
+    // state copies for this chunk's products, and its rows
+    for_tiles<DK, DVP>(w, [&](int i0, int j0, bool ok, int it) {
+      if (ok) {
+        st4(Ps + (i0 + nn) * Cfg::LDV + j0 + 4 * gq, P[it]);
+        if (OUT) st4(Es + (i0 + nn) * Cfg::LDV + j0 + 4 * gq, E[it]);
+      }
+    });
+    rq.put(Qs, Cfg::LDQ, tid);
+    rk.put(Ks, Cfg::LDQ, tid);
+    rv.put(Vs, Cfg::LDV, tid);
+    __syncthreads();
+    {
+      const int tn = tok0 + min(ch + 1, nch - 1) * BC;
+      rq.fetch(qh, a.d, tn, a.n, -1, tid);
+      rk.fetch(kh, a.d, tn, a.n, -1, tid);
+      rv.fetch(vh, a.dv, tn, a.n, NORM ? DV : -1, tid);
+    }
+    // Ad = L o D1 o (Q K^T)
+    for_tiles<BC, BC>(w, [&](int i0, int j0, bool ok, int) {
+      f32x4 x = pt<false, true, DK>(zero4(), Qs, Cfg::LDQ, Ks, Cfg::LDQ, i0, j0, lane);
+      const int tr = i0 + nn;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int ti = j0 + 4 * gq + e;
+        x[e] = ti <= tr ? x[e] * pw[tr - ti] : 0.f;
+      }
+      if (ok) st4(Ads + tr * Cfg::LDC + j0 + 4 * gq, x);
+    });
+    __syncthreads();
+    // Y = diag(g^(tau+1)) Q P0' + Ad V'
+    for_tiles<BC, DVP>(w, [&](int i0, int j0, bool ok, int) {
+      f32x4 x = pt<false, false, DK>(zero4(), Qs, Cfg::LDQ, Ps, Cfg::LDV, i0, j0, lane);
+      x *= pw[i0 + nn + 1];
+      x = pt<false, false, BC>(x, Ads, Cfg::LDC, Vs, Cfg::LDV, i0, j0, lane);
+      if (ok) st4(Ys + (i0 + nn) * Cfg::LDV + j0 + 4 * gq, x);
+    });
+    __syncthreads();
+    // outputs O = diag(g^(tau+1)) Q E0' + Ad Y (kept in registers until den is known)
+    f32x4 O[OUT ? TileCount<BC, DVP>::PER : 1];
+    if constexpr (OUT) {
+      for_tiles<BC, DVP>(w, [&](int i0, int j0, bool ok, int it) {
+        f32x4 x = pt<false, false, DK>(zero4(), Qs, Cfg::LDQ, Es, Cfg::LDV, i0, j0, lane);
+        x *= pw[i0 + nn + 1];
+        x = pt<false, false, BC>(x, Ads, Cfg::LDC, Ys, Cfg::LDV, i0, j0, lane);
+        O[it] = x;
+        if (NORM && ok && j0 + 4 * gq == DV) dens[i0 + nn] = x[0];
+      });
+    } else {
+      // M += K^T Q (no decay)
+      for_tiles<DK, DK>(w, [&](int i0, int j0, bool, int it) {
+        M[it] = pt<true, false, BC>(M[it], Ks, Cfg::LDQ, Qs, Cfg::LDQ, i0, j0, lane);
+      });
+    }
+    // P' <- g^BC P' + K^T diag(g^(BC-1-i)) V';  E' <- g^BC E' + K^T diag(g^(BC-1-j)) Y
+    const float gB = pw[BC];
+    for_tiles<DK, DVP>(w, [&](int i0, int j0, bool, int it) {
+      P[it] = ptw<true, false, BC>(gB * P[it], Ks, Cfg::LDQ, Vs, Cfg::LDV, i0, j0, lane,
+                                   [&](int i) { return pw[BC - 1 - i]; });
+      E[it] = ptw<true, false, BC>(gB * E[it], Ks, Cfg::LDQ, Ys, Cfg::LDV, i0, j0, lane,
+                                   [&](int i) { return pw[BC - 1 - i]; });
+    });
+    __syncthreads();  // dens complete; every read of this chunk's LDS done
+    if constexpr (OUT) {
+      T *oh = (T *)a.out + hv;
+      for_tiles<BC, DVP>(w, [&](int i0, int j0, bool ok, int it) {
+        const int tr = i0 + nn, t = t0 + tr;
+        f32x4 x = O[it];
+        if (NORM && a.normalize) x *= 1.f / dens[tr];
+        if (ok) st_out(oh, a.dv, t, j0 + 4 * gq, a.n, x);
+      });
+      if (NORM && a.den_out && tid < BC && t0 + tid < a.n) a.den_out[(long)bh * a.n + t0 + tid] = dens[tid];
+    }
+  }
+  if constexpr (!OUT) {
+    float *sb = a.sums + ((long)bh * (a.nseg - 1) + seg) * SB;
+    for_tiles<DK, DVP>(w, [&](int i0, int j0, bool ok, int it) {
+      const int o = (i0 + nn) * DVP + j0 + 4 * gq;
+      if (ok) {
+        *(f32x4 *)(sb + o) = P[it];
+        *(f32x4 *)(sb + DK * DVP + o) = E[it];
+      }
+    });
+    for_tiles<DK, DK>(w, [&](int i0, int j0, bool ok, int it) {
+      if (ok) *(f32x4 *)(sb + 2 * DK * DVP + (i0 + nn) * DK + j0 + 4 * gq) = M[it];
+    });
+  }
+}
+
+// Exclusive scan over segments, per (b, h), fp32 on VALU:
+//   prefix_0 = 0;  P'_{r+1} = G P'_r + P'(seg r),  E'_{r+1} = G E'_r + E'(seg r) + G M(seg r) P'_r.
+// Each step reads the prefix it wrote before (the block's own global writes,
+// ordered by the barrier) and stages its P' in LDS for the cross term.
+template <int DK, int DVP>
+__global__ void __launch_bounds__(256) ahla_scan_kernel(AhlaArgs a, float gseg) {
+  constexpr long PB = 2L * DK * DVP, SB = 2L * DK * DVP + (long)DK * DK;
+  __shared__ __attribute__((aligned(16))) float Pl[DK * DVP];
+  const int tid = threadIdx.x, bh = blockIdx.x;
+  float *pre = a.prefix + (long)bh * a.nseg * PB;
+  for (int e = tid; e < 2 * DK * DVP; e += 256) pre[e] = 0.f;
+  for (int r = 0; r + 1 < a.nseg; ++r) {
+    const float *pr = pre + (long)r * PB;
+    float *pn = pre + (long)(r + 1) * PB;
+    const float *sb = a.sums + ((long)bh * (a.nseg - 1) + r) * SB, *Mr = sb + 2 * DK * DVP;
+    __syncthreads();  // prefix r written
+    for (int e = tid; e < DK * DVP; e += 256) Pl[e] = pr[e];
+    __syncthreads();
+    for (int e = tid; e < DK * DVP; e += 256) {
+      const int f = e / DVP, c = e % DVP;
+      float s = 0.f;
+      for (int g2 = 0; g2 < DK; ++g2) s += Mr[f * DK + g2] * Pl[g2 * DVP + c];
+      pn[DK * DVP + e] = gseg * (pr[DK * DVP + e] + s) + sb[DK * DVP + e];
+      pn[e] = gseg * Pl[e] + sb[e];
+    }
+  }
+}
+
+template <typename T, int DK, int DV, bool NORM>
+static hipError_t launch_ahla_t(int phase, int BH, const AhlaArgs &a, float gseg, hipStream_t s) {
+  constexpr int DVP = DV + (NORM ? Ktile<T>::ROWS : 0);
+  constexpr int BC = (sizeof(T) == 4 || DK == 128) ? 32 : 64;
+  switch (phase) {
+    case AHLA_SUMMARY:
+      hipLaunchKernelGGL((ahla_walk_kernel<T, DK, DV, DVP, BC, false, NORM>), dim3(BH * (a.nseg - 1)),
+                         dim3(BWD_THREADS), 0, s, a);
+      return hipGetLastError();
+    case AHLA_SCAN:
+      hipLaunchKernelGGL((ahla_scan_kernel<DK, DVP>), dim3(BH), dim3(256), 0, s, a, gseg);
+      return hipGetLastError();
+    case AHLA_OUTPUT:
+      hipLaunchKernelGGL((ahla_walk_kernel<T, DK, DV, DVP, BC, true, NORM>), dim3(BH * a.nseg), dim3(BWD_THREADS),
+                         0, s, a);
+      return hipGetLastError();
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T, int DK, int DV>
+static hipError_t launch_ahla_n(bool norm, int phase, int BH, const AhlaArgs &a, float gseg, hipStream_t s) {
+  return norm ? launch_ahla_t<T, DK, DV, true>(phase, BH, a, gseg, s)
+              : launch_ahla_t<T, DK, DV, false>(phase, BH, a, gseg, s);
+}
+
+int ahla_chunk(int dtype, int DK) { return (dtype == 0 || DK == 128) ? 32 : 64; }
+int ahla_dvp(int dtype, int DV, bool norm) { return DV + (norm ? (dtype == 0 ? 16 : 32) : 0); }
+
+hipError_t launch_ahla(int dtype, int DK, int DV, bool norm, int phase, int BH, const AhlaArgs &a, float gseg,
+                       hipStream_t s) {
+  if (dtype == 0) {
+    if (DK == 16 && DV == 16) return launch_ahla_n<float, 16, 16>(norm, phase, BH, a, gseg, s);
+    if (DK == 64 && DV == 64) return launch_ahla_n<float, 64, 64>(norm, phase, BH, a, gseg, s);
+    return hipErrorInvalidValue;
+  }
+  if (DK == 64 && DV == 64) return launch_ahla_n<bf16, 64, 64>(norm, phase, BH, a, gseg, s);
+  if (DK == 64 && DV == 128) return launch_ahla_n<bf16, 64, 128>(norm, phase, BH, a, gseg, s);
+  if (DK == 128 && DV == 64) return launch_ahla_n<bf16, 128, 64>(norm, phase, BH, a, gseg, s);
+  if (DK == 128 && DV == 128) return launch_ahla_n<bf16, 128, 128>(norm, phase, BH, a, gseg, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace hla2

@@ -326,6 +326,70 @@ int hla2_backward(const void *q, const void *k, const void *v, const void *out, 
   return HLA2_OK;
 }
 
+static size_t ahla_workspace(const Plan &p, int dtype) {
+  const size_t DK = (size_t)p.DK, DVP = (size_t)hla2::ahla_dvp(dtype == HLA2_F32 ? 0 : 1, p.DV, true);
+  const size_t BH = (size_t)p.BH, R = (size_t)p.nseg;
+  if (R == 1) return 0;
+  return align256(BH * (R - 1) * (2 * DK * DVP + DK * DK) * 4) + BH * R * 2 * DK * DVP * 4;
+}
+
+static Plan ahla_plan(int B, int H, int n, int d, int dv, int dtype, int segments) {
+  return make_plan(B, H, n, d, dv, dtype == HLA2_BF16 ? 64 : 32, dtype, segments, 1);
+}
+
+size_t hla2_ahla_forward_workspace_bytes(int B, int H, int n, int d, int dv, hla2_dtype_t dtype, int segments) {
+  if (segments < 0 || (dtype != HLA2_F32 && dtype != HLA2_BF16)) return 0;
+  if (check_shape(B, H, n, d, dv, dtype == HLA2_BF16 ? 64 : 32, (int)dtype) != HLA2_OK) return 0;
+  return ahla_workspace(ahla_plan(B, H, n, d, dv, (int)dtype, segments), (int)dtype);
+}
+
+int hla2_ahla_forward(const void *q, const void *k, const void *v, void *out, int B, int H, int n, int d, int dv,
+                      float decay, int normalize, hla2_dtype_t dtype, float *den_out, void *workspace,
+                      size_t workspace_bytes_given, int segments, hipStream_t stream) {
+  if (!q || !k || !v || !out) return HLA2_ERR_INVALID;
+  if (normalize != 0 && normalize != 1) return HLA2_ERR_INVALID;
+  if (segments < 0) return HLA2_ERR_INVALID;
+  if (!(decay > 0.0f && decay <= 1.0f)) return HLA2_ERR_INVALID;
+  if (dtype != HLA2_F32 && dtype != HLA2_BF16) return HLA2_ERR_INVALID;
+  int rc = check_shape(B, H, n, d, dv, dtype == HLA2_BF16 ? 64 : 32, (int)dtype);
+  if (rc != HLA2_OK) return rc;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return HLA2_ERR_INVALID;
+  if (den_out && !aligned(den_out, 4)) return HLA2_ERR_INVALID;
+  const Plan p = ahla_plan(B, H, n, d, dv, (int)dtype, segments);
+  const size_t need = ahla_workspace(p, (int)dtype);
+  if (need > 0 && (!workspace || workspace_bytes_given < need || !aligned(workspace, 256))) return HLA2_ERR_WORKSPACE;
+  const int dt = dtype == HLA2_F32 ? 0 : 1;
+  const bool norm = normalize || den_out;
+  const size_t DK = (size_t)p.DK, DVP = (size_t)hla2::ahla_dvp(dt, p.DV, norm);
+  hla2::AhlaArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.den_out = den_out;
+  a.sums = need ? (float *)workspace : nullptr;
+  a.prefix = need ? (float *)((char *)workspace + align256((size_t)p.BH * (p.nseg - 1) * (2 * DK * DVP + DK * DK) * 4))
+                  : nullptr;
+  a.n = n;
+  a.d = d;
+  a.dv = dv;
+  a.nseg = p.nseg;
+  a.cps = p.cps;
+  a.kc = p.kc;
+  a.log2g = decay < 1.0f ? log2f(decay) : 0.0f;
+  a.normalize = normalize;
+  const float gseg = decay < 1.0f ? (float)pow((double)decay, (double)p.cps * p.kc) : 1.0f;
+  hipError_t e;
+  if (p.nseg > 1) {
+    e = hla2::launch_ahla(dt, p.DK, p.DV, norm, hla2::AHLA_SUMMARY, (int)p.BH, a, gseg, stream);
+    if (e != hipSuccess) return HLA2_ERR_LAUNCH;
+    e = hla2::launch_ahla(dt, p.DK, p.DV, norm, hla2::AHLA_SCAN, (int)p.BH, a, gseg, stream);
+    if (e != hipSuccess) return HLA2_ERR_LAUNCH;
+  }
+  e = hla2::launch_ahla(dt, p.DK, p.DV, norm, hla2::AHLA_OUTPUT, (int)p.BH, a, gseg, stream);
+  return e == hipSuccess ? HLA2_OK : HLA2_ERR_LAUNCH;
+}
+
 int hla2_decode_step(float *state, const void *q, const void *k, const void *v, void *out, int N, int H,
                      int d, int dv, float decay, int normalize, hla2_dtype_t dtype, hipStream_t stream) {
   if (!state || !q || !k || !v || !out) return HLA2_ERR_INVALID;

@@ -147,4 +147,24 @@ int bwd_dvp(int dtype, int DV, bool norm);
 hipError_t launch_bwd(int dtype, int DK, int DV, bool norm, int phase, int BH, const BwdArgs &a,
                       const BwdPrepArgs &pa, float gL, hipStream_t s);
 
+
+// Arguments of the AHLA kernels (hla2_ahla.hip).
+struct AhlaArgs {
+  const void *q, *k, *v;   // [BH, n, d], [BH, n, d], [BH, n, dv]
+  void *out;               // [BH, n, dv]
+  float *den_out;          // [BH, n] or null
+  float *prefix;           // [BH, nseg] blocks of P' | E' (DK x DVP each, fp32)
+  float *sums;             // [BH, nseg-1] blocks of P' | E' | M (M: DK x DK)
+  int n, d, dv;
+  int nseg, cps, kc;       // segments of cps chunks of kc tokens
+  float log2g;             // log2(decay)
+  int normalize;
+};
+enum { AHLA_SUMMARY = 0, AHLA_SCAN = 1, AHLA_OUTPUT = 2 };
+int ahla_chunk(int dtype, int DK);
+int ahla_dvp(int dtype, int DV, bool norm);
+// one phase of the AHLA forward; gseg = decay^(tokens per full segment) (scan)
+hipError_t launch_ahla(int dtype, int DK, int DV, bool norm, int phase, int BH, const AhlaArgs &a, float gseg,
+                       hipStream_t s);
+
 }  // namespace hla2

@@ -1,0 +1,127 @@
+// hla2_tiles.h -- generic MFMA tile machinery of the chunk walkers that take
+// all their operands from LDS (the backward pass and AHLA): tile products with
+// either operand transposed, the split of a result's 16x16 tiles over the
+// waves of a workgroup, and row tiles fetched from global memory a chunk ahead.
+#pragma once
+#include "hla2_mfma.h"
+
+namespace hla2 {
+
+// ---------------------------------------------------------------------------
+// Tile products.  mm: acc(m0.., n0..) += sum_k A(m, k) B(k, n) over k < K, with
+// A(m, k) = AT ? A[k*lda + m] : A[m*lda + k] and B(k, n) = BT ? B[n*ldb + k] : B[k*ldb + n].
+// A transposed A or a non-transposed B is read with the LDS transpose read, so
+// those operands must live in LDS; the others may be global.  wk(k) scales the
+// k-th term.
+template <bool AT, bool BT, int K, typename T, typename WF>
+__device__ __forceinline__ f32x4 mmw(f32x4 acc, const T *A, int lda, const T *B, int ldb, int m0, int n0,
+                                     int lane, WF &&wk) {
+  constexpr int KT = Ktile<T>::ROWS;
+  static_assert(K % KT == 0, "contraction length must be a whole number of k-tiles");
+  const int g = lane >> 4;
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += KT) {
+    auto a = AT ? ld_cols(A, lda, k0, m0, lane) : ld_rows(A, lda, m0, k0, lane);
+    auto b = BT ? ld_rows(B, ldb, n0, k0, lane) : ld_cols(B, ldb, k0, n0, lane);
+    a = scale_frag(a, g, [&](int kk) { return wk(k0 + kk); });
+    acc = mma(a, b, acc);
+  }
+  return acc;
+}
+template <bool AT, bool BT, int K, typename T>
+__device__ __forceinline__ f32x4 mm(f32x4 acc, const T *A, int lda, const T *B, int ldb, int m0, int n0,
+                                    int lane) {
+  constexpr int KT = Ktile<T>::ROWS;
+  static_assert(K % KT == 0, "contraction length must be a whole number of k-tiles");
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += KT) {
+    auto a = AT ? ld_cols(A, lda, k0, m0, lane) : ld_rows(A, lda, m0, k0, lane);
+    auto b = BT ? ld_rows(B, ldb, n0, k0, lane) : ld_cols(B, ldb, k0, n0, lane);
+    acc = mma(a, b, acc);
+  }
+  return acc;
+}
+// Tile of P = X Y at P-rows i0.., P-columns j0.., computed as P^T so that lane
+// (g, n) holds P[i0 + n][j0 + 4g + e], e = 0..3.  XT: X(i, k) stored at X[k*ldx + i];
+// YT: Y(k, j) stored at Y[j*ldy + k].
+template <bool XT, bool YT, int K, typename T>
+__device__ __forceinline__ f32x4 pt(f32x4 acc, const T *X, int ldx, const T *Y, int ldy, int i0, int j0, int lane) {
+  return mm<!YT, !XT, K>(acc, Y, ldy, X, ldx, j0, i0, lane);
+}
+// the same with weights w(k) on the contraction index: P = X diag(w) Y
+template <bool XT, bool YT, int K, typename T, typename WF>
+__device__ __forceinline__ f32x4 ptw(f32x4 acc, const T *X, int ldx, const T *Y, int ldy, int i0, int j0, int lane,
+                                     WF &&wk) {
+  return mmw<!YT, !XT, K>(acc, Y, ldy, X, ldx, j0, i0, lane, wk);
+}
+
+// Waves per workgroup of these walkers (two per SIMD).
+constexpr int BWD_WAVES = 8, BWD_THREADS = 64 * BWD_WAVES;
+
+// Iterate a wave's share of the 16x16 tiles of an I x J result: f(i0, j0, store_ok, slot).
+template <int I, int J, typename F>
+__device__ __forceinline__ void for_tiles(int w, F &&f) {
+  constexpr int NJ = J / 16, NT = (I / 16) * NJ, PER = (NT + BWD_WAVES - 1) / BWD_WAVES;
+#pragma unroll
+  for (int it = 0; it < PER; ++it) {
+    const int t = w + BWD_WAVES * it;
+    const int tt = t < NT ? t : NT - 1;
+    f(16 * (tt / NJ), 16 * (tt % NJ), t < NT, it);
+  }
+}
+template <int I, int J> struct TileCount {
+  static constexpr int NT = (I / 16) * (J / 16), PER = (NT + BWD_WAVES - 1) / BWD_WAVES;
+};
+
+// 16-byte vector of the element type
+template <typename T> struct Vec16;
+template <> struct Vec16<bf16> {
+  typedef bf16x8 type;
+  static constexpr int N = 8;
+};
+template <> struct Vec16<float> {
+  typedef f32x4 type;
+  static constexpr int N = 4;
+};
+
+// Rows [t0, t0+BC) of a [n][gc] global matrix, as LDS rows of width W (zero
+// past n and past column gc; with ones >= 0, column `ones` holds 1 for rows
+// before n).  fetch() reads a thread's share into registers, put() writes them
+// to LDS, so the global reads of the next chunk can fly during this one.
+template <typename T, int BC, int W>
+struct RowTile {
+  typedef typename Vec16<T>::type V;
+  static constexpr int VN = Vec16<T>::N, PERROW = W / VN, TOT = BC * PERROW,
+                       PER = (TOT + BWD_THREADS - 1) / BWD_THREADS;
+  V x[PER];
+  __device__ __forceinline__ void fetch(const T *src, int gc, int t0, int n, int ones, int tid) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int i = tid + j * BWD_THREADS;
+      const int r = i / PERROW, c = (i % PERROW) * VN, t = t0 + r;
+      V v{};
+      if (i < TOT && t < n && c < gc) v = *(const V *)(src + (long)t * gc + c);
+      if (i < TOT && c == ones && t < n) v[0] = (T)1.f;
+      x[j] = v;
+    }
+  }
+  __device__ __forceinline__ void put(T *dst, int ld, int tid) const {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int i = tid + j * BWD_THREADS;
+      if (i < TOT) *(V *)(dst + (i / PERROW) * ld + (i % PERROW) * VN) = x[j];
+    }
+  }
+};
+
+// Store four consecutive values of row t, columns c .. c+3, of a [n][ncols] matrix.
+__device__ __forceinline__ void st_out(bf16 *dst, int ncols, int t, int c, int n, f32x4 x) {
+  if (t < n && c < ncols) *(bf16x4 *)(dst + (long)t * ncols + c) = bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
+}
+__device__ __forceinline__ void st_out(float *dst, int ncols, int t, int c, int n, f32x4 x) {
+  if (t < n && c < ncols) *(f32x4 *)(dst + (long)t * ncols + c) = x;
+}
+__device__ __forceinline__ void st4g(bf16 *p, f32x4 x) { *(bf16x4 *)p = bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]}; }
+__device__ __forceinline__ void st4g(float *p, f32x4 x) { *(f32x4 *)p = x; }
+
+}  // namespace hla2

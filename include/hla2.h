@@ -219,6 +219,35 @@ int hla2_backward(const void *q, const void *k, const void *v, const void *out, 
                   hla2_dtype_t dtype, void *workspace, size_t workspace_bytes, int segments,
                   hipStream_t stream);
 
+/*
+ * AHLA, the asymmetric variant [SUM §2]: the operator Q (K^T Q)(K^T V), masked
+ * like the second-order case (all indices at or before t):
+ *   num_t = sum_{j<=t} sum_{i<=j} g^{t-i} (q_t.k_j)(q_j.k_i) v_i,   den_t the same with v_i -> 1,
+ *   out_t = num_t, or num_t / den_t when normalize = 1 (IEEE division),
+ * i.e. A_g A_g V with A_g = L o D_g o (Q K^T).  The pages name its summaries
+ * P^KV, m^K, E, n but print no update; the reading used: P^KV and m^K are the
+ * decayed key-value and key-mass prefixes and E_t = g E_{t-1} + k_t (q_t^T P^KV_t),
+ * n_t likewise with m^K, so num_t = q_t^T E_t and den_t = q_t^T n_t.  Computed
+ * chunk-parallel [SUM §4]: segment summaries (P^KV, m^K, E, n and the segment's
+ * sum of k q^T), an exclusive scan with the combine
+ *   E_AB = G_B E_A + E_B + G_B (sum_{j in B} k_j q_j^T) P^KV_A,
+ * and the chunk outputs from each segment's incoming state.
+ *   q, k : [B, H, n, d];  v, out : [B, H, n, dv]  element type `dtype`
+ *   den_out: nullable [B, H, n] fp32 (written whatever `normalize` says)
+ *   workspace: at least hla2_ahla_forward_workspace_bytes(...) bytes for the
+ *          same shape, dtype and `segments`, 256-byte aligned (may be NULL when
+ *          that is 0, i.e. one segment)
+ *   segments: 0 picks the plan; otherwise as for hla2_forward_ex
+ * Supported shapes, alignment and errors as for hla2_forward (the chunking is
+ * internal: 64 tokens for bf16 at d <= 64, else 32).
+ */
+size_t hla2_ahla_forward_workspace_bytes(int B, int H, int n, int d, int dv, hla2_dtype_t dtype,
+                                         int segments);
+int hla2_ahla_forward(const void *q, const void *k, const void *v, void *out,
+                      int B, int H, int n, int d, int dv, float decay, int normalize,
+                      hla2_dtype_t dtype, float *den_out, void *workspace, size_t workspace_bytes,
+                      int segments, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -218,3 +218,28 @@ def test_backward_validates(L):
     assert H.hla2_backward_workspace_bytes(1, 1, 64, 64, 64, 1, 1) > need
     assert H.hla2_backward_workspace_bytes(1, 1, 4096, 64, 64, 0, 1) > need
     assert H.hla2_backward_workspace_bytes(1, 1, 64, 24, 64, 0, 1) == 0
+
+
+def ahla(L, q=P, k=P, v=P, out=P, B_=1, H_=1, n=64, d=64, dv=64, decay=1.0, norm=0, dtype=1, den=None, ws=None,
+         wsb=0, segments=0):
+    return L.hla2_ahla_forward(q, k, v, out, B_, H_, n, d, dv, decay, norm, dtype, den, ws, wsb, segments, None)
+
+
+def test_ahla_validates(L):
+    big = dict(ws=P, wsb=1 << 40)
+    assert ahla(L, q=None, **big) == H.HLA2_ERR_INVALID
+    assert ahla(L, norm=3, **big) == H.HLA2_ERR_INVALID
+    assert ahla(L, decay=1.5, **big) == H.HLA2_ERR_INVALID
+    assert ahla(L, segments=-1, **big) == H.HLA2_ERR_INVALID
+    assert ahla(L, dtype=5, **big) == H.HLA2_ERR_INVALID
+    assert ahla(L, dv=200, **big) == H.HLA2_ERR_UNSUPPORTED
+    assert ahla(L, d=128, dtype=0, **big) == H.HLA2_ERR_UNSUPPORTED
+    assert ahla(L, out=ctypes.c_void_p(4100), **big) == H.HLA2_ERR_INVALID
+    assert ahla(L, den=ctypes.c_void_p(4098), **big) == H.HLA2_ERR_INVALID
+    # several segments need a workspace; one segment needs none
+    shape = (4, 8, 2048, 64, 64)
+    need = H.hla2_ahla_forward_workspace_bytes(*shape, 1, 0)
+    assert need > 0 and H.hla2_ahla_forward_workspace_bytes(*shape, 1, 1) == 0
+    args = dict(B_=4, H_=8, n=2048)
+    assert ahla(L, **args) == H.HLA2_ERR_WORKSPACE
+    assert ahla(L, ws=P, wsb=need - 1, **args) == H.HLA2_ERR_WORKSPACE
