@@ -224,6 +224,31 @@ def bench_backward(w, steps, warmup, torch, H, I):
             "workspace_bytes": ws.numel()}
 
 
+def ahla_flops_per_head_token(w):
+    """AHLA chunk outputs per head-token at chunk C: Ad 2Cd, Y and O 2(2d dv' + 2C dv'), the P' and E'
+    updates 4 d dv' (dv' = dv + 1 under the ratio)."""
+    C, d, dv = w.chunk, w.d, w.dv + (1 if w.normalize else 0)
+    return 2 * C * d + 8 * d * dv + 4 * C * dv
+
+
+def bench_ahla(w, steps, warmup, torch, H, I):
+    """Time `steps` AHLA forward calls (the asymmetric variant) on the workload's shape."""
+    dev = torch.device("cuda:0")
+    q, k, v = (x.to(dev) for x in I.make_qkv(w))
+    out = torch.empty_like(v)
+    code = H.HLA2_BF16 if q.dtype == torch.bfloat16 else H.HLA2_F32
+    ws = torch.empty(max(H.hla2_ahla_forward_workspace_bytes(w.B, w.H, w.n, w.d, w.dv, code), 1),
+                     dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def fn():
+        H.hla2_ahla_forward(q, k, v, out, decay=w.decay, normalize=w.normalize, workspace=ws)
+
+    t, wall = time_calls(fn, steps, warmup, torch)
+    fl = ahla_flops_per_head_token(w) * w.B * w.H * w.n
+    return {"seconds": t, "tokens_per_s": w.B * w.n / t, "tflops": fl / t / 1e12, "mfma_frac": fl / t / PEAK_BF16_MFMA}
+
+
 def cpu_baseline(w, heads_sample, I):
     """The fp64 oracle (as it stands) on a bounded sample of the workload's
     heads: the serial recurrence, threaded over heads."""
@@ -268,6 +293,7 @@ def main(argv=None):
     ap.add_argument("--cpu-heads", type=int, default=128, help="heads in the oracle's timed sample (0: skip)")
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--skip-backward", action="store_true")
+    ap.add_argument("--skip-ahla", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="finish with two 1 GiB device copies (reference for HBM byte counters)")
     args = ap.parse_args(argv)
@@ -339,6 +365,11 @@ def main(argv=None):
             "head_tokens_per_s": bw["head_tokens_per_s"], "vs_forward_time": bw["seconds"] / fw["seconds"],
             "workspace_bytes": bw["workspace_bytes"],
         }
+    if not args.skip_ahla:
+        ah = bench_ahla(w, args.steps, args.warmup, torch, H, I)
+        line["ahla"] = {"workload": w.name + " shape", "ms_per_step": ah["seconds"] * 1e3,
+                        "tokens_per_s": ah["tokens_per_s"], "tflops": ah["tflops"], "mfma_frac": ah["mfma_frac"],
+                        "flops_per_head_token": ahla_flops_per_head_token(w)}
     if args.cpu_heads > 0:
         line["cpu_baseline"] = cpu_baseline(w, min(args.cpu_heads, w.B * w.H), I)
     if args.copy_calibration:
