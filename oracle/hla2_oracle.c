@@ -696,3 +696,178 @@ void hla2_oracle_ahla_combine(int d, int dv, const double *A, const double *B, d
   memcpy(out, tmp, sizeof(double) * (size_t)hla2_oracle_ahla_summary_len(d, dv));
   free(tmp);
 }
+
+/* ===========================================================================
+ * Third-order HLA [SUM §3]: the interaction A A^T A with A = Q K^T, masked so
+ * that no index passes t.  Reading (the page names the moments S^K, S^Q, P^KV
+ * and six cross summaries but prints no formula): with the middle query index
+ * l, the key j of the A A^T factor and the key i of the last A factor,
+ *   num_t = sum_{l<=t} sum_{j<=l} sum_{i<=l} g^{(t-j)+(t-l)+(t-i)}
+ *                                 (q_t.k_j)(q_l.k_j)(q_l.k_i) v_i,
+ * den_t likewise with v_i -> 1; unmasked and undecayed this is
+ * q_t^T S^K S^Q P^KV, and every one of the three moments decays by g per token.
+ * In matrix form num = (L o D_{g^2} o (A_g A^T)) (A_g V) with A = L o (Q K^T)
+ * and A_g = D_g o A.
+ * Streaming form used here (the cross summaries are folded into one corrected
+ * accumulator, as U = S C - G for the second order): with z_l = S^K_l q_l and
+ * y'_l = P'_l^T q_l, P' = [P^KV | m^K] (key-value and key-mass prefixes),
+ *   W'_t = g^3 W'_{t-1} + z_t y'_t^T,   [num | den]_t = W'_t^T q_t.
+ * State block: S[d*d] | P[d*dv] | m[d] | W[d*dv] | w[d]  (W' = [W | w]).
+ * ------------------------------------------------------------------------- */
+long hla2_oracle_ho3_state_len(int d, int dv) { return (long)d * d + 2L * d * (dv + 1); }
+
+void hla2_oracle_ho3_step(int d, int dv, double gamma, double *state, const double *q, const double *k,
+                          const double *v, double *num, double *den) {
+  const int dvp = dv + 1;
+  double *S = state, *P = S + (long)d * d, *W = P + (long)d * dvp;  /* P, W with the extra column */
+  const double g3 = gamma * gamma * gamma;
+  int a, b, c;
+  double *z = (double *)calloc((size_t)d, sizeof(double));
+  double *y = (double *)calloc((size_t)dvp, sizeof(double));
+  for (a = 0; a < d; ++a) {
+    for (b = 0; b < d; ++b) S[(long)a * d + b] = gamma * S[(long)a * d + b] + k[b] * k[a];
+    for (c = 0; c < dv; ++c) P[(long)a * dvp + c] = gamma * P[(long)a * dvp + c] + k[a] * v[c];
+    P[(long)a * dvp + dv] = gamma * P[(long)a * dvp + dv] + k[a];
+  }
+  for (a = 0; a < d; ++a) {
+    for (b = 0; b < d; ++b) z[a] += S[(long)a * d + b] * q[b];
+    for (c = 0; c < dvp; ++c) y[c] += q[a] * P[(long)a * dvp + c];
+  }
+  for (a = 0; a < d; ++a)
+    for (c = 0; c < dvp; ++c) W[(long)a * dvp + c] = g3 * W[(long)a * dvp + c] + z[a] * y[c];
+  for (c = 0; c < dvp; ++c) {
+    double s = 0.0;
+    for (a = 0; a < d; ++a) s += q[a] * W[(long)a * dvp + c];
+    if (c < dv) num[c] = s;
+    else *den = s;
+  }
+  free(z);
+  free(y);
+}
+
+int hla2_oracle_ho3_serial(int n, int d, int dv, double gamma, const double *q, const double *k,
+                           const double *v, double *num, double *den, double *state) {
+  long L = hla2_oracle_ho3_state_len(d, dv);
+  double *st = state ? state : (double *)calloc((size_t)L, sizeof(double));
+  int t;
+  if (!st) return -2;
+  for (t = 0; t < n; ++t) {
+    double dd;
+    hla2_oracle_ho3_step(d, dv, gamma, st, q + (long)t * d, k + (long)t * d, v + (long)t * dv,
+                         num + (long)t * dv, &dd);
+    if (den) den[t] = dd;
+  }
+  if (!state) free(st);
+  return 0;
+}
+
+static double ho3_dot(int d, const double *x, const double *y) {
+  double s = 0.0;
+  int a;
+  for (a = 0; a < d; ++a) s += x[a] * y[a];
+  return s;
+}
+
+/* The definition as a quadruple sum (small n). */
+int hla2_oracle_ho3_bruteforce(int n, int d, int dv, double gamma, const double *q, const double *k,
+                               const double *v, double *num, double *den) {
+  int t, l, j, i, c;
+  for (t = 0; t < n; ++t) {
+    double sd = 0.0;
+    for (c = 0; c < dv; ++c) num[(long)t * dv + c] = 0.0;
+    for (l = 0; l <= t; ++l)
+      for (j = 0; j <= l; ++j) {
+        double f1 = ho3_dot(d, q + (long)t * d, k + (long)j * d) * ho3_dot(d, q + (long)l * d, k + (long)j * d);
+        for (i = 0; i <= l; ++i) {
+          double w = pow(gamma, (double)((t - j) + (t - l) + (t - i))) * f1 * ho3_dot(d, q + (long)l * d, k + (long)i * d);
+          for (c = 0; c < dv; ++c) num[(long)t * dv + c] += w * v[(long)i * dv + c];
+          sd += w;
+        }
+      }
+    if (den) den[t] = sd;
+  }
+  return 0;
+}
+
+/* Segment summary for the chunk-parallel form, from the zero state over len
+ * tokens (u = 0 .. len-1 inside the segment, z^B, y'^B the segment-local values):
+ *   the state part (S, P', W') and the maps that fold an incoming state
+ *   (S_A, P'_A) into W' at the segment end:
+ *     Q2 = sum_u g^{3len-1-u} q_u q_u^T            (d x d)
+ *     X1 = sum_u g^{3len-2-2u} q_u y'^B_u^T         (d x (dv+1))
+ *     X2 = sum_u g^{3len-2-2u} z^B_u q_u^T          (d x d)
+ *   W'_end = g^{3len} W'_A + W'_B + S_A Q2 P'_A + S_A X1 + X2 P'_A,
+ *   S_end = g^len S_A + S_B,  P'_end = g^len P'_A + P'_B.
+ * (Inside the segment z_u = g^{u+1} S_A q_u + z^B_u and y'_u = g^{u+1} P'_A^T q_u + y'^B_u;
+ * the powers collect into the weights above.)
+ * Layout: Gamma | state | Q2 | X1 | X2. */
+long hla2_oracle_ho3_summary_len(int d, int dv) {
+  return 1 + hla2_oracle_ho3_state_len(d, dv) + 2L * d * d + (long)d * (dv + 1);
+}
+
+void hla2_oracle_ho3_summary(int len, int d, int dv, double gamma, const double *q, const double *k,
+                             const double *v, double *sum) {
+  const int dvp = dv + 1;
+  long L = hla2_oracle_ho3_state_len(d, dv);
+  double *st = sum + 1, *Q2 = sum + 1 + L, *X1 = Q2 + (long)d * d, *X2 = X1 + (long)d * dvp;
+  double *num = (double *)malloc(sizeof(double) * (size_t)dv), dd;
+  double *S = st, *P = S + (long)d * d;
+  double *z = (double *)malloc(sizeof(double) * (size_t)d), *y = (double *)malloc(sizeof(double) * (size_t)dvp);
+  int u, a, b, c;
+  memset(sum, 0, sizeof(double) * (size_t)hla2_oracle_ho3_summary_len(d, dv));
+  sum[0] = pow(gamma, (double)len);
+  for (u = 0; u < len; ++u) {
+    const double *qu = q + (long)u * d;
+    hla2_oracle_ho3_step(d, dv, gamma, st, qu, k + (long)u * d, v + (long)u * dv, num, &dd);
+    /* segment-local z, y' after the token */
+    for (a = 0; a < d; ++a) {
+      z[a] = 0.0;
+      for (b = 0; b < d; ++b) z[a] += S[(long)a * d + b] * qu[b];
+    }
+    for (c = 0; c < dvp; ++c) {
+      y[c] = 0.0;
+      for (a = 0; a < d; ++a) y[c] += qu[a] * P[(long)a * dvp + c];
+    }
+    const double wq = pow(gamma, (double)(3 * len - 1 - u)), wx = pow(gamma, (double)(3 * len - 2 - 2 * u));
+    for (a = 0; a < d; ++a) {
+      for (b = 0; b < d; ++b) {
+        Q2[(long)a * d + b] += wq * qu[a] * qu[b];
+        X2[(long)a * d + b] += wx * z[a] * qu[b];
+      }
+      for (c = 0; c < dvp; ++c) X1[(long)a * dvp + c] += wx * qu[a] * y[c];
+    }
+  }
+  free(num); free(z); free(y);
+}
+
+/* Fold a segment summary into a state (the exclusive scan's step). */
+void hla2_oracle_ho3_apply(int d, int dv, const double *sum, double *state) {
+  const int dvp = dv + 1;
+  long L = hla2_oracle_ho3_state_len(d, dv);
+  const double G = sum[0], G3 = G * G * G;
+  const double *SB = sum + 1, *PB = SB + (long)d * d, *WB = PB + (long)d * dvp;
+  const double *Q2 = sum + 1 + L, *X1 = Q2 + (long)d * d, *X2 = X1 + (long)d * dvp;
+  double *S = state, *P = S + (long)d * d, *W = P + (long)d * dvp;
+  double *SQ = (double *)calloc((size_t)d * d, sizeof(double));
+  double *Wn = (double *)calloc((size_t)d * dvp, sizeof(double));
+  int a, b, c;
+  for (a = 0; a < d; ++a)
+    for (b = 0; b < d; ++b)
+      for (c = 0; c < d; ++c) SQ[(long)a * d + b] += S[(long)a * d + c] * Q2[(long)c * d + b];
+  for (a = 0; a < d; ++a)
+    for (c = 0; c < dvp; ++c) {
+      double s = G3 * W[(long)a * dvp + c] + WB[(long)a * dvp + c];
+      for (b = 0; b < d; ++b)
+        s += SQ[(long)a * d + b] * P[(long)b * dvp + c] + S[(long)a * d + b] * X1[(long)b * dvp + c] +
+             X2[(long)a * d + b] * P[(long)b * dvp + c];
+      Wn[(long)a * dvp + c] = s;
+    }
+  for (a = 0; a < d; ++a) {
+    for (b = 0; b < d; ++b) S[(long)a * d + b] = G * S[(long)a * d + b] + SB[(long)a * d + b];
+    for (c = 0; c < dvp; ++c) {
+      P[(long)a * dvp + c] = G * P[(long)a * dvp + c] + PB[(long)a * dvp + c];
+      W[(long)a * dvp + c] = Wn[(long)a * dvp + c];
+    }
+  }
+  free(SQ); free(Wn);
+}

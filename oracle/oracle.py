@@ -89,6 +89,18 @@ def _load(path: str | None = None):
             lib.hla2_oracle_ahla_summary.argtypes = [i, i, i, d_, _dp, _dp, _dp, _dp]
             lib.hla2_oracle_ahla_combine.restype = None
             lib.hla2_oracle_ahla_combine.argtypes = [i, i, _dp, _dp, _dp]
+            lib.hla2_oracle_ho3_state_len.restype = ctypes.c_long
+            lib.hla2_oracle_ho3_state_len.argtypes = [i, i]
+            lib.hla2_oracle_ho3_summary_len.restype = ctypes.c_long
+            lib.hla2_oracle_ho3_summary_len.argtypes = [i, i]
+            lib.hla2_oracle_ho3_serial.restype = i
+            lib.hla2_oracle_ho3_serial.argtypes = [i, i, i, d_, _dp, _dp, _dp, _dp, _dp, _dp]
+            lib.hla2_oracle_ho3_bruteforce.restype = i
+            lib.hla2_oracle_ho3_bruteforce.argtypes = [i, i, i, d_, _dp, _dp, _dp, _dp, _dp]
+            lib.hla2_oracle_ho3_summary.restype = None
+            lib.hla2_oracle_ho3_summary.argtypes = [i, i, i, d_, _dp, _dp, _dp, _dp]
+            lib.hla2_oracle_ho3_apply.restype = None
+            lib.hla2_oracle_ho3_apply.argtypes = [i, i, _dp, _dp]
             lib.hla2_oracle_backward_serial.restype = i
             lib.hla2_oracle_backward_serial.argtypes = [i, i, i, d_, i, _dp, _dp, _dp, _dp, _dp, _dp, _dp,
                                                         _dp, _dp]
@@ -454,4 +466,68 @@ def ahla_combine(a, b, d: int, dv: int, lib=None):
     out = np.empty(ahla_summary_len(d, dv, lib))
     lib.hla2_oracle_ahla_combine(d, dv, _p(a), _p(b), _p(out))
     return out
+
+
+# ---------------------------------------------------------------------------
+# Third-order HLA (see the third-order section of hla2_oracle.c).
+
+def ho3_state_len(d: int, dv: int, lib=None) -> int:
+    return int((lib or _load()).hla2_oracle_ho3_state_len(d, dv))
+
+
+def ho3_summary_len(d: int, dv: int, lib=None) -> int:
+    return int((lib or _load()).hla2_oracle_ho3_summary_len(d, dv))
+
+
+def ho3_serial(q, k, v, gamma: float = 1.0, state=None, threads: int | None = None, lib=None):
+    """Third-order serial recurrence over every head.  Returns (num, den, final_state);
+    state: optional [..., ho3_state_len] initial state (S | P' | W')."""
+    lib = lib or _load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    *lead, n, d = q.shape
+    dv = v.shape[-1]
+    H = int(np.prod(lead)) if lead else 1
+    qh, kh, vh = q.reshape(H, n, d), k.reshape(H, n, d), v.reshape(H, n, dv)
+    L = ho3_state_len(d, dv, lib)
+    st = np.zeros((H, L)) if state is None else _f64(state).reshape(H, L).copy()
+    num = np.empty((H, n, dv))
+    den = np.empty((H, n))
+
+    def one(h):
+        assert lib.hla2_oracle_ho3_serial(n, d, dv, float(gamma), _p(qh[h]), _p(kh[h]), _p(vh[h]), _p(num[h]),
+                                          _p(den[h]), _p(st[h])) == 0
+
+    _run_heads(one, H, threads)
+    lt = tuple(lead)
+    return num.reshape(lt + (n, dv)), den.reshape(lt + (n,)), st.reshape(lt + (L,))
+
+
+def ho3_bruteforce(q, k, v, gamma: float = 1.0, lib=None):
+    """Third-order definition as a quadruple sum, one head (small n).  Returns (num, den)."""
+    lib = lib or _load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    n, d = q.shape
+    dv = v.shape[-1]
+    num, den = np.empty((n, dv)), np.empty(n)
+    assert lib.hla2_oracle_ho3_bruteforce(n, d, dv, float(gamma), _p(q), _p(k), _p(v), _p(num), _p(den)) == 0
+    return num, den
+
+
+def ho3_summary(q, k, v, gamma: float = 1.0, lib=None):
+    """(Gamma, S, P', W', Q2, X1, X2) of one run of tokens."""
+    lib = lib or _load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    n, d = q.shape
+    dv = v.shape[-1]
+    out = np.empty(ho3_summary_len(d, dv, lib))
+    lib.hla2_oracle_ho3_summary(n, d, dv, float(gamma), _p(q), _p(k), _p(v), _p(out))
+    return out
+
+
+def ho3_apply(summary, state, d: int, dv: int, lib=None):
+    """The state after a segment, from the state before it and the segment's summary (copied)."""
+    lib = lib or _load()
+    st = _f64(state).copy()
+    lib.hla2_oracle_ho3_apply(d, dv, _p(_f64(summary)), _p(st))
+    return st
 
