@@ -390,6 +390,73 @@ int hla2_ahla_forward(const void *q, const void *k, const void *v, void *out, in
   return e == hipSuccess ? HLA2_OK : HLA2_ERR_LAUNCH;
 }
 
+static size_t ho3_sums_bytes(const Plan &p, int dt, bool norm) {
+  const size_t DK = (size_t)p.DK, DVP = (size_t)hla2::ho3_dvp(dt, p.DV, norm);
+  return (size_t)p.BH * (p.nseg - 1) * (DK * DK + 2 * DK * DVP + 2 * DK * DK + DK * DVP) * 4;
+}
+static size_t ho3_workspace(const Plan &p, int dtype) {
+  if (p.nseg == 1) return 0;
+  const int dt = dtype == HLA2_F32 ? 0 : 1;
+  const size_t DK = (size_t)p.DK, DVP = (size_t)hla2::ho3_dvp(dt, p.DV, true);
+  return align256(ho3_sums_bytes(p, dt, true)) + (size_t)p.BH * p.nseg * (DK * DK + 2 * DK * DVP) * 4;
+}
+static int ho3_check(int B, int H, int n, int d, int dv, int dtype) {
+  int rc = check_shape(B, H, n, d, dv, dtype == HLA2_BF16 ? 64 : 32, dtype);
+  if (rc != HLA2_OK) return rc;
+  return d > 64 ? HLA2_ERR_UNSUPPORTED : HLA2_OK;  // the third-order state (d x d twice) is held for d <= 64
+}
+
+size_t hla2_ho3_forward_workspace_bytes(int B, int H, int n, int d, int dv, hla2_dtype_t dtype, int segments) {
+  if (segments < 0 || (dtype != HLA2_F32 && dtype != HLA2_BF16)) return 0;
+  if (ho3_check(B, H, n, d, dv, (int)dtype) != HLA2_OK) return 0;
+  return ho3_workspace(ahla_plan(B, H, n, d, dv, (int)dtype, segments), (int)dtype);
+}
+
+int hla2_ho3_forward(const void *q, const void *k, const void *v, void *out, int B, int H, int n, int d, int dv,
+                     float decay, int normalize, hla2_dtype_t dtype, float *den_out, void *workspace,
+                     size_t workspace_bytes_given, int segments, hipStream_t stream) {
+  if (!q || !k || !v || !out) return HLA2_ERR_INVALID;
+  if (normalize != 0 && normalize != 1) return HLA2_ERR_INVALID;
+  if (segments < 0) return HLA2_ERR_INVALID;
+  if (!(decay > 0.0f && decay <= 1.0f)) return HLA2_ERR_INVALID;
+  if (dtype != HLA2_F32 && dtype != HLA2_BF16) return HLA2_ERR_INVALID;
+  int rc = ho3_check(B, H, n, d, dv, (int)dtype);
+  if (rc != HLA2_OK) return rc;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return HLA2_ERR_INVALID;
+  if (den_out && !aligned(den_out, 4)) return HLA2_ERR_INVALID;
+  const Plan p = ahla_plan(B, H, n, d, dv, (int)dtype, segments);
+  const size_t need = ho3_workspace(p, (int)dtype);
+  if (need > 0 && (!workspace || workspace_bytes_given < need || !aligned(workspace, 256))) return HLA2_ERR_WORKSPACE;
+  const int dt = dtype == HLA2_F32 ? 0 : 1;
+  const bool norm = normalize || den_out;
+  hla2::Ho3Args a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.den_out = den_out;
+  a.sums = need ? (float *)workspace : nullptr;
+  a.prefix = need ? (float *)((char *)workspace + align256(ho3_sums_bytes(p, dt, norm))) : nullptr;
+  a.n = n;
+  a.d = d;
+  a.dv = dv;
+  a.nseg = p.nseg;
+  a.cps = p.cps;
+  a.kc = p.kc;
+  a.log2g = decay < 1.0f ? log2f(decay) : 0.0f;
+  a.normalize = normalize;
+  const float gseg = decay < 1.0f ? (float)pow((double)decay, (double)p.cps * p.kc) : 1.0f;
+  hipError_t e;
+  if (p.nseg > 1) {
+    e = hla2::launch_ho3(dt, p.DK, p.DV, norm, hla2::HO3_SUMMARY, (int)p.BH, a, gseg, stream);
+    if (e != hipSuccess) return HLA2_ERR_LAUNCH;
+    e = hla2::launch_ho3(dt, p.DK, p.DV, norm, hla2::HO3_SCAN, (int)p.BH, a, gseg, stream);
+    if (e != hipSuccess) return HLA2_ERR_LAUNCH;
+  }
+  e = hla2::launch_ho3(dt, p.DK, p.DV, norm, hla2::HO3_OUTPUT, (int)p.BH, a, gseg, stream);
+  return e == hipSuccess ? HLA2_OK : HLA2_ERR_LAUNCH;
+}
+
 int hla2_decode_step(float *state, const void *q, const void *k, const void *v, void *out, int N, int H,
                      int d, int dv, float decay, int normalize, hla2_dtype_t dtype, hipStream_t stream) {
   if (!state || !q || !k || !v || !out) return HLA2_ERR_INVALID;

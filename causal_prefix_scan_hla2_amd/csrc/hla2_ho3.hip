@@ -1,0 +1,294 @@
+// hla2_ho3.hip -- third-order HLA (technical summary of arXiv 2510.27258 on
+// gist.science, §3): the interaction A A^T A with A = Q K^T, masked so that no
+// index passes t, row t
+//   num_t = sum_{l<=t} sum_{j<=l} sum_{i<=l} g^((t-j)+(t-l)+(t-i)) (q_t.k_j)(q_l.k_j)(q_l.k_i) v_i,
+// den_t likewise with v_i -> 1: num = (L o D_{g^2} o (A_g A^T)) (A_g V).  The three
+// prefix moments the page names (key moment S, the key-value prefix P and,
+// through the segment maps, the query moment) carry it; the cross summaries
+// are folded into one corrected accumulator W' (d x (dv+1)):
+//   z_t = S_t q_t,  y'_t = P'_t^T q_t,  W'_t = g^3 W'_{t-1} + z_t y'_t^T,  [num|den]_t = W'_t^T q_t.
+//
+// Chunk form (BC tokens, local tau, Ad = L o D1 o (Q K^T), D3[t][l] = g^(3(t-l))):
+//   Z = diag(g^(tau+1)) Q S0 + Ad K,   Y = diag(g^(tau+1)) Q P0' + Ad V',
+//   O = diag(g^(3(tau+1))) Q W0' + (L o D3 o (Q Z^T)) Y,
+//   S <- g^BC S + K^T diag(g^(BC-1-i)) K,  P' <- g^BC P' + K^T diag(g^(BC-1-i)) V',
+//   W' <- g^(3BC) W' + Z^T diag(g^(3(BC-1-l))) Y.
+// A segment of L tokens (u = 0..L-1) folds an incoming (S_A, P'_A, W'_A) as
+//   W' = g^(3L) W'_A + W'_B + S_A Q2 P'_A + S_A X1 + X2 P'_A,  S = g^L S_A + S_B,  P' = g^L P'_A + P'_B,
+// with the segment maps (the page's segment-level linear maps)
+//   Q2 = sum_u g^(3L-1-u) q_u q_u^T,  X1 = sum_u g^(3L-2-2u) q_u y'_u^T,  X2 = sum_u g^(3L-2-2u) z_u q_u^T
+// over the segment's own (zero-start) z, y'.
+#include "hla2_internal.h"
+#include "hla2_tiles.h"
+
+namespace hla2 {
+
+template <typename T, int DK, int DVP, int BC>
+struct Ho3Cfg {
+  static constexpr int PAD = 16 / sizeof(T);
+  static constexpr int LDQ = DK + PAD, LDV = DVP + PAD, LDC = BC + PAD;
+  static constexpr int Q_OFF = 0, K_OFF = BC * LDQ, V_OFF = K_OFF + BC * LDQ, Y_OFF = V_OFF + BC * LDV,
+                       Z_OFF = Y_OFF + BC * LDV, AD_OFF = Z_OFF + BC * LDQ, WM_OFF = AD_OFF + BC * LDC,
+                       S_OFF = WM_OFF + BC * LDC, P_OFF = S_OFF + DK * LDQ, W_OFF = P_OFF + DK * LDV,
+                       ELEMS = W_OFF + DK * LDV;
+  static constexpr long PB = (long)DK * DK + 2L * DK * DVP;                 // S | P' | W'
+  static constexpr long SB = PB + 2L * DK * DK + (long)DK * DVP;            // ... | Q2 | X1 | X2
+};
+
+template <typename T, int DK, int DV, int DVP, int BC, bool OUT, bool NORM>
+__global__ void __launch_bounds__(BWD_THREADS) ho3_walk_kernel(Ho3Args a) {
+  using Cfg = Ho3Cfg<T, DK, DVP, BC>;
+  __shared__ __attribute__((aligned(16))) T smem[Cfg::ELEMS];
+  __shared__ float pw[3 * BC + 4];
+  __shared__ float dens[OUT ? BC : 1];
+  T *const Qs = smem + Cfg::Q_OFF, *const Ks = smem + Cfg::K_OFF, *const Vs = smem + Cfg::V_OFF;
+  T *const Ys = smem + Cfg::Y_OFF, *const Zs = smem + Cfg::Z_OFF, *const Ads = smem + Cfg::AD_OFF;
+  T *const Wms = smem + Cfg::WM_OFF, *const Ss = smem + Cfg::S_OFF, *const Ps = smem + Cfg::P_OFF;
+  T *const Ws = smem + Cfg::W_OFF;
+  const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 4, nn = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nseg_here = OUT ? a.nseg : a.nseg - 1;
+  const int bh = blockIdx.x / nseg_here, seg = blockIdx.x % nseg_here;
+  const int seglen = a.cps * a.kc;
+  const int tok0 = seg * seglen, tokE = min(a.n, tok0 + seglen);
+  const int nch = (tokE - tok0 + BC - 1) / BC;
+  const long hq = (long)bh * a.n * a.d, hv = (long)bh * a.n * a.dv;
+  const T *qh = (const T *)a.q + hq, *kh = (const T *)a.k + hq, *vh = (const T *)a.v + hv;
+  for (int e = tid; e < 3 * BC + 4; e += BWD_THREADS) pw[e] = exp2f((float)e * a.log2g);
+
+  using TS = TileCount<DK, DK>;
+  using TU = TileCount<DK, DVP>;
+  f32x4 S[TS::PER], P[TU::PER], W[TU::PER];
+  const float *pref = (OUT && seg > 0) ? a.prefix + ((long)bh * a.nseg + seg) * Cfg::PB : nullptr;
+  for_tiles<DK, DK>(w, [&](int i0, int j0, bool, int it) {
+    S[it] = pref ? *(const f32x4 *)(pref + (i0 + nn) * DK + j0 + 4 * gq) : zero4();
+  });
+  for_tiles<DK, DVP>(w, [&](int i0, int j0, bool, int it) {
+    const int o = (i0 + nn) * DVP + j0 + 4 * gq;
+    P[it] = pref ? *(const f32x4 *)(pref + DK * DK + o) : zero4();
+    W[it] = pref ? *(const f32x4 *)(pref + DK * DK + DK * DVP + o) : zero4();
+  });
+  // segment maps (summary mode)
+  f32x4 Q2[OUT ? 1 : TS::PER], X1[OUT ? 1 : TU::PER], X2[OUT ? 1 : TS::PER];
+#pragma unroll
+  for (int i = 0; i < (OUT ? 1 : TS::PER); ++i) Q2[i] = X2[i] = zero4();
+#pragma unroll
+  for (int i = 0; i < (OUT ? 1 : TU::PER); ++i) X1[i] = zero4();
+
+  RowTile<T, BC, DK> rq, rk;
+  RowTile<T, BC, DVP> rv;
+  rq.fetch(qh, a.d, tok0, a.n, -1, tid);
+  rk.fetch(kh, a.d, tok0, a.n, -1, tid);
+  rv.fetch(vh, a.dv, tok0, a.n, NORM ? DV : -1, tid);
+
+  for (int ch = 0; ch < nch; ++ch) {
+    const int t0 = tok0 + ch * BC;
+    for_tiles<DK, DK>(w, [&](int i0, int j0, bool ok, int it) {
+      if (ok) st4(Ss + (i0 + nn) * Cfg::LDQ + j0 + 4 * gq, S[it]);
+    });
+    for_tiles<DK, DVP>(w, [&](int i0, int j0, bool ok, int it) {
+      if (ok) {
+        st4(Ps + (i0 + nn) * Cfg::LDV + j0 + 4 * gq, P[it]);
+        if (OUT) st4(Ws + (i0 + nn) * Cfg::LDV + j0 + 4 * gq, W[it]);
+      }
+    });
+    rq.put(Qs, Cfg::LDQ, tid);
+    rk.put(Ks, Cfg::LDQ, tid);
+    rv.put(Vs, Cfg::LDV, tid);
+    __syncthreads();
+    {
+      const int tn = tok0 + min(ch + 1, nch - 1) * BC;
+      rq.fetch(qh, a.d, tn, a.n, -1, tid);
+      rk.fetch(kh, a.d, tn, a.n, -1, tid);
+      rv.fetch(vh, a.dv, tn, a.n, NORM ? DV : -1, tid);
+    }
+    // Ad = L o D1 o (Q K^T)
+    for_tiles<BC, BC>(w, [&](int i0, int j0, bool ok, int) {
+      f32x4 x = pt<false, true, DK>(zero4(), Qs, Cfg::LDQ, Ks, Cfg::LDQ, i0, j0, lane);
+      const int tr = i0 + nn;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int ti = j0 + 4 * gq + e;
+        x[e] = ti <= tr ? x[e] * pw[tr - ti] : 0.f;
+      }
+      if (ok) st4(Ads + tr * Cfg::LDC + j0 + 4 * gq, x);
+    });
+    __syncthreads();
+    // Z = diag(g^(tau+1)) Q S0 + Ad K;  Y = diag(g^(tau+1)) Q P0' + Ad V'
+    for_tiles<BC, DK>(w, [&](int i0, int j0, bool ok, int) {
+      f32x4 x = pt<false, true, DK>(zero4(), Qs, Cfg::LDQ, Ss, Cfg::LDQ, i0, j0, lane);
+      x *= pw[i0 + nn + 1];
+      x = pt<false, false, BC>(x, Ads, Cfg::LDC, Ks, Cfg::LDQ, i0, j0, lane);
+      if (ok) st4(Zs + (i0 + nn) * Cfg::LDQ + j0 + 4 * gq, x);
+    });
+    for_tiles<BC, DVP>(w, [&](int i0, int j0, bool ok, int) {
+      f32x4 x = pt<false, false, DK>(zero4(), Qs, Cfg::LDQ, Ps, Cfg::LDV, i0, j0, lane);
+      x *= pw[i0 + nn + 1];
+      x = pt<false, false, BC>(x, Ads, Cfg::LDC, Vs, Cfg::LDV, i0, j0, lane);
+      if (ok) st4(Ys + (i0 + nn) * Cfg::LDV + j0 + 4 * gq, x);
+    });
+    __syncthreads();
+    f32x4 O[OUT ? TileCount<BC, DVP>::PER : 1];
+    if constexpr (OUT) {
+      // Wm = L o D3 o (Q Z^T)
+      for_tiles<BC, BC>(w, [&](int i0, int j0, bool ok, int) {
+        f32x4 x = pt<false, true, DK>(zero4(), Qs, Cfg::LDQ, Zs, Cfg::LDQ, i0, j0, lane);
+        const int tr = i0 + nn;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int l = j0 + 4 * gq + e;
+          x[e] = l <= tr ? x[e] * pw[3 * (tr - l)] : 0.f;
+        }
+        if (ok) st4(Wms + tr * Cfg::LDC + j0 + 4 * gq, x);
+      });
+      __syncthreads();
+      // O = diag(g^(3(tau+1))) Q W0' + Wm Y
+      for_tiles<BC, DVP>(w, [&](int i0, int j0, bool ok, int it) {
+        f32x4 x = pt<false, false, DK>(zero4(), Qs, Cfg::LDQ, Ws, Cfg::LDV, i0, j0, lane);
+        x *= pw[3 * (i0 + nn + 1)];
+        x = pt<false, false, BC>(x, Wms, Cfg::LDC, Ys, Cfg::LDV, i0, j0, lane);
+        O[it] = x;
+        if (NORM && ok && j0 + 4 * gq == DV) dens[i0 + nn] = x[0];
+      });
+    } else {
+      // segment maps: weights relative to the segment end (L = seglen tokens, u = u0 + tau)
+      const int u0 = ch * BC;
+      const float bq = exp2f(a.log2g * (float)(3 * seglen - u0 - BC));
+      const float bx = exp2f(a.log2g * (float)(3 * seglen - 2 * u0 - 2 * BC));
+      for_tiles<DK, DK>(w, [&](int i0, int j0, bool, int it) {
+        Q2[it] = ptw<true, false, BC>(Q2[it], Qs, Cfg::LDQ, Qs, Cfg::LDQ, i0, j0, lane,
+                                      [&](int t) { return bq * pw[BC - 1 - t]; });
+        X2[it] = ptw<true, false, BC>(X2[it], Zs, Cfg::LDQ, Qs, Cfg::LDQ, i0, j0, lane,
+                                      [&](int t) { return bx * pw[2 * (BC - 1 - t)]; });
+      });
+      for_tiles<DK, DVP>(w, [&](int i0, int j0, bool, int it) {
+        X1[it] = ptw<true, false, BC>(X1[it], Qs, Cfg::LDQ, Ys, Cfg::LDV, i0, j0, lane,
+                                      [&](int t) { return bx * pw[2 * (BC - 1 - t)]; });
+      });
+    }
+    // state updates
+    const float gB = pw[BC], gB3 = pw[3 * BC];
+    for_tiles<DK, DK>(w, [&](int i0, int j0, bool, int it) {
+      S[it] = ptw<true, false, BC>(gB * S[it], Ks, Cfg::LDQ, Ks, Cfg::LDQ, i0, j0, lane,
+                                   [&](int i) { return pw[BC - 1 - i]; });
+    });
+    for_tiles<DK, DVP>(w, [&](int i0, int j0, bool, int it) {
+      P[it] = ptw<true, false, BC>(gB * P[it], Ks, Cfg::LDQ, Vs, Cfg::LDV, i0, j0, lane,
+                                   [&](int i) { return pw[BC - 1 - i]; });
+      W[it] = ptw<true, false, BC>(gB3 * W[it], Zs, Cfg::LDQ, Ys, Cfg::LDV, i0, j0, lane,
+                                   [&](int l) { return pw[3 * (BC - 1 - l)]; });
+    });
+    __syncthreads();  // dens complete; every read of this chunk's LDS done
+    if constexpr (OUT) {
+      T *oh = (T *)a.out + hv;
+      for_tiles<BC, DVP>(w, [&](int i0, int j0, bool ok, int it) {
+        const int tr = i0 + nn;
+        f32x4 x = O[it];
+        if (NORM && a.normalize) x *= 1.f / dens[tr];
+        if (ok) st_out(oh, a.dv, t0 + tr, j0 + 4 * gq, a.n, x);
+      });
+      if (NORM && a.den_out && tid < BC && t0 + tid < a.n) a.den_out[(long)bh * a.n + t0 + tid] = dens[tid];
+    }
+  }
+  if constexpr (!OUT) {
+    float *sb = a.sums + ((long)bh * (a.nseg - 1) + seg) * Cfg::SB;
+    float *sQ2 = sb + Cfg::PB, *sX1 = sQ2 + DK * DK, *sX2 = sX1 + DK * DVP;
+    for_tiles<DK, DK>(w, [&](int i0, int j0, bool ok, int it) {
+      const int o = (i0 + nn) * DK + j0 + 4 * gq;
+      if (ok) {
+        *(f32x4 *)(sb + o) = S[it];
+        *(f32x4 *)(sQ2 + o) = Q2[it];
+        *(f32x4 *)(sX2 + o) = X2[it];
+      }
+    });
+    for_tiles<DK, DVP>(w, [&](int i0, int j0, bool ok, int it) {
+      const int o = (i0 + nn) * DVP + j0 + 4 * gq;
+      if (ok) {
+        *(f32x4 *)(sb + DK * DK + o) = P[it];
+        *(f32x4 *)(sb + DK * DK + DK * DVP + o) = W[it];
+        *(f32x4 *)(sX1 + o) = X1[it];
+      }
+    });
+  }
+}
+
+// Exclusive scan over segments (the fold of each full segment into the running
+// state), per (b, h), fp32 on VALU.  Each step stages the prefix's S and P'
+// and the product S Q2 in LDS.
+template <int DK, int DVP>
+__global__ void __launch_bounds__(256) ho3_scan_kernel(Ho3Args a, float G) {
+  constexpr long PB = (long)DK * DK + 2L * DK * DVP, SB = PB + 2L * DK * DK + (long)DK * DVP;
+  __shared__ __attribute__((aligned(16))) float Sl[DK * DK], Pl[DK * DVP], Tl[DK * DK];
+  const int tid = threadIdx.x, bh = blockIdx.x;
+  const float G3 = G * G * G;
+  float *pre = a.prefix + (long)bh * a.nseg * PB;
+  for (int e = tid; e < PB; e += 256) pre[e] = 0.f;
+  for (int r = 0; r + 1 < a.nseg; ++r) {
+    const float *pr = pre + (long)r * PB;
+    float *pn = pre + (long)(r + 1) * PB;
+    const float *sb = a.sums + ((long)bh * (a.nseg - 1) + r) * SB;
+    const float *Q2 = sb + PB, *X1 = Q2 + DK * DK, *X2 = X1 + DK * DVP;
+    __syncthreads();  // prefix r written
+    for (int e = tid; e < DK * DK; e += 256) Sl[e] = pr[e];
+    for (int e = tid; e < DK * DVP; e += 256) Pl[e] = pr[DK * DK + e];
+    __syncthreads();
+    for (int e = tid; e < DK * DK; e += 256) {  // T = S Q2
+      const int f = e / DK, c = e % DK;
+      float s = 0.f;
+      for (int b = 0; b < DK; ++b) s += Sl[f * DK + b] * Q2[b * DK + c];
+      Tl[e] = s;
+    }
+    __syncthreads();
+    for (int e = tid; e < DK * DVP; e += 256) {
+      const int f = e / DVP, c = e % DVP;
+      float s = 0.f;
+      for (int b = 0; b < DK; ++b)
+        s += (Tl[f * DK + b] + X2[f * DK + b]) * Pl[b * DVP + c] + Sl[f * DK + b] * X1[b * DVP + c];
+      pn[DK * DK + DK * DVP + e] = G3 * pr[DK * DK + DK * DVP + e] + sb[DK * DK + DK * DVP + e] + s;
+      pn[DK * DK + e] = G * Pl[e] + sb[DK * DK + e];
+    }
+    for (int e = tid; e < DK * DK; e += 256) pn[e] = G * Sl[e] + sb[e];
+  }
+}
+
+template <typename T, int DK, int DV, bool NORM>
+static hipError_t launch_ho3_t(int phase, int BH, const Ho3Args &a, float gseg, hipStream_t s) {
+  constexpr int DVP = DV + (NORM ? Ktile<T>::ROWS : 0);
+  constexpr int BC = sizeof(T) == 4 ? 32 : 64;
+  switch (phase) {
+    case HO3_SUMMARY:
+      hipLaunchKernelGGL((ho3_walk_kernel<T, DK, DV, DVP, BC, false, NORM>), dim3(BH * (a.nseg - 1)),
+                         dim3(BWD_THREADS), 0, s, a);
+      return hipGetLastError();
+    case HO3_SCAN:
+      hipLaunchKernelGGL((ho3_scan_kernel<DK, DVP>), dim3(BH), dim3(256), 0, s, a, gseg);
+      return hipGetLastError();
+    case HO3_OUTPUT:
+      hipLaunchKernelGGL((ho3_walk_kernel<T, DK, DV, DVP, BC, true, NORM>), dim3(BH * a.nseg), dim3(BWD_THREADS), 0,
+                         s, a);
+      return hipGetLastError();
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T, int DK, int DV>
+static hipError_t launch_ho3_n(bool norm, int phase, int BH, const Ho3Args &a, float gseg, hipStream_t s) {
+  return norm ? launch_ho3_t<T, DK, DV, true>(phase, BH, a, gseg, s)
+              : launch_ho3_t<T, DK, DV, false>(phase, BH, a, gseg, s);
+}
+
+int ho3_dvp(int dtype, int DV, bool norm) { return DV + (norm ? (dtype == 0 ? 16 : 32) : 0); }
+
+hipError_t launch_ho3(int dtype, int DK, int DV, bool norm, int phase, int BH, const Ho3Args &a, float gseg,
+                      hipStream_t s) {
+  if (dtype == 0) {
+    if (DK == 16 && DV == 16) return launch_ho3_n<float, 16, 16>(norm, phase, BH, a, gseg, s);
+    if (DK == 64 && DV == 64) return launch_ho3_n<float, 64, 64>(norm, phase, BH, a, gseg, s);
+    return hipErrorInvalidValue;
+  }
+  if (DK == 64 && DV == 64) return launch_ho3_n<bf16, 64, 64>(norm, phase, BH, a, gseg, s);
+  if (DK == 64 && DV == 128) return launch_ho3_n<bf16, 64, 128>(norm, phase, BH, a, gseg, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace hla2

@@ -167,4 +167,13 @@ int ahla_dvp(int dtype, int DV, bool norm);
 hipError_t launch_ahla(int dtype, int DK, int DV, bool norm, int phase, int BH, const AhlaArgs &a, float gseg,
                        hipStream_t s);
 
+
+// The third-order kernels (hla2_ho3.hip) take the same argument block; their
+// prefix blocks are S | P' | W' and their summary blocks S | P' | W' | Q2 | X1 | X2.
+using Ho3Args = AhlaArgs;
+enum { HO3_SUMMARY = 0, HO3_SCAN = 1, HO3_OUTPUT = 2 };
+int ho3_dvp(int dtype, int DV, bool norm);
+hipError_t launch_ho3(int dtype, int DK, int DV, bool norm, int phase, int BH, const Ho3Args &a, float gseg,
+                      hipStream_t s);
+
 }  // namespace hla2

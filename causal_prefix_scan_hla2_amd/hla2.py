@@ -21,7 +21,8 @@ EXPORTS = ("hla2_strerror", "hla2_abi_version", "hla2_forward_workspace_bytes", 
            "hla2_forward", "hla2_forward_ex_workspace_bytes", "hla2_forward_ex_segments", "hla2_forward_ex",
            "hla2_forward_timed", "hla2_decode_step", "hla2_state_floats", "hla2_forward_state_workspace_bytes",
            "hla2_forward_state", "hla2_backward_workspace_bytes", "hla2_backward",
-           "hla2_ahla_forward_workspace_bytes", "hla2_ahla_forward")
+           "hla2_ahla_forward_workspace_bytes", "hla2_ahla_forward", "hla2_ho3_forward_workspace_bytes",
+           "hla2_ho3_forward")
 
 _lock = threading.Lock()
 _lib = None
@@ -74,6 +75,10 @@ def lib():
             L.hla2_ahla_forward_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
             L.hla2_ahla_forward.restype = i
             L.hla2_ahla_forward.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, vp, sz, i, vp]
+            L.hla2_ho3_forward_workspace_bytes.restype = sz
+            L.hla2_ho3_forward_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+            L.hla2_ho3_forward.restype = i
+            L.hla2_ho3_forward.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, vp, sz, i, vp]
             L.hla2_backward.restype = i
             L.hla2_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, i, vp]
             _lib = L
@@ -236,6 +241,32 @@ def hla2_ahla_forward(q, k, v, out, decay=1.0, normalize=False, den_out=None, wo
                                  _stream(stream))
     if check and rc != HLA2_OK:
         raise HLA2Error(rc, "hla2_ahla_forward")
+    return rc
+
+
+def hla2_ho3_forward_workspace_bytes(B, H, n, d, dv, dtype_code, segments=0) -> int:
+    return int(lib().hla2_ho3_forward_workspace_bytes(B, H, n, d, dv, int(dtype_code), segments))
+
+
+def hla2_ho3_forward(q, k, v, out, decay=1.0, normalize=False, den_out=None, workspace=None, stream=None,
+                     segments=0, check=True) -> int:
+    """Call ``hla2_ho3_forward`` (third order) on torch tensors q, k: [B,H,n,d]; v, out: [B,H,n,dv]."""
+    import torch
+    B, H, n, d = q.shape
+    dv = v.shape[-1]
+    for t in (q, k, v, out):
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    code = _dtype_code(q)
+    need = hla2_ho3_forward_workspace_bytes(B, H, n, d, dv, code, segments)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().hla2_ho3_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, n, d, dv, float(decay),
+                                int(bool(normalize)), code, _ptr(den_out), _ptr(workspace), wbytes, int(segments),
+                                _stream(stream))
+    if check and rc != HLA2_OK:
+        raise HLA2Error(rc, "hla2_ho3_forward")
     return rc
 
 

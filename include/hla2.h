@@ -248,6 +248,30 @@ int hla2_ahla_forward(const void *q, const void *k, const void *v, void *out,
                       hla2_dtype_t dtype, float *den_out, void *workspace, size_t workspace_bytes,
                       int segments, hipStream_t stream);
 
+/*
+ * Third-order HLA [SUM §3]: the interaction A A^T A with A = Q K^T, masked so
+ * that no index passes t:
+ *   num_t = sum_{l<=t} sum_{j<=l} sum_{i<=l} g^{(t-j)+(t-l)+(t-i)} (q_t.k_j)(q_l.k_j)(q_l.k_i) v_i,
+ *   den_t the same with v_i -> 1,  out_t = num_t or num_t / den_t,
+ * i.e. (L o D_{g^2} o (A_g A^T)) (A_g V) with A = L o (Q K^T), A_g = D_g o A;
+ * unmasked and undecayed it is q_t^T S^K S^Q P^KV.  Reading (the pages name the
+ * moments and cross summaries but print no update): every moment decays by g
+ * per token; the cross summaries are carried as one corrected accumulator
+ * W_t = g^3 W_{t-1} + (S^K_t q_t)(P^KV_t^T q_t)^T.  Computed chunk-parallel
+ * [SUM §4, third-order scans]: segment summaries with the segment-level maps
+ * that fold an incoming (S^K, P^KV) into W, an exclusive scan, and the chunk
+ * outputs from each segment's incoming state.
+ *   Arguments, layouts, workspace and errors as for hla2_ahla_forward (with
+ *   hla2_ho3_forward_workspace_bytes).  Supported: d <= 64 (the d x d state and
+ *   maps are held on chip), dv as hla2_forward; fp32 up to 64.
+ */
+size_t hla2_ho3_forward_workspace_bytes(int B, int H, int n, int d, int dv, hla2_dtype_t dtype,
+                                        int segments);
+int hla2_ho3_forward(const void *q, const void *k, const void *v, void *out,
+                     int B, int H, int n, int d, int dv, float decay, int normalize,
+                     hla2_dtype_t dtype, float *den_out, void *workspace, size_t workspace_bytes,
+                     int segments, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

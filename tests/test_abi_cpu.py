@@ -243,3 +243,24 @@ def test_ahla_validates(L):
     args = dict(B_=4, H_=8, n=2048)
     assert ahla(L, **args) == H.HLA2_ERR_WORKSPACE
     assert ahla(L, ws=P, wsb=need - 1, **args) == H.HLA2_ERR_WORKSPACE
+
+
+def test_ho3_validates(L):
+    def ho3(**kw):
+        base = dict(q=P, k=P, v=P, out=P, B_=1, H_=1, n=64, d=64, dv=64, decay=1.0, norm=0, dtype=1, den=None,
+                    ws=P, wsb=1 << 40, segments=0)
+        base.update(kw)
+        b = base
+        return L.hla2_ho3_forward(b["q"], b["k"], b["v"], b["out"], b["B_"], b["H_"], b["n"], b["d"], b["dv"],
+                                  b["decay"], b["norm"], b["dtype"], b["den"], b["ws"], b["wsb"], b["segments"], None)
+    assert ho3(q=None) == H.HLA2_ERR_INVALID
+    assert ho3(norm=2) == H.HLA2_ERR_INVALID
+    assert ho3(decay=0.0) == H.HLA2_ERR_INVALID
+    assert ho3(d=128) == H.HLA2_ERR_UNSUPPORTED      # the third-order state is held for d <= 64
+    assert ho3(dv=40) == H.HLA2_ERR_UNSUPPORTED
+    assert ho3(k=ctypes.c_void_p(4104)) == H.HLA2_ERR_INVALID
+    need = H.hla2_ho3_forward_workspace_bytes(4, 8, 2048, 64, 64, 1, 0)
+    assert need > 0
+    assert ho3(B_=4, H_=8, n=2048, ws=None, wsb=0) == H.HLA2_ERR_WORKSPACE
+    assert ho3(B_=4, H_=8, n=2048, wsb=need - 1) == H.HLA2_ERR_WORKSPACE
+    assert H.hla2_ho3_forward_workspace_bytes(1, 1, 64, 128, 64, 1, 0) == 0

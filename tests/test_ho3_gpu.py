@@ -1,0 +1,136 @@
+"""GPU parity of hla2_ho3_forward (third order, through the C ABI) against the
+oracle's third-order recurrence.
+
+num and den are compared over all tokens (relative L2 at the forward's bars);
+under the ratio, the conditioning-normalised error e_t is bounded as for the
+second-order forward (its RMS at half the tolerance), with the conditioning
+taken from the den column w_t of the oracle's corrected accumulator
+(den_t = q_t . w_t); at the normalised workload's shape o is also compared on
+the well-conditioned tokens.
+"""
+import numpy as np
+import pytest
+import torch
+
+from causal_prefix_scan_hla2_amd import hla2 as H
+from causal_prefix_scan_hla2_amd import inputs as I
+from oracle import oracle as O
+from tests.parity import ratio_ok, ratio_report, rel_l2, tol_for
+
+pytestmark = pytest.mark.gpu
+
+
+def draw(B, H_, n, d, dv, dtype, seed):
+    w = I.Workload("ho3", B, H_, n, d, dv, dtype, 1.0, False, 64, seed=seed)
+    return I.make_qkv(w)
+
+
+def gpu_ho3(q, k, v, decay, normalize, segments=0):
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    out = torch.empty_like(vd)
+    den = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
+    H.hla2_ho3_forward(qd, kd, vd, out, decay=decay, normalize=normalize, den_out=den, segments=segments)
+    torch.cuda.synchronize()
+    return out.double().cpu().numpy(), den.double().cpu().numpy()
+
+
+def w_norms(q, k, gamma):
+    """|w_t| per token for every head: w_t = g^3 w_{t-1} + (S_t q_t)(m_t . q_t),
+    S_t = g S_{t-1} + k_t k_t^T, m_t = g m_{t-1} + k_t."""
+    q, k = np.asarray(q, np.float64), np.asarray(k, np.float64)
+    d = q.shape[-1]
+    S = np.zeros(q.shape[:-2] + (d, d))
+    m = np.zeros(q.shape[:-2] + (d,))
+    wv = np.zeros_like(m)
+    out = np.empty(q.shape[:-1])
+    for t in range(q.shape[-2]):
+        kt, qt = k[..., t, :], q[..., t, :]
+        S = gamma * S + kt[..., :, None] * kt[..., None, :]
+        m = gamma * m + kt
+        z = np.einsum("...ab,...b->...a", S, qt)
+        wv = gamma ** 3 * wv + z * np.sum(m * qt, axis=-1, keepdims=True)
+        out[..., t] = np.linalg.norm(wv, axis=-1)
+    return out
+
+
+def check(q, k, v, decay, normalize, dtype, segments=0, heads=None, subset=False):
+    tol = tol_for(dtype)
+    o_gpu, den_gpu = gpu_ho3(q, k, v, decay, normalize, segments)
+    num_gpu = gpu_ho3(q, k, v, decay, False, segments)[0] if normalize else o_gpu
+    if heads is not None:
+        idx = tuple(np.array(heads).T)
+        tidx = tuple(torch.as_tensor(x) for x in idx)
+        q, k, v = q[tidx], k[tidx], v[tidx]
+        o_gpu, den_gpu, num_gpu = o_gpu[idx], den_gpu[idx], num_gpu[idx]
+    num, den, _ = O.ho3_serial(q.double().numpy(), k.double().numpy(), v.double().numpy(), decay)
+    r_num, r_den = rel_l2(num_gpu, num), rel_l2(den_gpu, den)
+    msg = "num %.3g den %.3g" % (r_num, r_den)
+    ok = r_num <= tol and r_den <= tol
+    if normalize:
+        rep = ratio_report(o_gpu, den_gpu, num, den, w_norms(q.double().numpy(), k.double().numpy(), decay),
+                           q.double().numpy())
+        msg += " | e_rms %.3g ratio(well) %.3g excluded %.3f" % (rep["e_rms"], rep["ratio_well"], rep["excluded"])
+        ok = ok and ratio_ok(rep, tol, subset=subset)
+    print(msg)
+    assert ok, msg
+
+
+SMALL = [
+    # B, H, n, d, dv, dtype, decay, normalize, segments
+    (1, 1, 64, 16, 16, "f32", 1.0, False, 0),
+    (2, 3, 200, 32, 48, "f32", 0.9, True, 3),
+    (1, 2, 333, 64, 64, "f32", 0.97, False, 0),
+    (1, 1, 40, 64, 64, "f32", 0.9, True, 1),
+    (2, 3, 300, 64, 128, "bf16", 0.99, False, 0),
+    (1, 2, 1000, 64, 128, "bf16", 1.0, True, 4),
+    (1, 1, 1000, 64, 128, "bf16", 0.99, False, 7),
+    (1, 2, 700, 64, 64, "bf16", 0.98, True, 3),
+    (1, 1, 100, 16, 16, "bf16", 1.0, False, 1),
+    (1, 1, 200, 48, 80, "bf16", 0.9, True, 2),
+    (1, 2, 2048, 64, 64, "bf16", 1.0, True, 0),
+    (1, 1, 37, 64, 128, "bf16", 0.9, False, 0),
+]
+
+
+@pytest.mark.parametrize("B,H_,n,d,dv,dtype,decay,normalize,segments", SMALL)
+def test_ho3_matches_oracle(B, H_, n, d, dv, dtype, decay, normalize, segments):
+    print("case", B, H_, n, d, dv, dtype, decay, normalize, segments, flush=True)
+    q, k, v = draw(B, H_, n, d, dv, dtype, seed=500 + n + d)
+    check(q, k, v, decay, normalize, dtype, segments)
+
+
+def test_ho3_causal_bitwise():
+    q, k, v = draw(1, 2, 500, 64, 64, "bf16", seed=3)
+    a, ad = gpu_ho3(q, k, v, 0.95, False)
+    for tstar in (0, 63, 64, 200, 499):
+        q2, k2, v2 = q.clone(), k.clone(), v.clone()
+        q2[:, :, tstar:] *= -1
+        k2[:, :, tstar:] += 0.25
+        v2[:, :, tstar:] *= 2
+        b, bd = gpu_ho3(q2, k2, v2, 0.95, False)
+        assert np.array_equal(a[:, :, :tstar], b[:, :, :tstar]) and np.array_equal(ad[:, :, :tstar], bd[:, :, :tstar])
+
+
+def test_ho3_segments_change_rounding_only():
+    q, k, v = draw(1, 2, 900, 64, 64, "bf16", seed=4)
+    a, _ = gpu_ho3(q, k, v, 0.99, False, 1)
+    for seg in (2, 5, 14):
+        b, _ = gpu_ho3(q, k, v, 0.99, False, seg)
+        assert rel_l2(b, a) < 5e-3
+
+
+def test_ho3_decay_workload_shape_sampled():
+    """The decay workload's shape (B=8, H=16, n=8192, d=64, dv=128, decay 0.99), sampled heads."""
+    w = I.WORKLOADS["decay_8k"]
+    q, k, v = I.make_qkv(w)
+    check(q, k, v, w.decay, False, w.dtype, heads=I.sample_heads(w.B, w.H, 3))
+
+
+def test_ho3_norm_workload_shape_sampled():
+    """The normalised workload's shape (B=4, H=8, n=2048, d=dv=64, ratio), sampled heads,
+    including the well-conditioned subset criterion."""
+    w = I.WORKLOADS["norm_2k"]
+    q, k, v = I.make_qkv(w)
+    check(q, k, v, w.decay, True, w.dtype, heads=I.sample_heads(w.B, w.H, 3), subset=True)
+
