@@ -231,22 +231,31 @@ def ahla_flops_per_head_token(w):
     return 2 * C * d + 8 * d * dv + 4 * C * dv
 
 
-def bench_ahla(w, steps, warmup, torch, H, I):
-    """Time `steps` AHLA forward calls (the asymmetric variant) on the workload's shape."""
+def ho3_flops_per_head_token(w):
+    """Third-order chunk outputs per head-token at chunk C: Ad 2Cd, Z 2d^2 + 2Cd, Y 2d dv' + 2C dv',
+    the masked Q Z^T 2Cd, O 2d dv' + 2C dv', the S, P', W' updates 2d^2 + 4d dv'."""
+    C, d, dv = w.chunk, w.d, w.dv + (1 if w.normalize else 0)
+    return 6 * C * d + 4 * d * d + 8 * d * dv + 4 * C * dv
+
+
+def bench_variant(fn_name, w, steps, warmup, torch, H, I, flops_per_head_token):
+    """Time `steps` calls of a variant's forward (AHLA or third order) on the workload's shape."""
     dev = torch.device("cuda:0")
     q, k, v = (x.to(dev) for x in I.make_qkv(w))
     out = torch.empty_like(v)
     code = H.HLA2_BF16 if q.dtype == torch.bfloat16 else H.HLA2_F32
-    ws = torch.empty(max(H.hla2_ahla_forward_workspace_bytes(w.B, w.H, w.n, w.d, w.dv, code), 1),
+    fwd = getattr(H, fn_name)
+    ws = torch.empty(max(getattr(H, fn_name + "_workspace_bytes")(w.B, w.H, w.n, w.d, w.dv, code), 1),
                      dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     def fn():
-        H.hla2_ahla_forward(q, k, v, out, decay=w.decay, normalize=w.normalize, workspace=ws)
+        fwd(q, k, v, out, decay=w.decay, normalize=w.normalize, workspace=ws)
 
     t, wall = time_calls(fn, steps, warmup, torch)
-    fl = ahla_flops_per_head_token(w) * w.B * w.H * w.n
-    return {"seconds": t, "tokens_per_s": w.B * w.n / t, "tflops": fl / t / 1e12, "mfma_frac": fl / t / PEAK_BF16_MFMA}
+    fl = flops_per_head_token * w.B * w.H * w.n
+    return {"workload": w.name + " shape", "ms_per_step": t * 1e3, "tokens_per_s": w.B * w.n / t,
+            "tflops": fl / t / 1e12, "mfma_frac": fl / t / PEAK_BF16_MFMA, "flops_per_head_token": flops_per_head_token}
 
 
 def cpu_baseline(w, heads_sample, I):
@@ -293,7 +302,7 @@ def main(argv=None):
     ap.add_argument("--cpu-heads", type=int, default=128, help="heads in the oracle's timed sample (0: skip)")
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--skip-backward", action="store_true")
-    ap.add_argument("--skip-ahla", action="store_true")
+    ap.add_argument("--skip-variants", action="store_true", help="skip the AHLA and third-order legs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="finish with two 1 GiB device copies (reference for HBM byte counters)")
     args = ap.parse_args(argv)
@@ -365,11 +374,12 @@ def main(argv=None):
             "head_tokens_per_s": bw["head_tokens_per_s"], "vs_forward_time": bw["seconds"] / fw["seconds"],
             "workspace_bytes": bw["workspace_bytes"],
         }
-    if not args.skip_ahla:
-        ah = bench_ahla(w, args.steps, args.warmup, torch, H, I)
-        line["ahla"] = {"workload": w.name + " shape", "ms_per_step": ah["seconds"] * 1e3,
-                        "tokens_per_s": ah["tokens_per_s"], "tflops": ah["tflops"], "mfma_frac": ah["mfma_frac"],
-                        "flops_per_head_token": ahla_flops_per_head_token(w)}
+    if not args.skip_variants:
+        line["ahla"] = bench_variant("hla2_ahla_forward", w, args.steps, args.warmup, torch, H, I,
+                                     ahla_flops_per_head_token(w))
+        if w.d <= 64:
+            line["third_order"] = bench_variant("hla2_ho3_forward", w, args.steps, args.warmup, torch, H, I,
+                                                ho3_flops_per_head_token(w))
     if args.cpu_heads > 0:
         line["cpu_baseline"] = cpu_baseline(w, min(args.cpu_heads, w.B * w.H), I)
     if args.copy_calibration:
