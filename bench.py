@@ -59,6 +59,30 @@ def min_bytes_forward(w, esize):
     return w.B * w.H * w.n * (2 * w.d + 2 * w.dv) * esize
 
 
+def output_kernel_bytes(w, esize, nseg):
+    """Algorithmic HBM bytes of one chunk-output launch: q, k, v read once, out
+    written once, and the incoming state (S0, U0, u0) of every segment after
+    the first read once."""
+    state = (w.d * w.d + w.d * w.dv + w.d) * 4
+    return min_bytes_forward(w, esize) + w.B * w.H * (nseg - 1) * state
+
+
+def roofline(flops, nbytes, seconds):
+    """The binding roofline of a kernel that does `flops` and moves `nbytes` in
+    `seconds`: HBM when its arithmetic intensity is below the ridge
+    (peak FLOP/s over peak B/s), else the bf16 MFMA peak."""
+    hbm = nbytes / PEAK_HBM >= flops / PEAK_BF16_MFMA
+    out = {"bound": "hbm" if hbm else "mfma"}
+    if hbm:
+        out.update(achieved=nbytes / seconds / 1e9, peak=PEAK_HBM / 1e9, unit="GB/s", frac=nbytes / seconds / PEAK_HBM)
+    else:
+        out.update(achieved=flops / seconds / 1e12, peak=PEAK_BF16_MFMA / 1e12, unit="TFLOP/s",
+                   frac=flops / seconds / PEAK_BF16_MFMA)
+    out["arithmetic_intensity"] = flops / nbytes
+    out["ridge"] = PEAK_BF16_MFMA / PEAK_HBM
+    return out
+
+
 def decode_bytes_per_step(N, H, d, dv, esize=2):
     state = N * H * (d * d + 2 * d * dv + 2 * d) * 4
     return 2 * state + N * H * (2 * d + dv) * esize + N * H * dv * esize
@@ -151,6 +175,7 @@ def bench_forward(w, steps, warmup, torch, H, I):
         "mfma_frac": flops / t / PEAK_BF16_MFMA,
         "flops_per_call": flops,
         "min_bytes": min_bytes_forward(w, esize),
+        "output_bytes_per_call": output_kernel_bytes(w, esize, nseg),
         "segments": nseg,
     }
 
@@ -342,18 +367,17 @@ def main(argv=None):
         "mfma_frac": fw["mfma_frac"],
         "hbm_min_bytes_frac": fw["min_bytes"] / fw["seconds"] / PEAK_HBM,
         "kernel_ms": {key: val * 1e3 for key, val in fw["phases"].items()},
-        "roofline": {
-            "bound": "mfma",
-            "kernel": "walk3_kernel<%d,%d,out,decay=%d,den=%d> (chunk outputs)" % (
+        "roofline": dict(
+            roofline(fw["output_flops_per_call"], fw["output_bytes_per_call"], fw["phases"]["output"]),
+            kernel="walk3_kernel<%d,%d,out,decay=%d,den=%d> (chunk outputs)" % (
                 64 if w.d <= 64 else 128, 64 if w.dv <= 64 else 128, int(w.decay < 1), int(w.normalize)),
-            "achieved": fw["output_flops_per_call"] / fw["phases"]["output"] / 1e12,
-            "peak": PEAK_BF16_MFMA / 1e12,
-            "unit": "TFLOP/s",
-            "frac": fw["output_flops_per_call"] / fw["phases"]["output"] / PEAK_BF16_MFMA,
-            "traffic": load_traffic("output_" + w.name),
-            "avg_launch_ms": fw["phases"]["output"] * 1e3,
-            "algorithmic_flops_per_launch": fw["output_flops_per_call"],
-        },
+            traffic=load_traffic("output_" + w.name),
+            avg_launch_ms=fw["phases"]["output"] * 1e3,
+            algorithmic_bytes_per_launch=fw["output_bytes_per_call"],
+            algorithmic_flops_per_launch=fw["output_flops_per_call"],
+            mfma_tflops=fw["output_flops_per_call"] / fw["phases"]["output"] / 1e12,
+            mfma_frac=fw["output_flops_per_call"] / fw["phases"]["output"] / PEAK_BF16_MFMA,
+        ),
     }
     if not args.skip_decode:
         dw = I.DECODE
