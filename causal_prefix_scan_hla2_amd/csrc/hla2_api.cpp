@@ -315,11 +315,11 @@ int hla2_backward(const void *q, const void *k, const void *v, const void *out, 
   ba.cps = p.cps;
   ba.kc = p.kc;
   ba.nbc = b.nbc;
+  ba.nbh = (int)p.BH;
   ba.log2g = log2g;
   const float gL = decay < 1.0f ? (float)pow((double)decay, (double)p.cps * p.kc) : 1.0f;
-  const int phases[] = {hla2::BWD_STATE, hla2::BWD_RSUM, hla2::BWD_RSCAN, hla2::BWD_WALK};
+  const int phases[] = {hla2::BWD_PRE, hla2::BWD_RSCAN, hla2::BWD_WALK};
   for (int ph : phases) {
-    if (ph == hla2::BWD_RSUM && p.nseg == 1) continue;
     e = hla2::launch_bwd(dt, p.DK, p.DV, b.norm, ph, (int)p.BH, ba, pa, gL, stream);
     if (e != hipSuccess) return HLA2_ERR_LAUNCH;
   }

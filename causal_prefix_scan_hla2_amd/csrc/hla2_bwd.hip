@@ -153,11 +153,9 @@ static hipError_t launch_bwd_t(int phase, int BH, const BwdArgs &a, const BwdPre
       } else {
         return hipErrorInvalidValue;
       }
-    case BWD_STATE:
-      hipLaunchKernelGGL((bwd_state_kernel<T, DK, DV, DVP, BC, NORM>), dim3(BH * a.nseg), dim3(BWD_THREADS), 0, s, a);
-      return hipGetLastError();
-    case BWD_RSUM:
-      hipLaunchKernelGGL((bwd_rsum_kernel<T, DK, DV, DVP, BC, NORM>), dim3(BH * (a.nseg - 1)), dim3(BWD_THREADS), 0, s, a);
+    case BWD_PRE:
+      hipLaunchKernelGGL((bwd_pre_kernel<T, DK, DV, DVP, BC, NORM, DK <= 64 ? 2 : 1>), dim3(BH * a.nseg + BH * (a.nseg - 1)),
+                         dim3(BWD_PRE_THREADS), 0, s, a);
       return hipGetLastError();
     case BWD_RSCAN:
       hipLaunchKernelGGL((bwd_rscan_kernel<DK, DV, DVP, NORM>), dim3(BH), dim3(256), 0, s, a, gL);

@@ -129,6 +129,7 @@ struct BwdArgs {
   int n, d, dv, gld;       // gld: columns of a row of g
   int nseg, cps, kc;       // segments of cps chunks of kc tokens (the forward's plan)
   int nbc;                 // backward chunks per head
+  int nbh;                 // B * H
   float log2g;             // log2(decay)
 };
 // Arguments of the ratio's upstream-gradient preparation.
@@ -139,7 +140,8 @@ struct BwdPrepArgs {
   long rows;
   int dv;
 };
-enum { BWD_PREP = 0, BWD_STATE = 1, BWD_RSUM = 2, BWD_RSCAN = 3, BWD_WALK = 4 };
+// BWD_PRE: the forward-state walk and the adjoint summaries, one launch
+enum { BWD_PREP = 0, BWD_PRE = 1, BWD_RSCAN = 3, BWD_WALK = 4 };
 // backward chunk length and padded value width (values, plus the denominator column under the ratio)
 int bwd_chunk(int dtype, int DK);
 int bwd_dvp(int dtype, int DV, bool norm);

@@ -58,19 +58,20 @@ __device__ __forceinline__ f32x4 ptw(f32x4 acc, const T *X, int ldx, const T *Y,
 // Waves per workgroup of these walkers (two per SIMD).
 constexpr int BWD_WAVES = 8, BWD_THREADS = 64 * BWD_WAVES;
 
-// Iterate a wave's share of the 16x16 tiles of an I x J result: f(i0, j0, store_ok, slot).
-template <int I, int J, typename F>
+// Iterate a wave's share of the 16x16 tiles of an I x J result over NW waves:
+// f(i0, j0, store_ok, slot).  A wave with no tile left repeats the last one (not stored).
+template <int I, int J, int NW = BWD_WAVES, typename F>
 __device__ __forceinline__ void for_tiles(int w, F &&f) {
-  constexpr int NJ = J / 16, NT = (I / 16) * NJ, PER = (NT + BWD_WAVES - 1) / BWD_WAVES;
+  constexpr int NJ = J / 16, NT = (I / 16) * NJ, PER = (NT + NW - 1) / NW;
 #pragma unroll
   for (int it = 0; it < PER; ++it) {
-    const int t = w + BWD_WAVES * it;
+    const int t = w + NW * it;
     const int tt = t < NT ? t : NT - 1;
     f(16 * (tt / NJ), 16 * (tt % NJ), t < NT, it);
   }
 }
-template <int I, int J> struct TileCount {
-  static constexpr int NT = (I / 16) * (J / 16), PER = (NT + BWD_WAVES - 1) / BWD_WAVES;
+template <int I, int J, int NW = BWD_WAVES> struct TileCount {
+  static constexpr int NT = (I / 16) * (J / 16), PER = (NT + NW - 1) / NW;
 };
 
 // 16-byte vector of the element type
@@ -88,16 +89,15 @@ template <> struct Vec16<float> {
 // past n and past column gc; with ones >= 0, column `ones` holds 1 for rows
 // before n).  fetch() reads a thread's share into registers, put() writes them
 // to LDS, so the global reads of the next chunk can fly during this one.
-template <typename T, int BC, int W>
+template <typename T, int BC, int W, int NTH = BWD_THREADS>
 struct RowTile {
   typedef typename Vec16<T>::type V;
-  static constexpr int VN = Vec16<T>::N, PERROW = W / VN, TOT = BC * PERROW,
-                       PER = (TOT + BWD_THREADS - 1) / BWD_THREADS;
+  static constexpr int VN = Vec16<T>::N, PERROW = W / VN, TOT = BC * PERROW, PER = (TOT + NTH - 1) / NTH;
   V x[PER];
   __device__ __forceinline__ void fetch(const T *src, int gc, int t0, int n, int ones, int tid) {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-      const int i = tid + j * BWD_THREADS;
+      const int i = tid + j * NTH;
       const int r = i / PERROW, c = (i % PERROW) * VN, t = t0 + r;
       V v{};
       if (i < TOT && t < n && c < gc) v = *(const V *)(src + (long)t * gc + c);
@@ -108,11 +108,22 @@ struct RowTile {
   __device__ __forceinline__ void put(T *dst, int ld, int tid) const {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-      const int i = tid + j * BWD_THREADS;
+      const int i = tid + j * NTH;
       if (i < TOT) *(V *)(dst + (i / PERROW) * ld + (i % PERROW) * VN) = x[j];
     }
   }
 };
+
+// Tile of P = X Y where Y is symmetric or given as its transposed rows: the
+// fragments yf[k] = rows j0 .. j0+15 of Y^T over the k-tiles of the contraction
+// (read ahead by the caller), X row-major.  Lane (g, n) holds P[i0 + n][j0 + 4g + e].
+template <int K, typename T, typename FR>
+__device__ __forceinline__ f32x4 pt_frags(f32x4 acc, const FR *yf, const T *X, int ldx, int i0, int lane) {
+  constexpr int KT = Ktile<T>::ROWS;
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += KT) acc = mma(yf[k0 / KT], ld_rows(X, ldx, i0, k0, lane), acc);
+  return acc;
+}
 
 // Store four consecutive values of row t, columns c .. c+3, of a [n][ncols] matrix.
 __device__ __forceinline__ void st_out(bf16 *dst, int ncols, int t, int c, int n, f32x4 x) {
