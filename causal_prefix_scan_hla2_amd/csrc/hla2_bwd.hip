@@ -34,94 +34,78 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdPrepArgs a) {
 //   Shat <- g^L Shat + Shat_r + g^(L+1) (Ubar C'_r^T + C'_r Ubar^T)   (old Ubar),
 // taken from the last segment backwards; L = tokens per full segment and
 // C'_r = [C_r | m_r] the segment's forward summary.  fp32 on VALU.
+// Workgroup (bh, sp) owns rows 16 sp .. 16 sp + 15 of Shat; every workgroup of a
+// head keeps the whole Ubar sequence itself (elementwise and cheap), so the
+// workgroups never wait on each other.  Ubar is written by the sp = 0 group.
 template <int DK, int DV, int DVP, bool NORM>
 __global__ void __launch_bounds__(256) bwd_rscan_kernel(BwdArgs a, float gL) {
-  constexpr int CW = DVP / 2;                     // columns staged per pass
+  constexpr int CW = DVP / 2;                     // columns of C' staged per pass
   constexpr long RB = (long)DK * DVP + DK * DK;   // adjoint block
   constexpr int NU = (DK * DVP + 255) / 256;      // Ubar elements per thread
-  constexpr int NB = DK * DK / 16, NBT = (NB + 255) / 256;  // 4x4 blocks of Shat
-  __shared__ __attribute__((aligned(16))) float Us[DK * CW], Cs[DK * CW];
-  const int tid = threadIdx.x, bh = blockIdx.x;
+  constexpr int NO = 16 * DK / 256 > 0 ? 16 * DK / 256 : 1;  // Shat entries per thread (one row, NO columns)
+  __shared__ __attribute__((aligned(16))) float Us[DK * DVP], Cs[DK * CW];
+  const int tid = threadIdx.x, bh = blockIdx.x, sp = blockIdx.y;
+  // thread -> (row a in the group's 16, columns b0 .. b0 + NO - 1)
+  const bool active = tid * NO < 16 * DK;
+  const int a_row = 16 * sp + (active ? (tid * NO) / DK : 0), b0 = active ? (tid * NO) % DK : 0;
   const long SB = sum_block_floats(DK, DV);
   float *suf = a.suffix + (long)bh * a.nseg * RB;
   const float *rs = a.rsum + (long)bh * a.nseg * RB;
   const float gL1 = gL * exp2f(a.log2g), gL2 = gL * gL;
-  float U[NU];
-  f32x4 Sh[NBT][4];
+  float U[NU], Sh[NO];
 #pragma unroll
   for (int i = 0; i < NU; ++i) U[i] = 0.f;
 #pragma unroll
-  for (int b = 0; b < NBT; ++b)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) Sh[b][r] = zero4();
+  for (int o = 0; o < NO; ++o) Sh[o] = 0.f;
   auto store = [&](int r) {
-    float *o = suf + (long)r * RB;
+    float *out = suf + (long)r * RB;
+    if (sp == 0) {
 #pragma unroll
-    for (int i = 0; i < NU; ++i) {
-      const int e = tid + 256 * i;
-      if (e < DK * DVP) o[e] = U[i];
-    }
-#pragma unroll
-    for (int b = 0; b < NBT; ++b) {
-      const int blk = tid + 256 * b;
-      if (blk < NB) {
-        const int a0 = 4 * (blk / (DK / 4)), b0 = 4 * (blk % (DK / 4));
-#pragma unroll
-        for (int r2 = 0; r2 < 4; ++r2) *(f32x4 *)(o + DK * DVP + (a0 + r2) * DK + b0) = Sh[b][r2];
+      for (int i = 0; i < NU; ++i) {
+        const int e = tid + 256 * i;
+        if (e < DK * DVP) out[e] = U[i];
       }
+    }
+    if (active) {
+#pragma unroll
+      for (int o = 0; o < NO; ++o) out[DK * DVP + a_row * DK + b0 + o] = Sh[o];
     }
   };
   store(a.nseg - 1);
   for (int r = a.nseg - 1; r >= 1; --r) {
     const float *ad = rs + (long)r * RB;
-    // cross term with the old Ubar (zero for the last segment, whose C' is not needed)
-    f32x4 X[NBT][4];
+    float X[NO];
 #pragma unroll
-    for (int b = 0; b < NBT; ++b)
-#pragma unroll
-      for (int r2 = 0; r2 < 4; ++r2) X[b][r2] = zero4();
-    if (r < a.nseg - 1) {
+    for (int o = 0; o < NO; ++o) X[o] = 0.f;
+    if (r < a.nseg - 1) {  // the cross term with the old Ubar (zero before the first fold)
       const float *fs = a.fsum + ((long)bh * (a.nseg - 1) + r) * SB;
       const float *Cg = fs + DK * DK, *mg = fs + DK * DK + 2 * DK * DV;
+      __syncthreads();  // the previous step's reads of Us are done
+#pragma unroll
+      for (int i = 0; i < NU; ++i) {
+        const int e = tid + 256 * i;
+        if (e < DK * DVP) Us[e] = U[i];
+      }
       for (int h = 0; h < 2; ++h) {
         __syncthreads();
         for (int e = tid; e < DK * CW; e += 256) {
           const int row = e / CW, c = h * CW + e % CW;
-          // the old Ubar is the adjoint state stored for the end of segment r
-          Us[e] = suf[(long)r * RB + row * DVP + c];
           Cs[e] = c < DV ? Cg[row * DV + c] : ((NORM && c == DV) ? mg[row] : 0.f);
         }
         __syncthreads();
+        if (active) {
+          for (int c = 0; c < CW; ++c) {
+            const float ua = Us[a_row * DVP + h * CW + c], ca = Cs[a_row * CW + c];
 #pragma unroll
-        for (int b = 0; b < NBT; ++b) {
-          const int blk = tid + 256 * b;
-          if (blk < NB) {
-            const int a0 = 4 * (blk / (DK / 4)), b0 = 4 * (blk % (DK / 4));
-            for (int c = 0; c < CW; ++c) {
-              f32x4 ua, ub, ca, cb;
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                ua[i] = Us[(a0 + i) * CW + c];
-                ub[i] = Us[(b0 + i) * CW + c];
-                ca[i] = Cs[(a0 + i) * CW + c];
-                cb[i] = Cs[(b0 + i) * CW + c];
-              }
-#pragma unroll
-              for (int i = 0; i < 4; ++i) X[b][i] += ua[i] * cb + ca[i] * ub;
-            }
+            for (int o = 0; o < NO; ++o)
+              X[o] += ua * Cs[(b0 + o) * CW + c] + ca * Us[(b0 + o) * DVP + h * CW + c];
           }
         }
       }
     }
+    if (active) {
 #pragma unroll
-    for (int b = 0; b < NBT; ++b) {
-      const int blk = tid + 256 * b;
-      if (blk < NB) {
-        const int a0 = 4 * (blk / (DK / 4)), b0 = 4 * (blk % (DK / 4));
-#pragma unroll
-        for (int r2 = 0; r2 < 4; ++r2)
-          Sh[b][r2] = gL * Sh[b][r2] + *(const f32x4 *)(ad + DK * DVP + (a0 + r2) * DK + b0) + gL1 * X[b][r2];
-      }
+      for (int o = 0; o < NO; ++o) Sh[o] = gL * Sh[o] + ad[DK * DVP + a_row * DK + b0 + o] + gL1 * X[o];
     }
 #pragma unroll
     for (int i = 0; i < NU; ++i) {
@@ -158,7 +142,7 @@ static hipError_t launch_bwd_t(int phase, int BH, const BwdArgs &a, const BwdPre
                          dim3(BWD_PRE_THREADS), 0, s, a);
       return hipGetLastError();
     case BWD_RSCAN:
-      hipLaunchKernelGGL((bwd_rscan_kernel<DK, DV, DVP, NORM>), dim3(BH), dim3(256), 0, s, a, gL);
+      hipLaunchKernelGGL((bwd_rscan_kernel<DK, DV, DVP, NORM>), dim3(BH, DK / 16), dim3(256), 0, s, a, gL);
       return hipGetLastError();
     case BWD_WALK:
       hipLaunchKernelGGL((bwd_walk_kernel<T, DK, DV, DVP, BC, NORM>), dim3(BH * a.nseg), dim3(BWD_THREADS), 0, s, a);
