@@ -162,29 +162,45 @@ __global__ void __launch_bounds__(BWD_THREADS) ahla_walk_kernel(AhlaArgs a) {
 
 // Exclusive scan over segments, per (b, h), fp32 on VALU:
 //   prefix_0 = 0;  P'_{r+1} = G P'_r + P'(seg r),  E'_{r+1} = G E'_r + E'(seg r) + G M(seg r) P'_r.
-// Each step reads the prefix it wrote before (the block's own global writes,
-// ordered by the barrier) and stages its P' in LDS for the cross term.
+// Workgroup (bh, sp) owns rows 16 sp .. 16 sp + 15 of E' and writes those rows of
+// every prefix; each workgroup of a head keeps the whole P' sequence in LDS
+// (elementwise), so the workgroups never wait on each other.
 template <int DK, int DVP>
 __global__ void __launch_bounds__(256) ahla_scan_kernel(AhlaArgs a, float gseg) {
   constexpr long PB = 2L * DK * DVP, SB = 2L * DK * DVP + (long)DK * DK;
+  constexpr int NE = (16 * DVP + 255) / 256;  // E' entries per thread (16 rows)
   __shared__ __attribute__((aligned(16))) float Pl[DK * DVP];
-  const int tid = threadIdx.x, bh = blockIdx.x;
+  const int tid = threadIdx.x, bh = blockIdx.x, sp = blockIdx.y, r0 = 16 * sp;
   float *pre = a.prefix + (long)bh * a.nseg * PB;
-  for (int e = tid; e < 2 * DK * DVP; e += 256) pre[e] = 0.f;
-  for (int r = 0; r + 1 < a.nseg; ++r) {
-    const float *pr = pre + (long)r * PB;
-    float *pn = pre + (long)(r + 1) * PB;
-    const float *sb = a.sums + ((long)bh * (a.nseg - 1) + r) * SB, *Mr = sb + 2 * DK * DVP;
-    __syncthreads();  // prefix r written
-    for (int e = tid; e < DK * DVP; e += 256) Pl[e] = pr[e];
-    __syncthreads();
-    for (int e = tid; e < DK * DVP; e += 256) {
-      const int f = e / DVP, c = e % DVP;
-      float s = 0.f;
-      for (int g2 = 0; g2 < DK; ++g2) s += Mr[f * DK + g2] * Pl[g2 * DVP + c];
-      pn[DK * DVP + e] = gseg * (pr[DK * DVP + e] + s) + sb[DK * DVP + e];
-      pn[e] = gseg * Pl[e] + sb[e];
+  for (int e = tid; e < DK * DVP; e += 256) Pl[e] = 0.f;
+  float E[NE];
+#pragma unroll
+  for (int i = 0; i < NE; ++i) E[i] = 0.f;
+  for (int r = 0; r < a.nseg; ++r) {
+    float *pr = pre + (long)r * PB;
+    __syncthreads();  // Pl holds P'_r
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+      const int e = tid + 256 * i;
+      if (e < 16 * DVP) {
+        pr[r0 * DVP + e] = Pl[r0 * DVP + e];
+        pr[DK * DVP + r0 * DVP + e] = E[i];
+      }
     }
+    if (r == a.nseg - 1) break;
+    const float *sb = a.sums + ((long)bh * (a.nseg - 1) + r) * SB, *Mr = sb + 2 * DK * DVP;
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+      const int e = tid + 256 * i;
+      if (e < 16 * DVP) {
+        const int f = r0 + e / DVP, c = e % DVP;
+        float s = 0.f;
+        for (int g2 = 0; g2 < DK; ++g2) s += Mr[f * DK + g2] * Pl[g2 * DVP + c];
+        E[i] = gseg * (E[i] + s) + sb[DK * DVP + f * DVP + c];
+      }
+    }
+    __syncthreads();  // every read of P'_r done
+    for (int e = tid; e < DK * DVP; e += 256) Pl[e] = gseg * Pl[e] + sb[e];
   }
 }
 
@@ -198,7 +214,7 @@ static hipError_t launch_ahla_t(int phase, int BH, const AhlaArgs &a, float gseg
                          dim3(BWD_THREADS), 0, s, a);
       return hipGetLastError();
     case AHLA_SCAN:
-      hipLaunchKernelGGL((ahla_scan_kernel<DK, DVP>), dim3(BH), dim3(256), 0, s, a, gseg);
+      hipLaunchKernelGGL((ahla_scan_kernel<DK, DVP>), dim3(BH, DK / 16), dim3(256), 0, s, a, gseg);
       return hipGetLastError();
     case AHLA_OUTPUT:
       hipLaunchKernelGGL((ahla_walk_kernel<T, DK, DV, DVP, BC, true, NORM>), dim3(BH * a.nseg), dim3(BWD_THREADS),

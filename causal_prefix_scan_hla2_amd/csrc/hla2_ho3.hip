@@ -213,41 +213,60 @@ __global__ void __launch_bounds__(BWD_THREADS) ho3_walk_kernel(Ho3Args a) {
 }
 
 // Exclusive scan over segments (the fold of each full segment into the running
-// state), per (b, h), fp32 on VALU.  Each step stages the prefix's S and P'
-// and the product S Q2 in LDS.
+// state), per (b, h), fp32 on VALU.  Workgroup (bh, sp) owns rows 16 sp ..
+// 16 sp + 15 of S and W' (the fold of a row needs only that row of S, of X2
+// and of S Q2, plus all of P' and X1); every workgroup of a head keeps the
+// whole P' sequence in LDS (elementwise), so the workgroups never wait on
+// each other.  Each writes its rows of every prefix.
 template <int DK, int DVP>
 __global__ void __launch_bounds__(256) ho3_scan_kernel(Ho3Args a, float G) {
   constexpr long PB = (long)DK * DK + 2L * DK * DVP, SB = PB + 2L * DK * DK + (long)DK * DVP;
-  __shared__ __attribute__((aligned(16))) float Sl[DK * DK], Pl[DK * DVP], Tl[DK * DK];
-  const int tid = threadIdx.x, bh = blockIdx.x;
+  constexpr int NS = (16 * DK + 255) / 256, NW3 = (16 * DVP + 255) / 256;
+  __shared__ __attribute__((aligned(16))) float Pl[DK * DVP], Sl[16 * DK], Tl[16 * DK];
+  const int tid = threadIdx.x, bh = blockIdx.x, sp = blockIdx.y, r0 = 16 * sp;
   const float G3 = G * G * G;
   float *pre = a.prefix + (long)bh * a.nseg * PB;
-  for (int e = tid; e < PB; e += 256) pre[e] = 0.f;
-  for (int r = 0; r + 1 < a.nseg; ++r) {
-    const float *pr = pre + (long)r * PB;
-    float *pn = pre + (long)(r + 1) * PB;
+  for (int e = tid; e < DK * DVP; e += 256) Pl[e] = 0.f;
+  for (int e = tid; e < 16 * DK; e += 256) Sl[e] = 0.f;
+  float W[NW3];
+#pragma unroll
+  for (int i = 0; i < NW3; ++i) W[i] = 0.f;
+  for (int r = 0; r < a.nseg; ++r) {
+    float *pr = pre + (long)r * PB;
+    __syncthreads();  // Pl, Sl hold the state before segment r
+    for (int e = tid; e < 16 * DK; e += 256) pr[r0 * DK + e] = Sl[e];
+#pragma unroll
+    for (int i = 0; i < NW3; ++i) {
+      const int e = tid + 256 * i;
+      if (e < 16 * DVP) {
+        pr[DK * DK + r0 * DVP + e] = Pl[r0 * DVP + e];
+        pr[DK * DK + DK * DVP + r0 * DVP + e] = W[i];
+      }
+    }
+    if (r == a.nseg - 1) break;
     const float *sb = a.sums + ((long)bh * (a.nseg - 1) + r) * SB;
     const float *Q2 = sb + PB, *X1 = Q2 + DK * DK, *X2 = X1 + DK * DVP;
-    __syncthreads();  // prefix r written
-    for (int e = tid; e < DK * DK; e += 256) Sl[e] = pr[e];
-    for (int e = tid; e < DK * DVP; e += 256) Pl[e] = pr[DK * DK + e];
-    __syncthreads();
-    for (int e = tid; e < DK * DK; e += 256) {  // T = S Q2
+    // T = S Q2 + X2 for the group's rows
+    for (int e = tid; e < 16 * DK; e += 256) {
       const int f = e / DK, c = e % DK;
-      float s = 0.f;
+      float s = X2[(r0 + f) * DK + c];
       for (int b = 0; b < DK; ++b) s += Sl[f * DK + b] * Q2[b * DK + c];
       Tl[e] = s;
     }
     __syncthreads();
-    for (int e = tid; e < DK * DVP; e += 256) {
-      const int f = e / DVP, c = e % DVP;
-      float s = 0.f;
-      for (int b = 0; b < DK; ++b)
-        s += (Tl[f * DK + b] + X2[f * DK + b]) * Pl[b * DVP + c] + Sl[f * DK + b] * X1[b * DVP + c];
-      pn[DK * DK + DK * DVP + e] = G3 * pr[DK * DK + DK * DVP + e] + sb[DK * DK + DK * DVP + e] + s;
-      pn[DK * DK + e] = G * Pl[e] + sb[DK * DK + e];
+#pragma unroll
+    for (int i = 0; i < NW3; ++i) {
+      const int e = tid + 256 * i;
+      if (e < 16 * DVP) {
+        const int f = e / DVP, c = e % DVP;
+        float s = 0.f;
+        for (int b = 0; b < DK; ++b) s += Tl[f * DK + b] * Pl[b * DVP + c] + Sl[f * DK + b] * X1[b * DVP + c];
+        W[i] = G3 * W[i] + sb[DK * DK + DK * DVP + (r0 + f) * DVP + c] + s;
+      }
     }
-    for (int e = tid; e < DK * DK; e += 256) pn[e] = G * Sl[e] + sb[e];
+    __syncthreads();  // every read of the state before segment r done
+    for (int e = tid; e < DK * DVP; e += 256) Pl[e] = G * Pl[e] + sb[DK * DK + e];
+    for (int e = tid; e < 16 * DK; e += 256) Sl[e] = G * Sl[e] + sb[r0 * DK + e];
   }
 }
 
@@ -261,7 +280,7 @@ static hipError_t launch_ho3_t(int phase, int BH, const Ho3Args &a, float gseg, 
                          dim3(BWD_THREADS), 0, s, a);
       return hipGetLastError();
     case HO3_SCAN:
-      hipLaunchKernelGGL((ho3_scan_kernel<DK, DVP>), dim3(BH), dim3(256), 0, s, a, gseg);
+      hipLaunchKernelGGL((ho3_scan_kernel<DK, DVP>), dim3(BH, DK / 16), dim3(256), 0, s, a, gseg);
       return hipGetLastError();
     case HO3_OUTPUT:
       hipLaunchKernelGGL((ho3_walk_kernel<T, DK, DV, DVP, BC, true, NORM>), dim3(BH * a.nseg), dim3(BWD_THREADS), 0,
