@@ -169,7 +169,7 @@ template <int DK, int DVP>
 __global__ void __launch_bounds__(256) ahla_scan_kernel(AhlaArgs a, float gseg) {
   constexpr long PB = 2L * DK * DVP, SB = 2L * DK * DVP + (long)DK * DK;
   constexpr int NE = (16 * DVP + 255) / 256;  // E' entries per thread (16 rows)
-  __shared__ __attribute__((aligned(16))) float Pl[DK * DVP];
+  __shared__ __attribute__((aligned(16))) float Pl[DK * DVP], Ml[16 * DK];
   const int tid = threadIdx.x, bh = blockIdx.x, sp = blockIdx.y, r0 = 16 * sp;
   float *pre = a.prefix + (long)bh * a.nseg * PB;
   for (int e = tid; e < DK * DVP; e += 256) Pl[e] = 0.f;
@@ -189,13 +189,15 @@ __global__ void __launch_bounds__(256) ahla_scan_kernel(AhlaArgs a, float gseg) 
     }
     if (r == a.nseg - 1) break;
     const float *sb = a.sums + ((long)bh * (a.nseg - 1) + r) * SB, *Mr = sb + 2 * DK * DVP;
+    for (int e = tid; e < 16 * DK; e += 256) Ml[e] = Mr[r0 * DK + e];  // the group's rows of M
+    __syncthreads();
 #pragma unroll
     for (int i = 0; i < NE; ++i) {
       const int e = tid + 256 * i;
       if (e < 16 * DVP) {
         const int f = r0 + e / DVP, c = e % DVP;
         float s = 0.f;
-        for (int g2 = 0; g2 < DK; ++g2) s += Mr[f * DK + g2] * Pl[g2 * DVP + c];
+        for (int g2 = 0; g2 < DK; ++g2) s += Ml[(f - r0) * DK + g2] * Pl[g2 * DVP + c];
         E[i] = gseg * (E[i] + s) + sb[DK * DVP + f * DVP + c];
       }
     }

@@ -222,7 +222,7 @@ template <int DK, int DVP>
 __global__ void __launch_bounds__(256) ho3_scan_kernel(Ho3Args a, float G) {
   constexpr long PB = (long)DK * DK + 2L * DK * DVP, SB = PB + 2L * DK * DK + (long)DK * DVP;
   constexpr int NS = (16 * DK + 255) / 256, NW3 = (16 * DVP + 255) / 256;
-  __shared__ __attribute__((aligned(16))) float Pl[DK * DVP], Sl[16 * DK], Tl[16 * DK];
+  __shared__ __attribute__((aligned(16))) float Pl[DK * DVP], Sl[16 * DK], Tl[16 * DK], Ql[DK * DK], Xl[DK * DVP];
   const int tid = threadIdx.x, bh = blockIdx.x, sp = blockIdx.y, r0 = 16 * sp;
   const float G3 = G * G * G;
   float *pre = a.prefix + (long)bh * a.nseg * PB;
@@ -246,11 +246,14 @@ __global__ void __launch_bounds__(256) ho3_scan_kernel(Ho3Args a, float G) {
     if (r == a.nseg - 1) break;
     const float *sb = a.sums + ((long)bh * (a.nseg - 1) + r) * SB;
     const float *Q2 = sb + PB, *X1 = Q2 + DK * DK, *X2 = X1 + DK * DVP;
+    for (int e = tid; e < DK * DK; e += 256) Ql[e] = Q2[e];  // the segment maps, staged
+    for (int e = tid; e < DK * DVP; e += 256) Xl[e] = X1[e];
+    __syncthreads();
     // T = S Q2 + X2 for the group's rows
     for (int e = tid; e < 16 * DK; e += 256) {
       const int f = e / DK, c = e % DK;
       float s = X2[(r0 + f) * DK + c];
-      for (int b = 0; b < DK; ++b) s += Sl[f * DK + b] * Q2[b * DK + c];
+      for (int b = 0; b < DK; ++b) s += Sl[f * DK + b] * Ql[b * DK + c];
       Tl[e] = s;
     }
     __syncthreads();
@@ -260,7 +263,7 @@ __global__ void __launch_bounds__(256) ho3_scan_kernel(Ho3Args a, float G) {
       if (e < 16 * DVP) {
         const int f = e / DVP, c = e % DVP;
         float s = 0.f;
-        for (int b = 0; b < DK; ++b) s += Tl[f * DK + b] * Pl[b * DVP + c] + Sl[f * DK + b] * X1[b * DVP + c];
+        for (int b = 0; b < DK; ++b) s += Tl[f * DK + b] * Pl[b * DVP + c] + Sl[f * DK + b] * Xl[b * DVP + c];
         W[i] = G3 * W[i] + sb[DK * DK + DK * DVP + (r0 + f) * DVP + c] + s;
       }
     }
