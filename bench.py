@@ -320,8 +320,9 @@ def copy_calibration(torch, gib=1):
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # defaults reach steady clocks: 50 untimed steps, then 200 timed ones (about 70 ms of forward work)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="decay_8k")
     ap.add_argument("--decode-prefill", type=int, default=None, help="prefix tokens (default: the workload's)")
     ap.add_argument("--cpu-heads", type=int, default=128, help="heads in the oracle's timed sample (0: skip)")
