@@ -127,3 +127,14 @@ def test_backward_workload_sampled(wname):
                             out=None if out is None else out[idx].double().numpy(),
                             den=None if den is None else den[idx].double().numpy())
     compare(got, ref, tol_for(w.dtype))
+
+
+def test_backward_long_head():
+    """Two heads of 65,536 tokens (d = dv = 64, bf16, decay 0.999): many segments and a long
+    adjoint scan; every gradient is compared with the oracle's serial adjoint."""
+    print("case 1 2 65536 64 64 bf16 0.999", flush=True)
+    q, k, v, dout = draw(1, 2, 65536, 64, 64, "bf16", seed=88)
+    got = gpu_backward(q, k, v, dout, 0.999, False, None, None)
+    ref = O.backward_serial(q.double().numpy(), k.double().numpy(), v.double().numpy(), dout.double().numpy(),
+                            0.999, False)
+    compare(got, ref, tol_for("bf16"))

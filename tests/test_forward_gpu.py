@@ -188,3 +188,12 @@ def test_workload_long_64k_sampled():
     q, k, v = I.make_qkv(w)
     heads = I.sample_heads(w.B, w.H, 2)
     print(check_case(q, k, v, w.decay, w.normalize, w.chunk, w.dtype, heads=heads, subset=True))
+
+
+def test_long_single_head_max_segments():
+    """One head of 262,144 tokens (d = dv = 64, bf16, decay 0.999): the automatic plan cuts it into the
+    maximum of 64 segments of 64 chunks; every token is compared with the oracle."""
+    print("case 1 1 262144 64 64 bf16 0.999", flush=True)
+    assert H.hla2_forward_segments(1, 1, 262144, 64, 64, 64) == 64
+    q, k, v = draw(1, 1, 262144, 64, 64, "bf16", seed=77)
+    print(check_case(q, k, v, 0.999, False, 64, "bf16"))
