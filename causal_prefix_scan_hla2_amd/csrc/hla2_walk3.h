@@ -170,23 +170,20 @@ walk3_kernel(WalkArgs a) {
   u32x4 rgq[NVK], rgk[NVK], rgv[NVV];
   auto load_chunk = [&](int c) __attribute__((always_inline)) {
     const int t0 = tok0 + c * CP;
+    // padded columns (e0 >= d) read at an offset past the buffer, which returns zero, so
+    // no select waits on the data
 #pragma unroll
     for (int i = 0; i < NVK; ++i) {
       const int vi = tid + i * NT, t = vi / (DK / 8), e0 = 8 * (vi % (DK / 8));
-      const bool ok = e0 < d;
-      const int off = ((t0 + t) * d + (ok ? e0 : 0)) * 2;
-      u32x4 xq = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
-      u32x4 xk = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
-      rgq[i] = ok ? xq : u32x4{0, 0, 0, 0};
-      rgk[i] = ok ? xk : u32x4{0, 0, 0, 0};
+      const int off = e0 < d ? ((t0 + t) * d + e0) * 2 : 0x7ffffff0;
+      rgq[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
+      rgk[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < NVV; ++i) {
       const int vi = tid + i * NT, t = vi / (DV / 8), e0 = 8 * (vi % (DV / 8));
-      const bool ok = e0 < dv;
-      const int off = ((t0 + t) * dv + (ok ? e0 : 0)) * 2;
-      u32x4 xv = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
-      rgv[i] = ok ? xv : u32x4{0, 0, 0, 0};
+      const int off = e0 < dv ? ((t0 + t) * dv + e0) * 2 : 0x7ffffff0;
+      rgv[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
     }
   };
   auto store_chunk = [&]() __attribute__((always_inline)) {
@@ -308,6 +305,9 @@ walk3_kernel(WalkArgs a) {
     // the next chunk's loads fly during phase 1 and land in LDS after B1
     // (a repeat of the last chunk at the end; it is never read)
     load_chunk(min(c + 1, nch - 1));
+    // keep the loads here: left to itself the scheduler sinks them to just before B1 and
+    // waits on them at once, exposing the whole memory latency every chunk
+    __builtin_amdgcn_sched_barrier(0);
 
     // ======== phase 1: chunk-local products of the wave's token block ========
     bf16x8 qw[KD];
@@ -333,46 +333,42 @@ walk3_kernel(WalkArgs a) {
       for (int s = 0; s < KC; ++s) adf[s] = frag_from_acc(at[2 * s], at[2 * s + 1]);
     }
 
-    // K^T fragments (A operand over d rows, k = tokens): for Z and the S update
-    bf16x8 kt[RT][KC];
+    // token-weighted K columns of the wave's S column tiles (B operand of the S update)
+    bf16x8 kb[SCT][KC];
 #pragma unroll
-    for (int i = 0; i < RT; ++i)
-#pragma unroll
-      for (int s = 0; s < KC; ++s) kt[i][s] = ld_cols(Ks, LDK, 32 * s, 16 * i, lane);
-
-    // Z^T tiles (rows d, column tau): S0 Q_w^T scaled by g^{tau+1}, plus K^T Ad_w^T
-    {
-#pragma unroll
-      for (int i = 0; i < RT; ++i) {
-        f32x4 z = zero4();
-#pragma unroll
-        for (int s = 0; s < KD; ++s) z = mma(ld_rows_c(Sb, LDS0, 16 * i, 32 * s, lane), qw[s], z);
-        if (DEC) z *= zf;
-#pragma unroll
-        for (int s = 0; s < KC; ++s) z = mma(kt[i][s], adf[s], z);
-        // Z[tau][16 i + 4 g + r] and its decayed copy, as rows
-        if constexpr (OUT) st4(Zs + tau_w * LDZ + 16 * i + 4 * g, z);
-        st4(Zts + tau_w * LDT + 16 * i + 4 * g, DEC ? z * ztf : z);
-      }
-    }
-
-    // S <- g^64 S + K^T diag(g^{63-t}) K  (the wave's column tiles)
-#pragma unroll
-    for (int j = 0; j < SCT; ++j) {
-      bf16x8 kb[KC];
+    for (int j = 0; j < SCT; ++j)
 #pragma unroll
       for (int s = 0; s < KC; ++s) {
-        kb[s] = ld_cols(Ks, LDK, 32 * s, 16 * (w * SCT + j), lane);
+        kb[j][s] = ld_cols(Ks, LDK, 32 * s, 16 * (w * SCT + j), lane);
         if (DEC) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) kb[s][e] = (bf16)((float)kb[s][e] * kweight(s, e));
+          for (int e = 0; e < 8; ++e) kb[j][s][e] = (bf16)((float)kb[j][s][e] * kweight(s, e));
         }
       }
+
+    // per 16-row tile i of d, with the K^T fragments of that tile (A operand, k = tokens):
+    //   Z^T tile (rows d, column tau): S0 Q_w^T scaled by g^{tau+1}, plus K^T Ad_w^T;
+    //   S <- g^64 S + K^T diag(g^{63-t}) K on the wave's column tiles.
+    // One row tile at a time keeps few K^T fragments live.
 #pragma unroll
-      for (int i = 0; i < RT; ++i) {
+    for (int i = 0; i < RT; ++i) {
+      bf16x8 kt[KC];
+#pragma unroll
+      for (int s = 0; s < KC; ++s) kt[s] = ld_cols(Ks, LDK, 32 * s, 16 * i, lane);
+      f32x4 z = zero4();
+#pragma unroll
+      for (int s = 0; s < KD; ++s) z = mma(ld_rows_c(Sb, LDS0, 16 * i, 32 * s, lane), qw[s], z);
+      if (DEC) z *= zf;
+#pragma unroll
+      for (int s = 0; s < KC; ++s) z = mma(kt[s], adf[s], z);
+      // Z[tau][16 i + 4 g + r] and its decayed copy, as rows
+      if constexpr (OUT) st4(Zs + tau_w * LDZ + 16 * i + 4 * g, z);
+      st4(Zts + tau_w * LDT + 16 * i + 4 * g, DEC ? z * ztf : z);
+#pragma unroll
+      for (int j = 0; j < SCT; ++j) {
         f32x4 acc = DEC ? Sacc[i][j] * g64 : Sacc[i][j];
 #pragma unroll
-        for (int s = 0; s < KC; ++s) acc = mma(kt[i][s], kb[s], acc);
+        for (int s = 0; s < KC; ++s) acc = mma(kt[s], kb[j][s], acc);
         Sacc[i][j] = acc;
       }
     }
@@ -399,28 +395,29 @@ walk3_kernel(WalkArgs a) {
     }
 
     if constexpr (!OUT) {
-      // C <- g^64 C + Q^T diag(g^{63-t}) V, m likewise with the weighted ones column
-      bf16x8 qt[RT][KC];
+      // C <- g^64 C + Q^T diag(g^{63-t}) V, m likewise with the weighted ones column;
+      // one row tile of Q^T fragments at a time
+      bf16x8 vb[UCT][KC];
 #pragma unroll
-      for (int i = 0; i < RT; ++i)
-#pragma unroll
-        for (int s = 0; s < KC; ++s) qt[i][s] = ld_cols(Qs, LDQ, 32 * s, 16 * i, lane);
-#pragma unroll
-      for (int j = 0; j < UCT; ++j) {
-        bf16x8 vb[KC];
+      for (int j = 0; j < UCT; ++j)
 #pragma unroll
         for (int s = 0; s < KC; ++s) {
-          vb[s] = vf[j][s];
+          vb[j][s] = vf[j][s];
           if (DEC) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) vb[s][e] = (bf16)((float)vb[s][e] * kweight(s, e));
+            for (int e = 0; e < 8; ++e) vb[j][s][e] = (bf16)((float)vb[j][s][e] * kweight(s, e));
           }
         }
 #pragma unroll
-        for (int i = 0; i < RT; ++i) {
+      for (int i = 0; i < RT; ++i) {
+        bf16x8 qt[KC];
+#pragma unroll
+        for (int s = 0; s < KC; ++s) qt[s] = ld_cols(Qs, LDQ, 32 * s, 16 * i, lane);
+#pragma unroll
+        for (int j = 0; j < UCT; ++j) {
           f32x4 acc = DEC ? Cacc[i][j] * g64 : Cacc[i][j];
 #pragma unroll
-          for (int s = 0; s < KC; ++s) acc = mma(qt[i][s], vb[s], acc);
+          for (int s = 0; s < KC; ++s) acc = mma(qt[s], vb[j][s], acc);
           Cacc[i][j] = acc;
         }
       }
