@@ -31,8 +31,8 @@ int check_shape(int B, int H, int n, int d, int dv, int chunk, int dtype) {
   if (dtype == HLA2_F32 && (d > 64 || dv > 64)) return HLA2_ERR_UNSUPPORTED;
   const long BH = (long)B * H;
   if (BH > (1L << 24) || (long)n > (1L << 30) || BH * (long)n > (1L << 40)) return HLA2_ERR_UNSUPPORTED;
-  // one head's rows are addressed with 32-bit byte offsets
-  if ((long)n * (d > dv ? d : dv) * 4 > 0x7fffffffL) return HLA2_ERR_UNSUPPORTED;
+  // one head's rows (padded by up to 16 columns) are addressed with 32-bit byte offsets
+  if ((long)n * ((d > dv ? d : dv) + 16) * 4 > 0x7fffff00L) return HLA2_ERR_UNSUPPORTED;
   return HLA2_OK;
 }
 

@@ -153,7 +153,9 @@ __device__ __forceinline__ void bwd_state_body(const BwdArgs &a, T *smem, const 
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int ti = j0 + 4 * gq + e;
-        x[e] = ti <= tr ? x[e] * pw[tr - ti] : 0.f;
+        // the factor is read and applied on every lane (clamped index, masked value) so
+        // that no branch forms around the table read
+        x[e] = (ti <= tr ? x[e] : 0.f) * pw[ti <= tr ? tr - ti : 0];
       }
       if (ok) st4(Ads + tr * L::LDC + j0 + 4 * gq, x);
     });
@@ -194,7 +196,9 @@ __device__ __forceinline__ void bwd_bm_zb(T *smem, const float *pw, int w, int l
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int tau = j0 + 4 * gq + e;
-      x[e] = tau <= s ? x[e] * pw[2 * (s - tau)] : 0.f;
+      // the factor is read and applied on every lane (clamped index, masked value) so
+      // that no branch forms around the table read
+      x[e] = (tau <= s ? x[e] : 0.f) * pw[tau <= s ? 2 * (s - tau) : 0];
     }
     if (ok) st4(Bms + s * Lay::LDC + j0 + 4 * gq, x);
   });
@@ -398,7 +402,9 @@ __global__ void __launch_bounds__(BWD_THREADS) bwd_walk_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int ti = j0 + 4 * gq + e;
-        x[e] = ti <= tr ? x[e] * pw[tr - ti] : 0.f;
+        // the factor is read and applied on every lane (clamped index, masked value) so
+        // that no branch forms around the table read
+        x[e] = (ti <= tr ? x[e] : 0.f) * pw[ti <= tr ? tr - ti : 0];
       }
       if (ok) st4(Ads + tr * Cfg::LDC + j0 + 4 * gq, x);
     });
@@ -419,7 +425,9 @@ __global__ void __launch_bounds__(BWD_THREADS) bwd_walk_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int tau = j0 + 4 * gq + e;
-        x[e] = tau <= s ? x[e] * pw[2 * (s - tau)] : 0.f;
+        // the factor is read and applied on every lane (clamped index, masked value) so
+        // that no branch forms around the table read
+        x[e] = (tau <= s ? x[e] : 0.f) * pw[tau <= s ? 2 * (s - tau) : 0];
       }
       if (ok) st4(Ws + s * Cfg::LDC + j0 + 4 * gq, x);
     });
@@ -429,7 +437,9 @@ __global__ void __launch_bounds__(BWD_THREADS) bwd_walk_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int ti = j0 + 4 * gq + e;
-        x[e] = ti <= tr ? x[e] * pw[tr - ti] : 0.f;
+        // the factor is read and applied on every lane (clamped index, masked value) so
+        // that no branch forms around the table read
+        x[e] = (ti <= tr ? x[e] : 0.f) * pw[ti <= tr ? tr - ti : 0];
       }
       if (ok) st4(Eks + tr * Cfg::LDC + j0 + 4 * gq, x);
     });

@@ -109,7 +109,9 @@ __global__ void __launch_bounds__(BWD_THREADS) ho3_walk_kernel(Ho3Args a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int ti = j0 + 4 * gq + e;
-        x[e] = ti <= tr ? x[e] * pw[tr - ti] : 0.f;
+        // the factor is read and applied on every lane (clamped index, masked value) so
+        // that no branch forms around the table read
+        x[e] = (ti <= tr ? x[e] : 0.f) * pw[ti <= tr ? tr - ti : 0];
       }
       if (ok) st4(Ads + tr * Cfg::LDC + j0 + 4 * gq, x);
     });
@@ -137,7 +139,9 @@ __global__ void __launch_bounds__(BWD_THREADS) ho3_walk_kernel(Ho3Args a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int l = j0 + 4 * gq + e;
-          x[e] = l <= tr ? x[e] * pw[3 * (tr - l)] : 0.f;
+          // the factor is read and applied on every lane (clamped index, masked value) so
+          // that no branch forms around the table read
+          x[e] = (l <= tr ? x[e] : 0.f) * pw[l <= tr ? 3 * (tr - l) : 0];
         }
         if (ok) st4(Wms + tr * Cfg::LDC + j0 + 4 * gq, x);
       });

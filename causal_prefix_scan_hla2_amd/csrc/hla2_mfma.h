@@ -64,6 +64,18 @@ __device__ __forceinline__ f32x4 mma(const f32x4 &a, const f32x4 &b, f32x4 c) {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Raw buffer resource over `bytes` bytes at `base` (gfx9 data format word): loads
+// at or past `bytes` return zero and stores there are dropped, so guarded global
+// accesses need no branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
+}
+// a byte offset past the end of every buffer resource (sizes stay below 2^31)
+constexpr int OOB_OFFSET = 0x7ffffff0;
+
 // Load *p when ok, else zero.  The load itself always reads a valid global
 // address (`safe` when !ok) and the zeroing is a select on the value, so the
 // compiler never has to give a zero constant an address.

@@ -60,14 +60,17 @@ constexpr int BWD_WAVES = 8, BWD_THREADS = 64 * BWD_WAVES;
 
 // Iterate a wave's share of the 16x16 tiles of an I x J result over NW waves:
 // f(i0, j0, store_ok, slot).  A wave with no tile left repeats the last one (not stored).
+// When the waves divide the tiles evenly (w < NW), every tile is real and store_ok is
+// a compile-time true: no branch around the stores.
 template <int I, int J, int NW = BWD_WAVES, typename F>
 __device__ __forceinline__ void for_tiles(int w, F &&f) {
   constexpr int NJ = J / 16, NT = (I / 16) * NJ, PER = (NT + NW - 1) / NW;
+  constexpr bool EVEN = NT % NW == 0;
 #pragma unroll
   for (int it = 0; it < PER; ++it) {
     const int t = w + NW * it;
-    const int tt = t < NT ? t : NT - 1;
-    f(16 * (tt / NJ), 16 * (tt % NJ), t < NT, it);
+    const int tt = (EVEN || t < NT) ? t : NT - 1;
+    f(16 * (tt / NJ), 16 * (tt % NJ), EVEN || t < NT, it);
   }
 }
 template <int I, int J, int NW = BWD_WAVES> struct TileCount {
@@ -85,23 +88,28 @@ template <> struct Vec16<float> {
   static constexpr int N = 4;
 };
 
-// Rows [t0, t0+BC) of a [n][gc] global matrix, as LDS rows of width W (zero
-// past n and past column gc; with ones >= 0, column `ones` holds 1 for rows
-// before n).  fetch() reads a thread's share into registers, put() writes them
+// Rows [t0, t0+BC) of one head's [n][gc] global matrix at `src`, as LDS rows of
+// width W (zero past n and past column gc; with ones >= 0, column `ones` holds 1
+// for rows before n).  fetch() reads a thread's share into registers with buffer
+// loads (reads past the head's rows return zero, so no branch), put() writes them
 // to LDS, so the global reads of the next chunk can fly during this one.
 template <typename T, int BC, int W, int NTH = BWD_THREADS>
 struct RowTile {
   typedef typename Vec16<T>::type V;
   static constexpr int VN = Vec16<T>::N, PERROW = W / VN, TOT = BC * PERROW, PER = (TOT + NTH - 1) / NTH;
+  static constexpr bool EVEN = TOT % NTH == 0;  // every thread has PER vectors: no guard
   V x[PER];
   __device__ __forceinline__ void fetch(const T *src, int gc, int t0, int n, int ones, int tid) {
+    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(src, n * gc * (int)sizeof(T));
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int i = tid + j * NTH;
       const int r = i / PERROW, c = (i % PERROW) * VN, t = t0 + r;
-      V v{};
-      if (i < TOT && t < n && c < gc) v = *(const V *)(src + (long)t * gc + c);
-      if (i < TOT && c == ones && t < n) v[0] = (T)1.f;
+      const bool in = EVEN || i < TOT;
+      int off = (in && c < gc) ? (t * gc + c) * (int)sizeof(T) : OOB_OFFSET;
+      asm("" : "+v"(off));  // one load of a selected offset, not a load on each side of a branch
+      V v = __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+      if (in && c == ones && t < n) v[0] = (T)1.f;
       x[j] = v;
     }
   }
@@ -109,7 +117,7 @@ struct RowTile {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int i = tid + j * NTH;
-      if (i < TOT) *(V *)(dst + (i / PERROW) * ld + (i % PERROW) * VN) = x[j];
+      if (EVEN || i < TOT) *(V *)(dst + (i / PERROW) * ld + (i % PERROW) * VN) = x[j];
     }
   }
 };
@@ -125,12 +133,18 @@ __device__ __forceinline__ f32x4 pt_frags(f32x4 acc, const FR *yf, const T *X, i
   return acc;
 }
 
-// Store four consecutive values of row t, columns c .. c+3, of a [n][ncols] matrix.
-__device__ __forceinline__ void st_out(bf16 *dst, int ncols, int t, int c, int n, f32x4 x) {
-  if (t < n && c < ncols) *(bf16x4 *)(dst + (long)t * ncols + c) = bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
+// Store four consecutive values of row t, columns c .. c+3, of one head's [n][ncols]
+// matrix at `base` with a buffer store: rows past n and columns past ncols are dropped.
+__device__ __forceinline__ void st_out(bf16 *base, int ncols, int t, int c, int n, f32x4 x) {
+  const __amdgpu_buffer_rsrc_t r = buf_rsrc(base, n * ncols * 2);
+  const bf16x4 b = bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, b), r, c < ncols ? (t * ncols + c) * 2 : OOB_OFFSET,
+                                        0, 0);
 }
-__device__ __forceinline__ void st_out(float *dst, int ncols, int t, int c, int n, f32x4 x) {
-  if (t < n && c < ncols) *(f32x4 *)(dst + (long)t * ncols + c) = x;
+__device__ __forceinline__ void st_out(float *base, int ncols, int t, int c, int n, f32x4 x) {
+  const __amdgpu_buffer_rsrc_t r = buf_rsrc(base, n * ncols * 4);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, c < ncols ? (t * ncols + c) * 4 : OOB_OFFSET,
+                                         0, 0);
 }
 __device__ __forceinline__ void st4g(bf16 *p, f32x4 x) { *(bf16x4 *)p = bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]}; }
 __device__ __forceinline__ void st4g(float *p, f32x4 x) { *(f32x4 *)p = x; }

@@ -47,14 +47,6 @@
 
 namespace hla2 {
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-
-// raw buffer resource over `bytes` bytes at `base` (gfx9 data format word)
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
-}
-
 // Operand fragment in the contiguous k-order: lane (g, n) gets X[row0 + n][k0 + 8g + 0..7]
 // with one 16-byte read.  Used for products whose two operands both come from LDS (both
 // are read in this order).
@@ -175,14 +167,14 @@ walk3_kernel(WalkArgs a) {
 #pragma unroll
     for (int i = 0; i < NVK; ++i) {
       const int vi = tid + i * NT, t = vi / (DK / 8), e0 = 8 * (vi % (DK / 8));
-      const int off = e0 < d ? ((t0 + t) * d + e0) * 2 : 0x7ffffff0;
+      const int off = e0 < d ? ((t0 + t) * d + e0) * 2 : OOB_OFFSET;
       rgq[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
       rgk[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < NVV; ++i) {
       const int vi = tid + i * NT, t = vi / (DV / 8), e0 = 8 * (vi % (DV / 8));
-      const int off = e0 < dv ? ((t0 + t) * dv + e0) * 2 : 0x7ffffff0;
+      const int off = e0 < dv ? ((t0 + t) * dv + e0) * 2 : OOB_OFFSET;
       rgv[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
     }
   };
@@ -306,8 +298,10 @@ walk3_kernel(WalkArgs a) {
     // (a repeat of the last chunk at the end; it is never read)
     load_chunk(min(c + 1, nch - 1));
     // keep the loads here: left to itself the scheduler sinks them to just before B1 and
-    // waits on them at once, exposing the whole memory latency every chunk
-    __builtin_amdgcn_sched_barrier(0);
+    // waits on them at once, exposing the whole memory latency every chunk.  (Measured:
+    // the d = 128 output walk, one wave per SIMD and at its register limit, runs faster
+    // with the scheduler's placement.)
+    if constexpr (!(OUT && DK > 64)) __builtin_amdgcn_sched_barrier(0);
 
     // ======== phase 1: chunk-local products of the wave's token block ========
     bf16x8 qw[KD];

@@ -99,8 +99,9 @@ int hla2_forward_segments(int B, int H, int n, int d, int dv, int chunk);
  *          `normalize` says
  *   workspace: device buffer of at least hla2_forward_workspace_bytes(...)
  *          bytes (may be NULL when that is 0); contents on entry are ignored
- * Supported: d, dv multiples of 16 in [16, 128]; n >= 1; B, H >= 1; B*H*n*max(d,dv)
- * below 2^31.
+ * Supported: d, dv multiples of 16 in [16, 128]; n >= 1; B, H >= 1; one head's
+ * rows in bytes, n * (max(d, dv) + 16) * 4, below 2^31 - 256 (they are addressed
+ * with 32-bit offsets); B*H <= 2^24 and B*H*n <= 2^40.
  */
 int hla2_forward(const void *q, const void *k, const void *v, void *out,
                  int B, int H, int n, int d, int dv, float decay, int normalize, int chunk,

@@ -264,3 +264,11 @@ def test_ho3_validates(L):
     assert ho3(B_=4, H_=8, n=2048, ws=None, wsb=0) == H.HLA2_ERR_WORKSPACE
     assert ho3(B_=4, H_=8, n=2048, wsb=need - 1) == H.HLA2_ERR_WORKSPACE
     assert H.hla2_ho3_forward_workspace_bytes(1, 1, 64, 128, 64, 1, 0) == 0
+
+
+def test_head_rows_beyond_32bit_offsets_rejected():
+    """One head's rows are addressed with 32-bit byte offsets: a length whose padded rows
+    pass 2^31 - 256 bytes is refused before anything is launched."""
+    n_ok = (0x7FFFFF00 // ((64 + 16) * 4))
+    assert H.hla2_forward_segments(1, 1, n_ok, 64, 64, 64) > 0
+    assert H.hla2_forward_segments(1, 1, n_ok + 1, 64, 64, 64) == H.HLA2_ERR_UNSUPPORTED
