@@ -22,7 +22,7 @@ namespace hla2 {
 
 template <typename T, int DK, int DVP, int BC>
 struct AhlaCfg {
-  static constexpr int PAD = 16 / sizeof(T);
+  static constexpr int PAD = lds_pad_bytes<T>() / sizeof(T);
   static constexpr int LDQ = DK + PAD, LDV = DVP + PAD, LDC = BC + PAD;
   static constexpr int Q_OFF = 0, K_OFF = BC * LDQ, V_OFF = K_OFF + BC * LDQ, Y_OFF = V_OFF + BC * LDV,
                        AD_OFF = Y_OFF + BC * LDV, P_OFF = AD_OFF + BC * LDC, E_OFF = P_OFF + DK * LDV,
@@ -75,8 +75,8 @@ __global__ void __launch_bounds__(BWD_THREADS) ahla_walk_kernel(AhlaArgs a) {
     // state copies for this chunk's products, and its rows
     for_tiles<DK, DVP>(w, [&](int i0, int j0, bool ok, int it) {
       if (ok) {
-        st4(Ps + (i0 + nn) * Cfg::LDV + j0 + 4 * gq, P[it]);
-        if (OUT) st4(Es + (i0 + nn) * Cfg::LDV + j0 + 4 * gq, E[it]);
+        st4l(Ps, Cfg::LDV, (i0 + nn), j0 + 4 * gq, P[it]);
+        if (OUT) st4l(Es, Cfg::LDV, (i0 + nn), j0 + 4 * gq, E[it]);
       }
     });
     rq.put(Qs, Cfg::LDQ, tid);
@@ -100,7 +100,7 @@ __global__ void __launch_bounds__(BWD_THREADS) ahla_walk_kernel(AhlaArgs a) {
         // that no branch forms around the table read
         x[e] = (ti <= tr ? x[e] : 0.f) * pw[ti <= tr ? tr - ti : 0];
       }
-      if (ok) st4(Ads + tr * Cfg::LDC + j0 + 4 * gq, x);
+      if (ok) st4l(Ads, Cfg::LDC, tr, j0 + 4 * gq, x);
     });
     __syncthreads();
     // Y = diag(g^(tau+1)) Q P0' + Ad V'
@@ -108,7 +108,7 @@ __global__ void __launch_bounds__(BWD_THREADS) ahla_walk_kernel(AhlaArgs a) {
       f32x4 x = pt<false, false, DK>(zero4(), Qs, Cfg::LDQ, Ps, Cfg::LDV, i0, j0, lane);
       x *= pw[i0 + nn + 1];
       x = pt<false, false, BC>(x, Ads, Cfg::LDC, Vs, Cfg::LDV, i0, j0, lane);
-      if (ok) st4(Ys + (i0 + nn) * Cfg::LDV + j0 + 4 * gq, x);
+      if (ok) st4l(Ys, Cfg::LDV, (i0 + nn), j0 + 4 * gq, x);
     });
     __syncthreads();
     // outputs O = diag(g^(tau+1)) Q E0' + Ad Y (kept in registers until den is known)

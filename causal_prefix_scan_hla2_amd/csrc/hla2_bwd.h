@@ -51,10 +51,12 @@
 
 namespace hla2 {
 
-// LDS layouts (row pitches carry 16 bytes of padding).
-template <typename T, int DK, int DVP, int BC>
+// LDS layouts.  Row pitches carry lds_pad_bytes<T>() of padding, except in the adjoint-summary
+// role of the two-role pre-walk, which keeps 16 bytes so that two of its workgroups share a CU.
+constexpr int RSUM_PADB = 16;
+template <typename T, int DK, int DVP, int BC, int PADB = lds_pad_bytes<T>()>
 struct BwdPitch {
-  static constexpr int PAD = 16 / sizeof(T);
+  static constexpr int PAD = PADB / sizeof(T);
   static constexpr int LDQ = DK + PAD;   // Q, K, Z, Zb rows; S / Shat copy rows
   static constexpr int LDV = DVP + PAD;  // V', G' rows; Ubar copy rows
   static constexpr int LDC = BC + PAD;   // BC x BC masks
@@ -79,8 +81,8 @@ struct StateLay : BwdPitch<T, DK, DVP, BC> {
 };
 // adjoint-summary walk: Q, V', G', the Ubar copy, Bm, Zb
 template <typename T, int DK, int DVP, int BC>
-struct RsumLay : BwdPitch<T, DK, DVP, BC> {
-  using P = BwdPitch<T, DK, DVP, BC>;
+struct RsumLay : BwdPitch<T, DK, DVP, BC, RSUM_PADB> {
+  using P = BwdPitch<T, DK, DVP, BC, RSUM_PADB>;
   static constexpr int Q_OFF = 0, V_OFF = BC * P::LDQ, G_OFF = V_OFF + BC * P::LDV, U_OFF = G_OFF + BC * P::LDV,
                        BM_OFF = U_OFF + DK * P::LDV, ZB_OFF = BM_OFF + BC * P::LDC, ELEMS = ZB_OFF + BC * P::LDQ;
 };
@@ -129,7 +131,7 @@ __device__ __forceinline__ void bwd_state_body(const BwdArgs &a, T *smem, const 
     T *blk = cst + (long)ch * L::BLOCK;
     for_tiles<DK, DK, NW>(w, [&](int i0, int j0, bool ok, int it) {
       if (ok) {
-        st4(Ss + (i0 + nn) * L::LDQ + j0 + 4 * gq, S[it]);
+        st4l(Ss, L::LDQ, (i0 + nn), j0 + 4 * gq, S[it]);
         st4g(blk + (i0 + nn) * DK + j0 + 4 * gq, S[it]);
       }
     });
@@ -157,7 +159,7 @@ __device__ __forceinline__ void bwd_state_body(const BwdArgs &a, T *smem, const 
         // that no branch forms around the table read
         x[e] = (ti <= tr ? x[e] : 0.f) * pw[ti <= tr ? tr - ti : 0];
       }
-      if (ok) st4(Ads + tr * L::LDC + j0 + 4 * gq, x);
+      if (ok) st4l(Ads, L::LDC, tr, j0 + 4 * gq, x);
     });
     __syncthreads();
     // Z = diag(g^(tau+1)) Q S0 + Ad K
@@ -165,7 +167,7 @@ __device__ __forceinline__ void bwd_state_body(const BwdArgs &a, T *smem, const 
       f32x4 x = pt<false, true, DK>(zero4(), Qs, L::LDQ, Ss, L::LDQ, i0, j0, lane);
       x *= pw[i0 + nn + 1];
       x = pt<false, false, BC>(x, Ads, L::LDC, Ks, L::LDQ, i0, j0, lane);
-      if (ok) st4(Zs + (i0 + nn) * L::LDQ + j0 + 4 * gq, x);
+      if (ok) st4l(Zs, L::LDQ, (i0 + nn), j0 + 4 * gq, x);
     });
     __syncthreads();
     // S <- g^BC S + K^T diag(g^(BC-1-i)) K;  U' <- g^(2BC) U' + Z^T diag(g^(2(BC-1-tau))) V'
@@ -200,7 +202,7 @@ __device__ __forceinline__ void bwd_bm_zb(T *smem, const float *pw, int w, int l
       // that no branch forms around the table read
       x[e] = (tau <= s ? x[e] : 0.f) * pw[tau <= s ? 2 * (s - tau) : 0];
     }
-    if (ok) st4(Bms + s * Lay::LDC + j0 + 4 * gq, x);
+    if (ok) st4l(Bms, Lay::LDC, s, j0 + 4 * gq, x);
   });
   __syncthreads();
   // Zb = Bm^T Q + diag(g^(2(BC-tau))) V' Ubar^T
@@ -208,7 +210,7 @@ __device__ __forceinline__ void bwd_bm_zb(T *smem, const float *pw, int w, int l
     f32x4 x = pt<false, true, DVP>(zero4(), Vs, Lay::LDV, Ubs, Lay::LDV, i0, j0, lane);
     x *= pw[2 * (BC - (i0 + nn))];
     x = pt<true, false, BC>(x, Bms, Lay::LDC, Qs, Lay::LDQ, i0, j0, lane);
-    if (ok) st4(Zbs + (i0 + nn) * Lay::LDQ + j0 + 4 * gq, x);
+    if (ok) st4l(Zbs, Lay::LDQ, (i0 + nn), j0 + 4 * gq, x);
   });
 }
 
@@ -235,12 +237,12 @@ __device__ __forceinline__ void bwd_adjoint_copy(T *smem, int w, int lane, const
   const int gq = lane >> 4, nn = lane & 15;
   T *const Ubs = smem + Lay::U_OFF;
   for_tiles<DK, DVP, NW>(w, [&](int i0, int j0, bool ok, int it) {
-    if (ok) st4(Ubs + (i0 + nn) * Lay::LDV + j0 + 4 * gq, Ub[it]);
+    if (ok) st4l(Ubs, Lay::LDV, (i0 + nn), j0 + 4 * gq, Ub[it]);
   });
   if constexpr (WITH_S) {
     T *const Shs = smem + Lay::S_OFF;
     for_tiles<DK, DK, NW>(w, [&](int i0, int j0, bool ok, int it) {
-      if (ok) st4(Shs + (i0 + nn) * Lay::LDQ + j0 + 4 * gq, Sh[it]);
+      if (ok) st4l(Shs, Lay::LDQ, (i0 + nn), j0 + 4 * gq, Sh[it]);
     });
   }
 }
@@ -406,7 +408,7 @@ __global__ void __launch_bounds__(BWD_THREADS) bwd_walk_kernel(BwdArgs a) {
         // that no branch forms around the table read
         x[e] = (ti <= tr ? x[e] : 0.f) * pw[ti <= tr ? tr - ti : 0];
       }
-      if (ok) st4(Ads + tr * Cfg::LDC + j0 + 4 * gq, x);
+      if (ok) st4l(Ads, Cfg::LDC, tr, j0 + 4 * gq, x);
     });
     // Bm, then Zb (one barrier inside)
     bwd_bm_zb<T, DK, DVP, BC, NW, Cfg>(smem, pw, w, lane);
@@ -415,7 +417,7 @@ __global__ void __launch_bounds__(BWD_THREADS) bwd_walk_kernel(BwdArgs a) {
       f32x4 x = pt_frags<DK>(zero4(), s0f, Qs, Cfg::LDQ, i0, lane);
       x *= pw[i0 + nn + 1];
       x = pt<false, false, BC>(x, Ads, Cfg::LDC, Ks, Cfg::LDQ, i0, j0, lane);
-      if (ok) st4(Zs + (i0 + nn) * Cfg::LDQ + j0 + 4 * gq, x);
+      if (ok) st4l(Zs, Cfg::LDQ, (i0 + nn), j0 + 4 * gq, x);
     });
     __syncthreads();
     // W = L o D2 o (Q Z^T) (rows s, columns tau <= s);  Ek = L o D1 o (Zb K^T)
@@ -429,7 +431,7 @@ __global__ void __launch_bounds__(BWD_THREADS) bwd_walk_kernel(BwdArgs a) {
         // that no branch forms around the table read
         x[e] = (tau <= s ? x[e] : 0.f) * pw[tau <= s ? 2 * (s - tau) : 0];
       }
-      if (ok) st4(Ws + s * Cfg::LDC + j0 + 4 * gq, x);
+      if (ok) st4l(Ws, Cfg::LDC, s, j0 + 4 * gq, x);
     });
     for_tiles<BC, BC>(w, [&](int i0, int j0, bool ok, int) {
       f32x4 x = pt<false, true, DK>(zero4(), Zbs, Cfg::LDQ, Ks, Cfg::LDQ, i0, j0, lane);
@@ -441,7 +443,7 @@ __global__ void __launch_bounds__(BWD_THREADS) bwd_walk_kernel(BwdArgs a) {
         // that no branch forms around the table read
         x[e] = (ti <= tr ? x[e] : 0.f) * pw[ti <= tr ? tr - ti : 0];
       }
-      if (ok) st4(Eks + tr * Cfg::LDC + j0 + 4 * gq, x);
+      if (ok) st4l(Eks, Cfg::LDC, tr, j0 + 4 * gq, x);
     });
     __syncthreads();
     // dV' = W^T G' + diag(g^(2(BC-tau))) Z Ubar

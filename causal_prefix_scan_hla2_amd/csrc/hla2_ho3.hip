@@ -25,7 +25,7 @@ namespace hla2 {
 
 template <typename T, int DK, int DVP, int BC>
 struct Ho3Cfg {
-  static constexpr int PAD = 16 / sizeof(T);
+  static constexpr int PAD = lds_pad_bytes<T>() / sizeof(T);
   static constexpr int LDQ = DK + PAD, LDV = DVP + PAD, LDC = BC + PAD;
   static constexpr int Q_OFF = 0, K_OFF = BC * LDQ, V_OFF = K_OFF + BC * LDQ, Y_OFF = V_OFF + BC * LDV,
                        Z_OFF = Y_OFF + BC * LDV, AD_OFF = Z_OFF + BC * LDQ, WM_OFF = AD_OFF + BC * LDC,
@@ -84,12 +84,12 @@ __global__ void __launch_bounds__(BWD_THREADS) ho3_walk_kernel(Ho3Args a) {
   for (int ch = 0; ch < nch; ++ch) {
     const int t0 = tok0 + ch * BC;
     for_tiles<DK, DK>(w, [&](int i0, int j0, bool ok, int it) {
-      if (ok) st4(Ss + (i0 + nn) * Cfg::LDQ + j0 + 4 * gq, S[it]);
+      if (ok) st4l(Ss, Cfg::LDQ, (i0 + nn), j0 + 4 * gq, S[it]);
     });
     for_tiles<DK, DVP>(w, [&](int i0, int j0, bool ok, int it) {
       if (ok) {
-        st4(Ps + (i0 + nn) * Cfg::LDV + j0 + 4 * gq, P[it]);
-        if (OUT) st4(Ws + (i0 + nn) * Cfg::LDV + j0 + 4 * gq, W[it]);
+        st4l(Ps, Cfg::LDV, (i0 + nn), j0 + 4 * gq, P[it]);
+        if (OUT) st4l(Ws, Cfg::LDV, (i0 + nn), j0 + 4 * gq, W[it]);
       }
     });
     rq.put(Qs, Cfg::LDQ, tid);
@@ -113,7 +113,7 @@ __global__ void __launch_bounds__(BWD_THREADS) ho3_walk_kernel(Ho3Args a) {
         // that no branch forms around the table read
         x[e] = (ti <= tr ? x[e] : 0.f) * pw[ti <= tr ? tr - ti : 0];
       }
-      if (ok) st4(Ads + tr * Cfg::LDC + j0 + 4 * gq, x);
+      if (ok) st4l(Ads, Cfg::LDC, tr, j0 + 4 * gq, x);
     });
     __syncthreads();
     // Z = diag(g^(tau+1)) Q S0 + Ad K;  Y = diag(g^(tau+1)) Q P0' + Ad V'
@@ -121,13 +121,13 @@ __global__ void __launch_bounds__(BWD_THREADS) ho3_walk_kernel(Ho3Args a) {
       f32x4 x = pt<false, true, DK>(zero4(), Qs, Cfg::LDQ, Ss, Cfg::LDQ, i0, j0, lane);
       x *= pw[i0 + nn + 1];
       x = pt<false, false, BC>(x, Ads, Cfg::LDC, Ks, Cfg::LDQ, i0, j0, lane);
-      if (ok) st4(Zs + (i0 + nn) * Cfg::LDQ + j0 + 4 * gq, x);
+      if (ok) st4l(Zs, Cfg::LDQ, (i0 + nn), j0 + 4 * gq, x);
     });
     for_tiles<BC, DVP>(w, [&](int i0, int j0, bool ok, int) {
       f32x4 x = pt<false, false, DK>(zero4(), Qs, Cfg::LDQ, Ps, Cfg::LDV, i0, j0, lane);
       x *= pw[i0 + nn + 1];
       x = pt<false, false, BC>(x, Ads, Cfg::LDC, Vs, Cfg::LDV, i0, j0, lane);
-      if (ok) st4(Ys + (i0 + nn) * Cfg::LDV + j0 + 4 * gq, x);
+      if (ok) st4l(Ys, Cfg::LDV, (i0 + nn), j0 + 4 * gq, x);
     });
     __syncthreads();
     f32x4 O[OUT ? TileCount<BC, DVP>::PER : 1];
@@ -143,7 +143,7 @@ __global__ void __launch_bounds__(BWD_THREADS) ho3_walk_kernel(Ho3Args a) {
           // that no branch forms around the table read
           x[e] = (l <= tr ? x[e] : 0.f) * pw[l <= tr ? 3 * (tr - l) : 0];
         }
-        if (ok) st4(Wms + tr * Cfg::LDC + j0 + 4 * gq, x);
+        if (ok) st4l(Wms, Cfg::LDC, tr, j0 + 4 * gq, x);
       });
       __syncthreads();
       // O = diag(g^(3(tau+1))) Q W0' + Wm Y

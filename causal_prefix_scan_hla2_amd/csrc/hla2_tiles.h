@@ -8,11 +8,52 @@
 namespace hla2 {
 
 // ---------------------------------------------------------------------------
-// Tile products.  mm: acc(m0.., n0..) += sum_k A(m, k) B(k, n) over k < K, with
+// LDS row layout.  A bf16 operand fragment takes, per lane group g, the k-values
+// 4g..4g+3 and 16+4g..16+4g+3 of a 32-wide k-tile (hla2_mfma.h).  In LDS every
+// row keeps its 4-column groups permuted inside each 32 columns so that those two
+// groups sit side by side: a row fragment is then one 16-byte read instead of two
+// 8-byte reads 32 bytes apart (which the compiler pairs into one slow read).  The
+// LDS transpose read still finds any logical 4-column group, since every lane
+// supplies its own address.  fp32 rows are stored as they are.
+template <typename T> __device__ __forceinline__ int pcol(int c);
+template <> __device__ __forceinline__ int pcol<bf16>(int c) {
+  return (c & ~31) | (((c >> 2) & 3) << 3) | (((c >> 4) & 1) << 2) | (c & 3);
+}
+template <> __device__ __forceinline__ int pcol<float>(int c) { return c; }
+
+// Row padding in bytes.  bf16 rows 160 or 288 bytes apart (32 bytes of padding on 128- and
+// 256-byte rows) serve 16-byte row reads and LDS transpose reads without bank conflicts
+// (measured on gfx950); fp32 rows keep 16 bytes.
+template <typename T> constexpr int lds_pad_bytes() { return sizeof(T) == 2 ? 32 : 16; }
+
+// fragments of LDS rows / columns in that layout (k0, col0 multiples of the k-tile / 16)
+__device__ __forceinline__ bf16x8 ld_rows_l(const bf16 *X, int ld, int row0, int k0, int lane) {
+  return *(const bf16x8 *)(X + (row0 + (lane & 15)) * ld + k0 + 8 * (lane >> 4));
+}
+__device__ __forceinline__ f32x4 ld_rows_l(const float *X, int ld, int row0, int k0, int lane) {
+  return ld_rows(X, ld, row0, k0, lane);
+}
+__device__ __forceinline__ bf16x8 ld_cols_l(const bf16 *X, int ld, int k0, int col0, int lane) {
+  const int g = lane >> 4, src = lane & 15;
+  const bf16 *p = X + (k0 + 4 * g + (src >> 2)) * ld + pcol<bf16>(col0 + 4 * (src & 3));
+  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
+  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p + 16 * ld));
+  return cat8(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi));
+}
+__device__ __forceinline__ f32x4 ld_cols_l(const float *X, int ld, int k0, int col0, int lane) {
+  return ld_cols(X, ld, k0, col0, lane);
+}
+// four consecutive values of an LDS row at logical column c (a multiple of 4)
+template <typename T>
+__device__ __forceinline__ void st4l(T *X, int ld, int row, int c, f32x4 x) {
+  st4(X + row * ld + pcol<T>(c), x);
+}
+
+// ---------------------------------------------------------------------------
+// Tile products (operands in LDS, in the layout above).  mm: acc(m0.., n0..) += sum_k A(m, k) B(k, n) over k < K, with
 // A(m, k) = AT ? A[k*lda + m] : A[m*lda + k] and B(k, n) = BT ? B[n*ldb + k] : B[k*ldb + n].
-// A transposed A or a non-transposed B is read with the LDS transpose read, so
-// those operands must live in LDS; the others may be global.  wk(k) scales the
-// k-th term.
+// Both operands live in LDS (a transposed A or a non-transposed B is read with the
+// LDS transpose read).  wk(k) scales the k-th term.
 template <bool AT, bool BT, int K, typename T, typename WF>
 __device__ __forceinline__ f32x4 mmw(f32x4 acc, const T *A, int lda, const T *B, int ldb, int m0, int n0,
                                      int lane, WF &&wk) {
@@ -21,8 +62,8 @@ __device__ __forceinline__ f32x4 mmw(f32x4 acc, const T *A, int lda, const T *B,
   const int g = lane >> 4;
 #pragma unroll
   for (int k0 = 0; k0 < K; k0 += KT) {
-    auto a = AT ? ld_cols(A, lda, k0, m0, lane) : ld_rows(A, lda, m0, k0, lane);
-    auto b = BT ? ld_rows(B, ldb, n0, k0, lane) : ld_cols(B, ldb, k0, n0, lane);
+    auto a = AT ? ld_cols_l(A, lda, k0, m0, lane) : ld_rows_l(A, lda, m0, k0, lane);
+    auto b = BT ? ld_rows_l(B, ldb, n0, k0, lane) : ld_cols_l(B, ldb, k0, n0, lane);
     a = scale_frag(a, g, [&](int kk) { return wk(k0 + kk); });
     acc = mma(a, b, acc);
   }
@@ -35,8 +76,8 @@ __device__ __forceinline__ f32x4 mm(f32x4 acc, const T *A, int lda, const T *B, 
   static_assert(K % KT == 0, "contraction length must be a whole number of k-tiles");
 #pragma unroll
   for (int k0 = 0; k0 < K; k0 += KT) {
-    auto a = AT ? ld_cols(A, lda, k0, m0, lane) : ld_rows(A, lda, m0, k0, lane);
-    auto b = BT ? ld_rows(B, ldb, n0, k0, lane) : ld_cols(B, ldb, k0, n0, lane);
+    auto a = AT ? ld_cols_l(A, lda, k0, m0, lane) : ld_rows_l(A, lda, m0, k0, lane);
+    auto b = BT ? ld_rows_l(B, ldb, n0, k0, lane) : ld_cols_l(B, ldb, k0, n0, lane);
     acc = mma(a, b, acc);
   }
   return acc;
@@ -113,23 +154,33 @@ struct RowTile {
       x[j] = v;
     }
   }
+  // into the LDS row layout above: a bf16 vector's two 4-column groups go to their own places
   __device__ __forceinline__ void put(T *dst, int ld, int tid) const {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int i = tid + j * NTH;
-      if (EVEN || i < TOT) *(V *)(dst + (i / PERROW) * ld + (i % PERROW) * VN) = x[j];
+      if (EVEN || i < TOT) {
+        T *row = dst + (i / PERROW) * ld;
+        const int c = (i % PERROW) * VN;
+        if constexpr (VN == 8) {
+          *(bf16x4 *)(row + pcol<T>(c)) = bf16x4{x[j][0], x[j][1], x[j][2], x[j][3]};
+          *(bf16x4 *)(row + pcol<T>(c + 4)) = bf16x4{x[j][4], x[j][5], x[j][6], x[j][7]};
+        } else {
+          *(V *)(row + c) = x[j];
+        }
+      }
     }
   }
 };
 
 // Tile of P = X Y where Y is symmetric or given as its transposed rows: the
 // fragments yf[k] = rows j0 .. j0+15 of Y^T over the k-tiles of the contraction
-// (read ahead by the caller), X row-major.  Lane (g, n) holds P[i0 + n][j0 + 4g + e].
+// (read ahead by the caller), X row-major in LDS.  Lane (g, n) holds P[i0 + n][j0 + 4g + e].
 template <int K, typename T, typename FR>
 __device__ __forceinline__ f32x4 pt_frags(f32x4 acc, const FR *yf, const T *X, int ldx, int i0, int lane) {
   constexpr int KT = Ktile<T>::ROWS;
 #pragma unroll
-  for (int k0 = 0; k0 < K; k0 += KT) acc = mma(yf[k0 / KT], ld_rows(X, ldx, i0, k0, lane), acc);
+  for (int k0 = 0; k0 < K; k0 += KT) acc = mma(yf[k0 / KT], ld_rows_l(X, ldx, i0, k0, lane), acc);
   return acc;
 }
 
