@@ -120,6 +120,7 @@ walk3_kernel(WalkArgs a) {
   using Cfg = W3Cfg<DK, DV, OUT>;
   constexpr int CP = Cfg::CP, NB = Cfg::NB, NT = Cfg::NT, RT = Cfg::RT, KD = Cfg::KD, KC = Cfg::KC;
   constexpr int SCT = Cfg::SCT, UCT = Cfg::UCT, URT = Cfg::URT;
+  constexpr bool PAIR = UCT == 2 && DK == 64;  // interleaved value-column tiles (see vcol)
   constexpr int LDK = Cfg::LDK, LDQ = Cfg::LDQ, LDT = Cfg::LDT, LDS0 = Cfg::LDS0, LDZ = Cfg::LDZ;
   constexpr int LDV = Cfg::LDV, LDW = Cfg::LDW, NVK = Cfg::NVK, NVV = Cfg::NVV;
 
@@ -137,6 +138,15 @@ walk3_kernel(WalkArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Value column of lane n in the wave's column tile j (of U, C, V and the outputs).  With two
+  // tiles per wave at d <= 64 the tiles interleave in 4-column groups, so that a lane's outputs
+  // of both tiles are 8 consecutive columns (one 16-byte store); V is stored in LDS with the
+  // matching permutation so that its column fragments stay plain transpose reads.  (Measured:
+  // the d = 128 walker, one wave per SIMD, is slower with it.)
+  auto vcol = [&](int j, int nn) __attribute__((always_inline)) -> int {
+    if constexpr (PAIR) return 32 * w + 8 * (nn >> 2) + 4 * j + (nn & 3);
+    return 16 * (w * UCT + j) + nn;
+  };
   const int nseg_here = OUT ? a.nseg : walk_nsum(a);
   const int bh = blockIdx.x / nseg_here, seg = blockIdx.x % nseg_here;
   const int d = a.d, dv = a.dv;
@@ -188,7 +198,14 @@ walk3_kernel(WalkArgs a) {
 #pragma unroll
     for (int i = 0; i < NVV; ++i) {
       const int vi = tid + i * NT, t = vi / (DV / 8), e0 = 8 * (vi % (DV / 8));
-      *(u32x4 *)(Vs + t * LDV + e0) = rgv[i];
+      if constexpr (PAIR) {
+        // value columns 8a + 4j + b of each 32 are stored at 16j + 4a + b (see vcol)
+        const int base = (e0 & ~31) + 4 * ((e0 & 31) >> 3);
+        *(u32x2 *)(Vs + t * LDV + base) = u32x2{rgv[i][0], rgv[i][1]};
+        *(u32x2 *)(Vs + t * LDV + base + 16) = u32x2{rgv[i][2], rgv[i][3]};
+      } else {
+        *(u32x4 *)(Vs + t * LDV + e0) = rgv[i];
+      }
     }
   };
 
@@ -223,7 +240,7 @@ walk3_kernel(WalkArgs a) {
 #pragma unroll
       for (int j = 0; j < UCT; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Uacc[i][j][r] = pU[(16 * i + 4 * g + r) * DV + 16 * (w * UCT + j) + n];
+        for (int r = 0; r < 4; ++r) Uacc[i][j][r] = pU[(16 * i + 4 * g + r) * DV + vcol(j, n)];
     }
     if constexpr (DEN) {
 #pragma unroll
@@ -521,6 +538,7 @@ walk3_kernel(WalkArgs a) {
 #pragma unroll
         for (int s = 0; s < KC; ++s)
           if (32 * s <= 16 * r + 15) wb[s] = ld_rows_c(Ws, LDW, 16 * r, 32 * s, lane);
+        bf16x4 ob[UCT];
 #pragma unroll
         for (int j = 0; j < UCT; ++j) {
           f32x4 o = zero4();
@@ -531,11 +549,21 @@ walk3_kernel(WalkArgs a) {
           for (int s = 0; s < KC; ++s)
             if (32 * s <= 16 * r + 15) o = mma(vf[j][s], wb[s], o);
           if (DEN) o *= rden;
-          // rows past the end fall outside the buffer; padded columns are sent there too
-          const int col = 16 * (w * UCT + j) + 4 * g, t = t0 + 16 * r + n;
-          const bf16x4 ob = bf16x4{(bf16)o[0], (bf16)o[1], (bf16)o[2], (bf16)o[3]};
-          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ob), ro,
-                                                col < dv ? (t * dv + col) * 2 : 0x7fffffff, 0, 0);
+          ob[j] = bf16x4{(bf16)o[0], (bf16)o[1], (bf16)o[2], (bf16)o[3]};
+        }
+        // rows past the end fall outside the buffer; padded columns are sent there too
+        const int t = t0 + 16 * r + n;
+        if constexpr (PAIR) {
+          const int col = vcol(0, 4 * g);  // 8 consecutive columns: tile 0's four, then tile 1's
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, cat8(ob[0], ob[1])), ro,
+                                                 col < dv ? (t * dv + col) * 2 : 0x7fffffff, 0, 0);
+        } else {
+#pragma unroll
+          for (int j = 0; j < UCT; ++j) {
+            const int col = vcol(j, 4 * g);
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ob[j]), ro,
+                                                  col < dv ? (t * dv + col) * 2 : 0x7fffffff, 0, 0);
+          }
         }
       }
     }
@@ -555,8 +583,8 @@ walk3_kernel(WalkArgs a) {
       for (int j = 0; j < UCT; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          sC[(16 * i + 4 * g + r) * DV + 16 * (w * UCT + j) + n] = Cacc[i][j][r];
-          sU[(16 * i + 4 * g + r) * DV + 16 * (w * UCT + j) + n] = Uacc[i][j][r];
+          sC[(16 * i + 4 * g + r) * DV + vcol(j, n)] = Cacc[i][j][r];
+          sU[(16 * i + 4 * g + r) * DV + vcol(j, n)] = Uacc[i][j][r];
         }
     }
     if (n == 0) {
