@@ -59,6 +59,14 @@ def min_bytes_forward(w, esize):
     return w.B * w.H * w.n * (2 * w.d + 2 * w.dv) * esize
 
 
+def min_bytes_backward(w, esize):
+    """q, k, v, dout read once (out and the fp32 den too under the ratio), dq, dk, dv written once."""
+    per = (2 * w.d + 2 * w.dv) * esize + (2 * w.d + w.dv) * esize
+    if w.normalize:
+        per += w.dv * esize + 4
+    return w.B * w.H * w.n * per
+
+
 def output_kernel_bytes(w, esize, nseg):
     """Algorithmic HBM bytes of one chunk-output launch: q, k, v read once, out
     written once, and the incoming state (S0, U0, u0) of every segment after
@@ -398,6 +406,7 @@ def main(argv=None):
             "workload": w.name, "ms_per_step": bw["seconds"] * 1e3, "tokens_per_s": bw["tokens_per_s"],
             "head_tokens_per_s": bw["head_tokens_per_s"], "vs_forward_time": bw["seconds"] / fw["seconds"],
             "workspace_bytes": bw["workspace_bytes"],
+            "hbm_min_bytes_frac": min_bytes_backward(w, 2 if w.dtype == "bf16" else 4) / bw["seconds"] / PEAK_HBM,
         }
     if not args.skip_variants:
         line["ahla"] = bench_variant("hla2_ahla_forward", w, args.steps, args.warmup, torch, H, I,

@@ -79,6 +79,15 @@ SMALL = [
     (1, 1, 1000, 64, 128, "bf16", 0.99, False, 64, 2),
     (1, 1, 1000, 64, 128, "bf16", 0.99, False, 64, 7),
     (1, 2, 4100, 64, 64, "bf16", 1.0, True, 32, 0),
+    # Strong decays (the state shrinks by 2^-5 to 2^-47 per 64-token chunk), many chunks per
+    # segment, one and several segments, ratio on and off.
+    (1, 2, 3000, 64, 128, "bf16", 0.95, False, 64, 1),
+    (1, 2, 3000, 64, 128, "bf16", 0.95, True, 64, 3),
+    (1, 2, 3000, 64, 64, "bf16", 0.95, False, 64, 2),
+    (1, 2, 2000, 64, 128, "bf16", 0.7, False, 64, 2),
+    (1, 2, 2000, 48, 64, "bf16", 0.7, True, 64, 1),
+    (1, 2, 2000, 64, 128, "bf16", 0.6, True, 64, 2),
+    (1, 1, 2000, 64, 64, "bf16", 0.6, False, 64, 1),
 ]
 
 

@@ -56,6 +56,8 @@ CASES = [
     (1, 2, 700, 128, 64, "bf16", 0.98, True, 64, 4),
     (1, 1, 40, 64, 64, "bf16", 0.9, False, 64, 0),     # shorter than a chunk: all tail
     (1, 1, 100, 16, 16, "bf16", 1.0, False, 16, 1),
+    (1, 2, 3000, 64, 128, "bf16", 0.95, True, 64, 2),  # strong decays over many chunks
+    (1, 1, 2000, 64, 64, "bf16", 0.7, False, 64, 1),
 ]
 
 
