@@ -210,8 +210,8 @@ __global__ void __launch_bounds__(256) ahla_scan_kernel(AhlaArgs a, float gseg) 
 
 template <typename T, int DK, int DV, bool NORM>
 static hipError_t launch_ahla_t(int phase, int BH, const AhlaArgs &a, float gseg, hipStream_t s) {
-  constexpr int DVP = DV + (NORM ? Ktile<T>::ROWS : 0);
-  constexpr int BC = (sizeof(T) == 4 || DK == 128) ? 32 : 64;
+  constexpr int DVP = lds_walk_dvp(sizeof(T) == 4, DV, NORM);
+  constexpr int BC = lds_walk_chunk(sizeof(T) == 4, DK);
   switch (phase) {
     case AHLA_SUMMARY:
       hipLaunchKernelGGL((ahla_walk_kernel<T, DK, DV, DVP, BC, false, NORM>), dim3(BH * (a.nseg - 1)),
@@ -234,8 +234,6 @@ static hipError_t launch_ahla_n(bool norm, int phase, int BH, const AhlaArgs &a,
               : launch_ahla_t<T, DK, DV, false>(phase, BH, a, gseg, s);
 }
 
-int ahla_chunk(int dtype, int DK) { return (dtype == 0 || DK == 128) ? 32 : 64; }
-int ahla_dvp(int dtype, int DV, bool norm) { return DV + (norm ? (dtype == 0 ? 16 : 32) : 0); }
 
 hipError_t launch_ahla(int dtype, int DK, int DV, bool norm, int phase, int BH, const AhlaArgs &a, float gseg,
                        hipStream_t s) {

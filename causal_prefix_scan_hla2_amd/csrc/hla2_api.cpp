@@ -98,8 +98,8 @@ BwdPlan make_bwd_plan(int B, int H, int n, int d, int dv, int dtype, int normali
   const int chunk = dtype == HLA2_BF16 ? 64 : 32;
   b.p = make_plan(B, H, n, d, dv, chunk, dtype, segments, 1);
   b.norm = normalize != 0;
-  b.BC = hla2::bwd_chunk(dtype == HLA2_F32 ? 0 : 1, b.p.DK);
-  b.DVP = hla2::bwd_dvp(dtype == HLA2_F32 ? 0 : 1, b.p.DV, b.norm);
+  b.BC = hla2::lds_walk_chunk(dtype == HLA2_F32, b.p.DK);
+  b.DVP = hla2::lds_walk_dvp(dtype == HLA2_F32, b.p.DV, b.norm);
   b.nbc = (n + b.BC - 1) / b.BC;
   const size_t es = dtype == HLA2_F32 ? 4 : 2, BH = (size_t)b.p.BH, R = (size_t)b.p.nseg;
   const size_t DK = (size_t)b.p.DK, DVP = (size_t)b.DVP, adj = (DK * DVP + DK * DK) * 4;
@@ -327,7 +327,7 @@ int hla2_backward(const void *q, const void *k, const void *v, const void *out, 
 }
 
 static size_t ahla_workspace(const Plan &p, int dtype) {
-  const size_t DK = (size_t)p.DK, DVP = (size_t)hla2::ahla_dvp(dtype == HLA2_F32 ? 0 : 1, p.DV, true);
+  const size_t DK = (size_t)p.DK, DVP = (size_t)hla2::lds_walk_dvp(dtype == HLA2_F32, p.DV, true);
   const size_t BH = (size_t)p.BH, R = (size_t)p.nseg;
   if (R == 1) return 0;
   return align256(BH * (R - 1) * (2 * DK * DVP + DK * DK) * 4) + BH * R * 2 * DK * DVP * 4;
@@ -360,7 +360,7 @@ int hla2_ahla_forward(const void *q, const void *k, const void *v, void *out, in
   if (need > 0 && (!workspace || workspace_bytes_given < need || !aligned(workspace, 256))) return HLA2_ERR_WORKSPACE;
   const int dt = dtype == HLA2_F32 ? 0 : 1;
   const bool norm = normalize || den_out;
-  const size_t DK = (size_t)p.DK, DVP = (size_t)hla2::ahla_dvp(dt, p.DV, norm);
+  const size_t DK = (size_t)p.DK, DVP = (size_t)hla2::lds_walk_dvp(dt == 0, p.DV, norm);
   hla2::AhlaArgs a;
   a.q = q;
   a.k = k;
@@ -391,13 +391,13 @@ int hla2_ahla_forward(const void *q, const void *k, const void *v, void *out, in
 }
 
 static size_t ho3_sums_bytes(const Plan &p, int dt, bool norm) {
-  const size_t DK = (size_t)p.DK, DVP = (size_t)hla2::ho3_dvp(dt, p.DV, norm);
+  const size_t DK = (size_t)p.DK, DVP = (size_t)hla2::lds_walk_dvp(dt == 0, p.DV, norm);
   return (size_t)p.BH * (p.nseg - 1) * (DK * DK + 2 * DK * DVP + 2 * DK * DK + DK * DVP) * 4;
 }
 static size_t ho3_workspace(const Plan &p, int dtype) {
   if (p.nseg == 1) return 0;
   const int dt = dtype == HLA2_F32 ? 0 : 1;
-  const size_t DK = (size_t)p.DK, DVP = (size_t)hla2::ho3_dvp(dt, p.DV, true);
+  const size_t DK = (size_t)p.DK, DVP = (size_t)hla2::lds_walk_dvp(dt == 0, p.DV, true);
   return align256(ho3_sums_bytes(p, dt, true)) + (size_t)p.BH * p.nseg * (DK * DK + 2 * DK * DVP) * 4;
 }
 static int ho3_check(int B, int H, int n, int d, int dv, int dtype) {

@@ -121,8 +121,8 @@ __global__ void __launch_bounds__(256) bwd_rscan_kernel(BwdArgs a, float gL) {
 // each may use every register of its SIMD.
 template <typename T, int DK, int DV, bool NORM>
 struct BwdShape {
-  static constexpr int DVP = DV + (NORM ? Ktile<T>::ROWS : 0);
-  static constexpr int BC = (sizeof(T) == 4 || DK == 128) ? 32 : 64;
+  static constexpr int DVP = lds_walk_dvp(sizeof(T) == 4, DV, NORM);
+  static constexpr int BC = lds_walk_chunk(sizeof(T) == 4, DK);
 };
 
 template <typename T, int DK, int DV, bool NORM>
@@ -157,9 +157,6 @@ static hipError_t launch_bwd_n(bool norm, int phase, int BH, const BwdArgs &a, c
   return norm ? launch_bwd_t<T, DK, DV, true>(phase, BH, a, pa, gL, s)
               : launch_bwd_t<T, DK, DV, false>(phase, BH, a, pa, gL, s);
 }
-
-int bwd_chunk(int dtype, int DK) { return (dtype == 0 || DK == 128) ? 32 : 64; }
-int bwd_dvp(int dtype, int DV, bool norm) { return DV + (norm ? (dtype == 0 ? 16 : 32) : 0); }
 
 hipError_t launch_bwd(int dtype, int DK, int DV, bool norm, int phase, int BH, const BwdArgs &a,
                       const BwdPrepArgs &pa, float gL, hipStream_t s) {

@@ -279,8 +279,8 @@ __global__ void __launch_bounds__(256) ho3_scan_kernel(Ho3Args a, float G) {
 
 template <typename T, int DK, int DV, bool NORM>
 static hipError_t launch_ho3_t(int phase, int BH, const Ho3Args &a, float gseg, hipStream_t s) {
-  constexpr int DVP = DV + (NORM ? Ktile<T>::ROWS : 0);
-  constexpr int BC = sizeof(T) == 4 ? 32 : 64;
+  constexpr int DVP = lds_walk_dvp(sizeof(T) == 4, DV, NORM);
+  constexpr int BC = lds_walk_chunk(sizeof(T) == 4, DK);  // d <= 64 here
   switch (phase) {
     case HO3_SUMMARY:
       hipLaunchKernelGGL((ho3_walk_kernel<T, DK, DV, DVP, BC, false, NORM>), dim3(BH * (a.nseg - 1)),
@@ -303,7 +303,6 @@ static hipError_t launch_ho3_n(bool norm, int phase, int BH, const Ho3Args &a, f
               : launch_ho3_t<T, DK, DV, false>(phase, BH, a, gseg, s);
 }
 
-int ho3_dvp(int dtype, int DV, bool norm) { return DV + (norm ? (dtype == 0 ? 16 : 32) : 0); }
 
 hipError_t launch_ho3(int dtype, int DK, int DV, bool norm, int phase, int BH, const Ho3Args &a, float gseg,
                       hipStream_t s) {

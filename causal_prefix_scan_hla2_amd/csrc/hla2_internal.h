@@ -142,9 +142,13 @@ struct BwdPrepArgs {
 };
 // BWD_PRE: the forward-state walk and the adjoint summaries, one launch
 enum { BWD_PREP = 0, BWD_PRE = 1, BWD_RSCAN = 3, BWD_WALK = 4 };
-// backward chunk length and padded value width (values, plus the denominator column under the ratio)
-int bwd_chunk(int dtype, int DK);
-int bwd_dvp(int dtype, int DV, bool norm);
+// Chunk tokens and padded value width of the LDS-operand walkers (backward, AHLA, third order):
+// 32-token chunks for fp32 and at d = 128 (LDS), else 64; under the ratio the values gain the
+// denominator's ones column, padded to a whole k-tile (16 for fp32, 32 for bf16).
+__host__ __device__ constexpr int lds_walk_chunk(bool f32, int DK) { return (f32 || DK == 128) ? 32 : 64; }
+__host__ __device__ constexpr int lds_walk_dvp(bool f32, int DV, bool norm) {
+  return DV + (norm ? (f32 ? 16 : 32) : 0);
+}
 // one phase of the backward pass; gL = decay^(tokens per full segment) (reverse scan)
 hipError_t launch_bwd(int dtype, int DK, int DV, bool norm, int phase, int BH, const BwdArgs &a,
                       const BwdPrepArgs &pa, float gL, hipStream_t s);
@@ -163,8 +167,6 @@ struct AhlaArgs {
   int normalize;
 };
 enum { AHLA_SUMMARY = 0, AHLA_SCAN = 1, AHLA_OUTPUT = 2 };
-int ahla_chunk(int dtype, int DK);
-int ahla_dvp(int dtype, int DV, bool norm);
 // one phase of the AHLA forward; gseg = decay^(tokens per full segment) (scan)
 hipError_t launch_ahla(int dtype, int DK, int DV, bool norm, int phase, int BH, const AhlaArgs &a, float gseg,
                        hipStream_t s);
@@ -174,7 +176,6 @@ hipError_t launch_ahla(int dtype, int DK, int DV, bool norm, int phase, int BH, 
 // prefix blocks are S | P' | W' and their summary blocks S | P' | W' | Q2 | X1 | X2.
 using Ho3Args = AhlaArgs;
 enum { HO3_SUMMARY = 0, HO3_SCAN = 1, HO3_OUTPUT = 2 };
-int ho3_dvp(int dtype, int DV, bool norm);
 hipError_t launch_ho3(int dtype, int DK, int DV, bool norm, int phase, int BH, const Ho3Args &a, float gseg,
                       hipStream_t s);
 
