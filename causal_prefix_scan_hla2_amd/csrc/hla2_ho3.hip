@@ -225,54 +225,63 @@ __global__ void __launch_bounds__(BWD_THREADS) ho3_walk_kernel(Ho3Args a) {
 template <int DK, int DVP>
 __global__ void __launch_bounds__(256) ho3_scan_kernel(Ho3Args a, float G) {
   constexpr long PB = (long)DK * DK + 2L * DK * DVP, SB = PB + 2L * DK * DK + (long)DK * DVP;
-  constexpr int NS = (16 * DK + 255) / 256, NW3 = (16 * DVP + 255) / 256;
+  // a thread owns 4 consecutive columns of a row (reads of P', X1, Q2 as float4: 4 FMAs each)
+  constexpr int WQ = 16 * DVP / 4, NWQ = (WQ + 255) / 256;  // 4-column groups of the W' rows
+  constexpr int TQ = 16 * DK / 4, NTQ = (TQ + 255) / 256;   // of the S Q2 rows
   __shared__ __attribute__((aligned(16))) float Pl[DK * DVP], Sl[16 * DK], Tl[16 * DK], Ql[DK * DK], Xl[DK * DVP];
   const int tid = threadIdx.x, bh = blockIdx.x, sp = blockIdx.y, r0 = 16 * sp;
   const float G3 = G * G * G;
   float *pre = a.prefix + (long)bh * a.nseg * PB;
   for (int e = tid; e < DK * DVP; e += 256) Pl[e] = 0.f;
   for (int e = tid; e < 16 * DK; e += 256) Sl[e] = 0.f;
-  float W[NW3];
+  f32x4 W[NWQ];  // W'[r0 + f][c0 .. c0 + 3] for group q = tid + 256 i: f = q / (DVP/4), c0 = 4 (q % (DVP/4))
 #pragma unroll
-  for (int i = 0; i < NW3; ++i) W[i] = 0.f;
+  for (int i = 0; i < NWQ; ++i) W[i] = zero4();
   for (int r = 0; r < a.nseg; ++r) {
     float *pr = pre + (long)r * PB;
     __syncthreads();  // Pl, Sl hold the state before segment r
     for (int e = tid; e < 16 * DK; e += 256) pr[r0 * DK + e] = Sl[e];
 #pragma unroll
-    for (int i = 0; i < NW3; ++i) {
-      const int e = tid + 256 * i;
-      if (e < 16 * DVP) {
-        pr[DK * DK + r0 * DVP + e] = Pl[r0 * DVP + e];
-        pr[DK * DK + DK * DVP + r0 * DVP + e] = W[i];
+    for (int i = 0; i < NWQ; ++i) {
+      const int q = tid + 256 * i;
+      if (WQ % 256 == 0 || q < WQ) {
+        const int f = q / (DVP / 4), c0 = 4 * (q % (DVP / 4));
+        *(f32x4 *)(pr + DK * DK + (r0 + f) * DVP + c0) = *(const f32x4 *)(Pl + (r0 + f) * DVP + c0);
+        *(f32x4 *)(pr + DK * DK + DK * DVP + (r0 + f) * DVP + c0) = W[i];
       }
     }
     if (r == a.nseg - 1) break;
     const float *sb = a.sums + ((long)bh * (a.nseg - 1) + r) * SB;
     const float *Q2 = sb + PB, *X1 = Q2 + DK * DK, *X2 = X1 + DK * DVP;
-    for (int e = tid; e < DK * DK; e += 256) Ql[e] = Q2[e];  // the segment maps, staged
-    for (int e = tid; e < DK * DVP; e += 256) Xl[e] = X1[e];
+    for (int e = 4 * tid; e < DK * DK; e += 1024) *(f32x4 *)(Ql + e) = *(const f32x4 *)(Q2 + e);  // the maps, staged
+    for (int e = 4 * tid; e < DK * DVP; e += 1024) *(f32x4 *)(Xl + e) = *(const f32x4 *)(X1 + e);
     __syncthreads();
     // T = S Q2 + X2 for the group's rows
-    for (int e = tid; e < 16 * DK; e += 256) {
-      const int f = e / DK, c = e % DK;
-      float s = X2[(r0 + f) * DK + c];
-      for (int b = 0; b < DK; ++b) s += Sl[f * DK + b] * Ql[b * DK + c];
-      Tl[e] = s;
+#pragma unroll
+    for (int i = 0; i < NTQ; ++i) {
+      const int q = tid + 256 * i;
+      if (TQ % 256 == 0 || q < TQ) {
+        const int f = q / (DK / 4), c0 = 4 * (q % (DK / 4));
+        f32x4 t = *(const f32x4 *)(X2 + (r0 + f) * DK + c0);
+        for (int b = 0; b < DK; ++b) t += Sl[f * DK + b] * *(const f32x4 *)(Ql + b * DK + c0);
+        *(f32x4 *)(Tl + f * DK + c0) = t;
+      }
     }
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < NW3; ++i) {
-      const int e = tid + 256 * i;
-      if (e < 16 * DVP) {
-        const int f = e / DVP, c = e % DVP;
-        float s = 0.f;
-        for (int b = 0; b < DK; ++b) s += Tl[f * DK + b] * Pl[b * DVP + c] + Sl[f * DK + b] * Xl[b * DVP + c];
-        W[i] = G3 * W[i] + sb[DK * DK + DK * DVP + (r0 + f) * DVP + c] + s;
+    for (int i = 0; i < NWQ; ++i) {
+      const int q = tid + 256 * i;
+      if (WQ % 256 == 0 || q < WQ) {
+        const int f = q / (DVP / 4), c0 = 4 * (q % (DVP / 4));
+        f32x4 acc = zero4();
+        for (int b = 0; b < DK; ++b)
+          acc += Tl[f * DK + b] * *(const f32x4 *)(Pl + b * DVP + c0) + Sl[f * DK + b] * *(const f32x4 *)(Xl + b * DVP + c0);
+        W[i] = G3 * W[i] + *(const f32x4 *)(sb + DK * DK + DK * DVP + (r0 + f) * DVP + c0) + acc;
       }
     }
     __syncthreads();  // every read of the state before segment r done
-    for (int e = tid; e < DK * DVP; e += 256) Pl[e] = G * Pl[e] + sb[DK * DK + e];
+    for (int e = 4 * tid; e < DK * DVP; e += 1024)
+      *(f32x4 *)(Pl + e) = G * *(const f32x4 *)(Pl + e) + *(const f32x4 *)(sb + DK * DK + e);
     for (int e = tid; e < 16 * DK; e += 256) Sl[e] = G * Sl[e] + sb[r0 * DK + e];
   }
 }
