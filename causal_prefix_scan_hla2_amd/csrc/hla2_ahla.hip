@@ -170,23 +170,25 @@ __global__ void __launch_bounds__(BWD_THREADS) ahla_walk_kernel(AhlaArgs a) {
 template <int DK, int DVP>
 __global__ void __launch_bounds__(256) ahla_scan_kernel(AhlaArgs a, float gseg) {
   constexpr long PB = 2L * DK * DVP, SB = 2L * DK * DVP + (long)DK * DK;
-  constexpr int NE = (16 * DVP + 255) / 256;  // E' entries per thread (16 rows)
+  // a thread owns 4 consecutive columns of a row of E' (each float4 read of P' feeds 4 FMAs)
+  constexpr int EQ = 16 * DVP / 4, NEQ = (EQ + 255) / 256;
   __shared__ __attribute__((aligned(16))) float Pl[DK * DVP], Ml[16 * DK];
   const int tid = threadIdx.x, bh = blockIdx.x, sp = blockIdx.y, r0 = 16 * sp;
   float *pre = a.prefix + (long)bh * a.nseg * PB;
   for (int e = tid; e < DK * DVP; e += 256) Pl[e] = 0.f;
-  float E[NE];
+  f32x4 E[NEQ];  // E'[r0 + f][c0 .. c0 + 3] for group q = tid + 256 i: f = q / (DVP/4), c0 = 4 (q % (DVP/4))
 #pragma unroll
-  for (int i = 0; i < NE; ++i) E[i] = 0.f;
+  for (int i = 0; i < NEQ; ++i) E[i] = zero4();
   for (int r = 0; r < a.nseg; ++r) {
     float *pr = pre + (long)r * PB;
     __syncthreads();  // Pl holds P'_r
 #pragma unroll
-    for (int i = 0; i < NE; ++i) {
-      const int e = tid + 256 * i;
-      if (e < 16 * DVP) {
-        pr[r0 * DVP + e] = Pl[r0 * DVP + e];
-        pr[DK * DVP + r0 * DVP + e] = E[i];
+    for (int i = 0; i < NEQ; ++i) {
+      const int q = tid + 256 * i;
+      if (EQ % 256 == 0 || q < EQ) {
+        const int f = q / (DVP / 4), c0 = 4 * (q % (DVP / 4));
+        *(f32x4 *)(pr + (r0 + f) * DVP + c0) = *(const f32x4 *)(Pl + (r0 + f) * DVP + c0);
+        *(f32x4 *)(pr + DK * DVP + (r0 + f) * DVP + c0) = E[i];
       }
     }
     if (r == a.nseg - 1) break;
@@ -194,17 +196,19 @@ __global__ void __launch_bounds__(256) ahla_scan_kernel(AhlaArgs a, float gseg) 
     for (int e = tid; e < 16 * DK; e += 256) Ml[e] = Mr[r0 * DK + e];  // the group's rows of M
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < NE; ++i) {
-      const int e = tid + 256 * i;
-      if (e < 16 * DVP) {
-        const int f = r0 + e / DVP, c = e % DVP;
-        float s = 0.f;
-        for (int g2 = 0; g2 < DK; ++g2) s += Ml[(f - r0) * DK + g2] * Pl[g2 * DVP + c];
-        E[i] = gseg * (E[i] + s) + sb[DK * DVP + f * DVP + c];
+    for (int i = 0; i < NEQ; ++i) {
+      const int q = tid + 256 * i;
+      if (EQ % 256 == 0 || q < EQ) {
+        const int f = q / (DVP / 4), c0 = 4 * (q % (DVP / 4));
+        f32x4 acc = zero4();
+#pragma unroll 8
+        for (int g2 = 0; g2 < DK; ++g2) acc += Ml[f * DK + g2] * *(const f32x4 *)(Pl + g2 * DVP + c0);
+        E[i] = gseg * (E[i] + acc) + *(const f32x4 *)(sb + DK * DVP + (r0 + f) * DVP + c0);
       }
     }
     __syncthreads();  // every read of P'_r done
-    for (int e = tid; e < DK * DVP; e += 256) Pl[e] = gseg * Pl[e] + sb[e];
+    for (int e = 4 * tid; e < DK * DVP; e += 1024)
+      *(f32x4 *)(Pl + e) = gseg * *(const f32x4 *)(Pl + e) + *(const f32x4 *)(sb + e);
   }
 }
 
