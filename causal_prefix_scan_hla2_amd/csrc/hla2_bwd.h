@@ -132,11 +132,11 @@ __device__ __forceinline__ void bwd_state_body(const BwdArgs &a, T *smem, const 
     for_tiles<DK, DK, NW>(w, [&](int i0, int j0, bool ok, int it) {
       if (ok) {
         st4l(Ss, L::LDQ, (i0 + nn), j0 + 4 * gq, S[it]);
-        st4g(blk + (i0 + nn) * DK + j0 + 4 * gq, S[it]);
+        st4g(blk + (i0 + nn) * DK + pcol<T>(j0 + 4 * gq), S[it]);
       }
     });
     for_tiles<DK, DVP, NW>(w, [&](int i0, int j0, bool ok, int it) {
-      if (ok) st4g(blk + DK * DK + (i0 + nn) * DVP + j0 + 4 * gq, U[it]);
+      if (ok) st4g(blk + DK * DK + (i0 + nn) * DVP + pcol<T>(j0 + 4 * gq), U[it]);
     });
     rq.put(Qs, L::LDQ, tid);
     rk.put(Ks, L::LDQ, tid);
@@ -381,9 +381,9 @@ __global__ void __launch_bounds__(BWD_THREADS) bwd_walk_kernel(BwdArgs a) {
     {
       const T *S0 = cst + (long)ch * Cfg::BLOCK, *U0 = S0 + DK * DK;
 #pragma unroll
-      for (int k = 0; k < DK / KT; ++k) s0f[k] = ld_rows(S0, DK, jw, k * KT, lane);
+      for (int k = 0; k < DK / KT; ++k) s0f[k] = ld_rows_l(S0, DK, jw, k * KT, lane);
 #pragma unroll
-      for (int k = 0; k < DVP / KT; ++k) u0f[k] = ld_rows(U0, DVP, jw, k * KT, lane);
+      for (int k = 0; k < DVP / KT; ++k) u0f[k] = ld_rows_l(U0, DVP, jw, k * KT, lane);
     }
     rq.put(Qs, Cfg::LDQ, tid);
     rk.put(Ks, Cfg::LDQ, tid);
