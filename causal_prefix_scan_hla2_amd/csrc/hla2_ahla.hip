@@ -75,8 +75,8 @@ __global__ void __launch_bounds__(BWD_THREADS) ahla_walk_kernel(AhlaArgs a) {
     // state copies for this chunk's products, and its rows
     for_tiles<DK, DVP>(w, [&](int i0, int j0, bool ok, int it) {
       if (ok) {
-        st4l(Ps, Cfg::LDV, (i0 + nn), j0 + 4 * gq, P[it]);
-        if (OUT) st4l(Es, Cfg::LDV, (i0 + nn), j0 + 4 * gq, E[it]);
+        st4l(Ps, Cfg::LDV, i0 + nn, j0 + 4 * gq, P[it]);
+        if (OUT) st4l(Es, Cfg::LDV, i0 + nn, j0 + 4 * gq, E[it]);
       }
     });
     rq.put(Qs, Cfg::LDQ, tid);
@@ -108,7 +108,7 @@ __global__ void __launch_bounds__(BWD_THREADS) ahla_walk_kernel(AhlaArgs a) {
       f32x4 x = pt<false, false, DK>(zero4(), Qs, Cfg::LDQ, Ps, Cfg::LDV, i0, j0, lane);
       x *= pw[i0 + nn + 1];
       x = pt<false, false, BC>(x, Ads, Cfg::LDC, Vs, Cfg::LDV, i0, j0, lane);
-      if (ok) st4l(Ys, Cfg::LDV, (i0 + nn), j0 + 4 * gq, x);
+      if (ok) st4l(Ys, Cfg::LDV, i0 + nn, j0 + 4 * gq, x);
     });
     __syncthreads();
     // outputs O = diag(g^(tau+1)) Q E0' + Ad Y (kept in registers until den is known)

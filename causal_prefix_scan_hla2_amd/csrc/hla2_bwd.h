@@ -131,7 +131,7 @@ __device__ __forceinline__ void bwd_state_body(const BwdArgs &a, T *smem, const 
     T *blk = cst + (long)ch * L::BLOCK;
     for_tiles<DK, DK, NW>(w, [&](int i0, int j0, bool ok, int it) {
       if (ok) {
-        st4l(Ss, L::LDQ, (i0 + nn), j0 + 4 * gq, S[it]);
+        st4l(Ss, L::LDQ, i0 + nn, j0 + 4 * gq, S[it]);
         st4g(blk + (i0 + nn) * DK + pcol<T>(j0 + 4 * gq), S[it]);
       }
     });
@@ -167,7 +167,7 @@ __device__ __forceinline__ void bwd_state_body(const BwdArgs &a, T *smem, const 
       f32x4 x = pt<false, true, DK>(zero4(), Qs, L::LDQ, Ss, L::LDQ, i0, j0, lane);
       x *= pw[i0 + nn + 1];
       x = pt<false, false, BC>(x, Ads, L::LDC, Ks, L::LDQ, i0, j0, lane);
-      if (ok) st4l(Zs, L::LDQ, (i0 + nn), j0 + 4 * gq, x);
+      if (ok) st4l(Zs, L::LDQ, i0 + nn, j0 + 4 * gq, x);
     });
     __syncthreads();
     // S <- g^BC S + K^T diag(g^(BC-1-i)) K;  U' <- g^(2BC) U' + Z^T diag(g^(2(BC-1-tau))) V'
@@ -210,7 +210,7 @@ __device__ __forceinline__ void bwd_bm_zb(T *smem, const float *pw, int w, int l
     f32x4 x = pt<false, true, DVP>(zero4(), Vs, Lay::LDV, Ubs, Lay::LDV, i0, j0, lane);
     x *= pw[2 * (BC - (i0 + nn))];
     x = pt<true, false, BC>(x, Bms, Lay::LDC, Qs, Lay::LDQ, i0, j0, lane);
-    if (ok) st4l(Zbs, Lay::LDQ, (i0 + nn), j0 + 4 * gq, x);
+    if (ok) st4l(Zbs, Lay::LDQ, i0 + nn, j0 + 4 * gq, x);
   });
 }
 
@@ -237,12 +237,12 @@ __device__ __forceinline__ void bwd_adjoint_copy(T *smem, int w, int lane, const
   const int gq = lane >> 4, nn = lane & 15;
   T *const Ubs = smem + Lay::U_OFF;
   for_tiles<DK, DVP, NW>(w, [&](int i0, int j0, bool ok, int it) {
-    if (ok) st4l(Ubs, Lay::LDV, (i0 + nn), j0 + 4 * gq, Ub[it]);
+    if (ok) st4l(Ubs, Lay::LDV, i0 + nn, j0 + 4 * gq, Ub[it]);
   });
   if constexpr (WITH_S) {
     T *const Shs = smem + Lay::S_OFF;
     for_tiles<DK, DK, NW>(w, [&](int i0, int j0, bool ok, int it) {
-      if (ok) st4l(Shs, Lay::LDQ, (i0 + nn), j0 + 4 * gq, Sh[it]);
+      if (ok) st4l(Shs, Lay::LDQ, i0 + nn, j0 + 4 * gq, Sh[it]);
     });
   }
 }
@@ -417,7 +417,7 @@ __global__ void __launch_bounds__(BWD_THREADS) bwd_walk_kernel(BwdArgs a) {
       f32x4 x = pt_frags<DK>(zero4(), s0f, Qs, Cfg::LDQ, i0, lane);
       x *= pw[i0 + nn + 1];
       x = pt<false, false, BC>(x, Ads, Cfg::LDC, Ks, Cfg::LDQ, i0, j0, lane);
-      if (ok) st4l(Zs, Cfg::LDQ, (i0 + nn), j0 + 4 * gq, x);
+      if (ok) st4l(Zs, Cfg::LDQ, i0 + nn, j0 + 4 * gq, x);
     });
     __syncthreads();
     // W = L o D2 o (Q Z^T) (rows s, columns tau <= s);  Ek = L o D1 o (Zb K^T)

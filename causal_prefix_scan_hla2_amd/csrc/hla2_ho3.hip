@@ -84,12 +84,12 @@ __global__ void __launch_bounds__(BWD_THREADS) ho3_walk_kernel(Ho3Args a) {
   for (int ch = 0; ch < nch; ++ch) {
     const int t0 = tok0 + ch * BC;
     for_tiles<DK, DK>(w, [&](int i0, int j0, bool ok, int it) {
-      if (ok) st4l(Ss, Cfg::LDQ, (i0 + nn), j0 + 4 * gq, S[it]);
+      if (ok) st4l(Ss, Cfg::LDQ, i0 + nn, j0 + 4 * gq, S[it]);
     });
     for_tiles<DK, DVP>(w, [&](int i0, int j0, bool ok, int it) {
       if (ok) {
-        st4l(Ps, Cfg::LDV, (i0 + nn), j0 + 4 * gq, P[it]);
-        if (OUT) st4l(Ws, Cfg::LDV, (i0 + nn), j0 + 4 * gq, W[it]);
+        st4l(Ps, Cfg::LDV, i0 + nn, j0 + 4 * gq, P[it]);
+        if (OUT) st4l(Ws, Cfg::LDV, i0 + nn, j0 + 4 * gq, W[it]);
       }
     });
     rq.put(Qs, Cfg::LDQ, tid);
@@ -121,13 +121,13 @@ __global__ void __launch_bounds__(BWD_THREADS) ho3_walk_kernel(Ho3Args a) {
       f32x4 x = pt<false, true, DK>(zero4(), Qs, Cfg::LDQ, Ss, Cfg::LDQ, i0, j0, lane);
       x *= pw[i0 + nn + 1];
       x = pt<false, false, BC>(x, Ads, Cfg::LDC, Ks, Cfg::LDQ, i0, j0, lane);
-      if (ok) st4l(Zs, Cfg::LDQ, (i0 + nn), j0 + 4 * gq, x);
+      if (ok) st4l(Zs, Cfg::LDQ, i0 + nn, j0 + 4 * gq, x);
     });
     for_tiles<BC, DVP>(w, [&](int i0, int j0, bool ok, int) {
       f32x4 x = pt<false, false, DK>(zero4(), Qs, Cfg::LDQ, Ps, Cfg::LDV, i0, j0, lane);
       x *= pw[i0 + nn + 1];
       x = pt<false, false, BC>(x, Ads, Cfg::LDC, Vs, Cfg::LDV, i0, j0, lane);
-      if (ok) st4l(Ys, Cfg::LDV, (i0 + nn), j0 + 4 * gq, x);
+      if (ok) st4l(Ys, Cfg::LDV, i0 + nn, j0 + 4 * gq, x);
     });
     __syncthreads();
     f32x4 O[OUT ? TileCount<BC, DVP>::PER : 1];
