@@ -67,12 +67,21 @@ def min_bytes_backward(w, esize):
     return w.B * w.H * w.n * per
 
 
-def output_kernel_bytes(w, esize, nseg):
-    """Algorithmic HBM bytes of one chunk-output launch: q, k, v read once, out
-    written once, and the incoming state (S0, U0, u0) of every segment after
-    the first read once."""
+def output_launch_tokens(w, plan):
+    """Tokens per head that the chunk-output launch walks: every token under a
+    plain plan; under a lead plan those after segment 0 (walked, with its
+    outputs, in the launch before the scan)."""
+    nseg, c0, _, lead = plan
+    return max(w.n - c0 * 64, 0) if lead else w.n
+
+
+def output_kernel_bytes(w, esize, plan):
+    """Algorithmic HBM bytes of one chunk-output launch: q, k, v of its tokens
+    read once, their outputs written once, and the incoming state (S0, U0, u0)
+    of every segment after the first read once."""
     state = (w.d * w.d + w.d * w.dv + w.d) * 4
-    return min_bytes_forward(w, esize) + w.B * w.H * (nseg - 1) * state
+    return w.B * w.H * output_launch_tokens(w, plan) * (2 * w.d + 2 * w.dv) * esize + \
+        w.B * w.H * (plan[0] - 1) * state
 
 
 def roofline(flops, nbytes, seconds):
@@ -162,28 +171,32 @@ def bench_forward(w, steps, warmup, torch, H, I):
     for _ in range(warmup):
         fn()
     t, wall = time_calls(fn_timed, steps, 0, torch)
-    phases = {"summary": 0.0, "scan": 0.0, "output": 0.0}
+    plan = H.hla2_forward_plan(w.B, w.H, w.n, w.d, w.dv, w.chunk)
+    nseg = plan[0]
+    # the launch before the scan: segment summaries, plus segment 0's outputs under a lead plan
+    first = "lead" if plan[3] else "summary"
+    phases = {first: 0.0, "scan": 0.0, "output": 0.0}
     for row in evs[:steps]:
-        phases["summary"] += row[0].elapsed_time(row[1]) / 1e3
+        phases[first] += row[0].elapsed_time(row[1]) / 1e3
         phases["scan"] += row[1].elapsed_time(row[2]) / 1e3
         phases["output"] += row[2].elapsed_time(row[3]) / 1e3
     phases = {key: val / max(steps, 1) for key, val in phases.items()}
     esize = 4 if w.dtype == "f32" else 2
     flops = canonical_flops_per_head_token(w.d, w.dv, w.chunk, w.normalize) * w.head_tokens
-    nseg = H.hla2_forward_segments(w.B, w.H, w.n, w.d, w.dv, w.chunk)
     return {
         "seconds": t,
         "wall": wall,
         "phases": phases,
+        "plan": {"segments": nseg, "lead_chunks": plan[1], "seg_chunks": plan[2], "lead": plan[3]},
         "output_flops_per_call": output_kernel_flops_per_head_token(w.d, w.dv, w.chunk, w.normalize)
-                                 * w.head_tokens,
+                                 * w.B * w.H * output_launch_tokens(w, plan),
         "tokens_per_s": w.B * w.n / t,
         "head_tokens_per_s": w.head_tokens / t,
         "tflops": flops / t / 1e12,
         "mfma_frac": flops / t / PEAK_BF16_MFMA,
         "flops_per_call": flops,
         "min_bytes": min_bytes_forward(w, esize),
-        "output_bytes_per_call": output_kernel_bytes(w, esize, nseg),
+        "output_bytes_per_call": output_kernel_bytes(w, esize, plan),
         "segments": nseg,
     }
 
@@ -369,7 +382,7 @@ def main(argv=None):
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic (seeded N(0,1) draws with the workload's scaling, rounded to the element type)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "n": w.n, "d": w.d, "dv": w.dv, "chunk": w.chunk,
-                   "decay": w.decay, "normalize": w.normalize, "segments": fw["segments"],
+                   "decay": w.decay, "normalize": w.normalize, "segments": fw["segments"], "plan": fw["plan"],
                    "global_batch": w.B, "seq_len": w.n, "parallelism": "single GPU"},
         "head_tokens_per_s": fw["head_tokens_per_s"],
         "tflops": fw["tflops"],
@@ -378,8 +391,9 @@ def main(argv=None):
         "kernel_ms": {key: val * 1e3 for key, val in fw["phases"].items()},
         "roofline": dict(
             roofline(fw["output_flops_per_call"], fw["output_bytes_per_call"], fw["phases"]["output"]),
-            kernel="walk3_kernel<%d,%d,out,decay=%d,den=%d> (chunk outputs)" % (
-                64 if w.d <= 64 else 128, 64 if w.dv <= 64 else 128, int(w.decay < 1), int(w.normalize)),
+            kernel="walk3_kernel<%d,%d,out,decay=%d,den=%d> (chunk outputs%s)" % (
+                64 if w.d <= 64 else 128, 64 if w.dv <= 64 else 128, int(w.decay < 1), int(w.normalize),
+                " of segments 1 .. %d" % (fw["segments"] - 1) if fw["plan"]["lead"] else ""),
             traffic=load_traffic("output_" + w.name),
             avg_launch_ms=fw["phases"]["output"] * 1e3,
             algorithmic_bytes_per_launch=fw["output_bytes_per_call"],

@@ -12,8 +12,11 @@ namespace {
 struct Plan {
   int DK, DV, CP;  // padded head dims and chunk tile of the kernel instantiation
   int kc;          // tokens per chunk the walker steps by
-  int cps;         // chunks per segment
+  int cps;         // chunks per segment (segment 0: cps0; the last may be shorter)
+  int cps0;        // chunks of segment 0
   int nseg;        // segments per (b, h)
+  bool lead;       // lead plan: segment 0's output walk runs beside the summary walks and
+                   // leaves the prefix of segment 1 (bf16 forward without state export)
   long BH;
 };
 
@@ -21,6 +24,11 @@ struct Plan {
 constexpr long kComputeUnits = 256;
 constexpr int kMaxSegments = 64;
 constexpr long kMinChunksPerSegment = 4;
+// Lead plans: segment 0 holds about kLeadRatio times the chunks of the others, so that its
+// output walk (the slower walk per chunk: measured about 3.3 us against 2.3 us for a summary
+// chunk, one workgroup per CU, d = 64, dv = 128) ends with the summary walks it shares the
+// launch with.
+constexpr double kLeadRatio = 0.7;
 
 bool is_pow2_chunk(int c) { return c == 16 || c == 32 || c == 64 || c == 128; }
 
@@ -36,7 +44,8 @@ int check_shape(int B, int H, int n, int d, int dv, int chunk, int dtype) {
   return HLA2_OK;
 }
 
-Plan make_plan(int B, int H, int n, int d, int dv, int chunk, int dtype, int segments = 0, long groups_per_cu = 0) {
+Plan make_plan(int B, int H, int n, int d, int dv, int chunk, int dtype, int segments = 0, long groups_per_cu = 0,
+               bool lead = false) {
   Plan p;
   p.BH = (long)B * H;
   long gpc;  // workgroups of the output walker per CU
@@ -54,17 +63,43 @@ Plan make_plan(int B, int H, int n, int d, int dv, int chunk, int dtype, int seg
     gpc = hla2::walk_groups_per_cu(4, p.DK, p.DV, p.CP, true);
   }
   if (groups_per_cu > 0) gpc = groups_per_cu;
+  p.lead = lead && dtype == HLA2_BF16;
   const long nc = ((long)n + p.kc - 1) / p.kc;
   const long target = kComputeUnits * gpc;
-  long r = segments > 0 ? segments : (target + p.BH - 1) / p.BH;
+  long r;
+  if (segments > 0) {
+    r = segments;
+  } else if (p.lead) {
+    // the output walk of segments 1 .. r-1 (and the lead launch) put one workgroup on each
+    // CU: without a summary of segment 0, fewer and longer segments save more summary work
+    // than a second workgroup per CU gains (measured on the 8 x 16 x 8192, d = 64 workload:
+    // 3 segments 276 us, 5 segments 292 us)
+    r = p.BH >= kComputeUnits ? 1 : kComputeUnits / p.BH + 1;
+  } else {
+    r = (target + p.BH - 1) / p.BH;
+  }
   // automatic plans keep at least kMinChunksPerSegment chunks per segment: shorter
   // segments add scan steps faster than they shorten the walks
   if (segments == 0 && r > nc / kMinChunksPerSegment) r = nc / kMinChunksPerSegment;
   if (r > nc) r = nc;
   if (r > kMaxSegments) r = kMaxSegments;
   if (r < 1) r = 1;
-  p.cps = (int)((nc + r - 1) / r);
-  p.nseg = (int)((nc + p.cps - 1) / p.cps);
+  if (p.lead && segments == 0 && r > 1) {
+    // segment 0 about kLeadRatio times the others (at least that, when the chunks do not
+    // divide evenly: the last segment is then the shorter one)
+    const long cps = (long)ceil((double)nc / ((double)(r - 1) + kLeadRatio));
+    long cps0 = nc - (r - 1) * cps;
+    const long lo = (long)ceil(kLeadRatio * (double)cps);
+    if (cps0 < lo) cps0 = lo;
+    if (cps0 > cps) cps0 = cps;
+    p.cps = (int)cps;
+    p.cps0 = (int)cps0;
+    p.nseg = 1 + (int)((nc - cps0 + cps - 1) / cps);
+  } else {
+    p.cps = p.cps0 = (int)((nc + r - 1) / r);
+    p.nseg = (int)((nc + p.cps - 1) / p.cps);
+  }
+  if (p.nseg < 2) p.lead = false;
   return p;
 }
 
@@ -153,7 +188,7 @@ long hla2_state_floats(int d, int dv) {
 static size_t forward_workspace(int B, int H, int n, int d, int dv, int chunk, int segments, bool state) {
   // the plan does not depend on dtype beyond padding; size for the larger padding
   if (segments < 0 || check_shape(B, H, n, d, dv, chunk, HLA2_BF16) != HLA2_OK) return 0;
-  Plan pb = make_plan(B, H, n, d, dv, chunk, HLA2_BF16, segments);
+  Plan pb = make_plan(B, H, n, d, dv, chunk, HLA2_BF16, segments, 0, !state);
   size_t wb = workspace_bytes(pb, state);
   if (d <= 64 && dv <= 64) {
     Plan pf = make_plan(B, H, n, d, dv, chunk, HLA2_F32, segments);
@@ -179,7 +214,19 @@ int hla2_forward_ex_segments(int B, int H, int n, int d, int dv, int chunk, int 
   if (segments < 0) return HLA2_ERR_INVALID;
   int rc = check_shape(B, H, n, d, dv, chunk, HLA2_BF16);
   if (rc != HLA2_OK) return rc;
-  return make_plan(B, H, n, d, dv, chunk, HLA2_BF16, segments).nseg;
+  return make_plan(B, H, n, d, dv, chunk, HLA2_BF16, segments, 0, true).nseg;
+}
+
+int hla2_forward_ex_plan(int B, int H, int n, int d, int dv, int chunk, int segments, int *nseg, int *lead_chunks,
+                         int *seg_chunks) {
+  if (segments < 0 || !nseg || !lead_chunks || !seg_chunks) return HLA2_ERR_INVALID;
+  int rc = check_shape(B, H, n, d, dv, chunk, HLA2_BF16);
+  if (rc != HLA2_OK) return rc;
+  const Plan p = make_plan(B, H, n, d, dv, chunk, HLA2_BF16, segments, 0, true);
+  *nseg = p.nseg;
+  *lead_chunks = p.cps0;
+  *seg_chunks = p.cps;
+  return p.lead ? 1 : 0;
 }
 
 int hla2_forward_segments(int B, int H, int n, int d, int dv, int chunk) {
@@ -504,10 +551,14 @@ int run_forward(const void *q, const void *k, const void *v, void *out, int B, i
   if (den_out && !aligned(den_out, 4)) return HLA2_ERR_INVALID;
   if (state_out && !aligned(state_out, 4)) return HLA2_ERR_INVALID;
   const bool state = state_out != nullptr;
-  const Plan p = make_plan(B, H, n, d, dv, chunk, (int)dtype, segments);
+  const Plan p = make_plan(B, H, n, d, dv, chunk, (int)dtype, segments, 0, !state);
   const size_t need = workspace_bytes(p, state);
-  if (need > 0) {
-    if (!workspace || workspace_bytes_given < need || !aligned(workspace, 256)) return HLA2_ERR_WORKSPACE;
+  // callers are held to the size the workspace query reports (the larger of the bf16 and
+  // fp32 plans), whichever dtype this call uses
+  const size_t need_doc = forward_workspace(B, H, n, d, dv, chunk, segments, state);
+  if (need > 0 || need_doc > 0) {
+    if (!workspace || workspace_bytes_given < need_doc || workspace_bytes_given < need || !aligned(workspace, 256))
+      return HLA2_ERR_WORKSPACE;
   }
 
   hla2::WalkArgs a;
@@ -521,7 +572,9 @@ int run_forward(const void *q, const void *k, const void *v, void *out, int B, i
   a.dv = dv;
   a.chunk = p.kc;
   a.cps = p.cps;
+  a.cps0 = p.cps0;
   a.nseg = p.nseg;
+  a.nbh = (int)p.BH;
   a.log2g = decay < 1.0f ? log2f(decay) : 0.0f;
   a.decay_on = decay < 1.0f ? 1 : 0;
   a.normalize = normalize;
@@ -534,29 +587,39 @@ int run_forward(const void *q, const void *k, const void *v, void *out, int B, i
   }
   a.sums = sums;
   a.prefix = prefix;
+  a.prefix_out = prefix;
   const int dt = dtype == HLA2_F32 ? 0 : 1;
   const int ns = nsum(p, state);
 
+  // Plain plan: summary walk of segments 0 .. ns-1, scan from the zero state, output walk of
+  // every segment.  Lead plan: segment 0's output walk (leaving the prefix of segment 1) in
+  // one launch with the summary walks of segments 1 .. ns-1, the scan from that prefix, then
+  // the output walk of segments 1 .. nseg-1.
   auto mark = [&](int i) { return (events && events[i]) ? hipEventRecord(events[i], stream) : hipSuccess; };
   hipError_t e = mark(0);
   if (e != hipSuccess) return HLA2_ERR_LAUNCH;
-  if (ns > 0) {
+  if (p.lead) {
+    e = hla2::launch_walk_lead(p.DK, p.DV, dim3((unsigned)(p.BH * ns)), a, stream);
+    if (e != hipSuccess) return HLA2_ERR_LAUNCH;
+  } else if (ns > 0) {
     e = hla2::launch_walk(dt, p.DK, p.DV, p.CP, false, dim3((unsigned)(p.BH * ns)), a, stream);
     if (e != hipSuccess) return HLA2_ERR_LAUNCH;
   }
   if (mark(1) != hipSuccess) return HLA2_ERR_LAUNCH;
-  if (p.nseg > 1) {
+  if (p.nseg > (p.lead ? 2 : 1)) {
     hla2::ScanArgs s;
     s.sums = sums;
     s.nsum = ns;
     s.prefix = prefix;
     s.nseg = p.nseg;
     s.gamma_seg = decay < 1.0f ? (float)pow((double)decay, (double)p.cps * p.kc) : 1.0f;
+    s.first = p.lead ? 1 : 0;
     e = hla2::launch_scan(dt, p.DK, p.DV, (int)p.BH, s, stream);
     if (e != hipSuccess) return HLA2_ERR_LAUNCH;
   }
   if (mark(2) != hipSuccess) return HLA2_ERR_LAUNCH;
-  e = hla2::launch_walk(dt, p.DK, p.DV, p.CP, true, dim3((unsigned)(p.BH * p.nseg)), a, stream);
+  a.seg_lo = p.lead ? 1 : 0;
+  e = hla2::launch_walk(dt, p.DK, p.DV, p.CP, true, dim3((unsigned)(p.BH * (p.nseg - a.seg_lo))), a, stream);
   if (e != hipSuccess) return HLA2_ERR_LAUNCH;
   if (mark(3) != hipSuccess) return HLA2_ERR_LAUNCH;
   if (state) {

@@ -19,9 +19,21 @@ struct WalkArgs {
   int need_den;           // normalize || den_out: carry u (and m)
   int sum_all;            // summary mode: summarise every segment, the last one over its full
                           // chunks only (for the final state); else segments 0 .. nseg-2
+  int cps0 = 0;           // chunks of segment 0 (0: cps, like every other segment)
+  int seg_lo = 0;         // the launch walks segments seg_lo .. (nseg or nsum) - 1 of every head
+  int nbh = 0;            // heads B*H (lead launch: its first nbh workgroups walk segment 0)
+  float *prefix_out = nullptr;  // lead launch: the prefix blocks (the buffer `prefix` names), where
+                                // segment 0's walk writes the prefix of segment 1
 };
 // summary blocks per (b, h) in the workspace
 __host__ __device__ inline int walk_nsum(const WalkArgs &a) { return a.sum_all ? a.nseg : a.nseg - 1; }
+// Segment geometry in chunks: segment 0 holds cps0 chunks, every later one cps (the
+// last may be shorter).
+__host__ __device__ inline int walk_cps0(const WalkArgs &a) { return a.cps0 > 0 ? a.cps0 : a.cps; }
+__host__ __device__ inline int walk_seg_chunk0(const WalkArgs &a, int s) {
+  return s == 0 ? 0 : walk_cps0(a) + (s - 1) * a.cps;
+}
+__host__ __device__ inline int walk_seg_chunks(const WalkArgs &a, int s) { return s == 0 ? walk_cps0(a) : a.cps; }
 
 // Arguments of the segment-level exclusive scan.
 struct ScanArgs {
@@ -29,7 +41,9 @@ struct ScanArgs {
   int nsum;
   float *prefix;      // [BH, nseg] prefix blocks
   int nseg;
-  float gamma_seg;    // decay^(tokens per full segment)
+  float gamma_seg;    // decay^(tokens per full segment): segments first .. nseg-2 are full
+  int first = 0;      // 0: start from the zero state; 1: the prefix of segment 1 is given
+                      // (written by segment 0's output walk) and the fold starts there
 };
 
 // Per-(b,h,segment) block sizes in floats, for padded dims DK, DV.
@@ -88,6 +102,11 @@ hipError_t launch_walk_f32(int DK, int DV, int CP, bool output_mode, dim3 grid, 
                            hipStream_t s);
 hipError_t launch_walk3_dk64(int DV, bool output_mode, bool decay, bool den, dim3 grid, const WalkArgs &a,
                              hipStream_t s);
+// The lead launch of the bf16 forward: workgroups 0 .. nbh-1 walk segment 0 in output mode and
+// write the state after it as the prefix of segment 1; the rest summarise segments 1 .. nsum-1.
+hipError_t launch_walk_lead(int DK, int DV, dim3 grid, const WalkArgs &a, hipStream_t s);
+hipError_t launch_walk3_lead_dk64(int DV, bool decay, bool den, dim3 grid, const WalkArgs &a, hipStream_t s);
+hipError_t launch_walk3_lead_dk128(int DV, bool decay, bool den, dim3 grid, const WalkArgs &a, hipStream_t s);
 hipError_t launch_walk3_dk128(int DV, bool output_mode, bool decay, bool den, dim3 grid, const WalkArgs &a,
                               hipStream_t s);
 hipError_t launch_scan(int dtype, int DK, int DV, int BH, const ScanArgs &a, hipStream_t s);

@@ -177,8 +177,19 @@ __global__ void __launch_bounds__(64 * (DK / 16)) scan_bf16_kernel(ScanArgs a) {
   };
 
   const int steps = a.nseg - 1;
-  load_c(0);
-  for (int r = 0; r < steps; ++r) {
+  const int r0 = a.first;  // with a given prefix of segment 1 the fold starts from it
+  if (r0 > 0) {
+    const float *pb = a.prefix + ((long)bh * a.nseg + r0) * PB;
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) s0[jj] = *(const f32x4 *)(pb + (16 * w + n) * DK + 16 * jj + 4 * g);
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[ct][q] = pb[DK * DK + (16 * w + 4 * g + q) * DV + c0 + 16 * ct + n];
+    if (has_u && n == 0) acc[CT] = *(const f32x4 *)(pb + DK * DK + DK * DV + 16 * w + 4 * g);
+  }
+  load_c(r0);
+  for (int r = r0; r < steps; ++r) {
     load_su(r);
     bf16 *cb = Cb[r & 1];
 #pragma unroll
@@ -190,7 +201,7 @@ __global__ void __launch_bounds__(64 * (DK / 16)) scan_bf16_kernel(ScanArgs a) {
     __syncthreads();  // C_r visible; the other buffer is free again
     if (r + 1 < steps) load_c(r + 1);
 
-    store(r);
+    if (r > r0 || r0 == 0) store(r);  // a given prefix is already in place
     bf16x8 af[DK / 32];
 #pragma unroll
     for (int s = 0; s < DK / 32; ++s) af[s] = frag_from_acc(s0[2 * s], s0[2 * s + 1]);
@@ -209,6 +220,8 @@ __global__ void __launch_bounds__(64 * (DK / 16)) scan_bf16_kernel(ScanArgs a) {
 
 template <int DK, int DV>
 static hipError_t launch_scan_t(int BH, bool bf, const ScanArgs &a, hipStream_t s) {
+  if (a.first != 0 && !(bf && DK >= 64)) return hipErrorInvalidValue;  // only the bf16 fold takes a given prefix
+  if (a.first < 0 || a.first > 1 || (a.first == 1 && a.nseg < 3)) return hipErrorInvalidValue;
   if constexpr (DK >= 64) {
     if (bf) {
       hipLaunchKernelGGL((scan_bf16_kernel<DK, DV>), dim3(BH, 2), dim3(64 * (DK / 16)), 0, s, a);
@@ -226,6 +239,14 @@ hipError_t launch_scan(int dtype, int DK, int DV, int BH, const ScanArgs &a, hip
   if (DK == 64 && DV == 128) return launch_scan_t<64, 128>(BH, bf, a, s);
   if (DK == 128 && DV == 64) return launch_scan_t<128, 64>(BH, bf, a, s);
   if (DK == 128 && DV == 128) return launch_scan_t<128, 128>(BH, bf, a, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_walk_lead(int DK, int DV, dim3 grid, const WalkArgs &a, hipStream_t s) {
+  const bool dec = a.decay_on != 0, den = a.need_den != 0;
+  if (a.nseg < 2 || a.sum_all || a.nbh < 1 || !a.prefix_out) return hipErrorInvalidValue;
+  if (DK == 64) return launch_walk3_lead_dk64(DV, dec, den, grid, a, s);
+  if (DK == 128) return launch_walk3_lead_dk128(DV, dec, den, grid, a, s);
   return hipErrorInvalidValue;
 }
 

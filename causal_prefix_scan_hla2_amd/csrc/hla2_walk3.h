@@ -114,20 +114,37 @@ struct W3Cfg {
   static_assert(ELEMS * 2 + (2 * CP + 1 + CP + 2 * DK) * 4 <= LDS_BYTES, "LDS accounting");
 };
 
-template <int DK, int DV, bool OUT, bool DEC, bool DEN>
-__global__ void __launch_bounds__(256, (walk3_waves_per_eu(DK, DV, OUT)))
-walk3_kernel(WalkArgs a) {
+// LDS of one walker workgroup, carved from one byte array: the bf16 rows, u0 (double-
+// buffered), the decay table and the chunk's den values.
+template <int DK, int DV, bool OUT>
+struct W3Lds {
   using Cfg = W3Cfg<DK, DV, OUT>;
+  static constexpr int U0N = 2 * DK;  // u0s[2][DK]
+  static constexpr int U0_OFF = Cfg::ELEMS * 2;
+  static constexpr int PW_OFF = U0_OFF + U0N * 4;
+  static constexpr int DENS_OFF = PW_OFF + (2 * Cfg::CP + 1) * 4;
+  static constexpr int BYTES = DENS_OFF + Cfg::CP * 4;
+  static_assert(U0_OFF % 16 == 0, "u0 rows are read as 16-byte vectors");
+  static_assert(BYTES <= Cfg::LDS_BYTES, "LDS accounting");
+};
+
+// One workgroup's walk of segment `seg` of head `bh`.  With LEAD (output mode, segment 0 of
+// a plan with more than one segment) the state after the segment is written, in fp32, as
+// the prefix block of segment 1, so that no summary of segment 0 is needed.
+template <int DK, int DV, bool OUT, bool DEC, bool DEN, bool LEAD>
+__device__ __forceinline__ void walk3_body(const WalkArgs &a, const int bh, const int seg, unsigned char *lds) {
+  using Cfg = W3Cfg<DK, DV, OUT>;
+  using L = W3Lds<DK, DV, OUT>;
   constexpr int CP = Cfg::CP, NB = Cfg::NB, NT = Cfg::NT, RT = Cfg::RT, KD = Cfg::KD, KC = Cfg::KC;
   constexpr int SCT = Cfg::SCT, UCT = Cfg::UCT, URT = Cfg::URT;
   constexpr bool PAIR = UCT == 2 && DK == 64;  // interleaved value-column tiles (see vcol)
   constexpr int LDK = Cfg::LDK, LDQ = Cfg::LDQ, LDT = Cfg::LDT, LDS0 = Cfg::LDS0, LDZ = Cfg::LDZ;
   constexpr int LDV = Cfg::LDV, LDW = Cfg::LDW, NVK = Cfg::NVK, NVV = Cfg::NVV;
 
-  __shared__ __attribute__((aligned(16))) bf16 smem[Cfg::ELEMS];
-  __shared__ float pw[2 * CP + 1];            // decay^x, x = 0 .. 2 CP
-  __shared__ float dens[OUT ? CP : 1];        // den of the chunk's rows
-  __shared__ __attribute__((aligned(16))) float u0s[DEN ? 2 : 1][DEN ? DK : 4];  // u0, double-buffered
+  bf16 *const smem = (bf16 *)lds;
+  float *const pw = (float *)(lds + L::PW_OFF);      // decay^x, x = 0 .. 2 CP
+  float *const dens = (float *)(lds + L::DENS_OFF);  // den of the chunk's rows
+  float(*const u0s)[DK] = (float(*)[DK])(lds + L::U0_OFF);  // u0, double-buffered
   bf16 *const Qs = smem + Cfg::Q_OFF;
   bf16 *const Ks = smem + Cfg::K_OFF;
   bf16 *const Vs = smem + Cfg::V_OFF;
@@ -147,11 +164,9 @@ walk3_kernel(WalkArgs a) {
     if constexpr (PAIR) return 32 * w + 8 * (nn >> 2) + 4 * j + (nn & 3);
     return 16 * (w * UCT + j) + nn;
   };
-  const int nseg_here = OUT ? a.nseg : walk_nsum(a);
-  const int bh = blockIdx.x / nseg_here, seg = blockIdx.x % nseg_here;
   const int d = a.d, dv = a.dv;
-  const int tok0 = seg * a.cps * CP;  // first token of the segment
-  const int tokE = min(a.n, tok0 + a.cps * CP);
+  const int tok0 = walk_seg_chunk0(a, seg) * CP;  // first token of the segment
+  const int tokE = min(a.n, tok0 + walk_seg_chunks(a, seg) * CP);
   // a summary of the last segment (final state) stops at its last full chunk
   const int nch = (!OUT && seg == a.nseg - 1) ? (tokE - tok0) / CP : (tokE - tok0 + CP - 1) / CP;
 
@@ -271,15 +286,13 @@ walk3_kernel(WalkArgs a) {
   // Aᵀ / Wᵀ tile I of the wave's block: element r is (i = 16 I + 4 g + r, tau = tau_w).
   // Off-diagonal tiles (I < w) use g^{16(w-I-1)} * g^{16 + n - 4g - r}; the diagonal tile
   // masks i > tau.  All exponents are >= 0.
-  float fa_off[4], fa_dg[4], fw_off[4], fw_dg[4], kfh[4];
+  float fa_off[4], fa_dg[4], kfh[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int e = n - 4 * g - r;
     fa_off[r] = DEC ? pw[16 + e] : 1.f;
-    fw_off[r] = DEC ? pw[2 * (16 + e)] : 1.f;
     const int ep = e >= 0 ? e : 0;
     fa_dg[r] = e >= 0 ? (DEC ? pw[ep] : 1.f) : 0.f;
-    fw_dg[r] = e >= 0 ? (DEC ? pw[2 * ep] : 1.f) : 0.f;
     kfh[r] = DEC ? pw[15 - 4 * g - r] : 1.f;  // token weights g^{63-t}: see kweight()
   }
   const float zf = DEC ? pw[tau_w + 1] : 1.f;            // g^{tau+1}
@@ -468,7 +481,13 @@ walk3_kernel(WalkArgs a) {
         for (int s = 0; s < KD; ++s) wt = mma(ld_rows_c(Zs, LDZ, 16 * J, 32 * s, lane), qw[s], wt);
         const float sc = DEC ? pw[32 * max(w - J - 1, 0)] : 1.f;  // uniform
 #pragma unroll
-        for (int r = 0; r < 4; ++r) wt[r] *= J < w ? sc * fw_off[r] : (J == w ? fw_dg[r] : 0.f);
+        for (int r = 0; r < 4; ++r) {
+          // the W factors are the squares of the A factors; squared here rather than kept
+          // in registers across the chunk loop
+          float fo = fa_off[r], fd = fa_dg[r];
+          asm volatile("" : "+v"(fo), "+v"(fd));
+          wt[r] *= J < w ? sc * (fo * fo) : (J == w ? fd * fd : 0.f);
+        }
         if constexpr (DEN) rs += (wt[0] + wt[1]) + (wt[2] + wt[3]);
         st4(Ws + tau_w * LDW + wpos(16 * J + 4 * g), wt);
       }
@@ -596,6 +615,55 @@ walk3_kernel(WalkArgs a) {
       }
     }
   }
+
+  // ---------------- lead segment: its final state is the prefix S0 | U0 | u0 of segment 1 ----------------
+  // (the layout the prefix is read in above; u0 is zero when den is not carried)
+  if constexpr (OUT && LEAD) {
+    float *pb = a.prefix_out + ((long)bh * a.nseg + seg + 1) * prefix_block_floats(DK, DV);
+    float *pS = pb, *pU = pb + DK * DK, *pu = pU + DK * DV;
+#pragma unroll
+    for (int i = 0; i < RT; ++i) {
+#pragma unroll
+      for (int j = 0; j < SCT; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pS[(16 * i + 4 * g + r) * DK + 16 * (w * SCT + j) + n] = Sacc[i][j][r];
+#pragma unroll
+      for (int j = 0; j < UCT; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pU[(16 * i + 4 * g + r) * DV + vcol(j, n)] = Uacc[i][j][r];
+    }
+    if (n == 0) {
+#pragma unroll
+      for (int ur = 0; ur < URT; ++ur) *(f32x4 *)(pu + 16 * (w * URT + ur) + 4 * g) = DEN ? uacc[ur] : zero4();
+    }
+  }
+}
+
+// Walks segments seg_lo .. (nseg or nsum) - 1 of every head, one workgroup each.
+template <int DK, int DV, bool OUT, bool DEC, bool DEN>
+__global__ void __launch_bounds__(256, (walk3_waves_per_eu(DK, DV, OUT)))
+walk3_kernel(WalkArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[W3Lds<DK, DV, OUT>::BYTES];
+  const int nr = (OUT ? a.nseg : walk_nsum(a)) - a.seg_lo;  // segments of a head in this launch
+  walk3_body<DK, DV, OUT, DEC, DEN, false>(a, blockIdx.x / nr, a.seg_lo + blockIdx.x % nr, lds);
+}
+
+// The lead launch: workgroups 0 .. nbh-1 walk segment 0 of their head in output mode and
+// leave the prefix of segment 1; the rest summarise segments 1 .. nsum-1 of every head.
+// Both roles share one LDS allocation (the larger, output mode's), so the launch holds as
+// many workgroups per CU as the output walk.
+template <int DK, int DV, bool DEC, bool DEN>
+__global__ void __launch_bounds__(256, (walk3_waves_per_eu(DK, DV, true)))
+walk3_lead_kernel(WalkArgs a) {
+  constexpr int BO = W3Lds<DK, DV, true>::BYTES, BS = W3Lds<DK, DV, false>::BYTES;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[BO > BS ? BO : BS];
+  const int b = blockIdx.x;
+  if (b < a.nbh) {
+    walk3_body<DK, DV, true, DEC, DEN, true>(a, b, 0, lds);
+  } else {
+    const int i = b - a.nbh, nr = walk_nsum(a) - 1;
+    walk3_body<DK, DV, false, DEC, DEN, false>(a, i / nr, 1 + i % nr, lds);
+  }
 }
 
 template <int DK, int DV>
@@ -614,6 +682,21 @@ hipError_t launch_walk3_t(bool out, bool dec, bool den, dim3 grid, const WalkArg
   HLA2_W3(false, false, true)
   HLA2_W3(false, false, false)
 #undef HLA2_W3
+  return hipErrorInvalidValue;
+}
+
+template <int DK, int DV>
+hipError_t launch_walk3_lead_t(bool dec, bool den, dim3 grid, const WalkArgs &a, hipStream_t s) {
+#define HLA2_W3L(D, N)                                                                       \
+  if (dec == D && den == N) {                                                                \
+    hipLaunchKernelGGL((walk3_lead_kernel<DK, DV, D, N>), grid, dim3(256), 0, s, a);        \
+    return hipGetLastError();                                                                \
+  }
+  HLA2_W3L(true, true)
+  HLA2_W3L(true, false)
+  HLA2_W3L(false, true)
+  HLA2_W3L(false, false)
+#undef HLA2_W3L
   return hipErrorInvalidValue;
 }
 

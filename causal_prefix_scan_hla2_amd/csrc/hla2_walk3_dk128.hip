@@ -10,4 +10,10 @@ hipError_t launch_walk3_dk128(int DV, bool output_mode, bool decay, bool den, di
   return hipErrorInvalidValue;
 }
 
+hipError_t launch_walk3_lead_dk128(int DV, bool decay, bool den, dim3 grid, const WalkArgs &a, hipStream_t s) {
+  if (DV == 64) return launch_walk3_lead_t<128, 64>(decay, den, grid, a, s);
+  if (DV == 128) return launch_walk3_lead_t<128, 128>(decay, den, grid, a, s);
+  return hipErrorInvalidValue;
+}
+
 }  // namespace hla2

@@ -10,4 +10,10 @@ hipError_t launch_walk3_dk64(int DV, bool output_mode, bool decay, bool den, dim
   return hipErrorInvalidValue;
 }
 
+hipError_t launch_walk3_lead_dk64(int DV, bool decay, bool den, dim3 grid, const WalkArgs &a, hipStream_t s) {
+  if (DV == 64) return launch_walk3_lead_t<64, 64>(decay, den, grid, a, s);
+  if (DV == 128) return launch_walk3_lead_t<64, 128>(decay, den, grid, a, s);
+  return hipErrorInvalidValue;
+}
+
 }  // namespace hla2

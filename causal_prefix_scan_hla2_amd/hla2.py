@@ -18,7 +18,8 @@ HLA2_OK, HLA2_ERR_INVALID, HLA2_ERR_UNSUPPORTED, HLA2_ERR_WORKSPACE, HLA2_ERR_LA
 
 # every symbol include/hla2.h declares
 EXPORTS = ("hla2_strerror", "hla2_abi_version", "hla2_forward_workspace_bytes", "hla2_forward_segments",
-           "hla2_forward", "hla2_forward_ex_workspace_bytes", "hla2_forward_ex_segments", "hla2_forward_ex",
+           "hla2_forward", "hla2_forward_ex_workspace_bytes", "hla2_forward_ex_segments", "hla2_forward_ex_plan",
+           "hla2_forward_ex",
            "hla2_forward_timed", "hla2_decode_step", "hla2_state_floats", "hla2_forward_state_workspace_bytes",
            "hla2_forward_state", "hla2_backward_workspace_bytes", "hla2_backward",
            "hla2_ahla_forward_workspace_bytes", "hla2_ahla_forward", "hla2_ho3_forward_workspace_bytes",
@@ -57,6 +58,9 @@ def lib():
             L.hla2_forward_ex_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
             L.hla2_forward_ex_segments.restype = i
             L.hla2_forward_ex_segments.argtypes = [i, i, i, i, i, i, i]
+            ip = ctypes.POINTER(ctypes.c_int)
+            L.hla2_forward_ex_plan.restype = i
+            L.hla2_forward_ex_plan.argtypes = [i, i, i, i, i, i, i, ip, ip, ip]
             L.hla2_forward_ex.restype = i
             L.hla2_forward_ex.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, vp, sz, i, vp]
             L.hla2_forward_timed.restype = i
@@ -117,6 +121,17 @@ def hla2_forward_workspace_bytes(B, H, n, d, dv, chunk, segments=0) -> int:
 
 def hla2_forward_segments(B, H, n, d, dv, chunk, segments=0) -> int:
     return int(lib().hla2_forward_ex_segments(B, H, n, d, dv, chunk, segments))
+
+
+def hla2_forward_plan(B, H, n, d, dv, chunk, segments=0):
+    """The bf16 forward's segment plan: (nseg, chunks of segment 0, chunks of each later
+    segment, lead) where lead says segment 0's outputs are walked beside the summary walks."""
+    nseg, c0, cs = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    rc = lib().hla2_forward_ex_plan(B, H, n, d, dv, chunk, segments, ctypes.byref(nseg), ctypes.byref(c0),
+                                    ctypes.byref(cs))
+    if rc < 0:
+        raise HLA2Error(rc, "hla2_forward_ex_plan")
+    return nseg.value, c0.value, cs.value, bool(rc)
 
 
 def hla2_state_floats(d, dv) -> int:

@@ -135,6 +135,21 @@ int hla2_decode_step(float *state, const void *q, const void *k, const void *v, 
  */
 size_t hla2_forward_ex_workspace_bytes(int B, int H, int n, int d, int dv, int chunk, int segments);
 int hla2_forward_ex_segments(int B, int H, int n, int d, int dv, int chunk, int segments);
+
+/*
+ * The segment plan of a bf16 hla2_forward_ex call with these arguments
+ * [SUM §4: the sequence is cut into segments whose summaries are scanned].
+ * Writes the number of segments per (b, h), the 64-token chunks of segment 0
+ * and the chunks of every later segment (the last may hold fewer).  Returns 1
+ * for a lead plan (segment 0 is walked for its outputs beside the summary
+ * walks of segments 1 .. nseg-2 and leaves the incoming state of segment 1;
+ * the scan starts there and the output walk covers segments 1 .. nseg-1),
+ * 0 for a plain plan (summaries of segments 0 .. nseg-2, scan, output walk of
+ * every segment), or a negative code (null pointer, segments < 0, unsupported
+ * shape).  Host only: no device call.
+ */
+int hla2_forward_ex_plan(int B, int H, int n, int d, int dv, int chunk, int segments, int *nseg,
+                         int *lead_chunks, int *seg_chunks);
 int hla2_forward_ex(const void *q, const void *k, const void *v, void *out,
                     int B, int H, int n, int d, int dv, float decay, int normalize, int chunk,
                     hla2_dtype_t dtype, float *den_out, void *workspace, size_t workspace_bytes,
@@ -145,12 +160,15 @@ int hla2_forward_ex(const void *q, const void *k, const void *v, void *out,
  * launches, so a caller can time each phase of the chunk-parallel pass
  * [SUM §4] on the stream the kernels run on.  `events` is NULL or an array of
  * four hipEvent_t (entries may be NULL; the caller creates and owns them):
- *   events[0] before the segment-summary kernel,
+ *   events[0] before the segment-summary kernel (with a lead plan, see
+ *             hla2_forward_ex_plan: the launch that also walks segment 0's
+ *             outputs),
  *   events[1] after it (before the segment scan),
  *   events[2] after the scan (before the chunk-output kernel),
  *   events[3] after the chunk-output kernel.
  * With one segment only the chunk-output kernel runs and events[0..2] are
- * recorded back to back.  Results are those of hla2_forward_ex.  A failed
+ * recorded back to back; with a two-segment lead plan no scan runs and
+ * events[1..2] are back to back.  Results are those of hla2_forward_ex.  A failed
  * hipEventRecord is reported as HLA2_ERR_LAUNCH.
  */
 int hla2_forward_timed(const void *q, const void *k, const void *v, void *out,

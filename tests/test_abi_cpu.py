@@ -115,10 +115,44 @@ def test_workspace_and_segment_plan(L):
         nc = -(-n // 64)
         assert 1 <= r <= min(max(nc // 4, 1), 64)
         assert b * h * r >= min(256, b * h * min(nc // 4, 64)) - b * h  # within one segment of the target
-    assert H.hla2_forward_segments(4, 8, 2048, 64, 64, 64) == 8
+    assert H.hla2_forward_segments(4, 8, 2048, 64, 64, 64) == 7
+    assert H.hla2_forward_segments(8, 16, 8192, 64, 128, 64) == 3
     # invalid shapes report 0 bytes / an error code
     assert H.hla2_forward_workspace_bytes(1, 1, 64, 24, 16, 16) == 0
     assert H.hla2_forward_segments(1, 1, 64, 24, 16, 16) == H.HLA2_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("shape,segments", [
+    ((8, 16, 8192, 64, 128, 64), 0), ((4, 8, 2048, 64, 64, 64), 0), ((1, 16, 65536, 128, 128, 128), 0),
+    ((2, 3, 300, 64, 128, 64), 0), ((1, 1, 4000, 64, 64, 64), 0), ((2, 2, 777, 64, 64, 64), 3),
+    ((1, 1, 100, 64, 64, 64), 2), ((512, 1, 8192, 64, 64, 64), 0), ((1, 1, 64, 64, 64, 64), 0),
+])
+def test_lead_plan_covers_every_chunk(L, shape, segments):
+    b, h, n, d, dv, c = shape
+    nseg, c0, cs, lead = H.hla2_forward_plan(*shape, segments=segments)
+    nc = -(-n // 64)
+    assert nseg == H.hla2_forward_segments(*shape, segments=segments)
+    assert 1 <= c0 <= cs
+    # segment 0, then nseg-1 segments of cs chunks, the last one non-empty and at most cs
+    assert c0 + (nseg - 1) * cs >= nc > c0 + (nseg - 2) * cs if nseg > 1 else c0 >= nc
+    assert lead == (nseg > 1)
+    if segments == 0 and nseg > 1:
+        # the output walk of segments 1 .. nseg-1 puts at most one workgroup on each of 256 CUs
+        assert b * h * (nseg - 1) <= 256
+        # segment 0 is the shorter one (it shares its launch with the summary walks)
+        assert c0 < cs or nc <= 8
+    if segments > 0:
+        assert c0 == cs  # explicit counts split evenly
+
+
+def test_plan_query_rejects(L):
+    x = ctypes.c_int()
+    assert L.hla2_forward_ex_plan(1, 1, 64, 64, 64, 64, 0, None, ctypes.byref(x), ctypes.byref(x)) == \
+        H.HLA2_ERR_INVALID
+    assert L.hla2_forward_ex_plan(1, 1, 64, 64, 64, 64, -1, ctypes.byref(x), ctypes.byref(x), ctypes.byref(x)) == \
+        H.HLA2_ERR_INVALID
+    assert L.hla2_forward_ex_plan(1, 1, 64, 24, 64, 64, 0, ctypes.byref(x), ctypes.byref(x), ctypes.byref(x)) == \
+        H.HLA2_ERR_UNSUPPORTED
 
 
 def dec(L, state=P, q=P, k=P, v=P, out=P, N=1, H_=1, d=64, dv=64, decay=1.0, norm=1, dtype=1):

@@ -84,16 +84,29 @@ def test_final_state_matches_oracle(B, H_, n, d, dv, dtype, decay, normalize, ch
     assert ok_out, msg
 
 
-def test_state_export_leaves_outputs_unchanged():
-    """The activations of hla2_forward_state are those of hla2_forward (same plan)."""
+@pytest.mark.parametrize("normalize", [False, True])
+def test_state_export_leaves_outputs_unchanged(normalize):
+    """The activations of hla2_forward_state are those of hla2_forward up to rounding.
+
+    The two calls may use different segment plans (hla2_forward's lead plan walks segment
+    0's outputs beside the summaries; the export summarises every segment), so their
+    roundings differ.  The quotient num/den amplifies rounding where den is near zero, so
+    with normalisation the comparison is made on num = out * den and on den."""
     q, k, v = draw(2, 2, 777, 64, 64, "bf16", seed=5)
     dev = torch.device("cuda:0")
-    out_s, _ = gpu_forward_state(q, k, v, 0.99, True, 64, 0)
-    out = torch.empty_like(out_s)
-    H.hla2_forward(q.to(dev), k.to(dev), v.to(dev), out, decay=0.99, normalize=True, chunk=64)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    out_s, den_s = torch.empty_like(vd), torch.empty(2, 2, 777, dtype=torch.float32, device=dev)
+    st = torch.empty(2, 2, H.hla2_state_floats(64, 64), dtype=torch.float32, device=dev)
+    H.hla2_forward_state(qd, kd, vd, out_s, st, decay=0.99, normalize=normalize, chunk=64, den_out=den_s)
+    out, den = torch.empty_like(vd), torch.empty_like(den_s)
+    H.hla2_forward(qd, kd, vd, out, decay=0.99, normalize=normalize, chunk=64, den_out=den)
     torch.cuda.synchronize()
-    r = rel_l2(out_s.double().cpu().numpy(), out.double().cpu().numpy())
-    assert r <= 1e-3, r
+    o_s, o = out_s.double().cpu().numpy(), out.double().cpu().numpy()
+    d_s, d_ = den_s.double().cpu().numpy(), den.double().cpu().numpy()
+    if normalize:
+        o_s, o = o_s * d_s[..., None], o * d_[..., None]
+    assert rel_l2(o_s, o) <= 1e-2, rel_l2(o_s, o)
+    assert rel_l2(d_s, d_) <= 1e-2, rel_l2(d_s, d_)
 
 
 @pytest.mark.parametrize("d,dv,dtype,decay,normalize,prefix", [
