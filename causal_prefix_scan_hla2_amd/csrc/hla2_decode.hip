@@ -14,7 +14,10 @@
 // One workgroup (256 threads) owns one (sequence, head) block; each thread owns
 // 4 consecutive columns of a strip of rows, so every row is read and written
 // with coalesced 16-byte accesses.  The state is HBM-resident and touched once
-// per step (read + write), which is the whole cost of the step.
+// per step (read + write), which is the whole cost of the step.  Its loads and
+// stores are non-temporal: no block is touched again within a step, so keeping
+// it in the caches only evicts other blocks' lines (measured on the 256 x 32
+// head, d = dv = 64 workload: 154 -> 142 us per step).
 #include "hla2_internal.h"
 #include "hla2_mfma.h"
 
@@ -47,13 +50,13 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
     const int r = sr0 + i * RS;
-    Sr[i] = r < D ? *(const f32x4 *)(S + r * D + 4 * sc) : zero4();
+    Sr[i] = r < D ? __builtin_nontemporal_load((const f32x4 *)(S + r * D + 4 * sc)) : zero4();
   }
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int r = vr0 + i * RV;
-    Cr[i] = r < D ? *(const f32x4 *)(C + r * DV + 4 * vc) : zero4();
-    Gr[i] = r < D ? *(const f32x4 *)(G + r * DV + 4 * vc) : zero4();
+    Cr[i] = r < D ? __builtin_nontemporal_load((const f32x4 *)(C + r * DV + 4 * vc)) : zero4();
+    Gr[i] = r < D ? __builtin_nontemporal_load((const f32x4 *)(G + r * DV + 4 * vc)) : zero4();
   }
   if (tid < D) {
     qs[tid] = to_f(((const T *)a.q)[bh * D + tid]);
@@ -77,7 +80,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
         pq[e] += qr * Sr[i][e];
         nw[e] = gam * Sr[i][e] + kr * ks[4 * sc + e];
       }
-      *(f32x4 *)(S + r * D + 4 * sc) = nw;
+      __builtin_nontemporal_store(nw, (f32x4 *)(S + r * D + 4 * sc));
     }
   }
 #pragma unroll
@@ -91,7 +94,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
         pg[e] += qr * Gr[i][e];
         Cr[i][e] = gam * Cr[i][e] + qr * vs[4 * vc + e];  // C_new kept for the readout
       }
-      *(f32x4 *)(C + r * DV + 4 * vc) = Cr[i];
+      __builtin_nontemporal_store(Cr[i], (f32x4 *)(C + r * DV + 4 * vc));
     }
   }
   if (sr0 < RS) {
@@ -159,7 +162,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
         nw[e] = g2 * Gr[i][e] + gam * kr * kc4[e];
         pc[e] += pr * Cr[i][e];
       }
-      *(f32x4 *)(G + r * DV + 4 * vc) = nw;
+      __builtin_nontemporal_store(nw, (f32x4 *)(G + r * DV + 4 * vc));
     }
   }
   // m, h updates and the denominator
