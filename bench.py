@@ -350,6 +350,8 @@ def main(argv=None):
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--skip-backward", action="store_true")
     ap.add_argument("--skip-variants", action="store_true", help="skip the AHLA and third-order legs")
+    ap.add_argument("--skip-workloads", action="store_true",
+                    help="skip the other forward workloads (normalised 2k, long 64k)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="finish with two 1 GiB device copies (reference for HBM byte counters)")
     args = ap.parse_args(argv)
@@ -402,6 +404,22 @@ def main(argv=None):
             mfma_frac=fw["output_flops_per_call"] / fw["phases"]["output"] / PEAK_BF16_MFMA,
         ),
     }
+    if not args.skip_workloads:
+        # the other forward workloads, timed like the step (reported beside it, not in `value`)
+        line["forward_workloads"] = {}
+        for name in ("norm_2k", "long_64k"):
+            ow = I.WORKLOADS[name]
+            if ow.name == w.name:
+                continue
+            of = bench_forward(ow, args.steps, args.warmup, torch, H, I)
+            line["forward_workloads"][name] = {
+                "B": ow.B, "H": ow.H, "n": ow.n, "d": ow.d, "dv": ow.dv, "chunk": ow.chunk, "decay": ow.decay,
+                "normalize": ow.normalize, "plan": of["plan"], "ms_per_step": of["seconds"] * 1e3,
+                "tokens_per_s": of["tokens_per_s"], "head_tokens_per_s": of["head_tokens_per_s"],
+                "tflops": of["tflops"], "mfma_frac": of["mfma_frac"],
+                "hbm_min_bytes_frac": of["min_bytes"] / of["seconds"] / PEAK_HBM,
+                "kernel_ms": {key: val * 1e3 for key, val in of["phases"].items()},
+            }
     if not args.skip_decode:
         dw = I.DECODE
         pre = dw.prefix if args.decode_prefill is None else args.decode_prefill

@@ -24,11 +24,11 @@ struct Plan {
 constexpr long kComputeUnits = 256;
 constexpr int kMaxSegments = 64;
 constexpr long kMinChunksPerSegment = 4;
-// Lead plans: segment 0 holds about kLeadRatio times the chunks of the others, so that its
-// output walk (the slower walk per chunk: measured about 3.3 us against 2.3 us for a summary
-// chunk, one workgroup per CU, d = 64, dv = 128) ends with the summary walks it shares the
-// launch with.
-constexpr double kLeadRatio = 0.7;
+// Lead plans: segment 0 holds about lead_ratio(DK) times the chunks of the others, so that
+// its output walk (the slower walk per chunk) ends with the summary walks it shares the launch
+// with.  Measured per chunk, one workgroup per CU: d = 64, dv = 128: output 3.3 us, summary
+// 2.3 us; d = dv = 128: output 5.4 us, summary 4.5 us.
+double lead_ratio(int DK) { return DK > 64 ? 0.83 : 0.7; }
 
 bool is_pow2_chunk(int c) { return c == 16 || c == 32 || c == 64 || c == 128; }
 
@@ -85,11 +85,12 @@ Plan make_plan(int B, int H, int n, int d, int dv, int chunk, int dtype, int seg
   if (r > kMaxSegments) r = kMaxSegments;
   if (r < 1) r = 1;
   if (p.lead && segments == 0 && r > 1) {
-    // segment 0 about kLeadRatio times the others (at least that, when the chunks do not
+    // segment 0 about rho times the others (at least that, when the chunks do not
     // divide evenly: the last segment is then the shorter one)
-    const long cps = (long)ceil((double)nc / ((double)(r - 1) + kLeadRatio));
+    const double rho = lead_ratio(p.DK);
+    const long cps = (long)ceil((double)nc / ((double)(r - 1) + rho));
     long cps0 = nc - (r - 1) * cps;
-    const long lo = (long)ceil(kLeadRatio * (double)cps);
+    const long lo = (long)ceil(rho * (double)cps);
     if (cps0 < lo) cps0 = lo;
     if (cps0 > cps) cps0 = cps;
     p.cps = (int)cps;

@@ -95,22 +95,22 @@ SMALL = [
 # leaves the incoming state of segment 1; the scan continues from it): decay, ratio, ragged
 # tails, both padded head sizes, value widths 64 and 128.
 LEAD = [
-    # B, H, n, d, dv, decay, normalize
-    (2, 2, 777, 64, 64, 0.99, True),
-    (1, 4, 2000, 64, 128, 0.95, False),
-    (2, 2, 1500, 48, 80, 0.97, True),
-    (1, 2, 2100, 128, 128, 0.99, True),
-    (1, 2, 1800, 128, 64, 1.0, False),
+    # B, H, n, d, dv, decay, normalize, oracle heads (None: all)
+    (2, 2, 777, 64, 64, 0.99, True, None),
+    (1, 4, 2000, 64, 128, 0.95, False, None),
+    (2, 2, 1500, 48, 80, 0.97, True, None),
+    (4, 16, 1900, 128, 128, 0.99, True, [(0, 0), (1, 7), (3, 15)]),
+    (4, 16, 1700, 128, 64, 1.0, False, [(0, 3), (2, 9), (3, 14)]),
 ]
 
 
-@pytest.mark.parametrize("case", LEAD, ids=lambda c: "-".join(str(x) for x in c))
+@pytest.mark.parametrize("case", LEAD, ids=lambda c: "-".join(str(x) for x in c[:7]))
 def test_lead_plan_cases(case):
-    B, H_, n, d, dv, decay, norm = case
+    B, H_, n, d, dv, decay, norm, heads = case
     nseg, c0, cs, lead = H.hla2_forward_plan(B, H_, n, d, dv, 64)
     assert lead and nseg >= 3 and c0 < cs, (nseg, c0, cs)
     q, k, v = draw(B, H_, n, d, dv, "bf16", seed=n + d + dv + 1)
-    check_case(q, k, v, decay, norm, 64, "bf16")
+    check_case(q, k, v, decay, norm, 64, "bf16", heads=heads)
 
 
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: "-".join(str(x) for x in c))
