@@ -29,22 +29,28 @@ struct AhlaCfg {
                        ELEMS = E_OFF + DK * LDV;
 };
 
-// Summary mode (OUT = false): segments 0 .. nseg-2 from the zero state, writing
-// P' | E' | M.  Output mode: every segment from its scanned prefix P' | E'.
-template <typename T, int DK, int DV, int DVP, int BC, bool OUT, bool NORM>
-__global__ void __launch_bounds__(BWD_THREADS) ahla_walk_kernel(AhlaArgs a) {
+// LDS bytes of one walker workgroup: the element rows, then the decay table and den.
+template <typename T, int DK, int DVP, int BC>
+constexpr int ahla_lds_bytes() {
+  return AhlaCfg<T, DK, DVP, BC>::ELEMS * (int)sizeof(T) + (2 * BC + 3) * 4 + BC * 4;
+}
+
+// Summary mode (OUT = false): a segment from the zero state, writing P' | E' | M.  Output
+// mode: a segment from its scanned prefix P' | E'.  With LEAD (output mode, segment 0) the
+// state after the segment is written as the prefix of segment 1.
+template <typename T, int DK, int DV, int DVP, int BC, bool OUT, bool NORM, bool LEAD>
+__device__ __forceinline__ void ahla_walk_body(const AhlaArgs &a, const int bh, const int seg, unsigned char *lds) {
   using Cfg = AhlaCfg<T, DK, DVP, BC>;
-  __shared__ __attribute__((aligned(16))) T smem[Cfg::ELEMS];
-  __shared__ float pw[2 * BC + 3];
-  __shared__ float dens[OUT ? BC : 1];
+  static_assert((Cfg::ELEMS * sizeof(T)) % 4 == 0, "decay table alignment");
+  T *const smem = (T *)lds;
+  float *const pw = (float *)(lds + Cfg::ELEMS * sizeof(T));
+  float *const dens = pw + (2 * BC + 3);
   T *const Qs = smem + Cfg::Q_OFF, *const Ks = smem + Cfg::K_OFF, *const Vs = smem + Cfg::V_OFF;
   T *const Ys = smem + Cfg::Y_OFF, *const Ads = smem + Cfg::AD_OFF, *const Ps = smem + Cfg::P_OFF;
   T *const Es = smem + Cfg::E_OFF;
   const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 4, nn = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nseg_here = OUT ? a.nseg : a.nseg - 1;
-  const int bh = blockIdx.x / nseg_here, seg = blockIdx.x % nseg_here;
-  const int tok0 = seg * a.cps * a.kc, tokE = min(a.n, tok0 + a.cps * a.kc);
+  const int tok0 = ahla_seg_chunk0(a, seg) * a.kc, tokE = min(a.n, tok0 + ahla_seg_chunks(a, seg) * a.kc);
   const int nch = (tokE - tok0 + BC - 1) / BC;
   const long hq = (long)bh * a.n * a.d, hv = (long)bh * a.n * a.dv;
   const T *qh = (const T *)a.q + hq, *kh = (const T *)a.k + hq, *vh = (const T *)a.v + hv;
@@ -160,6 +166,39 @@ __global__ void __launch_bounds__(BWD_THREADS) ahla_walk_kernel(AhlaArgs a) {
       if (ok) *(f32x4 *)(sb + 2 * DK * DVP + (i0 + nn) * DK + j0 + 4 * gq) = M[it];
     });
   }
+  if constexpr (OUT && LEAD) {
+    // the state after segment 0 is the prefix of segment 1 (the layout the prefix is read in)
+    float *pb = a.prefix + ((long)bh * a.nseg + seg + 1) * PB;
+    for_tiles<DK, DVP>(w, [&](int i0, int j0, bool ok, int it) {
+      const int o = (i0 + nn) * DVP + j0 + 4 * gq;
+      if (ok) {
+        *(f32x4 *)(pb + o) = P[it];
+        *(f32x4 *)(pb + DK * DVP + o) = E[it];
+      }
+    });
+  }
+}
+
+// Walks segments (OUT ? seg_lo .. nseg-1 : 0 .. nseg-2) of every head, one workgroup each.
+template <typename T, int DK, int DV, int DVP, int BC, bool OUT, bool NORM>
+__global__ void __launch_bounds__(BWD_THREADS) ahla_walk_kernel(AhlaArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[ahla_lds_bytes<T, DK, DVP, BC>()];
+  const int lo = OUT ? a.seg_lo : 0, nr = (OUT ? a.nseg : a.nseg - 1) - lo;
+  ahla_walk_body<T, DK, DV, DVP, BC, OUT, NORM, false>(a, blockIdx.x / nr, lo + blockIdx.x % nr, lds);
+}
+
+// The lead launch: workgroups 0 .. nbh-1 walk segment 0 of their head for its outputs and
+// leave the prefix of segment 1; the rest summarise segments 1 .. nseg-2 of every head.
+template <typename T, int DK, int DV, int DVP, int BC, bool NORM>
+__global__ void __launch_bounds__(BWD_THREADS) ahla_lead_kernel(AhlaArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[ahla_lds_bytes<T, DK, DVP, BC>()];
+  const int b = blockIdx.x;
+  if (b < a.nbh) {
+    ahla_walk_body<T, DK, DV, DVP, BC, true, NORM, true>(a, b, 0, lds);
+  } else {
+    const int i = b - a.nbh, nr = a.nseg - 2;
+    ahla_walk_body<T, DK, DV, DVP, BC, false, NORM, false>(a, i / nr, 1 + i % nr, lds);
+  }
 }
 
 // Exclusive scan over segments, per (b, h), fp32 on VALU:
@@ -175,17 +214,23 @@ __global__ void __launch_bounds__(256) ahla_scan_kernel(AhlaArgs a, float gseg) 
   __shared__ __attribute__((aligned(16))) float Pl[DK * DVP], Ml[16 * DK];
   const int tid = threadIdx.x, bh = blockIdx.x, sp = blockIdx.y, r0 = 16 * sp;
   float *pre = a.prefix + (long)bh * a.nseg * PB;
-  for (int e = tid; e < DK * DVP; e += 256) Pl[e] = 0.f;
+  const int rs = a.first;  // 1: the prefix of segment 1 is given (written by segment 0's walk)
+  const float *given = pre + (long)rs * PB;
+  for (int e = tid; e < DK * DVP; e += 256) Pl[e] = rs ? given[e] : 0.f;
   f32x4 E[NEQ];  // E'[r0 + f][c0 .. c0 + 3] for group q = tid + 256 i: f = q / (DVP/4), c0 = 4 (q % (DVP/4))
 #pragma unroll
-  for (int i = 0; i < NEQ; ++i) E[i] = zero4();
-  for (int r = 0; r < a.nseg; ++r) {
+  for (int i = 0; i < NEQ; ++i) {
+    const int q = tid + 256 * i;
+    const int f = q / (DVP / 4), c0 = 4 * (q % (DVP / 4));
+    E[i] = (rs && (EQ % 256 == 0 || q < EQ)) ? *(const f32x4 *)(given + DK * DVP + (r0 + f) * DVP + c0) : zero4();
+  }
+  for (int r = rs; r < a.nseg; ++r) {
     float *pr = pre + (long)r * PB;
     __syncthreads();  // Pl holds P'_r
 #pragma unroll
     for (int i = 0; i < NEQ; ++i) {
       const int q = tid + 256 * i;
-      if (EQ % 256 == 0 || q < EQ) {
+      if ((r > rs || rs == 0) && (EQ % 256 == 0 || q < EQ)) {  // a given prefix is in place
         const int f = q / (DVP / 4), c0 = 4 * (q % (DVP / 4));
         *(f32x4 *)(pr + (r0 + f) * DVP + c0) = *(const f32x4 *)(Pl + (r0 + f) * DVP + c0);
         *(f32x4 *)(pr + DK * DVP + (r0 + f) * DVP + c0) = E[i];
@@ -225,7 +270,12 @@ static hipError_t launch_ahla_t(int phase, int BH, const AhlaArgs &a, float gseg
       hipLaunchKernelGGL((ahla_scan_kernel<DK, DVP>), dim3(BH, DK / 16), dim3(256), 0, s, a, gseg);
       return hipGetLastError();
     case AHLA_OUTPUT:
-      hipLaunchKernelGGL((ahla_walk_kernel<T, DK, DV, DVP, BC, true, NORM>), dim3(BH * a.nseg), dim3(BWD_THREADS),
+      hipLaunchKernelGGL((ahla_walk_kernel<T, DK, DV, DVP, BC, true, NORM>), dim3(BH * (a.nseg - a.seg_lo)),
+                         dim3(BWD_THREADS), 0, s, a);
+      return hipGetLastError();
+    case AHLA_LEAD:
+      if (a.nseg < 2 || a.nbh != BH) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((ahla_lead_kernel<T, DK, DV, DVP, BC, NORM>), dim3(BH * (a.nseg - 1)), dim3(BWD_THREADS),
                          0, s, a);
       return hipGetLastError();
   }

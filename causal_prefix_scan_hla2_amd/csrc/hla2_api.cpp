@@ -45,7 +45,7 @@ int check_shape(int B, int H, int n, int d, int dv, int chunk, int dtype) {
 }
 
 Plan make_plan(int B, int H, int n, int d, int dv, int chunk, int dtype, int segments = 0, long groups_per_cu = 0,
-               bool lead = false) {
+               bool lead = false, double lead_rho = 0.0) {
   Plan p;
   p.BH = (long)B * H;
   long gpc;  // workgroups of the output walker per CU
@@ -87,7 +87,7 @@ Plan make_plan(int B, int H, int n, int d, int dv, int chunk, int dtype, int seg
   if (p.lead && segments == 0 && r > 1) {
     // segment 0 about rho times the others (at least that, when the chunks do not
     // divide evenly: the last segment is then the shorter one)
-    const double rho = lead_ratio(p.DK);
+    const double rho = lead_rho > 0.0 ? lead_rho : lead_ratio(p.DK);
     const long cps = (long)ceil((double)nc / ((double)(r - 1) + rho));
     long cps0 = nc - (r - 1) * cps;
     const long lo = (long)ceil(rho * (double)cps);
@@ -381,8 +381,14 @@ static size_t ahla_workspace(const Plan &p, int dtype) {
   return align256(BH * (R - 1) * (2 * DK * DVP + DK * DK) * 4) + BH * R * 2 * DK * DVP * 4;
 }
 
-static Plan ahla_plan(int B, int H, int n, int d, int dv, int dtype, int segments) {
-  return make_plan(B, H, n, d, dv, dtype == HLA2_BF16 ? 64 : 32, dtype, segments, 1);
+// AHLA and third order: one workgroup per CU; bf16 runs a lead plan.  Segment 0's share is
+// the ratio of a summary chunk to an output chunk of that walker (measured, d = 64, dv = 128,
+// one workgroup per CU: AHLA 2.75 against 3.8 us, third order 4.5 against 5.1 us).
+static Plan ahla_plan(int B, int H, int n, int d, int dv, int dtype, int segments, double rho = 0.72) {
+  return make_plan(B, H, n, d, dv, dtype == HLA2_BF16 ? 64 : 32, dtype, segments, 1, true, rho);
+}
+static Plan ho3_plan(int B, int H, int n, int d, int dv, int dtype, int segments) {
+  return ahla_plan(B, H, n, d, dv, dtype, segments, 0.88);
 }
 
 size_t hla2_ahla_forward_workspace_bytes(int B, int H, int n, int d, int dv, hla2_dtype_t dtype, int segments) {
@@ -426,9 +432,22 @@ int hla2_ahla_forward(const void *q, const void *k, const void *v, void *out, in
   a.kc = p.kc;
   a.log2g = decay < 1.0f ? log2f(decay) : 0.0f;
   a.normalize = normalize;
+  a.cps0 = p.cps0;
+  a.nbh = (int)p.BH;
   const float gseg = decay < 1.0f ? (float)pow((double)decay, (double)p.cps * p.kc) : 1.0f;
   hipError_t e;
-  if (p.nseg > 1) {
+  if (p.lead) {
+    // segment 0's outputs beside the summaries of segments 1 .. nseg-2; the scan from the
+    // prefix segment 0 leaves; the outputs of segments 1 .. nseg-1
+    e = hla2::launch_ahla(dt, p.DK, p.DV, norm, hla2::AHLA_LEAD, (int)p.BH, a, gseg, stream);
+    if (e != hipSuccess) return HLA2_ERR_LAUNCH;
+    if (p.nseg > 2) {
+      a.first = 1;
+      e = hla2::launch_ahla(dt, p.DK, p.DV, norm, hla2::AHLA_SCAN, (int)p.BH, a, gseg, stream);
+      if (e != hipSuccess) return HLA2_ERR_LAUNCH;
+    }
+    a.seg_lo = 1;
+  } else if (p.nseg > 1) {
     e = hla2::launch_ahla(dt, p.DK, p.DV, norm, hla2::AHLA_SUMMARY, (int)p.BH, a, gseg, stream);
     if (e != hipSuccess) return HLA2_ERR_LAUNCH;
     e = hla2::launch_ahla(dt, p.DK, p.DV, norm, hla2::AHLA_SCAN, (int)p.BH, a, gseg, stream);
@@ -457,7 +476,7 @@ static int ho3_check(int B, int H, int n, int d, int dv, int dtype) {
 size_t hla2_ho3_forward_workspace_bytes(int B, int H, int n, int d, int dv, hla2_dtype_t dtype, int segments) {
   if (segments < 0 || (dtype != HLA2_F32 && dtype != HLA2_BF16)) return 0;
   if (ho3_check(B, H, n, d, dv, (int)dtype) != HLA2_OK) return 0;
-  return ho3_workspace(ahla_plan(B, H, n, d, dv, (int)dtype, segments), (int)dtype);
+  return ho3_workspace(ho3_plan(B, H, n, d, dv, (int)dtype, segments), (int)dtype);
 }
 
 int hla2_ho3_forward(const void *q, const void *k, const void *v, void *out, int B, int H, int n, int d, int dv,
@@ -472,7 +491,7 @@ int hla2_ho3_forward(const void *q, const void *k, const void *v, void *out, int
   if (rc != HLA2_OK) return rc;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return HLA2_ERR_INVALID;
   if (den_out && !aligned(den_out, 4)) return HLA2_ERR_INVALID;
-  const Plan p = ahla_plan(B, H, n, d, dv, (int)dtype, segments);
+  const Plan p = ho3_plan(B, H, n, d, dv, (int)dtype, segments);
   const size_t need = ho3_workspace(p, (int)dtype);
   if (need > 0 && (!workspace || workspace_bytes_given < need || !aligned(workspace, 256))) return HLA2_ERR_WORKSPACE;
   const int dt = dtype == HLA2_F32 ? 0 : 1;
@@ -493,9 +512,21 @@ int hla2_ho3_forward(const void *q, const void *k, const void *v, void *out, int
   a.kc = p.kc;
   a.log2g = decay < 1.0f ? log2f(decay) : 0.0f;
   a.normalize = normalize;
+  a.cps0 = p.cps0;
+  a.nbh = (int)p.BH;
   const float gseg = decay < 1.0f ? (float)pow((double)decay, (double)p.cps * p.kc) : 1.0f;
   hipError_t e;
-  if (p.nseg > 1) {
+  if (p.lead) {
+    // as for AHLA: segment 0's outputs beside the summaries, the scan from its prefix, the rest
+    e = hla2::launch_ho3(dt, p.DK, p.DV, norm, hla2::HO3_LEAD, (int)p.BH, a, gseg, stream);
+    if (e != hipSuccess) return HLA2_ERR_LAUNCH;
+    if (p.nseg > 2) {
+      a.first = 1;
+      e = hla2::launch_ho3(dt, p.DK, p.DV, norm, hla2::HO3_SCAN, (int)p.BH, a, gseg, stream);
+      if (e != hipSuccess) return HLA2_ERR_LAUNCH;
+    }
+    a.seg_lo = 1;
+  } else if (p.nseg > 1) {
     e = hla2::launch_ho3(dt, p.DK, p.DV, norm, hla2::HO3_SUMMARY, (int)p.BH, a, gseg, stream);
     if (e != hipSuccess) return HLA2_ERR_LAUNCH;
     e = hla2::launch_ho3(dt, p.DK, p.DV, norm, hla2::HO3_SCAN, (int)p.BH, a, gseg, stream);

@@ -35,22 +35,31 @@ struct Ho3Cfg {
   static constexpr long SB = PB + 2L * DK * DK + (long)DK * DVP;            // ... | Q2 | X1 | X2
 };
 
-template <typename T, int DK, int DV, int DVP, int BC, bool OUT, bool NORM>
-__global__ void __launch_bounds__(BWD_THREADS) ho3_walk_kernel(Ho3Args a) {
+// LDS bytes of one walker workgroup: the element rows, then the decay table and den.
+template <typename T, int DK, int DVP, int BC>
+constexpr int ho3_lds_bytes() {
+  return Ho3Cfg<T, DK, DVP, BC>::ELEMS * (int)sizeof(T) + (3 * BC + 4) * 4 + BC * 4;
+}
+
+// Summary mode (OUT = false): a segment from the zero state, writing S | P' | W' and its
+// maps.  Output mode: a segment from its scanned prefix.  With LEAD (output mode, segment 0)
+// the state after the segment is written as the prefix of segment 1.
+template <typename T, int DK, int DV, int DVP, int BC, bool OUT, bool NORM, bool LEAD>
+__device__ __forceinline__ void ho3_walk_body(const Ho3Args &a, const int bh, const int seg, unsigned char *lds) {
   using Cfg = Ho3Cfg<T, DK, DVP, BC>;
-  __shared__ __attribute__((aligned(16))) T smem[Cfg::ELEMS];
-  __shared__ float pw[3 * BC + 4];
-  __shared__ float dens[OUT ? BC : 1];
+  static_assert((Cfg::ELEMS * sizeof(T)) % 4 == 0, "decay table alignment");
+  T *const smem = (T *)lds;
+  float *const pw = (float *)(lds + Cfg::ELEMS * sizeof(T));
+  float *const dens = pw + (3 * BC + 4);
   T *const Qs = smem + Cfg::Q_OFF, *const Ks = smem + Cfg::K_OFF, *const Vs = smem + Cfg::V_OFF;
   T *const Ys = smem + Cfg::Y_OFF, *const Zs = smem + Cfg::Z_OFF, *const Ads = smem + Cfg::AD_OFF;
   T *const Wms = smem + Cfg::WM_OFF, *const Ss = smem + Cfg::S_OFF, *const Ps = smem + Cfg::P_OFF;
   T *const Ws = smem + Cfg::W_OFF;
   const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 4, nn = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nseg_here = OUT ? a.nseg : a.nseg - 1;
-  const int bh = blockIdx.x / nseg_here, seg = blockIdx.x % nseg_here;
+  const int tok0 = ahla_seg_chunk0(a, seg) * a.kc, tokE = min(a.n, tok0 + ahla_seg_chunks(a, seg) * a.kc);
+  // summarised segments are full, cps chunks (segment 0 of a lead plan is never summarised)
   const int seglen = a.cps * a.kc;
-  const int tok0 = seg * seglen, tokE = min(a.n, tok0 + seglen);
   const int nch = (tokE - tok0 + BC - 1) / BC;
   const long hq = (long)bh * a.n * a.d, hv = (long)bh * a.n * a.dv;
   const T *qh = (const T *)a.q + hq, *kh = (const T *)a.k + hq, *vh = (const T *)a.v + hv;
@@ -214,6 +223,42 @@ __global__ void __launch_bounds__(BWD_THREADS) ho3_walk_kernel(Ho3Args a) {
       }
     });
   }
+  if constexpr (OUT && LEAD) {
+    // the state after segment 0 is the prefix S | P' | W' of segment 1 (the layout it is read in)
+    float *pb = a.prefix + ((long)bh * a.nseg + seg + 1) * Cfg::PB;
+    for_tiles<DK, DK>(w, [&](int i0, int j0, bool ok, int it) {
+      if (ok) *(f32x4 *)(pb + (i0 + nn) * DK + j0 + 4 * gq) = S[it];
+    });
+    for_tiles<DK, DVP>(w, [&](int i0, int j0, bool ok, int it) {
+      const int o = (i0 + nn) * DVP + j0 + 4 * gq;
+      if (ok) {
+        *(f32x4 *)(pb + DK * DK + o) = P[it];
+        *(f32x4 *)(pb + DK * DK + DK * DVP + o) = W[it];
+      }
+    });
+  }
+}
+
+// Walks segments (OUT ? seg_lo .. nseg-1 : 0 .. nseg-2) of every head, one workgroup each.
+template <typename T, int DK, int DV, int DVP, int BC, bool OUT, bool NORM>
+__global__ void __launch_bounds__(BWD_THREADS) ho3_walk_kernel(Ho3Args a) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[ho3_lds_bytes<T, DK, DVP, BC>()];
+  const int lo = OUT ? a.seg_lo : 0, nr = (OUT ? a.nseg : a.nseg - 1) - lo;
+  ho3_walk_body<T, DK, DV, DVP, BC, OUT, NORM, false>(a, blockIdx.x / nr, lo + blockIdx.x % nr, lds);
+}
+
+// The lead launch: workgroups 0 .. nbh-1 walk segment 0 of their head for its outputs and
+// leave the prefix of segment 1; the rest summarise segments 1 .. nseg-2 of every head.
+template <typename T, int DK, int DV, int DVP, int BC, bool NORM>
+__global__ void __launch_bounds__(BWD_THREADS) ho3_lead_kernel(Ho3Args a) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[ho3_lds_bytes<T, DK, DVP, BC>()];
+  const int b = blockIdx.x;
+  if (b < a.nbh) {
+    ho3_walk_body<T, DK, DV, DVP, BC, true, NORM, true>(a, b, 0, lds);
+  } else {
+    const int i = b - a.nbh, nr = a.nseg - 2;
+    ho3_walk_body<T, DK, DV, DVP, BC, false, NORM, false>(a, i / nr, 1 + i % nr, lds);
+  }
 }
 
 // Exclusive scan over segments (the fold of each full segment into the running
@@ -232,19 +277,28 @@ __global__ void __launch_bounds__(256) ho3_scan_kernel(Ho3Args a, float G) {
   const int tid = threadIdx.x, bh = blockIdx.x, sp = blockIdx.y, r0 = 16 * sp;
   const float G3 = G * G * G;
   float *pre = a.prefix + (long)bh * a.nseg * PB;
-  for (int e = tid; e < DK * DVP; e += 256) Pl[e] = 0.f;
-  for (int e = tid; e < 16 * DK; e += 256) Sl[e] = 0.f;
+  const int rs = a.first;  // 1: the prefix of segment 1 is given (written by segment 0's walk)
+  const float *given = pre + (long)rs * PB;
+  for (int e = tid; e < DK * DVP; e += 256) Pl[e] = rs ? given[DK * DK + e] : 0.f;
+  for (int e = tid; e < 16 * DK; e += 256) Sl[e] = rs ? given[r0 * DK + e] : 0.f;
   f32x4 W[NWQ];  // W'[r0 + f][c0 .. c0 + 3] for group q = tid + 256 i: f = q / (DVP/4), c0 = 4 (q % (DVP/4))
 #pragma unroll
-  for (int i = 0; i < NWQ; ++i) W[i] = zero4();
-  for (int r = 0; r < a.nseg; ++r) {
+  for (int i = 0; i < NWQ; ++i) {
+    const int q = tid + 256 * i;
+    const int f = q / (DVP / 4), c0 = 4 * (q % (DVP / 4));
+    W[i] = (rs && (WQ % 256 == 0 || q < WQ)) ? *(const f32x4 *)(given + DK * DK + DK * DVP + (r0 + f) * DVP + c0)
+                                             : zero4();
+  }
+  for (int r = rs; r < a.nseg; ++r) {
     float *pr = pre + (long)r * PB;
+    const bool put = r > rs || rs == 0;  // a given prefix is already in place
     __syncthreads();  // Pl, Sl hold the state before segment r
-    for (int e = tid; e < 16 * DK; e += 256) pr[r0 * DK + e] = Sl[e];
+    if (put)
+      for (int e = tid; e < 16 * DK; e += 256) pr[r0 * DK + e] = Sl[e];
 #pragma unroll
     for (int i = 0; i < NWQ; ++i) {
       const int q = tid + 256 * i;
-      if (WQ % 256 == 0 || q < WQ) {
+      if (put && (WQ % 256 == 0 || q < WQ)) {
         const int f = q / (DVP / 4), c0 = 4 * (q % (DVP / 4));
         *(f32x4 *)(pr + DK * DK + (r0 + f) * DVP + c0) = *(const f32x4 *)(Pl + (r0 + f) * DVP + c0);
         *(f32x4 *)(pr + DK * DK + DK * DVP + (r0 + f) * DVP + c0) = W[i];
@@ -299,8 +353,13 @@ static hipError_t launch_ho3_t(int phase, int BH, const Ho3Args &a, float gseg, 
       hipLaunchKernelGGL((ho3_scan_kernel<DK, DVP>), dim3(BH, DK / 16), dim3(256), 0, s, a, gseg);
       return hipGetLastError();
     case HO3_OUTPUT:
-      hipLaunchKernelGGL((ho3_walk_kernel<T, DK, DV, DVP, BC, true, NORM>), dim3(BH * a.nseg), dim3(BWD_THREADS), 0,
-                         s, a);
+      hipLaunchKernelGGL((ho3_walk_kernel<T, DK, DV, DVP, BC, true, NORM>), dim3(BH * (a.nseg - a.seg_lo)),
+                         dim3(BWD_THREADS), 0, s, a);
+      return hipGetLastError();
+    case HO3_LEAD:
+      if (a.nseg < 2 || a.nbh != BH) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((ho3_lead_kernel<T, DK, DV, DVP, BC, NORM>), dim3(BH * (a.nseg - 1)), dim3(BWD_THREADS),
+                         0, s, a);
       return hipGetLastError();
   }
   return hipErrorInvalidValue;

@@ -184,8 +184,22 @@ struct AhlaArgs {
   int nseg, cps, kc;       // segments of cps chunks of kc tokens
   float log2g;             // log2(decay)
   int normalize;
+  int cps0 = 0;            // chunks of segment 0 (0: cps)
+  int seg_lo = 0;          // output launch: walks segments seg_lo .. nseg-1
+  int nbh = 0;             // heads B*H (lead launch: its first nbh workgroups walk segment 0)
+  int first = 0;           // scan: 1 when the prefix of segment 1 is given (lead plans)
 };
-enum { AHLA_SUMMARY = 0, AHLA_SCAN = 1, AHLA_OUTPUT = 2 };
+// Segment geometry of the AHLA / third-order plans, in chunks of kc tokens.
+__host__ __device__ inline int ahla_seg_chunk0(const AhlaArgs &a, int s) {
+  return s == 0 ? 0 : (a.cps0 > 0 ? a.cps0 : a.cps) + (s - 1) * a.cps;
+}
+__host__ __device__ inline int ahla_seg_chunks(const AhlaArgs &a, int s) {
+  return s == 0 && a.cps0 > 0 ? a.cps0 : a.cps;
+}
+// AHLA_LEAD: workgroups 0 .. nbh-1 walk segment 0 in output mode and leave the prefix of
+// segment 1; the rest summarise segments 1 .. nseg-2.  AHLA_OUTPUT walks segments
+// seg_lo .. nseg-1.
+enum { AHLA_SUMMARY = 0, AHLA_SCAN = 1, AHLA_OUTPUT = 2, AHLA_LEAD = 3 };
 // one phase of the AHLA forward; gseg = decay^(tokens per full segment) (scan)
 hipError_t launch_ahla(int dtype, int DK, int DV, bool norm, int phase, int BH, const AhlaArgs &a, float gseg,
                        hipStream_t s);
@@ -194,7 +208,7 @@ hipError_t launch_ahla(int dtype, int DK, int DV, bool norm, int phase, int BH, 
 // The third-order kernels (hla2_ho3.hip) take the same argument block; their
 // prefix blocks are S | P' | W' and their summary blocks S | P' | W' | Q2 | X1 | X2.
 using Ho3Args = AhlaArgs;
-enum { HO3_SUMMARY = 0, HO3_SCAN = 1, HO3_OUTPUT = 2 };
+enum { HO3_SUMMARY = 0, HO3_SCAN = 1, HO3_OUTPUT = 2, HO3_LEAD = 3 };
 hipError_t launch_ho3(int dtype, int DK, int DV, bool norm, int phase, int BH, const Ho3Args &a, float gseg,
                       hipStream_t s);
 

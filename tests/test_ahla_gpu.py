@@ -86,6 +86,24 @@ SMALL = [
 ]
 
 
+# Lead plans (bf16, automatic): segment 0's output walk leaves segment 1's prefix and the scan
+# starts there; these shapes give a segment 0 shorter than the others and a ragged tail.
+LEAD = [
+    # B, H, n, d, dv, decay, normalize, oracle heads (None: all)
+    (2, 2, 777, 64, 64, 0.99, True, None),
+    (4, 16, 1900, 128, 128, 0.99, True, [(0, 0), (1, 7), (3, 15)]),
+    (4, 16, 1700, 64, 128, 0.97, False, [(0, 3), (2, 9), (3, 14)]),
+]
+
+
+@pytest.mark.parametrize("case", LEAD, ids=lambda c: "-".join(str(x) for x in c[:7]))
+def test_ahla_lead_plan_cases(case):
+    B, H_, n, d, dv, decay, normalize, heads = case
+    print("case", case, flush=True)
+    q, k, v = draw(B, H_, n, d, dv, "bf16", seed=700 + n + d)
+    check(q, k, v, decay, normalize, "bf16", heads=heads)
+
+
 @pytest.mark.parametrize("B,H_,n,d,dv,dtype,decay,normalize,segments", SMALL)
 def test_ahla_matches_oracle(B, H_, n, d, dv, dtype, decay, normalize, segments):
     print("case", B, H_, n, d, dv, dtype, decay, normalize, segments, flush=True)

@@ -93,6 +93,23 @@ SMALL = [
 ]
 
 
+# Lead plans (bf16, automatic): segment 0's output walk leaves segment 1's prefix and the scan
+# starts there; these shapes give a segment 0 shorter than the others and a ragged tail.
+LEAD = [
+    # B, H, n, d, dv, decay, normalize, oracle heads (None: all)
+    (4, 16, 2900, 64, 128, 0.99, False, [(0, 0), (1, 7), (3, 15)]),
+    (4, 16, 2900, 64, 64, 0.98, True, [(0, 5), (2, 10), (3, 1)]),
+]
+
+
+@pytest.mark.parametrize("case", LEAD, ids=lambda c: "-".join(str(x) for x in c[:7]))
+def test_ho3_lead_plan_cases(case):
+    B, H_, n, d, dv, decay, normalize, heads = case
+    print("case", case, flush=True)
+    q, k, v = draw(B, H_, n, d, dv, "bf16", seed=800 + n + d)
+    check(q, k, v, decay, normalize, "bf16", heads=heads)
+
+
 @pytest.mark.parametrize("B,H_,n,d,dv,dtype,decay,normalize,segments", SMALL)
 def test_ho3_matches_oracle(B, H_, n, d, dv, dtype, decay, normalize, segments):
     print("case", B, H_, n, d, dv, dtype, decay, normalize, segments, flush=True)
