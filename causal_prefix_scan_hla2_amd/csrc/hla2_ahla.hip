@@ -216,7 +216,8 @@ __global__ void __launch_bounds__(256) ahla_scan_kernel(AhlaArgs a, float gseg) 
   float *pre = a.prefix + (long)bh * a.nseg * PB;
   const int rs = a.first;  // 1: the prefix of segment 1 is given (written by segment 0's walk)
   const float *given = pre + (long)rs * PB;
-  for (int e = tid; e < DK * DVP; e += 256) Pl[e] = rs ? given[e] : 0.f;
+  for (int e = 4 * tid; e < DK * DVP; e += 1024)
+    *(f32x4 *)(Pl + e) = rs ? *(const f32x4 *)(given + e) : zero4();
   f32x4 E[NEQ];  // E'[r0 + f][c0 .. c0 + 3] for group q = tid + 256 i: f = q / (DVP/4), c0 = 4 (q % (DVP/4))
 #pragma unroll
   for (int i = 0; i < NEQ; ++i) {

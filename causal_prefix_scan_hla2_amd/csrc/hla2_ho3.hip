@@ -279,8 +279,10 @@ __global__ void __launch_bounds__(256) ho3_scan_kernel(Ho3Args a, float G) {
   float *pre = a.prefix + (long)bh * a.nseg * PB;
   const int rs = a.first;  // 1: the prefix of segment 1 is given (written by segment 0's walk)
   const float *given = pre + (long)rs * PB;
-  for (int e = tid; e < DK * DVP; e += 256) Pl[e] = rs ? given[DK * DK + e] : 0.f;
-  for (int e = tid; e < 16 * DK; e += 256) Sl[e] = rs ? given[r0 * DK + e] : 0.f;
+  for (int e = 4 * tid; e < DK * DVP; e += 1024)
+    *(f32x4 *)(Pl + e) = rs ? *(const f32x4 *)(given + DK * DK + e) : zero4();
+  for (int e = 4 * tid; e < 16 * DK; e += 1024)
+    *(f32x4 *)(Sl + e) = rs ? *(const f32x4 *)(given + r0 * DK + e) : zero4();
   f32x4 W[NWQ];  // W'[r0 + f][c0 .. c0 + 3] for group q = tid + 256 i: f = q / (DVP/4), c0 = 4 (q % (DVP/4))
 #pragma unroll
   for (int i = 0; i < NWQ; ++i) {
