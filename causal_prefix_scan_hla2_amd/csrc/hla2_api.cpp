@@ -127,6 +127,11 @@ struct BwdPlan {
   Plan p;
   int BC, DVP, nbc;
   bool norm;
+  // Split prefix (bf16, two segments): the incoming state of segment 1 is formed from the
+  // summaries of segment 0's two halves, walked by two workgroups per head, so that the
+  // summary walk fills every CU instead of half of them.
+  bool split;
+  int half0, half1;  // chunks of the two halves
   size_t off_fsum, off_prefix, off_cst, off_rsum, off_suffix, off_gprep, total;
 };
 BwdPlan make_bwd_plan(int B, int H, int n, int d, int dv, int dtype, int normalize, int segments) {
@@ -139,9 +144,12 @@ BwdPlan make_bwd_plan(int B, int H, int n, int d, int dv, int dtype, int normali
   b.nbc = (n + b.BC - 1) / b.BC;
   const size_t es = dtype == HLA2_F32 ? 4 : 2, BH = (size_t)b.p.BH, R = (size_t)b.p.nseg;
   const size_t DK = (size_t)b.p.DK, DVP = (size_t)b.DVP, adj = (DK * DVP + DK * DK) * 4;
+  b.split = dtype == HLA2_BF16 && R == 2 && b.p.cps >= 2;
+  b.half1 = b.p.cps / 2;
+  b.half0 = b.p.cps - b.half1;
   size_t o = 0;
   b.off_fsum = o;
-  o += align256(BH * (R - 1) * (size_t)hla2::sum_block_floats(b.p.DK, b.p.DV) * 4);
+  o += align256(BH * (b.split ? 2 : R - 1) * (size_t)hla2::sum_block_floats(b.p.DK, b.p.DV) * 4);
   b.off_prefix = o;
   o += R > 1 ? align256(BH * R * (size_t)hla2::prefix_block_floats(b.p.DK, b.p.DV) * 4) : 0;
   b.off_cst = o;
@@ -310,7 +318,8 @@ int hla2_backward(const void *q, const void *k, const void *v, const void *out, 
     e = hla2::launch_bwd(dt, p.DK, p.DV, true, hla2::BWD_PREP, (int)p.BH, hla2::BwdArgs{}, pa, 1.f, stream);
     if (e != hipSuccess) return HLA2_ERR_LAUNCH;
   }
-  // incoming forward state of every segment: the forward's summary walk and scan
+  // incoming forward state of every segment: the forward's summary walk and scan (with a split
+  // prefix: the two halves of segment 0 summarised and folded, only segment 1's prefix kept)
   if (p.nseg > 1) {
     hla2::WalkArgs a;
     a.q = q;
@@ -331,14 +340,25 @@ int hla2_backward(const void *q, const void *k, const void *v, const void *out, 
     a.normalize = normalize;
     a.need_den = normalize;
     a.sum_all = 0;
-    e = hla2::launch_walk(dt, p.DK, p.DV, p.CP, false, dim3((unsigned)(p.BH * (p.nseg - 1))), a, stream);
+    if (b.split) {  // segments 0 | 1 | 2 of the walk: the two halves, then the whole segment 1
+      a.nseg = 3;
+      a.cps0 = b.half0;
+      a.cps = b.half1;
+    }
+    e = hla2::launch_walk(dt, p.DK, p.DV, p.CP, false, dim3((unsigned)(p.BH * (a.nseg - 1))), a, stream);
     if (e != hipSuccess) return HLA2_ERR_LAUNCH;
     hla2::ScanArgs sa;
     sa.sums = fsum;
-    sa.nsum = p.nseg - 1;
+    sa.nsum = a.nseg - 1;
     sa.prefix = prefix;
-    sa.nseg = p.nseg;
-    sa.gamma_seg = decay < 1.0f ? (float)pow((double)decay, (double)p.cps * p.kc) : 1.0f;
+    sa.nseg = a.nseg;
+    // the fold of the first summary starts from zero, so only the later segments' length counts
+    sa.gamma_seg = decay < 1.0f ? (float)pow((double)decay, (double)a.cps * p.kc) : 1.0f;
+    if (b.split) {  // keep the prefix after both halves, as block 1 of the two-segment layout
+      sa.pnseg = 2;
+      sa.pmin = 2;
+      sa.pshift = 1;
+    }
     e = hla2::launch_scan(dt, p.DK, p.DV, (int)p.BH, sa, stream);
     if (e != hipSuccess) return HLA2_ERR_LAUNCH;
   }

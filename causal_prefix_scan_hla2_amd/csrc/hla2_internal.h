@@ -44,6 +44,9 @@ struct ScanArgs {
   float gamma_seg;    // decay^(tokens per full segment): segments first .. nseg-2 are full
   int first = 0;      // 0: start from the zero state; 1: the prefix of segment 1 is given
                       // (written by segment 0's output walk) and the fold starts there
+  int pnseg = 0;      // prefix blocks per head in `prefix` (0: nseg)
+  int pmin = 0;       // the prefixes of segments pmin .. nseg-1 are written, the one of segment r
+  int pshift = 0;     //   at block r - pshift (bf16 path)
 };
 
 // Per-(b,h,segment) block sizes in floats, for padded dims DK, DV.

@@ -164,7 +164,8 @@ __global__ void __launch_bounds__(64 * (DK / 16)) scan_bf16_kernel(ScanArgs a) {
   };
   // the exclusive prefix of segment r (S0 rows written by the first group only)
   auto store = [&](int r) __attribute__((always_inline)) {
-    float *pb = a.prefix + ((long)bh * a.nseg + r) * PB;
+    if (r < a.pmin) return;
+    float *pb = a.prefix + ((long)bh * (a.pnseg > 0 ? a.pnseg : a.nseg) + r - a.pshift) * PB;
     if (!has_u) {
 #pragma unroll
       for (int jj = 0; jj < NJ; ++jj) *(f32x4 *)(pb + (16 * w + n) * DK + 16 * jj + 4 * g) = s0[jj];
@@ -222,6 +223,8 @@ template <int DK, int DV>
 static hipError_t launch_scan_t(int BH, bool bf, const ScanArgs &a, hipStream_t s) {
   if (a.first != 0 && !(bf && DK >= 64)) return hipErrorInvalidValue;  // only the bf16 fold takes a given prefix
   if (a.first < 0 || a.first > 1 || (a.first == 1 && a.nseg < 3)) return hipErrorInvalidValue;
+  if ((a.pnseg != 0 || a.pmin != 0 || a.pshift != 0) && !(bf && DK >= 64)) return hipErrorInvalidValue;
+  if (a.pshift < 0 || a.pshift > a.pmin) return hipErrorInvalidValue;
   if constexpr (DK >= 64) {
     if (bf) {
       hipLaunchKernelGGL((scan_bf16_kernel<DK, DV>), dim3(BH, 2), dim3(64 * (DK / 16)), 0, s, a);
