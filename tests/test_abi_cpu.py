@@ -145,6 +145,27 @@ def test_lead_plan_covers_every_chunk(L, shape, segments):
         assert c0 == cs  # explicit counts split evenly
 
 
+def test_lead_plan_sweep(L):
+    # every automatic and explicit plan over a spread of shapes covers each 64-token chunk once,
+    # keeps segment 0 no longer than the others and stays within 64 segments
+    for bh in (1, 2, 3, 7, 16, 32, 100, 128, 255, 256, 300, 1024):
+        for n in (1, 63, 64, 65, 257, 1000, 4096, 8191, 8192, 65536):
+            for d, dv in ((64, 64), (64, 128), (128, 128), (16, 48)):
+                for segments in (0, 1, 2, 3, 17, 1000):
+                    nseg, c0, cs, lead = H.hla2_forward_plan(bh, 1, n, d, dv, 64, segments=segments)
+                    nc = -(-n // 64)
+                    key = (bh, n, d, dv, segments, nseg, c0, cs)
+                    assert 1 <= nseg <= min(nc, 64), key
+                    assert 1 <= c0 <= cs, key
+                    assert lead == (nseg > 1), key
+                    if nseg == 1:
+                        assert c0 >= nc, key
+                    else:
+                        assert c0 + (nseg - 2) * cs < nc <= c0 + (nseg - 1) * cs, key
+                    if segments == 0 and nseg > 1:
+                        assert bh * (nseg - 1) <= 256, key
+
+
 def test_plan_query_rejects(L):
     x = ctypes.c_int()
     assert L.hla2_forward_ex_plan(1, 1, 64, 64, 64, 64, 0, None, ctypes.byref(x), ctypes.byref(x)) == \
