@@ -99,8 +99,13 @@ __global__ void __launch_bounds__(64) scan_kernel(ScanArgs a) {
   store(steps);
 }
 
-// bf16 path: two workgroups per head, each owning half of the value columns (the second
-// also the u column) for all rows, with one wave per 16-row tile.  The cross term S0 C_r
+// Column groups (workgroups per head) of the bf16 scan: each keeps all of S0 and owns DV/G value
+// columns.  At d = 128 a step moves 128 KB per group with two groups; four halve its columns and
+// double the loads in flight (the walk is a chain of latency-bound steps).
+__host__ __device__ constexpr int scan_groups(int DK) { return DK >= 128 ? 4 : 2; }
+
+// bf16 path: scan_groups(DK) workgroups per head, each owning a slice of the value columns (the
+// last also the u column) for all rows, with one wave per 16-row tile.  The cross term S0 C_r
 // runs on bf16 MFMA, like every other state product of the bf16 walkers: each step the
 // group's columns of C_r (and m_r) are converted to bf16 into LDS once and read by every
 // wave, while the next step's C_r is already being fetched.
@@ -109,20 +114,21 @@ __global__ void __launch_bounds__(64 * (DK / 16)) scan_bf16_kernel(ScanArgs a) {
   constexpr int NWV = DK / 16;        // waves = row tiles
   constexpr int NT = 64 * NWV;
   constexpr int NJ = DK / 16;         // f32x4 per lane of an S0 row
-  constexpr int HC = DV / 2;          // value columns per workgroup
+  constexpr int NG = scan_groups(DK);
+  constexpr int HC = DV / NG;         // value columns per workgroup
   constexpr int CT = HC / 16;         // value column tiles per workgroup
-  constexpr int LDC = HC + 16;        // bf16 C_r rows: HC values, then m_r (second group), zeros
+  constexpr int LDC = HC + 16;        // bf16 C_r rows: HC values, then m_r (last group), zeros
   constexpr int NC4 = DK * HC / 4 / NT;  // f32x4 of C_r per thread
   static_assert(NC4 * 4 * NT == DK * HC, "C staging split");
   const long SB = sum_block_floats(DK, DV), PB = prefix_block_floats(DK, DV);
-  const int bh = blockIdx.x, half = blockIdx.y, c0 = half * HC;  // first value column
-  const bool has_u = half == 1;
+  const int bh = blockIdx.x, grp = blockIdx.y, c0 = grp * HC;  // first value column
+  const bool has_u = grp == NG - 1;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const float G1 = a.gamma_seg, G2 = a.gamma_seg * a.gamma_seg;
   __shared__ __attribute__((aligned(16))) bf16 Cb[2][DK * LDC];
 
-  // columns HC .. HC+15 hold m_r (column HC, second group) and zeros; zero them once
+  // columns HC .. HC+15 hold m_r (column HC, last group) and zeros; zero them once
   for (int x = tid; x < 2 * DK * 16; x += NT) {
     const int b = x / (DK * 16), r = (x / 16) % DK, c = HC + x % 16;
     Cb[b][r * LDC + c] = (bf16)0.f;
@@ -166,7 +172,7 @@ __global__ void __launch_bounds__(64 * (DK / 16)) scan_bf16_kernel(ScanArgs a) {
   auto store = [&](int r) __attribute__((always_inline)) {
     if (r < a.pmin) return;
     float *pb = a.prefix + ((long)bh * (a.pnseg > 0 ? a.pnseg : a.nseg) + r - a.pshift) * PB;
-    if (!has_u) {
+    if (grp == 0) {
 #pragma unroll
       for (int jj = 0; jj < NJ; ++jj) *(f32x4 *)(pb + (16 * w + n) * DK + 16 * jj + 4 * g) = s0[jj];
     }
@@ -227,7 +233,7 @@ static hipError_t launch_scan_t(int BH, bool bf, const ScanArgs &a, hipStream_t 
   if (a.pshift < 0 || a.pshift > a.pmin) return hipErrorInvalidValue;
   if constexpr (DK >= 64) {
     if (bf) {
-      hipLaunchKernelGGL((scan_bf16_kernel<DK, DV>), dim3(BH, 2), dim3(64 * (DK / 16)), 0, s, a);
+      hipLaunchKernelGGL((scan_bf16_kernel<DK, DV>), dim3(BH, scan_groups(DK)), dim3(64 * (DK / 16)), 0, s, a);
       return hipGetLastError();
     }
   }
