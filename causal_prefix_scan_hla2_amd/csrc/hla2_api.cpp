@@ -88,11 +88,15 @@ Plan make_plan(int B, int H, int n, int d, int dv, int chunk, int dtype, int seg
     // segment 0 about rho times the others (at least that, when the chunks do not
     // divide evenly: the last segment is then the shorter one)
     const double rho = lead_rho > 0.0 ? lead_rho : lead_ratio(p.DK);
-    const long cps = (long)ceil((double)nc / ((double)(r - 1) + rho));
+    long cps = (long)ceil((double)nc / ((double)(r - 1) + rho));
     long cps0 = nc - (r - 1) * cps;
     const long lo = (long)ceil(rho * (double)cps);
     if (cps0 < lo) cps0 = lo;
     if (cps0 > cps) cps0 = cps;
+    // spread the chunks after segment 0 evenly (never below segment 0's length), so that the
+    // last segment is not the only short one
+    const long even = (nc - cps0 + r - 2) / (r - 1);
+    if (even >= cps0 && even < cps) cps = even;
     p.cps = (int)cps;
     p.cps0 = (int)cps0;
     p.nseg = 1 + (int)((nc - cps0 + cps - 1) / cps);

@@ -115,7 +115,7 @@ def test_workspace_and_segment_plan(L):
         nc = -(-n // 64)
         assert 1 <= r <= min(max(nc // 4, 1), 64)
         assert b * h * r >= min(256, b * h * min(nc // 4, 64)) - b * h  # within one segment of the target
-    assert H.hla2_forward_segments(4, 8, 2048, 64, 64, 64) == 7
+    assert H.hla2_forward_segments(4, 8, 2048, 64, 64, 64) == 8
     assert H.hla2_forward_segments(8, 16, 8192, 64, 128, 64) == 3
     # invalid shapes report 0 bytes / an error code
     assert H.hla2_forward_workspace_bytes(1, 1, 64, 24, 16, 16) == 0
@@ -139,8 +139,9 @@ def test_lead_plan_covers_every_chunk(L, shape, segments):
     if segments == 0 and nseg > 1:
         # the output walk of segments 1 .. nseg-1 puts at most one workgroup on each of 256 CUs
         assert b * h * (nseg - 1) <= 256
-        # segment 0 is the shorter one (it shares its launch with the summary walks)
-        assert c0 < cs or nc <= 8
+        # segment 0 is the shorter one (it shares its launch with the summary walks) when the
+        # chunks allow it; the chunks after it are spread evenly
+        assert c0 < cs or nc < 64
     if segments > 0:
         assert c0 == cs  # explicit counts split evenly
 

@@ -97,9 +97,9 @@ SMALL = [
 LEAD = [
     # B, H, n, d, dv, decay, normalize, oracle heads (None: all)
     (2, 2, 777, 64, 64, 0.99, True, None),
-    (1, 4, 2000, 64, 128, 0.95, False, None),
-    (2, 2, 1500, 48, 80, 0.97, True, None),
-    (4, 16, 1900, 128, 128, 0.99, True, [(0, 0), (1, 7), (3, 15)]),
+    (1, 4, 2074, 64, 128, 0.95, False, None),
+    (2, 2, 1537, 48, 80, 0.97, True, None),
+    (4, 16, 1937, 128, 128, 0.99, True, [(0, 0), (1, 7), (3, 15)]),
     (4, 16, 1700, 128, 64, 1.0, False, [(0, 3), (2, 9), (3, 14)]),
 ]
 
