@@ -158,10 +158,13 @@ def test_repeatable_bitwise():
     np.testing.assert_array_equal(da, db)
 
 
-def test_timed_entry_point_matches_and_records_phases():
-    # the phase events change nothing in the results and bracket every kernel
+@pytest.mark.parametrize("segs", [3, 2])
+def test_timed_entry_point_matches_and_records_phases(segs):
+    # the phase events change nothing in the results and bracket every kernel (with two
+    # segments under the lead plan no scan runs: events 1 and 2 are back to back)
     q, k, v = draw(2, 4, 1500, 64, 128, "bf16", seed=3)
-    a, da = gpu_forward(q, k, v, 0.99, True, 64, segments=3)
+    assert H.hla2_forward_plan(2, 4, 1500, 64, 128, 64, segments=segs)[0] == segs
+    a, da = gpu_forward(q, k, v, 0.99, True, 64, segments=segs)
     dev = torch.device("cuda:0")
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     out = torch.empty_like(vd)
@@ -169,7 +172,7 @@ def test_timed_entry_point_matches_and_records_phases():
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     for e in evs:
         e.record()
-    H.hla2_forward(qd, kd, vd, out, decay=0.99, normalize=True, chunk=64, den_out=den, segments=3, events=evs)
+    H.hla2_forward(qd, kd, vd, out, decay=0.99, normalize=True, chunk=64, den_out=den, segments=segs, events=evs)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(out.double().cpu().numpy(), a)
     np.testing.assert_array_equal(den.double().cpu().numpy(), da)
