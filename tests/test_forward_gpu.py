@@ -113,6 +113,22 @@ def test_lead_plan_cases(case):
     check_case(q, k, v, decay, norm, 64, "bf16", heads=heads)
 
 
+# Degenerate lengths: a single token, one short of a chunk, one past a chunk, exactly one chunk
+# (both element types, ratio and decay on).
+SHORT = [
+    # B, H, n, d, dv, dtype
+    (2, 2, 1, 64, 64, "bf16"), (1, 2, 63, 64, 128, "bf16"), (1, 2, 65, 128, 64, "bf16"),
+    (1, 1, 64, 64, 64, "bf16"), (2, 1, 1, 16, 16, "f32"), (1, 2, 17, 32, 48, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", SHORT, ids=lambda c: "-".join(str(x) for x in c))
+def test_short_sequences(case):
+    B, H_, n, d, dv, dt = case
+    q, k, v = draw(B, H_, n, d, dv, dt, seed=31 + n + d)
+    check_case(q, k, v, 0.97, True, 16 if dt == "f32" else 64, dt)
+
+
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: "-".join(str(x) for x in c))
 def test_small_cases(case):
     B, H_, n, d, dv, dt, decay, norm, chunk, segs = case
