@@ -345,7 +345,11 @@ __global__ void __launch_bounds__(256) ho3_scan_kernel(Ho3Args a, float G) {
 template <typename T, int DK, int DV, bool NORM>
 static hipError_t launch_ho3_t(int phase, int BH, const Ho3Args &a, float gseg, hipStream_t s) {
   constexpr int DVP = lds_walk_dvp(sizeof(T) == 4, DV, NORM);
-  constexpr int BC = lds_walk_chunk(sizeof(T) == 4, DK);  // d <= 64 here
+  // d <= 64 here.  Under the ratio at dv = 128 the state is 160 columns wide (P', W'), and 64-token
+  // chunks spilled about 100 registers to scratch per wave; 32-token chunks halve the chunk-sized tiles
+  // and keep the walk in registers (decay workload's shape with the ratio: 1.94 -> 0.78 ms).  At dv = 64
+  // the 64-token chunk is faster.
+  constexpr int BC = (NORM && DVP > 128) ? 32 : lds_walk_chunk(sizeof(T) == 4, DK);
   switch (phase) {
     case HO3_SUMMARY:
       hipLaunchKernelGGL((ho3_walk_kernel<T, DK, DV, DVP, BC, false, NORM>), dim3(BH * (a.nseg - 1)),

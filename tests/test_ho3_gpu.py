@@ -99,6 +99,7 @@ LEAD = [
     # B, H, n, d, dv, decay, normalize, oracle heads (None: all)
     (4, 16, 2900, 64, 128, 0.99, False, [(0, 0), (1, 7), (3, 15)]),
     (4, 16, 2900, 64, 64, 0.98, True, [(0, 5), (2, 10), (3, 1)]),
+    (4, 16, 2900, 64, 128, 0.99, True, [(1, 2), (2, 13), (3, 9)]),  # ratio at dv = 128: 32-token chunks
 ]
 
 
