@@ -143,8 +143,8 @@ BwdPlan make_bwd_plan(int B, int H, int n, int d, int dv, int dtype, int normali
   const int chunk = dtype == HLA2_BF16 ? 64 : 32;
   b.p = make_plan(B, H, n, d, dv, chunk, dtype, segments, 1);
   b.norm = normalize != 0;
-  b.BC = hla2::lds_walk_chunk(dtype == HLA2_F32, b.p.DK);
   b.DVP = hla2::lds_walk_dvp(dtype == HLA2_F32, b.p.DV, b.norm);
+  b.BC = hla2::lds_bwd_chunk(dtype == HLA2_F32, b.p.DK, b.DVP);
   b.nbc = (n + b.BC - 1) / b.BC;
   const size_t es = dtype == HLA2_F32 ? 4 : 2, BH = (size_t)b.p.BH, R = (size_t)b.p.nseg;
   const size_t DK = (size_t)b.p.DK, DVP = (size_t)b.DVP, adj = (DK * DVP + DK * DK) * 4;

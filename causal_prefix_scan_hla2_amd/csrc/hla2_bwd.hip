@@ -122,7 +122,7 @@ __global__ void __launch_bounds__(256) bwd_rscan_kernel(BwdArgs a, float gL) {
 template <typename T, int DK, int DV, bool NORM>
 struct BwdShape {
   static constexpr int DVP = lds_walk_dvp(sizeof(T) == 4, DV, NORM);
-  static constexpr int BC = lds_walk_chunk(sizeof(T) == 4, DK);
+  static constexpr int BC = lds_bwd_chunk(sizeof(T) == 4, DK, DVP);
 };
 
 template <typename T, int DK, int DV, bool NORM>

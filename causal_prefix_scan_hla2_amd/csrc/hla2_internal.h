@@ -171,6 +171,12 @@ __host__ __device__ constexpr int lds_walk_chunk(bool f32, int DK) { return (f32
 __host__ __device__ constexpr int lds_walk_dvp(bool f32, int DV, bool norm) {
   return DV + (norm ? (f32 ? 16 : 32) : 0);
 }
+// Chunk of the backward walkers: that of lds_walk_chunk, and 32 tokens when the padded value width
+// passes 128 (the ratio at dv = 128), where 64-token chunks spill registers.  The host sizes the
+// per-chunk state buffer with the same function.
+__host__ __device__ constexpr int lds_bwd_chunk(bool f32, int DK, int DVP) {
+  return DVP > 128 ? 32 : lds_walk_chunk(f32, DK);
+}
 // one phase of the backward pass; gL = decay^(tokens per full segment) (reverse scan)
 hipError_t launch_bwd(int dtype, int DK, int DV, bool norm, int phase, int BH, const BwdArgs &a,
                       const BwdPrepArgs &pa, float gL, hipStream_t s);

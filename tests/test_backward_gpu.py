@@ -70,6 +70,7 @@ SMALL = [
     (1, 2, 1024, 64, 64, "bf16", 0.999, True, 0),
     (1, 1, 200, 48, 80, "bf16", 0.9, True, 2),
     (1, 1, 37, 128, 128, "bf16", 0.9, False, 0),
+    (1, 2, 777, 64, 128, "bf16", 0.97, True, 3),  # ratio at dv = 128: 32-token chunks
 ]
 
 
