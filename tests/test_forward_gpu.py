@@ -233,6 +233,25 @@ def test_workload_decay_8k_sampled():
     print(check_case(q, k, v, w.decay, w.normalize, w.chunk, w.dtype, heads=heads))
 
 
+def test_workload_decay_8k_benchmark_call_sampled():
+    """The exact call the benchmark times: the decay workload with no den buffer (so the walkers run
+    without the den state, the instantiation bench.py measures), automatic lead plan; sampled heads
+    against the oracle, and bitwise equal to the same call repeated."""
+    w = I.WORKLOADS["decay_8k"]
+    q, k, v = I.make_qkv(w)
+    o_gpu, _ = gpu_forward(q, k, v, w.decay, w.normalize, w.chunk, want_den=False)
+    o_again, _ = gpu_forward(q, k, v, w.decay, w.normalize, w.chunk, want_den=False)
+    np.testing.assert_array_equal(o_gpu, o_again)
+    heads = I.sample_heads(w.B, w.H, 4)
+    idx = tuple(np.array(heads).T)
+    tidx = tuple(torch.as_tensor(x) for x in idx)
+    num, _, _, _ = O.serial_unorm(q[tidx].double().numpy(), k[tidx].double().numpy(), v[tidx].double().numpy(),
+                                  w.decay)
+    r = rel_l2(o_gpu[idx], num)
+    print("num %.3g" % r)
+    assert r <= tol_for(w.dtype), r
+
+
 def test_workload_long_64k_sampled():
     w = I.WORKLOADS["long_64k"]
     q, k, v = I.make_qkv(w)
