@@ -152,3 +152,45 @@ def test_ho3_norm_workload_shape_sampled():
     q, k, v = I.make_qkv(w)
     check(q, k, v, w.decay, True, w.dtype, heads=I.sample_heads(w.B, w.H, 3), subset=True)
 
+# Without a den buffer and without the ratio the walkers carry no den column (the instantiations the
+# benchmark times): the outputs are compared with the oracle's num.
+NODEN = [
+    # B, H, n, d, dv, decay, segments, oracle heads (None: all)
+    (2, 3, 300, 64, 128, 0.99, 0, None),
+    (1, 2, 777, 64, 64, 0.97, 3, None),
+    (1, 1, 1000, 64, 128, 1.0, 2, None),
+    (1, 1, 200, 48, 80, 0.9, 0, None),
+]
+
+
+def gpu_ho3_noden(q, k, v, decay, segments=0):
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    out = torch.empty_like(vd)
+    H.hla2_ho3_forward(qd, kd, vd, out, decay=decay, normalize=False, den_out=None, segments=segments)
+    torch.cuda.synchronize()
+    return out.double().cpu().numpy()
+
+
+@pytest.mark.parametrize("case", NODEN, ids=lambda c: "-".join(str(x) for x in c[:7]))
+def test_ho3_without_den_matches_oracle(case):
+    B, H_, n, d, dv, decay, segments, heads = case
+    print("case", case, flush=True)
+    q, k, v = draw(B, H_, n, d, dv, "bf16", seed=950 + n + d)
+    o = gpu_ho3_noden(q, k, v, decay, segments)
+    num, _, _ = O.ho3_serial(q.double().numpy(), k.double().numpy(), v.double().numpy(), decay)
+    r = rel_l2(o, num)
+    assert r <= tol_for("bf16"), r
+
+
+def test_ho3_without_den_decay_workload_sampled():
+    """The benchmark's call on the decay workload's shape (no den buffer, no ratio), sampled heads."""
+    w = I.WORKLOADS["decay_8k"]
+    q, k, v = I.make_qkv(w)
+    o = gpu_ho3_noden(q, k, v, w.decay)
+    heads = I.sample_heads(w.B, w.H, 3)
+    idx = tuple(np.array(heads).T)
+    tidx = tuple(torch.as_tensor(x) for x in idx)
+    num, _, _ = O.ho3_serial(q[tidx].double().numpy(), k[tidx].double().numpy(), v[tidx].double().numpy(), w.decay)
+    r = rel_l2(o[idx], num)
+    assert r <= tol_for(w.dtype), r
