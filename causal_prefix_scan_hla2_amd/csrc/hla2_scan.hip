@@ -134,6 +134,9 @@ __global__ void __launch_bounds__(64 * (DK / 16)) scan_bf16_kernel(ScanArgs a) {
     const int b = x / (DK * 16), r = (x / 16) % DK, c = HC + x % 16;
     Cb[b][r * LDC + c] = (bf16)0.f;
   }
+  // the fill writes column HC of rows that other waves own; the first step's m_r goes into
+  // that column, so every zero must land before any thread writes it
+  __syncthreads();
 
   f32x4 s0[NJ];       // S0[16 w + n][16 jj + 4 g + e]
   f32x4 acc[CT + 1];  // U0[16 w + 4 g + q][c0 + 16 ct + n]; tile CT holds u0 in column 0
