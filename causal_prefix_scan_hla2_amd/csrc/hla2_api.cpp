@@ -110,6 +110,13 @@ Plan make_plan(int B, int H, int n, int d, int dv, int chunk, int dtype, int seg
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// A launch of `groups` workgroups of `threads` work-items along one grid dimension must stay
+// below 2^32 work-items; shapes whose grids would not fit are rejected before any launch.
+bool grid_fits(long groups, long threads) { return groups > 0 && groups * threads <= 0xFFFFFFFFL; }
+// every forward launch of a plan: walkers (up to 512 threads, one workgroup per head and
+// segment), the scan (one column of up to 512 threads per head) and the state export
+bool forward_grids_fit(const Plan &p) { return grid_fits(p.BH * p.nseg, 512) && grid_fits(p.BH, 512); }
+
 // summary blocks per (b, h): segments 0 .. nseg-2 for the scan; every segment when the final
 // state is exported
 int nsum(const Plan &p, bool state) { return state ? p.nseg : p.nseg - 1; }
@@ -303,6 +310,10 @@ int hla2_backward(const void *q, const void *k, const void *v, const void *out, 
     if (!aligned(t, 16)) return HLA2_ERR_INVALID;
   if (normalize && (!aligned(out, 16) || !aligned(den, 4))) return HLA2_ERR_INVALID;
   const BwdPlan b = make_bwd_plan(B, H, n, d, dv, (int)dtype, normalize, segments);
+  // the pre-walk runs two roles per segment; the ratio's preparation one thread per 4 values
+  if (!forward_grids_fit(b.p) || !grid_fits(2 * b.p.BH * b.p.nseg, 512) ||
+      (b.norm && !grid_fits((b.p.BH * n + 3) / 4, 256)))
+    return HLA2_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes_given < b.total || !aligned(workspace, 256)) return HLA2_ERR_WORKSPACE;
   const Plan &p = b.p;
   const int dt = dtype == HLA2_F32 ? 0 : 1;
@@ -434,6 +445,7 @@ int hla2_ahla_forward(const void *q, const void *k, const void *v, void *out, in
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return HLA2_ERR_INVALID;
   if (den_out && !aligned(den_out, 4)) return HLA2_ERR_INVALID;
   const Plan p = ahla_plan(B, H, n, d, dv, (int)dtype, segments);
+  if (!forward_grids_fit(p)) return HLA2_ERR_UNSUPPORTED;
   const size_t need = ahla_workspace(p, (int)dtype);
   if (need > 0 && (!workspace || workspace_bytes_given < need || !aligned(workspace, 256))) return HLA2_ERR_WORKSPACE;
   const int dt = dtype == HLA2_F32 ? 0 : 1;
@@ -516,6 +528,7 @@ int hla2_ho3_forward(const void *q, const void *k, const void *v, void *out, int
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return HLA2_ERR_INVALID;
   if (den_out && !aligned(den_out, 4)) return HLA2_ERR_INVALID;
   const Plan p = ho3_plan(B, H, n, d, dv, (int)dtype, segments);
+  if (!forward_grids_fit(p)) return HLA2_ERR_UNSUPPORTED;
   const size_t need = ho3_workspace(p, (int)dtype);
   if (need > 0 && (!workspace || workspace_bytes_given < need || !aligned(workspace, 256))) return HLA2_ERR_WORKSPACE;
   const int dt = dtype == HLA2_F32 ? 0 : 1;
@@ -570,7 +583,7 @@ int hla2_decode_step(float *state, const void *q, const void *k, const void *v, 
   auto ok = [](int x) { return x == 16 || x == 32 || x == 64 || x == 128; };
   if (!ok(d) || !ok(dv)) return HLA2_ERR_UNSUPPORTED;
   const long NH = (long)N * H;
-  if (NH > (1L << 30)) return HLA2_ERR_UNSUPPORTED;
+  if (!grid_fits(NH, 256)) return HLA2_ERR_UNSUPPORTED;  // one 256-thread workgroup per (sequence, head)
   if (!aligned(state, 16)) return HLA2_ERR_INVALID;
   const size_t esz = dtype == HLA2_F32 ? 4 : 2;
   if (!aligned(q, esz) || !aligned(k, esz) || !aligned(v, esz) || !aligned(out, esz)) return HLA2_ERR_INVALID;
@@ -608,6 +621,7 @@ int run_forward(const void *q, const void *k, const void *v, void *out, int B, i
   if (state_out && !aligned(state_out, 4)) return HLA2_ERR_INVALID;
   const bool state = state_out != nullptr;
   const Plan p = make_plan(B, H, n, d, dv, chunk, (int)dtype, segments, 0, !state);
+  if (!forward_grids_fit(p)) return HLA2_ERR_UNSUPPORTED;
   const size_t need = workspace_bytes(p, state);
   // callers are held to the size the workspace query reports (the larger of the bf16 and
   // fp32 plans), whichever dtype this call uses

@@ -87,21 +87,33 @@ size_t hla2_forward_workspace_bytes(int B, int H, int n, int d, int dv, int chun
 int hla2_forward_segments(int B, int H, int n, int d, int dv, int chunk);
 
 /*
- * Masked second-order HLA forward pass.
+ * Masked second-order HLA forward pass: out_t = q_t^T (S_t C_t - G_t), or that
+ * over q_t^T (S_t m_t - h_t) [SUM §1, output formula and normalisation],
+ * computed chunk-parallel through segment summaries and an exclusive scan with
+ * the semidirect-product combine [SUM §4, associative operators and scan
+ * equivalence].
  *   q, k : [B, H, n, d]    element type `dtype`
  *   v    : [B, H, n, dv]   element type `dtype`
  *   out  : [B, H, n, dv]   element type `dtype` (written)
  *   decay: g in (0, 1]; 1 = no decay
  *   normalize: 0 -> out = num;  1 -> out = num / den
- *   chunk: tokens per chunk, one of 16, 32, 64, 128 (128 needs d, dv <= 128;
- *          chunk only changes rounding, not the result)
+ *   chunk: tokens per chunk, one of 16, 32, 64, 128.  The result does not
+ *          depend on it beyond rounding [SUM §4, scan equivalence].  The fp32
+ *          path uses it as its tile; the bf16 path always walks 64-token chunks,
+ *          so bf16 results are bitwise the same for every valid `chunk`.
  *   den_out: nullable [B, H, n] fp32; when given, den_t is written whatever
  *          `normalize` says
  *   workspace: device buffer of at least hla2_forward_workspace_bytes(...)
  *          bytes (may be NULL when that is 0); contents on entry are ignored
  * Supported: d, dv multiples of 16 in [16, 128]; n >= 1; B, H >= 1; one head's
  * rows in bytes, n * (max(d, dv) + 16) * 4, below 2^31 - 256 (they are addressed
- * with 32-bit offsets); B*H <= 2^24 and B*H*n <= 2^40.
+ * with 32-bit offsets); B*H <= 2^24 and B*H*n <= 2^40; and B*H*segments*512 below
+ * 2^32 (one workgroup per head and segment; larger grids give
+ * HLA2_ERR_UNSUPPORTED).
+ * Causality: for finite inputs, out_t and den_t are bitwise unchanged by any
+ * change of tokens after t [SUM "Resultaten en claims"].  A NaN or Inf in a
+ * later token can still reach earlier outputs, because the masked products
+ * multiply it by zero (0 * Inf = NaN).
  */
 int hla2_forward(const void *q, const void *k, const void *v, void *out,
                  int B, int H, int n, int d, int dv, float decay, int normalize, int chunk,
@@ -119,7 +131,8 @@ int hla2_forward(const void *q, const void *k, const void *v, void *out,
  *   out  : [N, H, dv]  element type `dtype` (written)
  * Order inside the step: the cross summaries take the new key against the
  * OLD C and m, then S, C, m absorb the token, then the readout uses the new
- * state.  Supported: d, dv in {16, 32, 64, 128}.
+ * state.  Supported: d, dv in {16, 32, 64, 128}; N*H below 2^24 (one 256-thread
+ * workgroup per (sequence, head); larger counts give HLA2_ERR_UNSUPPORTED).
  */
 int hla2_decode_step(float *state, const void *q, const void *k, const void *v, void *out,
                      int N, int H, int d, int dv, float decay, int normalize,

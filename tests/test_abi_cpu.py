@@ -328,3 +328,22 @@ def test_head_rows_beyond_32bit_offsets_rejected():
     n_ok = (0x7FFFFF00 // ((64 + 16) * 4))
     assert H.hla2_forward_segments(1, 1, n_ok, 64, 64, 64) > 0
     assert H.hla2_forward_segments(1, 1, n_ok + 1, 64, 64, 64) == H.HLA2_ERR_UNSUPPORTED
+
+
+def test_grids_beyond_2_32_work_items_rejected(L):
+    """Every launch keeps its work-items along one grid dimension below 2^32: counts of heads (or
+    heads times segments) whose grids would not fit are refused on the host, not at launch."""
+    # decode: one 256-thread workgroup per (sequence, head)
+    assert dec(L, N=1 << 12, H_=1 << 12) == H.HLA2_ERR_UNSUPPORTED   # 2^24 workgroups
+    assert dec(L, N=1 << 14, H_=1 << 12) == H.HLA2_ERR_UNSUPPORTED
+    # forward: up to 512 threads per workgroup, one per head and segment (here one segment)
+    assert fwd(L, B_=1 << 13, H_=1 << 10, n=64, d=16, dv=16, chunk=16, dtype=0) == H.HLA2_ERR_UNSUPPORTED
+    assert fwd(L, B_=1 << 13, H_=1 << 10, n=64, d=64, dv=64, chunk=64, dtype=1) == H.HLA2_ERR_UNSUPPORTED
+    # an explicit segment count multiplies the grid: 2^18 heads x 64 segments
+    assert fwd(L, B_=1 << 9, H_=1 << 9, n=64 * 64, d=64, dv=64, chunk=64, dtype=1, segments=64, ws=P,
+               wsb=1 << 62) == H.HLA2_ERR_UNSUPPORTED
+    big = dict(ws=P, wsb=1 << 62)
+    assert bwd(L, B_=1 << 12, H_=1 << 12, n=64, **big) == H.HLA2_ERR_UNSUPPORTED
+    # the ratio's upstream-gradient preparation: one thread per 4 values of dout
+    assert bwd(L, B_=1 << 7, H_=1 << 7, n=1 << 14, norm=1, out=P, den=P, **big) == H.HLA2_ERR_UNSUPPORTED
+    assert ahla(L, B_=1 << 13, H_=1 << 10, n=64, **big) == H.HLA2_ERR_UNSUPPORTED
