@@ -69,7 +69,8 @@ long hla2_oracle_summary_len(int d, int dv) { return 1 + hla2_oracle_state_len(d
 /* ---------------------------------------------------------------------------
  * One streaming step [SUM §1; ABS: constant-size state, per-token update].
  * state (in/out) is the layout above; q[d], k[d], v[dv] are token t.
- * Writes num[dv] and *den for token t.
+ * Writes num[dv] and *den for token t; with num == NULL only the state is
+ * updated (the readout does not touch it).
  * Order: the cross summaries use C_{t-1}, m_{t-1}; then S, C, m take token t;
  * then the readout uses the updated state.
  * ------------------------------------------------------------------------- */
@@ -103,6 +104,10 @@ void hla2_oracle_step(int d, int dv, double gamma, double *state,
     for (c = 0; c < dv; ++c) C[(long)a * dv + c] = gamma * C[(long)a * dv + c] + q[a] * v[c];
     m[a] = gamma * m[a] + q[a];
   }
+  if (!num) {
+    free(kC);
+    return;
+  }
   /* readout: p = S^T q (S is symmetric), num = p^T C - q^T G, den = p.m - q.h */
   double *p = (double *)calloc((size_t)d, sizeof(double));
   for (a = 0; a < d; ++a)
@@ -123,7 +128,8 @@ void hla2_oracle_step(int d, int dv, double gamma, double *state,
  * Serial recurrence over a whole sequence (one head).
  * state: nullable.  If given, it is the state before token 0 and receives the
  * state after token n-1; if NULL the run starts from the all-zero state.
- * num: n*dv, den: n (nullable).
+ * num: n*dv, den: n (nullable).  num == NULL skips the readouts (den is then
+ * ignored): only the state advances, as when a prefix is absorbed.
  * ------------------------------------------------------------------------- */
 int hla2_oracle_serial(int n, int d, int dv, double gamma,
                        const double *q, const double *k, const double *v,
@@ -135,7 +141,7 @@ int hla2_oracle_serial(int n, int d, int dv, double gamma,
   int t;
   for (t = 0; t < n; ++t)
     hla2_oracle_step(d, dv, gamma, st, q + (long)t * d, k + (long)t * d, v + (long)t * dv,
-                     num + (long)t * dv, den ? den + t : &dummy);
+                     num ? num + (long)t * dv : NULL, den ? den + t : &dummy);
   if (!state) free(st);
   return 0;
 }

@@ -155,11 +155,13 @@ def _run_heads(fn, count: int, threads: int | None):
         list(ex.map(fn, range(count)))
 
 
-def serial(q, k, v, gamma: float = 1.0, state=None, threads: int | None = None, lib=None):
+def serial(q, k, v, gamma: float = 1.0, state=None, threads: int | None = None, lib=None, outputs: bool = True):
     """Serial recurrence over every head.
 
     q, k: [..., n, d]; v: [..., n, dv]; state: optional [..., state_len] initial
     state.  Returns (num [..., n, dv], den [..., n], final_state [..., state_len]).
+    With outputs=False the readouts are skipped and only final_state is
+    returned (the same state, bit for bit: the readout does not touch it).
     """
     lib = lib or _load()
     q, k, v = _f64(q), _f64(k), _f64(v)
@@ -170,6 +172,14 @@ def serial(q, k, v, gamma: float = 1.0, state=None, threads: int | None = None, 
     qh, kh, vh = q.reshape(H, n, d), k.reshape(H, n, d), v.reshape(H, n, dv)
     L = state_len(d, dv, lib)
     st = np.zeros((H, L)) if state is None else _f64(state).reshape(H, L).copy()
+    if not outputs:
+        def only_state(h):
+            rc = lib.hla2_oracle_serial(n, d, dv, float(gamma), _p(qh[h]), _p(kh[h]), _p(vh[h]), None, None,
+                                        _p(st[h]))
+            assert rc == 0
+
+        _run_heads(only_state, H, threads)
+        return st.reshape(*lead, L)
     num = np.empty((H, n, dv))
     den = np.empty((H, n))
 

@@ -267,3 +267,18 @@ def test_unorm_matches_state_and_serial():
     assert un[-1] == pytest.approx(np.linalg.norm(u), rel=1e-13)
     # den_t = q_t . u_t, so |den_t| <= |q_t| |u_t|
     assert np.all(np.abs(den) <= np.linalg.norm(q, axis=1) * un * (1 + 1e-12))
+
+
+def test_state_only_run_equals_serial_state():
+    # skipping the readouts (a prefix absorbed into the state) leaves the state bit for bit as the
+    # full serial run's, which the matrix form and the decode continuation pin; multi-head, from a
+    # given state too
+    r = _rng(41)
+    q, k, v = r.standard_normal((3, 26, 5)), r.standard_normal((3, 26, 5)), r.standard_normal((3, 26, 4))
+    for g in (1.0, 0.9):
+        _, _, st = O.serial(q, k, v, g)
+        only = O.serial(q, k, v, g, outputs=False)
+        np.testing.assert_array_equal(only, st)
+        _, _, st_a = O.serial(q[:, :11], k[:, :11], v[:, :11], g)
+        _, _, full = O.serial(q[:, 11:], k[:, 11:], v[:, 11:], g, state=st_a)
+        np.testing.assert_array_equal(O.serial(q[:, 11:], k[:, 11:], v[:, 11:], g, state=st_a, outputs=False), full)
