@@ -28,3 +28,10 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_sessionfinish(session, exitstatus):
+    out = os.environ.get("HLA2_PARITY_DIR")
+    if out:
+        from tests import parity
+        parity.write_records(out)

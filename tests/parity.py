@@ -25,6 +25,9 @@ that changes sign and num_t / den_t amplifies rounding without bound where
 """
 from __future__ import annotations
 
+import json
+import os
+
 import numpy as np
 
 TOL_F32 = 1e-4
@@ -74,3 +77,82 @@ def ratio_ok(rep, tol, subset=False) -> bool:
     if subset:
         ok = ok and rep["ratio_well"] <= tol
     return ok
+
+
+def per_row_rel_l2(x, ref, axes):
+    """rel-L2 of every leading index, reducing over `axes` (e.g. per head)."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    num = np.sqrt(np.sum((x - ref) ** 2, axis=axes))
+    nr = np.sqrt(np.sum(ref ** 2, axis=axes))
+    return num / np.where(nr > 0, nr, 1.0)
+
+
+def segment_bounds(n: int, nseg: int, lead_chunks: int, seg_chunks: int, kc: int = 64):
+    """Token ranges [t0, t1) of the segments of a forward plan (segment 0 holds lead_chunks
+    chunks of kc tokens, every later one seg_chunks, the last possibly fewer)."""
+    out, t0 = [], 0
+    for s in range(nseg):
+        c = lead_chunks if s == 0 else seg_chunks
+        t1 = min(n, t0 + c * kc)
+        out.append((t0, t1))
+        t0 = t1
+    assert t0 == n, (n, nseg, lead_chunks, seg_chunks)
+    return out
+
+
+# Parity figures of the workload-size tests, written at the end of the session to
+# $HLA2_PARITY_DIR (parity_workloads.json and .md) when that variable is set.
+RECORDS: dict = {}
+
+
+def record(name: str, **figures):
+    RECORDS[name] = figures
+
+
+def write_records(path_dir: str):
+    if not RECORDS:
+        return
+    os.makedirs(path_dir, exist_ok=True)
+    with open(os.path.join(path_dir, "parity_workloads.json"), "w") as f:
+        json.dump(RECORDS, f, indent=1, sort_keys=True)
+    keys = ["heads", "tokens", "num", "num_head_max", "num_seg_max", "den", "den_head_max", "den_seg_max",
+            "e_rms", "e_rms_head_max", "e_max", "ratio_well", "ratio_well_head_max", "excluded", "state",
+            "state_head_max"]
+    lines = ["| test | " + " | ".join(keys) + " |", "|---|" + "---|" * len(keys)]
+
+    def fmt(x):
+        if x is None:
+            return "-"
+        if isinstance(x, (int, np.integer)):
+            return str(int(x))
+        return "%.3g" % x
+    for name in sorted(RECORDS):
+        r = RECORDS[name]
+        lines.append("| %s | " % name + " | ".join(fmt(r.get(k)) for k in keys) + " |")
+    with open(os.path.join(path_dir, "parity_workloads.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def ratio_per_head(o_gpu, num_ref, den_ref, unorm_ref, q, head_axes=2):
+    """Per-head figures of the ratio criterion: e_rms and e_max over each head's tokens, and the
+    rel-L2 of o over each head's well-conditioned tokens (shape: the leading head axes)."""
+    q = np.asarray(q, dtype=np.float64)
+    o_gpu = np.asarray(o_gpu, dtype=np.float64)
+    well = well_conditioned(den_ref, unorm_ref, q)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        o_ref = num_ref / den_ref[..., None]
+        e = (np.linalg.norm(o_gpu - o_ref, axis=-1) * np.abs(den_ref)
+             / (np.linalg.norm(num_ref, axis=-1) + np.linalg.norm(o_ref, axis=-1) * np.linalg.norm(q, axis=-1)
+                * unorm_ref))
+    e = np.where(np.isfinite(e), e, np.inf)
+    tok_axes = tuple(range(head_axes, e.ndim))
+    e_rms = np.sqrt(np.mean(e ** 2, axis=tok_axes))
+    e_max = np.max(e, axis=tok_axes)
+    diff = np.where(well[..., None], o_gpu - o_ref, 0.0)
+    ref = np.where(well[..., None], o_ref, 0.0)
+    all_axes = tuple(range(head_axes, diff.ndim))
+    nr = np.sqrt(np.sum(ref ** 2, axis=all_axes))
+    well_head = np.sqrt(np.sum(diff ** 2, axis=all_axes)) / np.where(nr > 0, nr, 1.0)
+    return {"e_rms": e_rms, "e_max": e_max, "ratio_well": well_head,
+            "excluded": 1.0 - np.mean(well, axis=tok_axes)}
