@@ -129,10 +129,33 @@ def load_traffic(key):
     return ent.get("bytes_per_call")
 
 
-def time_calls(fn, steps, warmup, torch):
+# Untimed calls before each timed region run for at least this long (whatever --warmup says):
+# after the host-side input generation the device idles and its clocks drop, and a few
+# warm-up calls do not bring them back (5 warm-up and 20 timed forward calls read about 25%
+# slower than steady clocks).  Set with --min-warm-ms.
+MIN_WARM_S = 0.5
+
+
+def warm(fn, warmup, torch, min_seconds=None):
+    """`warmup` untimed calls, then more in batches of 10 until `min_seconds` of wall time
+    have passed.  Returns the number of untimed calls made."""
+    min_seconds = MIN_WARM_S if min_seconds is None else min_seconds
+    t0 = time.perf_counter()
+    calls = 0
     for _ in range(warmup):
         fn()
+        calls += 1
     torch.cuda.synchronize()
+    while time.perf_counter() - t0 < min_seconds:
+        for _ in range(10):
+            fn()
+        calls += 10
+        torch.cuda.synchronize()
+    return calls
+
+
+def time_calls(fn, steps, warmup, torch):
+    warm(fn, warmup, torch)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     start.record()
@@ -171,8 +194,7 @@ def bench_forward(w, steps, warmup, torch, H, I):
         H.hla2_forward(q, k, v, out, decay=w.decay, normalize=w.normalize, chunk=w.chunk, workspace=ws,
                        events=row)
 
-    for _ in range(warmup):
-        fn()
+    warm_calls = warm(fn, warmup, torch)
     t, wall = time_calls(fn, steps, 0, torch)
     time_calls(fn_timed, steps, 0, torch)
     plan = H.hla2_forward_plan(w.B, w.H, w.n, w.d, w.dv, w.chunk)
@@ -190,6 +212,7 @@ def bench_forward(w, steps, warmup, torch, H, I):
     return {
         "seconds": t,
         "wall": wall,
+        "warm_calls": warm_calls,
         "phases": phases,
         "plan": {"segments": nseg, "lead_chunks": plan[1], "seg_chunks": plan[2], "lead": plan[3]},
         "output_flops_per_call": output_kernel_flops_per_head_token(w.d, w.dv, w.chunk, w.normalize)
@@ -308,13 +331,25 @@ def bench_variant(fn_name, w, steps, warmup, torch, H, I, flops_per_head_token):
             "tflops": fl / t / 1e12, "mfma_frac": fl / t / PEAK_BF16_MFMA, "flops_per_head_token": flops_per_head_token}
 
 
+def cpu_single_thread(w, I):
+    """The fp64 oracle (as it stands) on one host thread over every head of a (small) workload."""
+    from oracle import oracle as O
+    q, k, v = (x.double().numpy() for x in I.make_qkv(w))
+    t0 = time.perf_counter()
+    O.serial(q, k, v, w.decay, threads=1)
+    dt = time.perf_counter() - t0
+    return {"workload": w.name, "value": w.B * w.n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": "all %d heads of %d tokens, fp64 serial recurrence on 1 thread, %.2f s wall"
+                      % (w.B * w.H, w.n, dt)}
+
+
 def cpu_baseline(w, heads_sample, I):
     """The fp64 oracle (as it stands) on a bounded sample of the workload's
     heads: the serial recurrence, threaded over heads."""
     from oracle import oracle as O
     q, k, v = I.make_qkv(w)
     q, k, v = (x.reshape(w.B * w.H, w.n, -1)[:heads_sample].double().numpy() for x in (q, k, v))
-    threads = O.default_threads()
+    threads = min(O.default_threads(), 16)  # the host share of one GPU
     t0 = time.perf_counter()
     O.serial(q, k, v, w.decay, threads=threads)
     dt = time.perf_counter() - t0
@@ -343,6 +378,7 @@ def copy_calibration(torch, gib=1):
 
 
 def main(argv=None):
+    global MIN_WARM_S
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     # defaults reach steady clocks: 50 untimed steps, then 200 timed ones (about 70 ms of forward work)
@@ -358,7 +394,10 @@ def main(argv=None):
                     help="skip the other forward workloads (normalised 2k, long 64k)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="finish with two 1 GiB device copies (reference for HBM byte counters)")
+    ap.add_argument("--min-warm-ms", type=float, default=MIN_WARM_S * 1e3,
+                    help="untimed calls before each timed region last at least this long (0: only --warmup)")
     args = ap.parse_args(argv)
+    MIN_WARM_S = max(args.min_warm_ms, 0.0) / 1e3
 
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -381,6 +420,8 @@ def main(argv=None):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_calls": fw["warm_calls"],
+        "warmup_min_ms": MIN_WARM_S * 1e3,
         "ms_per_step": fw["seconds"] * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
@@ -452,6 +493,7 @@ def main(argv=None):
                                                 ho3_flops_per_head_token(w))
     if args.cpu_heads > 0:
         line["cpu_baseline"] = cpu_baseline(w, min(args.cpu_heads, w.B * w.H), I)
+        line["cpu_baseline"]["single_thread"] = cpu_single_thread(I.WORKLOADS["norm_2k"], I)
     if args.copy_calibration:
         copy_calibration(torch)
     print(json.dumps(line))
