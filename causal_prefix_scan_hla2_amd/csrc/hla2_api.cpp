@@ -175,11 +175,13 @@ BwdPlan make_bwd_plan(int B, int H, int n, int d, int dv, int dtype, int normali
   return b;
 }
 
-// Shared body of every forward entry point (arguments already validated).
 int run_forward(const void *q, const void *k, const void *v, void *out, int B, int H, int n, int d, int dv,
                 float decay, int normalize, int chunk, hla2_dtype_t dtype, float *den_out, float *state_out,
                 void *workspace, size_t workspace_bytes_given, int segments, hipEvent_t const *events,
-                hipStream_t stream);
+                hipStream_t stream) {
+  return hla2::forward_run(q, k, v, out, B, H, n, d, dv, decay, normalize, chunk, (int)dtype, den_out, state_out,
+                           workspace, workspace_bytes_given, segments, events, stream);
+}
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -604,31 +606,44 @@ int hla2_decode_step(float *state, const void *q, const void *k, const void *v, 
 
 }  // extern "C"
 
-namespace {
+namespace hla2 {
 
-int run_forward(const void *q, const void *k, const void *v, void *out, int B, int H, int n, int d, int dv,
-                float decay, int normalize, int chunk, hla2_dtype_t dtype, float *den_out, float *state_out,
-                void *workspace, size_t workspace_bytes_given, int segments, hipEvent_t const *events,
-                hipStream_t stream) {
+int forward_check(const void *q, const void *k, const void *v, const void *out, int B, int H, int n, int d, int dv,
+                  float decay, int normalize, int chunk, int dtype, const float *den_out, const float *state_out,
+                  int segments, size_t *need_out) {
   if (!q || !k || !v || !out) return HLA2_ERR_INVALID;
   if (segments < 0) return HLA2_ERR_INVALID;
   if (!(decay > 0.0f && decay <= 1.0f)) return HLA2_ERR_INVALID;  // also rejects NaN
   if (normalize != 0 && normalize != 1) return HLA2_ERR_INVALID;
-  int rc = check_shape(B, H, n, d, dv, chunk, (int)dtype);
+  int rc = check_shape(B, H, n, d, dv, chunk, dtype);
   if (rc != HLA2_OK) return rc;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return HLA2_ERR_INVALID;
   if (den_out && !aligned(den_out, 4)) return HLA2_ERR_INVALID;
   if (state_out && !aligned(state_out, 4)) return HLA2_ERR_INVALID;
   const bool state = state_out != nullptr;
-  const Plan p = make_plan(B, H, n, d, dv, chunk, (int)dtype, segments, 0, !state);
+  const Plan p = make_plan(B, H, n, d, dv, chunk, dtype, segments, 0, !state);
   if (!forward_grids_fit(p)) return HLA2_ERR_UNSUPPORTED;
-  const size_t need = workspace_bytes(p, state);
   // callers are held to the size the workspace query reports (the larger of the bf16 and
   // fp32 plans), whichever dtype this call uses
-  const size_t need_doc = forward_workspace(B, H, n, d, dv, chunk, segments, state);
-  if (need > 0 || need_doc > 0) {
-    if (!workspace || workspace_bytes_given < need_doc || workspace_bytes_given < need || !aligned(workspace, 256))
-      return HLA2_ERR_WORKSPACE;
+  const size_t need = workspace_bytes(p, state), need_doc = forward_workspace(B, H, n, d, dv, chunk, segments, state);
+  *need_out = need > need_doc ? need : need_doc;
+  return HLA2_OK;
+}
+
+int forward_run(const void *q, const void *k, const void *v, void *out, int B, int H, int n, int d, int dv,
+                float decay, int normalize, int chunk, int dtype_i, float *den_out, float *state_out,
+                void *workspace, size_t workspace_bytes_given, int segments, hipEvent_t const *events,
+                hipStream_t stream) {
+  const hla2_dtype_t dtype = (hla2_dtype_t)dtype_i;
+  size_t need_all = 0;
+  int rc = forward_check(q, k, v, out, B, H, n, d, dv, decay, normalize, chunk, dtype_i, den_out, state_out,
+                         segments, &need_all);
+  if (rc != HLA2_OK) return rc;
+  const bool state = state_out != nullptr;
+  const Plan p = make_plan(B, H, n, d, dv, chunk, (int)dtype, segments, 0, !state);
+  const size_t need = workspace_bytes(p, state);
+  if (need_all > 0) {
+    if (!workspace || workspace_bytes_given < need_all || !aligned(workspace, 256)) return HLA2_ERR_WORKSPACE;
   }
 
   hla2::WalkArgs a;
@@ -714,4 +729,4 @@ int run_forward(const void *q, const void *k, const void *v, void *out, int B, i
   return HLA2_OK;
 }
 
-}  // namespace
+}  // namespace hla2

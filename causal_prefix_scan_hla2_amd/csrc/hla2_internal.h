@@ -221,4 +221,15 @@ enum { HO3_SUMMARY = 0, HO3_SCAN = 1, HO3_OUTPUT = 2, HO3_LEAD = 3 };
 hipError_t launch_ho3(int dtype, int DK, int DV, bool norm, int phase, int BH, const Ho3Args &a, float gseg,
                       hipStream_t s);
 
+// The forward pass behind every forward entry point (hla2_api.cpp).  forward_check validates a
+// call on the host (everything but the workspace) and reports the workspace bytes it needs;
+// forward_run validates again and enqueues the kernels.  dtype is an hla2_dtype_t value.
+int forward_check(const void *q, const void *k, const void *v, const void *out, int B, int H, int n, int d, int dv,
+                  float decay, int normalize, int chunk, int dtype, const float *den_out, const float *state_out,
+                  int segments, size_t *need_out);
+int forward_run(const void *q, const void *k, const void *v, void *out, int B, int H, int n, int d, int dv,
+                float decay, int normalize, int chunk, int dtype, float *den_out, float *state_out,
+                void *workspace, size_t workspace_bytes_given, int segments, hipEvent_t const *events,
+                hipStream_t stream);
+
 }  // namespace hla2

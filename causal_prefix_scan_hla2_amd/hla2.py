@@ -23,7 +23,8 @@ EXPORTS = ("hla2_strerror", "hla2_abi_version", "hla2_forward_workspace_bytes", 
            "hla2_forward_timed", "hla2_decode_step", "hla2_state_floats", "hla2_forward_state_workspace_bytes",
            "hla2_forward_state", "hla2_backward_workspace_bytes", "hla2_backward",
            "hla2_ahla_forward_workspace_bytes", "hla2_ahla_forward", "hla2_ho3_forward_workspace_bytes",
-           "hla2_ho3_forward")
+           "hla2_ho3_forward", "hla2_forward_noalloc")
+HLA2_NOALLOC_SCRATCH_BYTES = 96 << 20  # the fixed workspace of hla2_forward_noalloc (include/hla2.h)
 
 _lock = threading.Lock()
 _lib = None
@@ -83,6 +84,8 @@ def lib():
             L.hla2_ho3_forward_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
             L.hla2_ho3_forward.restype = i
             L.hla2_ho3_forward.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, vp, sz, i, vp]
+            L.hla2_forward_noalloc.restype = i
+            L.hla2_forward_noalloc.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, vp]
             L.hla2_backward.restype = i
             L.hla2_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, i, vp]
             _lib = L
@@ -171,6 +174,22 @@ def hla2_forward(q, k, v, out, decay=1.0, normalize=False, chunk=64, den_out=Non
         rc = lib().hla2_forward(*args, _stream(stream))
     if check and rc != HLA2_OK:
         raise HLA2Error(rc, "hla2_forward")
+    return rc
+
+
+def hla2_forward_noalloc(q, k, v, out, decay=1.0, normalize=False, chunk=64, den_out=None, stream=None,
+                         check=True) -> int:
+    """Call the C forward pass that uses the library's fixed device workspace (no allocation here
+    or in the library).  Same tensors and results as hla2_forward."""
+    B, H, n, d = q.shape
+    dv = v.shape[-1]
+    for t in (q, k, v, out):
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    rc = lib().hla2_forward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, n, d, dv, float(decay),
+                                    int(bool(normalize)), int(chunk), _dtype_code(q), _ptr(den_out), _stream(stream))
+    if check and rc != HLA2_OK:
+        raise HLA2Error(rc, "hla2_forward_noalloc")
     return rc
 
 

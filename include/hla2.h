@@ -304,6 +304,32 @@ int hla2_ho3_forward(const void *q, const void *k, const void *v, void *out,
                      hla2_dtype_t dtype, float *den_out, void *workspace, size_t workspace_bytes,
                      int segments, hipStream_t stream);
 
+/*
+ * hla2_forward for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * caller passes inputs and outputs only; the workspace hla2_forward would take
+ * (segment summaries and prefixes) is a fixed device array the library holds,
+ * HLA2_NOALLOC_SCRATCH_BYTES (96 MiB) on each device it runs on, from the
+ * first call on that device until the process ends.  The call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine).
+ *   Arguments, layouts, results and errors as for hla2_forward, and
+ *   HLA2_ERR_UNSUPPORTED when hla2_forward_workspace_bytes(...) for the shape
+ *   exceeds HLA2_NOALLOC_SCRATCH_BYTES (96 MiB holds the workspace of, e.g.,
+ *   8 x 16 heads of 8192 tokens at d = 64, dv = 128, or 16 heads of 65536
+ *   tokens at d = dv = 128); HLA2_ERR_LAUNCH when the array's device address
+ *   cannot be obtained.
+ *   The array's contents on entry are ignored (every byte the call reads it
+ *   writes first), so nothing has to be cleared between calls.
+ *   Every call on one device shares that device's array: calls that overlap on
+ *   one device (different streams, threads or processes' graphs without
+ *   ordering) race on it and give wrong results.  Order them (one stream, or
+ *   events).
+ */
+#define HLA2_NOALLOC_SCRATCH_BYTES (96u << 20)
+int hla2_forward_noalloc(const void *q, const void *k, const void *v, void *out,
+                         int B, int H, int n, int d, int dv, float decay, int normalize, int chunk,
+                         hla2_dtype_t dtype, float *den_out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

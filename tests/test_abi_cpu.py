@@ -347,3 +347,25 @@ def test_grids_beyond_2_32_work_items_rejected(L):
     # the ratio's upstream-gradient preparation: one thread per 4 values of dout
     assert bwd(L, B_=1 << 7, H_=1 << 7, n=1 << 14, norm=1, out=P, den=P, **big) == H.HLA2_ERR_UNSUPPORTED
     assert ahla(L, B_=1 << 13, H_=1 << 10, n=64, **big) == H.HLA2_ERR_UNSUPPORTED
+
+
+def test_noalloc_validates_on_the_host(L):
+    """The no-allocation forward rejects bad calls, and workspaces beyond its fixed array, before any
+    device call (no kernel runs here)."""
+    def na(**kw):
+        b = dict(q=P, k=P, v=P, out=P, B_=1, H_=1, n=64, d=64, dv=64, decay=1.0, norm=0, chunk=64, dtype=1, den=None)
+        b.update(kw)
+        return L.hla2_forward_noalloc(b["q"], b["k"], b["v"], b["out"], b["B_"], b["H_"], b["n"], b["d"], b["dv"],
+                                      b["decay"], b["norm"], b["chunk"], b["dtype"], b["den"], None)
+    assert na(q=None) == H.HLA2_ERR_INVALID
+    assert na(decay=0.0) == H.HLA2_ERR_INVALID
+    assert na(norm=2) == H.HLA2_ERR_INVALID
+    assert na(d=24) == H.HLA2_ERR_UNSUPPORTED
+    assert na(k=ctypes.c_void_p(4098)) == H.HLA2_ERR_INVALID
+    assert na(den=ctypes.c_void_p(4098)) == H.HLA2_ERR_INVALID
+    # 255 heads of 65536 tokens at d = dv = 128 (two segments each) need more than the fixed array holds
+    assert H.hla2_forward_workspace_bytes(1, 255, 65536, 128, 128, 128) > H.HLA2_NOALLOC_SCRATCH_BYTES
+    assert na(B_=1, H_=255, n=65536, d=128, dv=128, chunk=128) == H.HLA2_ERR_UNSUPPORTED
+    # the benchmark's forward workloads fit
+    for shape in [(8, 16, 8192, 64, 128, 64), (4, 8, 2048, 64, 64, 64), (1, 16, 65536, 128, 128, 128)]:
+        assert H.hla2_forward_workspace_bytes(*shape) <= H.HLA2_NOALLOC_SCRATCH_BYTES
