@@ -438,7 +438,7 @@ def main(argv=None):
         "kernel_ms": {key: val * 1e3 for key, val in fw["phases"].items()},
         "roofline": dict(
             roofline(fw["output_flops_per_call"], fw["output_bytes_per_call"], fw["phases"]["output"]),
-            kernel="walk3_kernel<%d,%d,out,decay=%d,den=%d> (chunk outputs%s)" % (
+            kernel="walk8_kernel<%d,%d,out,decay=%d,den=%d> (chunk outputs%s)" % (
                 64 if w.d <= 64 else 128, 64 if w.dv <= 64 else 128, int(w.decay < 1), int(w.normalize),
                 " of segments 1 .. %d" % (fw["segments"] - 1) if fw["plan"]["lead"] else ""),
             traffic=load_traffic("output_" + w.name),

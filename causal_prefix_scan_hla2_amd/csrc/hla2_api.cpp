@@ -54,7 +54,7 @@ Plan make_plan(int B, int H, int n, int d, int dv, int chunk, int dtype, int seg
     p.DK = d <= 64 ? 64 : 128;
     p.DV = dv <= 64 ? 64 : 128;
     p.CP = p.kc = 64;
-    gpc = hla2::walk3_groups_per_cu(p.DK, p.DV, true);
+    gpc = hla2::walk8_groups_per_cu();
   } else {
     const int m = d > dv ? d : dv;
     p.DK = p.DV = m <= 16 ? 16 : 64;

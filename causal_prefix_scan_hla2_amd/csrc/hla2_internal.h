@@ -79,23 +79,21 @@ __host__ __device__ constexpr int walk_waves_per_eu(int esize, int DK, int DV, i
   return w < 1 ? 1 : (w > 2 ? 2 : w);
 }
 
-// The bf16 walker (hla2_walk3.h): 64-token chunks, 4 waves.  LDS bytes of an
-// instantiation: Q, K, V, Z~ and bf16 S0 rows, plus Z and W rows in output
-// mode, each row padded (16 or 32 bytes); then the decay table, den and u0.
-__host__ __device__ constexpr int walk3_lds_bytes(int DK, int DV, bool out) {
+// The 8-wave bf16 walker (hla2_walk8.h): 64-token chunks.  LDS elements (bf16) of an
+// instantiation: two Q buffers in output mode (one in summary mode), K, V, Z~ and bf16 S0 rows,
+// plus Z and W rows in output mode (and at d <= 64 the staged output rows), each row padded; then
+// (bytes) u0 twice, the decay table and
+// the two halves' den parts.  One workgroup per CU (eight waves, two per SIMD).
+__host__ __device__ constexpr int walk8_lds_elems(int DK, int DV, bool out) {
   const int CP = 64, ldk = DK + 16, ldq = out ? DK + 8 : DK + 16, ldt = DK + 16, lds0 = DK + 16, ldz = DK + 16;
   const int ldv = DV + 16, ldw = CP + 16;
-  const int elems = CP * ldq + CP * ldk + CP * ldt + CP * ldv + DK * lds0 + (out ? CP * ldz + CP * ldw : 0);
-  return elems * 2 + (2 * CP + 1 + CP + 2 * DK) * 4;
+  return (out ? 2 : 1) * CP * ldq + CP * ldk + CP * ldv + CP * ldt + DK * lds0 + (out ? CP * ldz + CP * ldw : 0) +
+         (out && DK <= 64 ? CP * (DV + 8) : 0);
 }
-__host__ __device__ constexpr int walk3_groups_per_cu(int DK, int DV, bool out) {
-  const int by_lds = (160 * 1024) / walk3_lds_bytes(DK, DV, out);
-  return by_lds < 1 ? 1 : (by_lds > 2 ? 2 : by_lds);
+__host__ __device__ constexpr int walk8_lds_bytes(int DK, int DV, bool out) {
+  return walk8_lds_elems(DK, DV, out) * 2 + 2 * DK * 4 + (2 * 64 + 4) * 4 + 2 * 64 * 4;
 }
-// each 4-wave group puts one wave on every SIMD
-__host__ __device__ constexpr int walk3_waves_per_eu(int DK, int DV, bool out) {
-  return walk3_groups_per_cu(DK, DV, out);
-}
+constexpr int walk8_groups_per_cu() { return 1; }
 
 // dtype: 0 = f32, 1 = bf16.  Returns hipErrorInvalidValue when no kernel exists
 // for (dtype, DK, DV, CP).
@@ -103,14 +101,14 @@ hipError_t launch_walk(int dtype, int DK, int DV, int CP, bool output_mode, dim3
                        const WalkArgs &a, hipStream_t s);
 hipError_t launch_walk_f32(int DK, int DV, int CP, bool output_mode, dim3 grid, const WalkArgs &a,
                            hipStream_t s);
-hipError_t launch_walk3_dk64(int DV, bool output_mode, bool decay, bool den, dim3 grid, const WalkArgs &a,
+hipError_t launch_walk8_dk64(int DV, bool output_mode, bool decay, bool den, dim3 grid, const WalkArgs &a,
                              hipStream_t s);
 // The lead launch of the bf16 forward: workgroups 0 .. nbh-1 walk segment 0 in output mode and
 // write the state after it as the prefix of segment 1; the rest summarise segments 1 .. nsum-1.
 hipError_t launch_walk_lead(int DK, int DV, dim3 grid, const WalkArgs &a, hipStream_t s);
-hipError_t launch_walk3_lead_dk64(int DV, bool decay, bool den, dim3 grid, const WalkArgs &a, hipStream_t s);
-hipError_t launch_walk3_lead_dk128(int DV, bool decay, bool den, dim3 grid, const WalkArgs &a, hipStream_t s);
-hipError_t launch_walk3_dk128(int DV, bool output_mode, bool decay, bool den, dim3 grid, const WalkArgs &a,
+hipError_t launch_walk8_lead_dk64(int DV, bool decay, bool den, dim3 grid, const WalkArgs &a, hipStream_t s);
+hipError_t launch_walk8_lead_dk128(int DV, bool decay, bool den, dim3 grid, const WalkArgs &a, hipStream_t s);
+hipError_t launch_walk8_dk128(int DV, bool output_mode, bool decay, bool den, dim3 grid, const WalkArgs &a,
                               hipStream_t s);
 hipError_t launch_scan(int dtype, int DK, int DV, int BH, const ScanArgs &a, hipStream_t s);
 

@@ -258,8 +258,8 @@ hipError_t launch_scan(int dtype, int DK, int DV, int BH, const ScanArgs &a, hip
 hipError_t launch_walk_lead(int DK, int DV, dim3 grid, const WalkArgs &a, hipStream_t s) {
   const bool dec = a.decay_on != 0, den = a.need_den != 0;
   if (a.nseg < 2 || a.sum_all || a.nbh < 1 || !a.prefix_out) return hipErrorInvalidValue;
-  if (DK == 64) return launch_walk3_lead_dk64(DV, dec, den, grid, a, s);
-  if (DK == 128) return launch_walk3_lead_dk128(DV, dec, den, grid, a, s);
+  if (DK == 64) return launch_walk8_lead_dk64(DV, dec, den, grid, a, s);
+  if (DK == 128) return launch_walk8_lead_dk128(DV, dec, den, grid, a, s);
   return hipErrorInvalidValue;
 }
 
@@ -268,8 +268,8 @@ hipError_t launch_walk(int dtype, int DK, int DV, int CP, bool output_mode, dim3
   if (dtype == 0) return launch_walk_f32(DK, DV, CP, output_mode, grid, a, s);
   if (CP != 64) return hipErrorInvalidValue;
   const bool dec = a.decay_on != 0, den = a.need_den != 0;
-  if (DK == 64) return launch_walk3_dk64(DV, output_mode, dec, den, grid, a, s);
-  if (DK == 128) return launch_walk3_dk128(DV, output_mode, dec, den, grid, a, s);
+  if (DK == 64) return launch_walk8_dk64(DV, output_mode, dec, den, grid, a, s);
+  if (DK == 128) return launch_walk8_dk128(DV, output_mode, dec, den, grid, a, s);
   return hipErrorInvalidValue;
 }
 
