@@ -37,7 +37,8 @@ __host__ __device__ inline int walk_seg_chunks(const WalkArgs &a, int s) { retur
 
 // Arguments of the segment-level exclusive scan.
 struct ScanArgs {
-  const float *sums;  // [BH, nsum] summary blocks (the first nseg-1 are scanned)
+  float *sums;        // [BH, nsum] summary blocks (the first nseg-1 are scanned; the parallel
+                      // form overwrites U and u of the scanned blocks with its cross terms)
   int nsum;
   float *prefix;      // [BH, nseg] prefix blocks
   int nseg;

@@ -229,6 +229,142 @@ __global__ void __launch_bounds__(64 * (DK / 16)) scan_bf16_kernel(ScanArgs a) {
   store(steps);
 }
 
+// ---------------------------------------------------------------------------------------------
+// Parallel form of the same exclusive scan (bf16 path, forward plans).  With every folded segment
+// of the same length (factor G), the prefix recurrences separate:
+//   S0_{r+1} = G S0_r + S_r                       a decayed prefix sum of the S summaries;
+//   U0_{r+1} = G^2 U0_r + T_r,  T_r = U_r + G S0_r C_r   (u likewise with m_r)
+// so the cross products S0_r C_r, which carry all the arithmetic, are independent once every
+// S0_r is known.  Three launches of constant depth replace the chain of steps:
+//   scan_s_kernel     the S0 prefix sums (elementwise over r),
+//   scan_t_kernel     every T_r, t_r at once (bf16 MFMA, as the fold), written over U_r, u_r in
+//                     the summary blocks (which nothing reads afterwards),
+//   scan_u_kernel     the U0, u0 prefix sums (elementwise over r).
+// The steps fold summaries r0 .. steps-1 (r0 = first), and write prefixes r0+1 .. steps (and the
+// zero prefix 0 when r0 = 0).
+constexpr int SCAN_ELEM_THREADS = 256;
+
+// S0 prefix: thread x owns one f32x4 of S (d x d) of one head.
+template <int DK, int DV>
+__global__ void __launch_bounds__(SCAN_ELEM_THREADS) scan_s_kernel(ScanArgs a) {
+  const long SB = sum_block_floats(DK, DV), PB = prefix_block_floats(DK, DV);
+  const int bh = blockIdx.x, e = 4 * (blockIdx.y * SCAN_ELEM_THREADS + threadIdx.x);
+  if (e >= DK * DK) return;
+  const float G = a.gamma_seg;
+  const int r0 = a.first, steps = a.nseg - 1;
+  float *pref = a.prefix + (long)bh * a.nseg * PB;
+  const float *sums = a.sums + (long)bh * a.nsum * SB;
+  f32x4 s0 = r0 > 0 ? *(const f32x4 *)(pref + r0 * PB + e) : zero4();
+  if (r0 == 0) *(f32x4 *)(pref + e) = s0;
+  for (int r = r0; r < steps; r += 8) {
+    f32x4 x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = r + j < steps ? *(const f32x4 *)(sums + (r + j) * SB + e) : zero4();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (r + j < steps) {
+        s0 = G * s0 + x[j];
+        *(f32x4 *)(pref + (r + j + 1) * PB + e) = s0;
+      }
+    }
+  }
+}
+
+// U0 and u0 prefix: thread x owns one f32x4 of U (d x dv) or of u (d) of one head.
+template <int DK, int DV>
+__global__ void __launch_bounds__(SCAN_ELEM_THREADS) scan_u_kernel(ScanArgs a) {
+  const long SB = sum_block_floats(DK, DV), PB = prefix_block_floats(DK, DV);
+  const int bh = blockIdx.x, e = 4 * (blockIdx.y * SCAN_ELEM_THREADS + threadIdx.x);
+  if (e >= DK * DV + DK) return;
+  const float G2 = a.gamma_seg * a.gamma_seg;
+  const int r0 = a.first, steps = a.nseg - 1;
+  // U0 | u0 are contiguous in a prefix block; in a summary block T (over U) is followed by m, then t
+  const int po = DK * DK + e, so = e < DK * DV ? DK * DK + DK * DV + e : DK * DK + 2 * DK * DV + DK + (e - DK * DV);
+  float *pref = a.prefix + (long)bh * a.nseg * PB;
+  const float *sums = a.sums + (long)bh * a.nsum * SB;
+  f32x4 u0 = r0 > 0 ? *(const f32x4 *)(pref + r0 * PB + po) : zero4();
+  if (r0 == 0) *(f32x4 *)(pref + po) = u0;
+  for (int r = r0; r < steps; r += 8) {
+    f32x4 x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = r + j < steps ? *(const f32x4 *)(sums + (r + j) * SB + so) : zero4();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (r + j < steps) {
+        u0 = G2 * u0 + x[j];
+        *(f32x4 *)(pref + (r + j + 1) * PB + po) = u0;
+      }
+    }
+  }
+}
+
+// T_r = U_r + G S0_r C_r (and t_r = u_r + G S0_r m_r) for one folded summary r (blockIdx.y, from
+// r0) and one group of value columns (blockIdx.z; the last group also t_r); one wave per 16-row
+// tile of S0, C_r's columns staged in LDS as bf16.
+template <int DK, int DV>
+__global__ void __launch_bounds__(64 * (DK / 16)) scan_t_kernel(ScanArgs a) {
+  constexpr int NT = 64 * (DK / 16);
+  constexpr int NJ = DK / 16;
+  constexpr int NG = scan_groups(DK);
+  constexpr int HC = DV / NG, CT = HC / 16, LDC = HC + 16;
+  constexpr int NC4 = DK * HC / 4 / NT;
+  static_assert(NC4 * 4 * NT == DK * HC, "C staging split");
+  const long SB = sum_block_floats(DK, DV), PB = prefix_block_floats(DK, DV);
+  const int bh = blockIdx.x, r = a.first + blockIdx.y, grp = blockIdx.z, c0 = grp * HC;
+  const bool has_u = grp == NG - 1;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const float G = a.gamma_seg;
+  __shared__ __attribute__((aligned(16))) bf16 Cb[DK * LDC];
+  float *sb = a.sums + ((long)bh * a.nsum + r) * SB;
+  const float *sC = sb + DK * DK, *sm = sC + 2 * DK * DV;
+  float *sU = sb + DK * DK + DK * DV, *su = sU + DK * DV + DK;
+  const float *pS = a.prefix + ((long)bh * a.nseg + r) * PB;
+  // C_r's columns (and m_r in column HC of the last group; zeros elsewhere) into LDS
+#pragma unroll
+  for (int i = 0; i < NC4; ++i) {
+    const int e = 4 * (tid + i * NT), row = e / HC, col = e % HC;
+    st4(Cb + row * LDC + col, *(const f32x4 *)(sC + row * DV + c0 + col));
+  }
+  for (int x = tid; x < DK * 16; x += NT) {
+    const int row = x / 16, col = x % 16;
+    Cb[row * LDC + HC + col] = (bf16)((has_u && col == 0) ? sm[row] : 0.f);
+  }
+  // the wave's rows of S0_r as bf16 A fragments, and its tiles of U_r (u_r)
+  bf16x8 af[DK / 32];
+#pragma unroll
+  for (int s = 0; s < DK / 32; ++s) {
+    const f32x4 lo = *(const f32x4 *)(pS + (16 * w + n) * DK + 32 * s + 4 * g);
+    const f32x4 hi = *(const f32x4 *)(pS + (16 * w + n) * DK + 32 * s + 16 + 4 * g);
+    af[s] = frag_from_acc(lo, hi);
+  }
+  f32x4 ur[CT + 1];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ur[ct][q] = sU[(16 * w + 4 * g + q) * DV + c0 + 16 * ct + n];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) ur[CT][q] = (has_u && n == 0) ? su[16 * w + 4 * g + q] : 0.f;
+  __syncthreads();  // C_r staged
+#pragma unroll
+  for (int ct = 0; ct <= CT; ++ct) {
+    f32x4 mm = zero4();
+#pragma unroll
+    for (int s = 0; s < DK / 32; ++s) mm = mma(af[s], ld_cols(Cb, LDC, 32 * s, 16 * ct, lane), mm);
+    ur[ct] = ur[ct] + G * mm;
+  }
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) sU[(16 * w + 4 * g + q) * DV + c0 + 16 * ct + n] = ur[ct][q];
+  if (has_u && n == 0) *(f32x4 *)(su + 16 * w + 4 * g) = ur[CT];
+}
+
+// The parallel form takes the forward plans with at least this many folded summaries; shorter
+// scans (and the backward's split prefix) keep the fold.  Measured: 15 folds at d = dv = 128, 65 ->
+// 30 us; 6 folds at d = dv = 64, the fold is faster than the three launches.
+constexpr int SCAN_PAR_MIN_STEPS = 8;
+
 template <int DK, int DV>
 static hipError_t launch_scan_t(int BH, bool bf, const ScanArgs &a, hipStream_t s) {
   if (a.first != 0 && !(bf && DK >= 64)) return hipErrorInvalidValue;  // only the bf16 fold takes a given prefix
@@ -237,6 +373,15 @@ static hipError_t launch_scan_t(int BH, bool bf, const ScanArgs &a, hipStream_t 
   if (a.pshift < 0 || a.pshift > a.pmin) return hipErrorInvalidValue;
   if constexpr (DK >= 64) {
     if (bf) {
+      const int folds = a.nseg - 1 - a.first;
+      if (folds >= SCAN_PAR_MIN_STEPS && a.pnseg == 0 && a.pmin == 0 && a.pshift == 0) {
+        const int nbs = (DK * DK / 4 + SCAN_ELEM_THREADS - 1) / SCAN_ELEM_THREADS;
+        const int nbu = ((DK * DV + DK) / 4 + SCAN_ELEM_THREADS - 1) / SCAN_ELEM_THREADS;
+        hipLaunchKernelGGL((scan_s_kernel<DK, DV>), dim3(BH, nbs), dim3(SCAN_ELEM_THREADS), 0, s, a);
+        hipLaunchKernelGGL((scan_t_kernel<DK, DV>), dim3(BH, folds, scan_groups(DK)), dim3(64 * (DK / 16)), 0, s, a);
+        hipLaunchKernelGGL((scan_u_kernel<DK, DV>), dim3(BH, nbu), dim3(SCAN_ELEM_THREADS), 0, s, a);
+        return hipGetLastError();
+      }
       hipLaunchKernelGGL((scan_bf16_kernel<DK, DV>), dim3(BH, scan_groups(DK)), dim3(64 * (DK / 16)), 0, s, a);
       return hipGetLastError();
     }
