@@ -154,6 +154,20 @@ def warm(fn, warmup, torch, min_seconds=None):
     return calls
 
 
+def load_counters(key):
+    """SQ counter figures of one kernel (profiles/counters.json: MFMA busy, VALU busy, ...), or None
+    when the kernel sources changed since they were taken."""
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    try:
+        with open(path) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if data.get("sources") != sources_digest():
+        return None
+    return data.get(key)
+
+
 def time_calls(fn, steps, warmup, torch):
     warm(fn, warmup, torch)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -447,6 +461,9 @@ def main(argv=None):
             algorithmic_flops_per_launch=fw["output_flops_per_call"],
             mfma_tflops=fw["output_flops_per_call"] / fw["phases"]["output"] / 1e12,
             mfma_frac=fw["output_flops_per_call"] / fw["phases"]["output"] / PEAK_BF16_MFMA,
+            # measured share of time the MFMA units were busy in this kernel (rocprofv3
+            # SQ_VALU_MFMA_BUSY_CYCLES over busy cycles x SIMDs; null when the kernels changed since)
+            mfma_busy_counter=(load_counters(w.name + ":output walk") or {}).get("mfma_busy"),
         ),
     }
     if not args.skip_workloads:
