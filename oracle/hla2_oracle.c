@@ -630,6 +630,29 @@ int hla2_oracle_ahla_serial(int n, int d, int dv, double gamma, const double *q,
   return 0;
 }
 
+/* Serial recurrence that also reports, per token, |n_t|, the norm of the den column of the state
+ * (den_t = q_t . n_t): the natural scale of den_t, against which its cancellation is measured
+ * [SUM §1 "Normalisatie", as for the second order's u_t].  Arguments as hla2_oracle_ahla_serial plus
+ * unorm (n). */
+int hla2_oracle_ahla_serial_unorm(int n, int d, int dv, double gamma, const double *q, const double *k,
+                                  const double *v, double *num, double *den, double *unorm, double *state) {
+  long L = hla2_oracle_ahla_state_len(d, dv);
+  double *st = state ? state : (double *)calloc((size_t)L, sizeof(double));
+  const double *nn = st + 2L * d * dv + d;
+  int t, a;
+  if (!st) return -2;
+  for (t = 0; t < n; ++t) {
+    double dd, ss = 0.0;
+    hla2_oracle_ahla_step(d, dv, gamma, st, q + (long)t * d, k + (long)t * d, v + (long)t * dv,
+                          num + (long)t * dv, &dd);
+    if (den) den[t] = dd;
+    for (a = 0; a < d; ++a) ss += nn[a] * nn[a];
+    unorm[t] = sqrt(ss);
+  }
+  if (!state) free(st);
+  return 0;
+}
+
 /* The definition as a triple sum (small n). */
 int hla2_oracle_ahla_bruteforce(int n, int d, int dv, double gamma, const double *q, const double *k,
                                 const double *v, double *num, double *den) {
@@ -762,6 +785,29 @@ int hla2_oracle_ho3_serial(int n, int d, int dv, double gamma, const double *q, 
     hla2_oracle_ho3_step(d, dv, gamma, st, q + (long)t * d, k + (long)t * d, v + (long)t * dv,
                          num + (long)t * dv, &dd);
     if (den) den[t] = dd;
+  }
+  if (!state) free(st);
+  return 0;
+}
+
+/* Serial recurrence that also reports, per token, |w_t|, the norm of the den column of the corrected
+ * accumulator W' (den_t = q_t . w_t): the natural scale of den_t [SUM §1 "Normalisatie", as for the
+ * second order's u_t].  Arguments as hla2_oracle_ho3_serial plus unorm (n). */
+int hla2_oracle_ho3_serial_unorm(int n, int d, int dv, double gamma, const double *q, const double *k,
+                                 const double *v, double *num, double *den, double *unorm, double *state) {
+  long L = hla2_oracle_ho3_state_len(d, dv);
+  double *st = state ? state : (double *)calloc((size_t)L, sizeof(double));
+  const int dvp = dv + 1;
+  const double *W = st + (long)d * d + (long)d * dvp;
+  int t, a;
+  if (!st) return -2;
+  for (t = 0; t < n; ++t) {
+    double dd, ss = 0.0;
+    hla2_oracle_ho3_step(d, dv, gamma, st, q + (long)t * d, k + (long)t * d, v + (long)t * dv,
+                         num + (long)t * dv, &dd);
+    if (den) den[t] = dd;
+    for (a = 0; a < d; ++a) ss += W[(long)a * dvp + dv] * W[(long)a * dvp + dv];
+    unorm[t] = sqrt(ss);
   }
   if (!state) free(st);
   return 0;

@@ -83,6 +83,10 @@ def _load(path: str | None = None):
             lib.hla2_oracle_ahla_summary_len.argtypes = [i, i]
             lib.hla2_oracle_ahla_serial.restype = i
             lib.hla2_oracle_ahla_serial.argtypes = [i, i, i, d_, _dp, _dp, _dp, _dp, _dp, _dp]
+            lib.hla2_oracle_ahla_serial_unorm.restype = i
+            lib.hla2_oracle_ahla_serial_unorm.argtypes = [i, i, i, d_, _dp, _dp, _dp, _dp, _dp, _dp, _dp]
+            lib.hla2_oracle_ho3_serial_unorm.restype = i
+            lib.hla2_oracle_ho3_serial_unorm.argtypes = [i, i, i, d_, _dp, _dp, _dp, _dp, _dp, _dp, _dp]
             lib.hla2_oracle_ahla_bruteforce.restype = i
             lib.hla2_oracle_ahla_bruteforce.argtypes = [i, i, i, d_, _dp, _dp, _dp, _dp, _dp]
             lib.hla2_oracle_ahla_summary.restype = None
@@ -541,3 +545,37 @@ def ho3_apply(summary, state, d: int, dv: int, lib=None):
     lib.hla2_oracle_ho3_apply(d, dv, _p(_f64(summary)), _p(st))
     return st
 
+
+
+def _serial_unorm_variant(fn_name, len_fn, q, k, v, gamma, state, threads, lib):
+    lib = lib or _load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    *lead, n, d = q.shape
+    dv = v.shape[-1]
+    H = int(np.prod(lead)) if lead else 1
+    qh, kh, vh = q.reshape(H, n, d), k.reshape(H, n, d), v.reshape(H, n, dv)
+    L = len_fn(d, dv, lib)
+    st = np.zeros((H, L)) if state is None else _f64(state).reshape(H, L).copy()
+    num = np.empty((H, n, dv))
+    den = np.empty((H, n))
+    un = np.empty((H, n))
+    fn = getattr(lib, fn_name)
+
+    def one(h):
+        rc = fn(n, d, dv, float(gamma), _p(qh[h]), _p(kh[h]), _p(vh[h]), _p(num[h]), _p(den[h]), _p(un[h]), _p(st[h]))
+        assert rc == 0
+
+    _run_heads(one, H, threads)
+    return num.reshape(*lead, n, dv), den.reshape(*lead, n), un.reshape(*lead, n), st.reshape(*lead, L)
+
+
+def ahla_serial_unorm(q, k, v, gamma: float = 1.0, state=None, threads: int | None = None, lib=None):
+    """ahla_serial() plus |n_t| per token, the norm of the den column n_t of the state
+    (den_t = q_t . n_t).  Returns (num, den, unorm [..., n], final_state)."""
+    return _serial_unorm_variant("hla2_oracle_ahla_serial_unorm", ahla_state_len, q, k, v, gamma, state, threads, lib)
+
+
+def ho3_serial_unorm(q, k, v, gamma: float = 1.0, state=None, threads: int | None = None, lib=None):
+    """ho3_serial() plus |w_t| per token, the norm of the den column w_t of the corrected accumulator
+    (den_t = q_t . w_t).  Returns (num, den, unorm [..., n], final_state)."""
+    return _serial_unorm_variant("hla2_oracle_ho3_serial_unorm", ho3_state_len, q, k, v, gamma, state, threads, lib)

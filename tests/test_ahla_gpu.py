@@ -34,19 +34,6 @@ def gpu_ahla(q, k, v, decay, normalize, segments=0):
     return out.double().cpu().numpy(), den.double().cpu().numpy()
 
 
-def n_norms(q, k, gamma):
-    """|n_t| per token for every head: n_t = gamma n_{t-1} + k_t (q_t . m_t), m_t = gamma m_{t-1} + k_t."""
-    q, k = np.asarray(q, np.float64), np.asarray(k, np.float64)
-    m = np.zeros(q.shape[:-2] + (q.shape[-1],))
-    nv = np.zeros_like(m)
-    out = np.empty(q.shape[:-1])
-    for t in range(q.shape[-2]):
-        m = gamma * m + k[..., t, :]
-        nv = gamma * nv + k[..., t, :] * np.sum(q[..., t, :] * m, axis=-1, keepdims=True)
-        out[..., t] = np.linalg.norm(nv, axis=-1)
-    return out
-
-
 def check(q, k, v, decay, normalize, dtype, segments=0, heads=None, subset=False):
     tol = tol_for(dtype)
     o_gpu, den_gpu = gpu_ahla(q, k, v, decay, normalize, segments)
@@ -56,13 +43,12 @@ def check(q, k, v, decay, normalize, dtype, segments=0, heads=None, subset=False
         tidx = tuple(torch.as_tensor(x) for x in idx)
         q, k, v = q[tidx], k[tidx], v[tidx]
         o_gpu, den_gpu, num_gpu = o_gpu[idx], den_gpu[idx], num_gpu[idx]
-    num, den, _ = O.ahla_serial(q.double().numpy(), k.double().numpy(), v.double().numpy(), decay)
+    num, den, unorm, _ = O.ahla_serial_unorm(q.double().numpy(), k.double().numpy(), v.double().numpy(), decay)
     r_num, r_den = rel_l2(num_gpu, num), rel_l2(den_gpu, den)
     msg = "num %.3g den %.3g" % (r_num, r_den)
     ok = r_num <= tol and r_den <= tol
     if normalize:
-        rep = ratio_report(o_gpu, den_gpu, num, den, n_norms(q.double().numpy(), k.double().numpy(), decay),
-                           q.double().numpy())
+        rep = ratio_report(o_gpu, den_gpu, num, den, unorm, q.double().numpy())
         msg += " | e_rms %.3g ratio(well) %.3g excluded %.3f" % (rep["e_rms"], rep["ratio_well"], rep["excluded"])
         ok = ok and ratio_ok(rep, tol, subset=subset)
     print(msg)

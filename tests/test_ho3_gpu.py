@@ -35,25 +35,6 @@ def gpu_ho3(q, k, v, decay, normalize, segments=0):
     return out.double().cpu().numpy(), den.double().cpu().numpy()
 
 
-def w_norms(q, k, gamma):
-    """|w_t| per token for every head: w_t = g^3 w_{t-1} + (S_t q_t)(m_t . q_t),
-    S_t = g S_{t-1} + k_t k_t^T, m_t = g m_{t-1} + k_t."""
-    q, k = np.asarray(q, np.float64), np.asarray(k, np.float64)
-    d = q.shape[-1]
-    S = np.zeros(q.shape[:-2] + (d, d))
-    m = np.zeros(q.shape[:-2] + (d,))
-    wv = np.zeros_like(m)
-    out = np.empty(q.shape[:-1])
-    for t in range(q.shape[-2]):
-        kt, qt = k[..., t, :], q[..., t, :]
-        S = gamma * S + kt[..., :, None] * kt[..., None, :]
-        m = gamma * m + kt
-        z = np.einsum("...ab,...b->...a", S, qt)
-        wv = gamma ** 3 * wv + z * np.sum(m * qt, axis=-1, keepdims=True)
-        out[..., t] = np.linalg.norm(wv, axis=-1)
-    return out
-
-
 def check(q, k, v, decay, normalize, dtype, segments=0, heads=None, subset=False):
     tol = tol_for(dtype)
     o_gpu, den_gpu = gpu_ho3(q, k, v, decay, normalize, segments)
@@ -63,13 +44,12 @@ def check(q, k, v, decay, normalize, dtype, segments=0, heads=None, subset=False
         tidx = tuple(torch.as_tensor(x) for x in idx)
         q, k, v = q[tidx], k[tidx], v[tidx]
         o_gpu, den_gpu, num_gpu = o_gpu[idx], den_gpu[idx], num_gpu[idx]
-    num, den, _ = O.ho3_serial(q.double().numpy(), k.double().numpy(), v.double().numpy(), decay)
+    num, den, unorm, _ = O.ho3_serial_unorm(q.double().numpy(), k.double().numpy(), v.double().numpy(), decay)
     r_num, r_den = rel_l2(num_gpu, num), rel_l2(den_gpu, den)
     msg = "num %.3g den %.3g" % (r_num, r_den)
     ok = r_num <= tol and r_den <= tol
     if normalize:
-        rep = ratio_report(o_gpu, den_gpu, num, den, w_norms(q.double().numpy(), k.double().numpy(), decay),
-                           q.double().numpy())
+        rep = ratio_report(o_gpu, den_gpu, num, den, unorm, q.double().numpy())
         msg += " | e_rms %.3g ratio(well) %.3g excluded %.3f" % (rep["e_rms"], rep["ratio_well"], rep["excluded"])
         ok = ok and ratio_ok(rep, tol, subset=subset)
     print(msg)

@@ -36,6 +36,18 @@ def matrix_form(q, k, v, gamma):
     return M @ v, M.sum(axis=1)
 
 
+def den_column_norms(q, k, gamma):
+    """|n_t| from the matrix form: n_t = sum_{j<=t} g^{t-j} (q_j . m_j) k_j with q_j . m_j = (A_g 1)_j,
+    i.e. the rows of (L o D_g) diag(A_g 1) K (so den = Q n = A_g A_g 1 row by row)."""
+    n = q.shape[0]
+    t = np.arange(n)
+    low = t[:, None] >= t[None, :]
+    Dg = np.where(low, gamma ** np.where(low, t[:, None] - t[None, :], 0), 0.0)
+    Ag = Dg * (q @ k.T)
+    N = Dg @ ((Ag @ np.ones(n))[:, None] * k)
+    return np.linalg.norm(N, axis=1)
+
+
 def draw(seed, n, d, dv):
     r = np.random.default_rng(seed)
     return r.standard_normal((n, d)), r.standard_normal((n, d)), r.standard_normal((n, dv))
@@ -49,6 +61,10 @@ def pin_failures(lib):
         num, den, st = O.ahla_serial(q, k, v, gamma, lib=lib)
         if rel(num, rn) > 1e-12 or rel(den, rd) > 1e-12:
             bad.append("serial vs matrix form gamma=%g" % gamma)
+        un_num, un_den, un, _ = O.ahla_serial_unorm(q, k, v, gamma, lib=lib)
+        if rel(un, den_column_norms(q, k, gamma)) > 1e-12 or not np.array_equal(un_num, num) or \
+                not np.array_equal(un_den, den):
+            bad.append("den-column norms vs matrix form gamma=%g" % gamma)
         bn, bd = O.ahla_bruteforce(q, k, v, gamma, lib=lib)
         if rel(bn, rn) > 1e-12 or rel(bd, rd) > 1e-12:
             bad.append("bruteforce vs matrix form gamma=%g" % gamma)
@@ -164,6 +180,8 @@ MUTANTS = {
         "Eo[(long)a * dv + c] = GB * EA[(long)a * dv + c] + EB[(long)a * dv + c] + s;"),
     "summary M transposed": ("M[(long)a * d + b] += k[(long)t * d + a] * q[(long)t * d + b];",
                              "M[(long)a * d + b] += q[(long)t * d + a] * k[(long)t * d + b];"),
+    "den-column norm of m instead of n": ("const double *nn = st + 2L * d * dv + d;",
+                                          "const double *nn = st + (long)d * dv;"),
     "brute force decays by the middle index": ("double w = pow(gamma, (double)(t - i)) * qk_tj * qk_ji;",
                                                "double w = pow(gamma, (double)(t - j)) * qk_tj * qk_ji;"),
 }
@@ -180,3 +198,20 @@ def test_mutant_is_caught(tmp_path, name):
     subprocess.run(["gcc", "-std=c99", "-O1", "-ffp-contract=off", "-fPIC", "-shared", str(src), "-o", str(lib),
                     "-lm"], check=True)
     assert pin_failures(O._load(str(lib))), "planted slip not caught: " + name
+
+
+@pytest.mark.parametrize("gamma", [1.0, 0.8])
+def test_den_column_norms_equal_matrix_form(gamma):
+    # |n_t| (the conditioning scale of the ratio) against its matrix form, and num, den unchanged from
+    # ahla_serial; multi-head and threaded
+    r = np.random.default_rng(9)
+    q, k, v = r.standard_normal((2, 3, 40, 4)), r.standard_normal((2, 3, 40, 4)), r.standard_normal((2, 3, 40, 3))
+    num, den, un, st = O.ahla_serial_unorm(q, k, v, gamma, threads=3)
+    num2, den2, st2 = O.ahla_serial(q, k, v, gamma)
+    np.testing.assert_array_equal(num, num2)
+    np.testing.assert_array_equal(den, den2)
+    np.testing.assert_array_equal(st, st2)
+    for a in range(2):
+        for b in range(3):
+            assert rel(un[a, b], den_column_norms(q[a, b], k[a, b], gamma)) < 1e-12
+    assert np.all(np.abs(den) <= np.linalg.norm(q, axis=-1) * un * (1 + 1e-12))

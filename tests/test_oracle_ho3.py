@@ -42,6 +42,21 @@ def matrix_form(q, k, v, gamma):
     return M @ (Ag @ v), M @ (Ag @ np.ones(n))
 
 
+def den_column_norms(q, k, gamma):
+    """|w_t| from the matrix form: w_t = sum_{l<=t} g^{3(t-l)} (q_l . m_l) z_l with z_l = S_l q_l, i.e. the
+    rows of (L o D_{g^3}) diag(A_g 1) (A_g K) (so den = Q w row by row)."""
+    n = q.shape[0]
+    t = np.arange(n)
+    low = t[:, None] >= t[None, :]
+
+    def D(p):
+        return np.where(low, p ** np.where(low, t[:, None] - t[None, :], 0), 0.0)
+
+    Ag = D(gamma) * (q @ k.T)
+    Wd = D(gamma ** 3) @ ((Ag @ np.ones(n))[:, None] * (Ag @ k))
+    return np.linalg.norm(Wd, axis=1)
+
+
 def closed_form(n, gamma):
     g = Fraction(gamma)
     return [float(sum(g ** (3 * t - j - l - i) for l in range(t + 1) for j in range(l + 1) for i in range(l + 1)))
@@ -63,6 +78,10 @@ def pin_failures(lib):
         num, den, st = O.ho3_serial(q, k, v, gamma, lib=lib)
         if rel(num, rn) > 1e-11 or rel(den, rd) > 1e-11:
             bad.append("serial vs matrix form gamma=%g" % gamma)
+        un_num, un_den, un, _ = O.ho3_serial_unorm(q, k, v, gamma, lib=lib)
+        if rel(un, den_column_norms(q, k, gamma)) > 1e-11 or not np.array_equal(un_num, num) or \
+                not np.array_equal(un_den, den):
+            bad.append("den-column norms vs matrix form gamma=%g" % gamma)
         bn, bd = O.ho3_bruteforce(q[:12], k[:12], v[:12], gamma, lib=lib)
         if rel(bn, rn[:12]) > 1e-11 or rel(bd, rd[:12]) > 1e-11:
             bad.append("bruteforce vs matrix form gamma=%g" % gamma)
@@ -163,6 +182,8 @@ MUTANTS = {
     "fold drops S_A X1": ("s += SQ[(long)a * d + b] * P[(long)b * dvp + c] + S[(long)a * d + b] * X1[(long)b * dvp + c] +",
                           "s += SQ[(long)a * d + b] * P[(long)b * dvp + c] + 0.0 * X1[(long)b * dvp + c] +"),
     "fold W decays once": ("const double G = sum[0], G3 = G * G * G;", "const double G = sum[0], G3 = G;"),
+    "den-column norm of P instead of W": ("const double *W = st + (long)d * d + (long)d * dvp;",
+                                          "const double *W = st + (long)d * d;"),
     "brute force decays the middle index once": (
         "double w = pow(gamma, (double)((t - j) + (t - l) + (t - i))) * f1",
         "double w = pow(gamma, (double)((t - j) + (t - i))) * f1"),
@@ -180,3 +201,21 @@ def test_mutant_is_caught(tmp_path, name):
     subprocess.run(["gcc", "-std=c99", "-O1", "-ffp-contract=off", "-fPIC", "-shared", str(src), "-o", str(lib),
                     "-lm"], check=True)
     assert pin_failures(O._load(str(lib))), "planted slip not caught: " + name
+
+
+@pytest.mark.parametrize("gamma", [1.0, 0.8])
+def test_den_column_norms_equal_matrix_form(gamma):
+    # |w_t| (the conditioning scale of the ratio) against its matrix form, and num, den unchanged from
+    # ho3_serial; multi-head and threaded
+    r = np.random.default_rng(11)
+    q, k, v = (0.5 * r.standard_normal((2, 3, 36, 4)), 0.5 * r.standard_normal((2, 3, 36, 4)),
+               r.standard_normal((2, 3, 36, 3)))
+    num, den, un, st = O.ho3_serial_unorm(q, k, v, gamma, threads=3)
+    num2, den2, st2 = O.ho3_serial(q, k, v, gamma)
+    np.testing.assert_array_equal(num, num2)
+    np.testing.assert_array_equal(den, den2)
+    np.testing.assert_array_equal(st, st2)
+    for a in range(2):
+        for b in range(3):
+            assert rel(un[a, b], den_column_norms(q[a, b], k[a, b], gamma)) < 1e-11
+    assert np.all(np.abs(den) <= np.linalg.norm(q, axis=-1) * un * (1 + 1e-12))
