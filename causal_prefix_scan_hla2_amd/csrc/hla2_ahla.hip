@@ -20,19 +20,31 @@
 
 namespace hla2 {
 
-template <typename T, int DK, int DVP, int BC>
+// Under the ratio with bf16 operands the carried state (P', E') and Y enter their products as two
+// bf16 halves (hla2_tiles.h): the ratio of two AHLA sums cancels, and with one bf16 rounding of each
+// operand the rel-L2 of o over the well-conditioned tokens of 32 heads of 2048 tokens (d = dv = 64)
+// is 2.0e-2 measured; with these three split a CPU model of the chunk walk's rounding points gives
+// 0.7e-2 (splitting Ad as well buys little more).
+template <typename T, bool NORM>
+constexpr bool ahla_split() { return NORM && sizeof(T) == 2; }
+
+template <typename T, int DK, int DVP, int BC, bool SPLIT>
 struct AhlaCfg {
   static constexpr int PAD = lds_pad_bytes<T>() / sizeof(T);
   static constexpr int LDQ = DK + PAD, LDV = DVP + PAD, LDC = BC + PAD;
+  // With SPLIT, E' is copied into P''s slot once Y is formed (P' is read only for Y), so that the low
+  // halves of Y and of the state copy fit beside it.
   static constexpr int Q_OFF = 0, K_OFF = BC * LDQ, V_OFF = K_OFF + BC * LDQ, Y_OFF = V_OFF + BC * LDV,
-                       AD_OFF = Y_OFF + BC * LDV, P_OFF = AD_OFF + BC * LDC, E_OFF = P_OFF + DK * LDV,
-                       ELEMS = E_OFF + DK * LDV;
+                       AD_OFF = Y_OFF + BC * LDV, P_OFF = AD_OFF + BC * LDC,
+                       E_OFF = SPLIT ? P_OFF : P_OFF + DK * LDV, YL_OFF = E_OFF + DK * LDV,
+                       PL_OFF = YL_OFF + BC * LDV, EL_OFF = PL_OFF,
+                       ELEMS = SPLIT ? PL_OFF + DK * LDV : E_OFF + DK * LDV;
 };
 
 // LDS bytes of one walker workgroup: the element rows, then the decay table and den.
-template <typename T, int DK, int DVP, int BC>
+template <typename T, int DK, int DVP, int BC, bool SPLIT>
 constexpr int ahla_lds_bytes() {
-  return AhlaCfg<T, DK, DVP, BC>::ELEMS * (int)sizeof(T) + (2 * BC + 3) * 4 + BC * 4;
+  return AhlaCfg<T, DK, DVP, BC, SPLIT>::ELEMS * (int)sizeof(T) + (2 * BC + 3) * 4 + BC * 4;
 }
 
 // Summary mode (OUT = false): a segment from the zero state, writing P' | E' | M.  Output
@@ -40,14 +52,16 @@ constexpr int ahla_lds_bytes() {
 // state after the segment is written as the prefix of segment 1.
 template <typename T, int DK, int DV, int DVP, int BC, bool OUT, bool NORM, bool LEAD>
 __device__ __forceinline__ void ahla_walk_body(const AhlaArgs &a, const int bh, const int seg, unsigned char *lds) {
-  using Cfg = AhlaCfg<T, DK, DVP, BC>;
+  constexpr bool SPLIT = ahla_split<T, NORM>();
+  using Cfg = AhlaCfg<T, DK, DVP, BC, SPLIT>;
   static_assert((Cfg::ELEMS * sizeof(T)) % 4 == 0, "decay table alignment");
   T *const smem = (T *)lds;
   float *const pw = (float *)(lds + Cfg::ELEMS * sizeof(T));
   float *const dens = pw + (2 * BC + 3);
   T *const Qs = smem + Cfg::Q_OFF, *const Ks = smem + Cfg::K_OFF, *const Vs = smem + Cfg::V_OFF;
   T *const Ys = smem + Cfg::Y_OFF, *const Ads = smem + Cfg::AD_OFF, *const Ps = smem + Cfg::P_OFF;
-  T *const Es = smem + Cfg::E_OFF;
+  T *const Es = smem + Cfg::E_OFF, *const Yls = smem + Cfg::YL_OFF, *const Pls = smem + Cfg::PL_OFF;
+  T *const Els = smem + Cfg::EL_OFF;
   const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 4, nn = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tok0 = ahla_seg_chunk0(a, seg) * a.kc, tokE = min(a.n, tok0 + ahla_seg_chunks(a, seg) * a.kc);
@@ -81,8 +95,8 @@ __device__ __forceinline__ void ahla_walk_body(const AhlaArgs &a, const int bh, 
     // state copies for this chunk's products, and its rows
     for_tiles<DK, DVP>(w, [&](int i0, int j0, bool ok, int it) {
       if (ok) {
-        st4l(Ps, Cfg::LDV, i0 + nn, j0 + 4 * gq, P[it]);
-        if (OUT) st4l(Es, Cfg::LDV, i0 + nn, j0 + 4 * gq, E[it]);
+        st4_split<SPLIT>(Ps, Pls, Cfg::LDV, i0 + nn, j0 + 4 * gq, P[it]);
+        if (OUT && !SPLIT) st4l(Es, Cfg::LDV, i0 + nn, j0 + 4 * gq, E[it]);
       }
     });
     rq.put(Qs, Cfg::LDQ, tid);
@@ -111,19 +125,25 @@ __device__ __forceinline__ void ahla_walk_body(const AhlaArgs &a, const int bh, 
     __syncthreads();
     // Y = diag(g^(tau+1)) Q P0' + Ad V'
     for_tiles<BC, DVP>(w, [&](int i0, int j0, bool ok, int) {
-      f32x4 x = pt<false, false, DK>(zero4(), Qs, Cfg::LDQ, Ps, Cfg::LDV, i0, j0, lane);
+      f32x4 x = pt2y<SPLIT, false, false, DK>(zero4(), Qs, Cfg::LDQ, Ps, Pls, Cfg::LDV, i0, j0, lane);
       x *= pw[i0 + nn + 1];
       x = pt<false, false, BC>(x, Ads, Cfg::LDC, Vs, Cfg::LDV, i0, j0, lane);
-      if (ok) st4l(Ys, Cfg::LDV, i0 + nn, j0 + 4 * gq, x);
+      if (ok) st4_split<SPLIT>(Ys, Yls, Cfg::LDV, i0 + nn, j0 + 4 * gq, x);
     });
     __syncthreads();
+    if constexpr (OUT && SPLIT) {  // every read of P''s copy is done: E' takes its slot
+      for_tiles<DK, DVP>(w, [&](int i0, int j0, bool ok, int it) {
+        if (ok) st4_split<SPLIT>(Es, Els, Cfg::LDV, i0 + nn, j0 + 4 * gq, E[it]);
+      });
+      __syncthreads();
+    }
     // outputs O = diag(g^(tau+1)) Q E0' + Ad Y (kept in registers until den is known)
     f32x4 O[OUT ? TileCount<BC, DVP>::PER : 1];
     if constexpr (OUT) {
       for_tiles<BC, DVP>(w, [&](int i0, int j0, bool ok, int it) {
-        f32x4 x = pt<false, false, DK>(zero4(), Qs, Cfg::LDQ, Es, Cfg::LDV, i0, j0, lane);
+        f32x4 x = pt2y<SPLIT, false, false, DK>(zero4(), Qs, Cfg::LDQ, Es, Els, Cfg::LDV, i0, j0, lane);
         x *= pw[i0 + nn + 1];
-        x = pt<false, false, BC>(x, Ads, Cfg::LDC, Ys, Cfg::LDV, i0, j0, lane);
+        x = pt2y<SPLIT, false, false, BC>(x, Ads, Cfg::LDC, Ys, Yls, Cfg::LDV, i0, j0, lane);
         O[it] = x;
         if (NORM && ok && j0 + 4 * gq == DV) dens[i0 + nn] = x[0];
       });
@@ -140,6 +160,9 @@ __device__ __forceinline__ void ahla_walk_body(const AhlaArgs &a, const int bh, 
                                    [&](int i) { return pw[BC - 1 - i]; });
       E[it] = ptw<true, false, BC>(gB * E[it], Ks, Cfg::LDQ, Ys, Cfg::LDV, i0, j0, lane,
                                    [&](int i) { return pw[BC - 1 - i]; });
+      if constexpr (SPLIT)
+        E[it] = ptw<true, false, BC>(E[it], Ks, Cfg::LDQ, Yls, Cfg::LDV, i0, j0, lane,
+                                     [&](int i) { return pw[BC - 1 - i]; });
     });
     __syncthreads();  // dens complete; every read of this chunk's LDS done
     if constexpr (OUT) {
@@ -182,7 +205,7 @@ __device__ __forceinline__ void ahla_walk_body(const AhlaArgs &a, const int bh, 
 // Walks segments (OUT ? seg_lo .. nseg-1 : 0 .. nseg-2) of every head, one workgroup each.
 template <typename T, int DK, int DV, int DVP, int BC, bool OUT, bool NORM>
 __global__ void __launch_bounds__(BWD_THREADS) ahla_walk_kernel(AhlaArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[ahla_lds_bytes<T, DK, DVP, BC>()];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[ahla_lds_bytes<T, DK, DVP, BC, ahla_split<T, NORM>()>()];
   const int lo = OUT ? a.seg_lo : 0, nr = (OUT ? a.nseg : a.nseg - 1) - lo;
   ahla_walk_body<T, DK, DV, DVP, BC, OUT, NORM, false>(a, blockIdx.x / nr, lo + blockIdx.x % nr, lds);
 }
@@ -191,7 +214,7 @@ __global__ void __launch_bounds__(BWD_THREADS) ahla_walk_kernel(AhlaArgs a) {
 // leave the prefix of segment 1; the rest summarise segments 1 .. nseg-2 of every head.
 template <typename T, int DK, int DV, int DVP, int BC, bool NORM>
 __global__ void __launch_bounds__(BWD_THREADS) ahla_lead_kernel(AhlaArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[ahla_lds_bytes<T, DK, DVP, BC>()];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[ahla_lds_bytes<T, DK, DVP, BC, ahla_split<T, NORM>()>()];
   const int b = blockIdx.x;
   if (b < a.nbh) {
     ahla_walk_body<T, DK, DV, DVP, BC, true, NORM, true>(a, b, 0, lds);

@@ -23,22 +23,34 @@
 
 namespace hla2 {
 
-template <typename T, int DK, int DVP, int BC>
+// Under the ratio with bf16 operands the carried state (S, P', W') and the chunk weights Ad and Wm
+// enter their products as two bf16 halves, hi = bf16(x) and lo = bf16(x - hi), about 16 significant
+// bits.  The ratio of two third-order sums cancels: with one bf16 rounding of each operand the rel-L2
+// of o over the well-conditioned tokens of 32 heads of 2048 tokens (d = dv = 64) is 2.0e-2, with these
+// five split 0.9e-2 (a CPU model of the chunk walk's rounding points, which reproduces the measured
+// 2.0e-2 and, with four split, 1.0e-2).  Z and Y stay single: their low halves do not fit in LDS.
+template <typename T, bool NORM>
+constexpr bool ho3_split() { return NORM && sizeof(T) == 2; }
+
+template <typename T, int DK, int DVP, int BC, bool SPLIT>
 struct Ho3Cfg {
   static constexpr int PAD = lds_pad_bytes<T>() / sizeof(T);
   static constexpr int LDQ = DK + PAD, LDV = DVP + PAD, LDC = BC + PAD;
+  // With SPLIT the second BC x BC slot holds Ad's low half; Wm and its low half (written once Ad is
+  // consumed) take the two slots of Ad; the low halves of S, P', W' follow W'.
   static constexpr int Q_OFF = 0, K_OFF = BC * LDQ, V_OFF = K_OFF + BC * LDQ, Y_OFF = V_OFF + BC * LDV,
-                       Z_OFF = Y_OFF + BC * LDV, AD_OFF = Z_OFF + BC * LDQ, WM_OFF = AD_OFF + BC * LDC,
-                       S_OFF = WM_OFF + BC * LDC, P_OFF = S_OFF + DK * LDQ, W_OFF = P_OFF + DK * LDV,
-                       ELEMS = W_OFF + DK * LDV;
+                       Z_OFF = Y_OFF + BC * LDV, AD_OFF = Z_OFF + BC * LDQ, ADL_OFF = AD_OFF + BC * LDC,
+                       WM_OFF = SPLIT ? AD_OFF : ADL_OFF, WML_OFF = ADL_OFF, S_OFF = ADL_OFF + BC * LDC, P_OFF = S_OFF + DK * LDQ,
+                       W_OFF = P_OFF + DK * LDV, SL_OFF = W_OFF + DK * LDV, PL_OFF = SL_OFF + DK * LDQ,
+                       WL_OFF = PL_OFF + DK * LDV, ELEMS = SPLIT ? WL_OFF + DK * LDV : SL_OFF;
   static constexpr long PB = (long)DK * DK + 2L * DK * DVP;                 // S | P' | W'
   static constexpr long SB = PB + 2L * DK * DK + (long)DK * DVP;            // ... | Q2 | X1 | X2
 };
 
 // LDS bytes of one walker workgroup: the element rows, then the decay table and den.
-template <typename T, int DK, int DVP, int BC>
+template <typename T, int DK, int DVP, int BC, bool SPLIT>
 constexpr int ho3_lds_bytes() {
-  return Ho3Cfg<T, DK, DVP, BC>::ELEMS * (int)sizeof(T) + (3 * BC + 4) * 4 + BC * 4;
+  return Ho3Cfg<T, DK, DVP, BC, SPLIT>::ELEMS * (int)sizeof(T) + (3 * BC + 4) * 4 + BC * 4;
 }
 
 // Summary mode (OUT = false): a segment from the zero state, writing S | P' | W' and its
@@ -46,7 +58,8 @@ constexpr int ho3_lds_bytes() {
 // the state after the segment is written as the prefix of segment 1.
 template <typename T, int DK, int DV, int DVP, int BC, bool OUT, bool NORM, bool LEAD>
 __device__ __forceinline__ void ho3_walk_body(const Ho3Args &a, const int bh, const int seg, unsigned char *lds) {
-  using Cfg = Ho3Cfg<T, DK, DVP, BC>;
+  constexpr bool SPLIT = ho3_split<T, NORM>();
+  using Cfg = Ho3Cfg<T, DK, DVP, BC, SPLIT>;
   static_assert((Cfg::ELEMS * sizeof(T)) % 4 == 0, "decay table alignment");
   T *const smem = (T *)lds;
   float *const pw = (float *)(lds + Cfg::ELEMS * sizeof(T));
@@ -54,7 +67,8 @@ __device__ __forceinline__ void ho3_walk_body(const Ho3Args &a, const int bh, co
   T *const Qs = smem + Cfg::Q_OFF, *const Ks = smem + Cfg::K_OFF, *const Vs = smem + Cfg::V_OFF;
   T *const Ys = smem + Cfg::Y_OFF, *const Zs = smem + Cfg::Z_OFF, *const Ads = smem + Cfg::AD_OFF;
   T *const Wms = smem + Cfg::WM_OFF, *const Ss = smem + Cfg::S_OFF, *const Ps = smem + Cfg::P_OFF;
-  T *const Ws = smem + Cfg::W_OFF;
+  T *const Ws = smem + Cfg::W_OFF, *const Adls = smem + Cfg::ADL_OFF, *const Sls = smem + Cfg::SL_OFF;
+  T *const Pls = smem + Cfg::PL_OFF, *const Wls = smem + Cfg::WL_OFF, *const Wmls = smem + Cfg::WML_OFF;
   const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 4, nn = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tok0 = ahla_seg_chunk0(a, seg) * a.kc, tokE = min(a.n, tok0 + ahla_seg_chunks(a, seg) * a.kc);
@@ -93,12 +107,12 @@ __device__ __forceinline__ void ho3_walk_body(const Ho3Args &a, const int bh, co
   for (int ch = 0; ch < nch; ++ch) {
     const int t0 = tok0 + ch * BC;
     for_tiles<DK, DK>(w, [&](int i0, int j0, bool ok, int it) {
-      if (ok) st4l(Ss, Cfg::LDQ, i0 + nn, j0 + 4 * gq, S[it]);
+      if (ok) st4_split<SPLIT>(Ss, Sls, Cfg::LDQ, i0 + nn, j0 + 4 * gq, S[it]);
     });
     for_tiles<DK, DVP>(w, [&](int i0, int j0, bool ok, int it) {
       if (ok) {
-        st4l(Ps, Cfg::LDV, i0 + nn, j0 + 4 * gq, P[it]);
-        if (OUT) st4l(Ws, Cfg::LDV, i0 + nn, j0 + 4 * gq, W[it]);
+        st4_split<SPLIT>(Ps, Pls, Cfg::LDV, i0 + nn, j0 + 4 * gq, P[it]);
+        if (OUT) st4_split<SPLIT>(Ws, Wls, Cfg::LDV, i0 + nn, j0 + 4 * gq, W[it]);
       }
     });
     rq.put(Qs, Cfg::LDQ, tid);
@@ -122,20 +136,20 @@ __device__ __forceinline__ void ho3_walk_body(const Ho3Args &a, const int bh, co
         // that no branch forms around the table read
         x[e] = (ti <= tr ? x[e] : 0.f) * pw[ti <= tr ? tr - ti : 0];
       }
-      if (ok) st4l(Ads, Cfg::LDC, tr, j0 + 4 * gq, x);
+      if (ok) st4_split<SPLIT>(Ads, Adls, Cfg::LDC, tr, j0 + 4 * gq, x);
     });
     __syncthreads();
     // Z = diag(g^(tau+1)) Q S0 + Ad K;  Y = diag(g^(tau+1)) Q P0' + Ad V'
     for_tiles<BC, DK>(w, [&](int i0, int j0, bool ok, int) {
-      f32x4 x = pt<false, true, DK>(zero4(), Qs, Cfg::LDQ, Ss, Cfg::LDQ, i0, j0, lane);
+      f32x4 x = pt2y<SPLIT, false, true, DK>(zero4(), Qs, Cfg::LDQ, Ss, Sls, Cfg::LDQ, i0, j0, lane);
       x *= pw[i0 + nn + 1];
-      x = pt<false, false, BC>(x, Ads, Cfg::LDC, Ks, Cfg::LDQ, i0, j0, lane);
+      x = pt2x<SPLIT, false, false, BC>(x, Ads, Adls, Cfg::LDC, Ks, Cfg::LDQ, i0, j0, lane);
       if (ok) st4l(Zs, Cfg::LDQ, i0 + nn, j0 + 4 * gq, x);
     });
     for_tiles<BC, DVP>(w, [&](int i0, int j0, bool ok, int) {
-      f32x4 x = pt<false, false, DK>(zero4(), Qs, Cfg::LDQ, Ps, Cfg::LDV, i0, j0, lane);
+      f32x4 x = pt2y<SPLIT, false, false, DK>(zero4(), Qs, Cfg::LDQ, Ps, Pls, Cfg::LDV, i0, j0, lane);
       x *= pw[i0 + nn + 1];
-      x = pt<false, false, BC>(x, Ads, Cfg::LDC, Vs, Cfg::LDV, i0, j0, lane);
+      x = pt2x<SPLIT, false, false, BC>(x, Ads, Adls, Cfg::LDC, Vs, Cfg::LDV, i0, j0, lane);
       if (ok) st4l(Ys, Cfg::LDV, i0 + nn, j0 + 4 * gq, x);
     });
     __syncthreads();
@@ -152,14 +166,14 @@ __device__ __forceinline__ void ho3_walk_body(const Ho3Args &a, const int bh, co
           // that no branch forms around the table read
           x[e] = (l <= tr ? x[e] : 0.f) * pw[l <= tr ? 3 * (tr - l) : 0];
         }
-        if (ok) st4l(Wms, Cfg::LDC, tr, j0 + 4 * gq, x);
+        if (ok) st4_split<SPLIT>(Wms, Wmls, Cfg::LDC, tr, j0 + 4 * gq, x);
       });
       __syncthreads();
       // O = diag(g^(3(tau+1))) Q W0' + Wm Y
       for_tiles<BC, DVP>(w, [&](int i0, int j0, bool ok, int it) {
-        f32x4 x = pt<false, false, DK>(zero4(), Qs, Cfg::LDQ, Ws, Cfg::LDV, i0, j0, lane);
+        f32x4 x = pt2y<SPLIT, false, false, DK>(zero4(), Qs, Cfg::LDQ, Ws, Wls, Cfg::LDV, i0, j0, lane);
         x *= pw[3 * (i0 + nn + 1)];
-        x = pt<false, false, BC>(x, Wms, Cfg::LDC, Ys, Cfg::LDV, i0, j0, lane);
+        x = pt2x<SPLIT, false, false, BC>(x, Wms, Wmls, Cfg::LDC, Ys, Cfg::LDV, i0, j0, lane);
         O[it] = x;
         if (NORM && ok && j0 + 4 * gq == DV) dens[i0 + nn] = x[0];
       });
@@ -242,7 +256,7 @@ __device__ __forceinline__ void ho3_walk_body(const Ho3Args &a, const int bh, co
 // Walks segments (OUT ? seg_lo .. nseg-1 : 0 .. nseg-2) of every head, one workgroup each.
 template <typename T, int DK, int DV, int DVP, int BC, bool OUT, bool NORM>
 __global__ void __launch_bounds__(BWD_THREADS) ho3_walk_kernel(Ho3Args a) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[ho3_lds_bytes<T, DK, DVP, BC>()];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[ho3_lds_bytes<T, DK, DVP, BC, ho3_split<T, NORM>()>()];
   const int lo = OUT ? a.seg_lo : 0, nr = (OUT ? a.nseg : a.nseg - 1) - lo;
   ho3_walk_body<T, DK, DV, DVP, BC, OUT, NORM, false>(a, blockIdx.x / nr, lo + blockIdx.x % nr, lds);
 }
@@ -251,7 +265,7 @@ __global__ void __launch_bounds__(BWD_THREADS) ho3_walk_kernel(Ho3Args a) {
 // leave the prefix of segment 1; the rest summarise segments 1 .. nseg-2 of every head.
 template <typename T, int DK, int DV, int DVP, int BC, bool NORM>
 __global__ void __launch_bounds__(BWD_THREADS) ho3_lead_kernel(Ho3Args a) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[ho3_lds_bytes<T, DK, DVP, BC>()];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[ho3_lds_bytes<T, DK, DVP, BC, ho3_split<T, NORM>()>()];
   const int b = blockIdx.x;
   if (b < a.nbh) {
     ho3_walk_body<T, DK, DV, DVP, BC, true, NORM, true>(a, b, 0, lds);

@@ -96,6 +96,41 @@ __device__ __forceinline__ f32x4 ptw(f32x4 acc, const T *X, int ldx, const T *Y,
   return mmw<!YT, !XT, K>(acc, Y, ldy, X, ldx, j0, i0, lane, wk);
 }
 
+// ---------------------------------------------------------------------------
+// Two-term operands.  Where one bf16 rounding of an operand costs too much accuracy the
+// operand is kept as two bf16 halves, hi = bf16(x) and lo = bf16(x - hi) (about 16
+// significant bits), and a product takes one MFMA per half.
+// Four values of an LDS row, as one bf16 value (or fp32) or, with SPLIT, as hi and lo halves.
+template <bool SPLIT, typename T>
+__device__ __forceinline__ void st4_split(T *hi, T *lo, int ld, int row, int c, f32x4 x) {
+  if constexpr (SPLIT) {
+    f32x4 h;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) h[e] = (float)(T)x[e];
+    st4l(hi, ld, row, c, h);
+    st4l(lo, ld, row, c, x - h);
+  } else {
+    st4l(hi, ld, row, c, x);
+  }
+}
+
+// acc + X Y (the pt product), with Y's low half added under SPLIT
+template <bool SPLIT, bool XT, bool YT, int K, typename T>
+__device__ __forceinline__ f32x4 pt2y(f32x4 acc, const T *X, int ldx, const T *Yh, const T *Yl, int ldy, int i0,
+                                      int j0, int lane) {
+  acc = pt<XT, YT, K>(acc, X, ldx, Yh, ldy, i0, j0, lane);
+  if constexpr (SPLIT) acc = pt<XT, YT, K>(acc, X, ldx, Yl, ldy, i0, j0, lane);
+  return acc;
+}
+// acc + X Y with X's low half added under SPLIT
+template <bool SPLIT, bool XT, bool YT, int K, typename T>
+__device__ __forceinline__ f32x4 pt2x(f32x4 acc, const T *Xh, const T *Xl, int ldx, const T *Y, int ldy, int i0,
+                                      int j0, int lane) {
+  acc = pt<XT, YT, K>(acc, Xh, ldx, Y, ldy, i0, j0, lane);
+  if constexpr (SPLIT) acc = pt<XT, YT, K>(acc, Xl, ldx, Y, ldy, i0, j0, lane);
+  return acc;
+}
+
 // Waves per workgroup of these walkers (two per SIMD).
 constexpr int BWD_WAVES = 8, BWD_THREADS = 64 * BWD_WAVES;
 

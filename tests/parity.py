@@ -161,3 +161,33 @@ def ratio_per_head(o_gpu, num_ref, den_ref, unorm_ref, q, head_axes=2):
     well_head = np.sqrt(np.sum(diff ** 2, axis=all_axes)) / np.where(nr > 0, nr, 1.0)
     return {"e_rms": e_rms, "e_max": e_max, "e_rms_well": e_rms_well, "ratio_well": well_head,
             "excluded": 1.0 - np.mean(well, axis=tok_axes)}
+
+
+def ratio_workload_figures(o_gpu, den_gpu, num_gpu, num_ref, den_ref, unorm_ref, q):
+    """Every head of a normalised call: num and den rel-L2 overall and per head, and the ratio
+    criterion overall and per head.  Returns (figures, message)."""
+    num_head = per_row_rel_l2(num_gpu, num_ref, (-2, -1))
+    den_head = per_row_rel_l2(den_gpu, den_ref, (-1,))
+    rep = ratio_report(o_gpu, den_gpu, num_ref, den_ref, unorm_ref, q)
+    ph = ratio_per_head(o_gpu, num_ref, den_ref, unorm_ref, q)
+    fig = {"heads": int(np.prod(num_head.shape)), "tokens": int(num_ref.shape[-2]),
+           "num": rel_l2(num_gpu, num_ref), "num_head_max": float(num_head.max()),
+           "den": rep["den"], "den_head_max": float(den_head.max()),
+           "e_rms": rep["e_rms"], "e_rms_head_max": float(ph["e_rms"].max()),
+           "e_rms_well_head_max": float(ph["e_rms_well"].max()), "e_max": rep["e_max"],
+           "ratio_well": rep["ratio_well"], "ratio_well_head_max": float(ph["ratio_well"].max()),
+           "excluded": rep["excluded"]}
+    msg = ("num %.3g (head max %.3g) den %.3g (head max %.3g) | e_rms %.3g (head max %.3g) | ratio(well) %.3g "
+           "(head max %.3g) excluded %.3f" % (fig["num"], fig["num_head_max"], fig["den"], fig["den_head_max"],
+                                              fig["e_rms"], fig["e_rms_head_max"], fig["ratio_well"],
+                                              fig["ratio_well_head_max"], fig["excluded"]))
+    return fig, msg
+
+
+def ratio_workload_ok(fig, tol) -> bool:
+    """num and den of every head within tol; e_t's RMS over all tokens within tol/2 and, per head, over
+    its well-conditioned tokens; the rel-L2 of o over the well-conditioned tokens of the call within tol
+    (the per-head figure is reported: a head's few tokens just above the conditioning cut-off carry
+    their relative error of up to e_t / 1e-2 into it)."""
+    return (fig["num_head_max"] <= tol and fig["den_head_max"] <= tol and fig["e_rms"] <= tol / 2
+            and fig["e_rms_well_head_max"] <= tol / 2 and fig["ratio_well"] <= tol)

@@ -15,7 +15,8 @@ import torch
 from causal_prefix_scan_hla2_amd import hla2 as H
 from causal_prefix_scan_hla2_amd import inputs as I
 from oracle import oracle as O
-from tests.parity import ratio_ok, ratio_report, rel_l2, tol_for
+from tests.parity import (ratio_ok, ratio_report, ratio_workload_figures, ratio_workload_ok, record, rel_l2,
+                          tol_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -125,12 +126,21 @@ def test_ho3_decay_workload_shape_sampled():
     check(q, k, v, w.decay, False, w.dtype, heads=I.sample_heads(w.B, w.H, 3))
 
 
-def test_ho3_norm_workload_shape_sampled():
-    """The normalised workload's shape (B=4, H=8, n=2048, d=dv=64, ratio), sampled heads,
-    including the well-conditioned subset criterion."""
+def test_ho3_norm_workload_all_heads():
+    """The normalised workload's shape (B=4, H=8, n=2048, d=dv=64, ratio), every head against the
+    oracle: num and den per head, and the ratio criterion per head with the well-conditioned subset."""
     w = I.WORKLOADS["norm_2k"]
     q, k, v = I.make_qkv(w)
-    check(q, k, v, w.decay, True, w.dtype, heads=I.sample_heads(w.B, w.H, 3), subset=True)
+    o_gpu, den_gpu = gpu_ho3(q, k, v, w.decay, True)
+    num_gpu = gpu_ho3(q, k, v, w.decay, False)[0]
+    qn = q.double().numpy()
+    num, den, un, _ = O.ho3_serial_unorm(qn, k.double().numpy(), v.double().numpy(), w.decay,
+                                        threads=min(16, O.default_threads()))
+    fig, msg = ratio_workload_figures(o_gpu, den_gpu, num_gpu, num, den, un, qn)
+    record("third_order_norm_2k", **fig)
+    print(msg)
+    assert ratio_workload_ok(fig, tol_for(w.dtype)), msg
+
 
 # Without a den buffer and without the ratio the walkers carry no den column (the instantiations the
 # benchmark times): the outputs are compared with the oracle's num.
