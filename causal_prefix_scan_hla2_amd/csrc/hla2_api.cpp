@@ -24,6 +24,12 @@ struct Plan {
 constexpr long kComputeUnits = 256;
 constexpr int kMaxSegments = 64;
 constexpr long kMinChunksPerSegment = 4;
+// Lead plans at d = 64 with at most this many summaries to fold fold them in the output walk's
+// prologue instead of launching the scan.  A fold step there is latency-bound (about 2 us: the
+// summary's loads, then two barriers), so the launch is worth saving for one step only (decay
+// workload: 0.2472 -> 0.2443 ms); at six steps (normalised 2k workload) the fold took 13 us of
+// the output walk against 9.7 us for the scan launch.
+constexpr int kMaxPrologueFolds = 1;
 // Lead plans: segment 0 holds about lead_ratio(DK) times the chunks of the others, so that
 // its output walk (the slower walk per chunk) ends with the summary walks it shares the launch
 // with.  Measured per chunk, one workgroup per CU: d = 64, dv = 128: output 3.3 us, summary
@@ -691,19 +697,25 @@ int forward_run(const void *q, const void *k, const void *v, void *out, int B, i
     if (e != hipSuccess) return HLA2_ERR_LAUNCH;
   }
   if (mark(1) != hipSuccess) return HLA2_ERR_LAUNCH;
-  if (p.nseg > (p.lead ? 2 : 1)) {
+  // a lead plan at d <= 64 with few segments folds the summaries in the output walk's prologue
+  // (segment s folds s - 1 of them) instead of launching the scan
+  const float gseg = decay < 1.0f ? (float)pow((double)decay, (double)p.cps * p.kc) : 1.0f;
+  const bool pfold = p.lead && dt == 1 && p.DK == 64 && p.nseg > 2 && p.nseg - 2 <= kMaxPrologueFolds;
+  if (p.nseg > (p.lead ? 2 : 1) && !pfold) {
     hla2::ScanArgs s;
     s.sums = sums;
     s.nsum = ns;
     s.prefix = prefix;
     s.nseg = p.nseg;
-    s.gamma_seg = decay < 1.0f ? (float)pow((double)decay, (double)p.cps * p.kc) : 1.0f;
+    s.gamma_seg = gseg;
     s.first = p.lead ? 1 : 0;
     e = hla2::launch_scan(dt, p.DK, p.DV, (int)p.BH, s, stream);
     if (e != hipSuccess) return HLA2_ERR_LAUNCH;
   }
   if (mark(2) != hipSuccess) return HLA2_ERR_LAUNCH;
   a.seg_lo = p.lead ? 1 : 0;
+  a.pfold = pfold ? 1 : 0;
+  a.gamma_seg = gseg;
   e = hla2::launch_walk(dt, p.DK, p.DV, p.CP, true, dim3((unsigned)(p.BH * (p.nseg - a.seg_lo))), a, stream);
   if (e != hipSuccess) return HLA2_ERR_LAUNCH;
   if (mark(3) != hipSuccess) return HLA2_ERR_LAUNCH;

@@ -24,6 +24,9 @@ struct WalkArgs {
   int nbh = 0;            // heads B*H (lead launch: its first nbh workgroups walk segment 0)
   float *prefix_out = nullptr;  // lead launch: the prefix blocks (the buffer `prefix` names), where
                                 // segment 0's walk writes the prefix of segment 1
+  int pfold = 0;          // output launch of a lead plan without a scan launch: segment s >= 2 folds
+                          // the summaries of segments 1 .. s-1 onto segment 1's prefix itself
+  float gamma_seg = 1.f;  // decay^(tokens per full segment), for pfold
 };
 // summary blocks per (b, h) in the workspace
 __host__ __device__ inline int walk_nsum(const WalkArgs &a) { return a.sum_all ? a.nseg : a.nseg - 1; }

@@ -78,6 +78,10 @@ SMALL = [
     (1, 1, 1000, 64, 128, "bf16", 0.99, False, 64, 2),
     (1, 1, 1000, 64, 128, "bf16", 0.99, False, 64, 7),
     (1, 2, 4100, 64, 64, "bf16", 1.0, True, 32, 0),
+    # lead plans at d = 64 with 8 and 9 segments (6 and 7 summaries to fold, a ragged last
+    # segment in the first)
+    (1, 2, 2304, 64, 64, "bf16", 0.98, True, 64, 8),
+    (1, 2, 2304, 64, 128, "bf16", 0.98, True, 64, 9),
     # Strong decays (the state shrinks by 2^-5 to 2^-47 per 64-token chunk), many chunks per
     # segment, one and several segments, ratio on and off.
     (1, 2, 3000, 64, 128, "bf16", 0.95, False, 64, 1),
