@@ -75,13 +75,29 @@ def output_launch_tokens(w, plan):
     return max(w.n - c0 * 64, 0) if lead else w.n
 
 
+# Lead plans at d <= 64 with at most this many summaries to fold fold them in the output launch's
+# prologue instead of a scan launch (the library's rule).
+MAX_PROLOGUE_FOLDS = 1
+
+
+def prologue_folds(w, plan):
+    """Summaries per head that the output launch folds in its workgroups' prologues: segment s of a
+    lead plan without a scan launch folds s - 1 of them (none when the plan launches the scan)."""
+    nseg, _, _, lead = plan
+    if not (lead and w.dtype == "bf16" and w.d <= 64 and 2 < nseg <= 2 + MAX_PROLOGUE_FOLDS):
+        return 0
+    return (nseg - 2) * (nseg - 1) // 2
+
+
 def output_kernel_bytes(w, esize, plan):
     """Algorithmic HBM bytes of one chunk-output launch: q, k, v of its tokens
-    read once, their outputs written once, and the incoming state (S0, U0, u0)
-    of every segment after the first read once."""
+    read once, their outputs written once, the incoming state (S0, U0, u0) of
+    every segment after the first read once, and the summaries (S, C, U, m, u)
+    folded in the prologue read once each."""
     state = (w.d * w.d + w.d * w.dv + w.d) * 4
+    summary = (w.d * w.d + 2 * w.d * w.dv + 2 * w.d) * 4
     return w.B * w.H * output_launch_tokens(w, plan) * (2 * w.d + 2 * w.dv) * esize + \
-        w.B * w.H * (plan[0] - 1) * state
+        w.B * w.H * (plan[0] - 1) * state + w.B * w.H * prologue_folds(w, plan) * summary
 
 
 def roofline(flops, nbytes, seconds):
@@ -230,7 +246,8 @@ def bench_forward(w, steps, warmup, torch, H, I):
         "phases": phases,
         "plan": {"segments": nseg, "lead_chunks": plan[1], "seg_chunks": plan[2], "lead": plan[3]},
         "output_flops_per_call": output_kernel_flops_per_head_token(w.d, w.dv, w.chunk, w.normalize)
-                                 * w.B * w.H * output_launch_tokens(w, plan),
+                                 * w.B * w.H * output_launch_tokens(w, plan)
+                                 + w.B * w.H * prologue_folds(w, plan) * 2 * w.d * w.d * (w.dv + int(w.normalize)),
         "tokens_per_s": w.B * w.n / t,
         "head_tokens_per_s": w.head_tokens / t,
         "tflops": flops / t / 1e12,
