@@ -73,7 +73,9 @@ __device__ __forceinline__ void ahla_walk_body(const AhlaArgs &a, const int bh, 
 
   using TU = TileCount<DK, DVP>;
   f32x4 P[TU::PER], E[TU::PER];
-  const float *pref = (OUT && seg > 0) ? a.prefix + ((long)bh * a.nseg + seg) * PB : nullptr;
+  // with a prologue fold (below) segment 2 starts from segment 1's prefix
+  const bool pfold = OUT && !LEAD && a.pfold && seg == 2;
+  const float *pref = (OUT && seg > 0) ? a.prefix + ((long)bh * a.nseg + (pfold ? 1 : seg)) * PB : nullptr;
   for_tiles<DK, DVP>(w, [&](int i0, int j0, bool, int it) {
     const int o = (i0 + nn) * DVP + j0 + 4 * gq;
     P[it] = pref ? *(const f32x4 *)(pref + o) : zero4();
@@ -89,6 +91,33 @@ __device__ __forceinline__ void ahla_walk_body(const AhlaArgs &a, const int bh, 
   rq.fetch(qh, a.d, tok0, a.n, -1, tid);
   rk.fetch(kh, a.d, tok0, a.n, -1, tid);
   rv.fetch(vh, a.dv, tok0, a.n, NORM ? DV : -1, tid);
+
+  // Prologue fold (a three-segment lead plan has no scan launch): segment 2 folds segment 1's
+  // summary (P'_1, E'_1, M_1) onto segment 1's prefix with the scan's combine,
+  //   E' <- G E' + E'_1 + G M_1 P',   P' <- G P' + P'_1   (G = decay^(tokens per segment)),
+  // the product on MFMA from M_1 and P' in LDS (two-term operands under the ratio), while the
+  // first chunk's rows are in flight.  The Q, K and P' slots are free until the walk starts; M_1's
+  // halves take the Q and K slots, which hold DK rows when the chunk is DK tokens (d = 64).
+  if constexpr (OUT && !LEAD && BC == DK) {
+    if (pfold) {
+      const float G = a.gseg;
+      const float *sb = a.sums + ((long)bh * (a.nseg - 1) + 1) * SB, *Ms = sb + 2 * DK * DVP;
+      for (int e = 4 * tid; e < DK * DK; e += 4 * BWD_THREADS)
+        st4_split<SPLIT>(Qs, Ks, Cfg::LDQ, e / DK, e % DK, *(const f32x4 *)(Ms + e));
+      for_tiles<DK, DVP>(w, [&](int i0, int j0, bool ok, int it) {
+        if (ok) st4_split<SPLIT>(Ps, Pls, Cfg::LDV, i0 + nn, j0 + 4 * gq, P[it]);
+      });
+      __syncthreads();
+      for_tiles<DK, DVP>(w, [&](int i0, int j0, bool, int it) {
+        f32x4 x = pt2x<SPLIT, false, false, DK>(zero4(), Qs, Ks, Cfg::LDQ, Ps, Cfg::LDV, i0, j0, lane);
+        if constexpr (SPLIT) x = pt<false, false, DK>(x, Qs, Cfg::LDQ, Pls, Cfg::LDV, i0, j0, lane);
+        const int o = (i0 + nn) * DVP + j0 + 4 * gq;
+        E[it] = G * E[it] + *(const f32x4 *)(sb + DK * DVP + o) + G * x;
+        P[it] = G * P[it] + *(const f32x4 *)(sb + o);
+      });
+      __syncthreads();  // every read of the staged operands done
+    }
+  }
 
   for (int ch = 0; ch < nch; ++ch) {
     const int t0 = tok0 + ch * BC;

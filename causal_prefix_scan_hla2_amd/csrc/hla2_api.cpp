@@ -485,7 +485,11 @@ int hla2_ahla_forward(const void *q, const void *k, const void *v, void *out, in
     // prefix segment 0 leaves; the outputs of segments 1 .. nseg-1
     e = hla2::launch_ahla(dt, p.DK, p.DV, norm, hla2::AHLA_LEAD, (int)p.BH, a, gseg, stream);
     if (e != hipSuccess) return HLA2_ERR_LAUNCH;
-    if (p.nseg > 2) {
+    if (p.nseg == 3 && p.DK == 64) {
+      // one summary to fold: segment 2's output workgroups fold it in their prologue
+      a.pfold = 1;
+      a.gseg = gseg;
+    } else if (p.nseg > 2) {
       a.first = 1;
       e = hla2::launch_ahla(dt, p.DK, p.DV, norm, hla2::AHLA_SCAN, (int)p.BH, a, gseg, stream);
       if (e != hipSuccess) return HLA2_ERR_LAUNCH;

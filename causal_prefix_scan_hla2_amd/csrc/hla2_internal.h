@@ -199,6 +199,9 @@ struct AhlaArgs {
   int seg_lo = 0;          // output launch: walks segments seg_lo .. nseg-1
   int nbh = 0;             // heads B*H (lead launch: its first nbh workgroups walk segment 0)
   int first = 0;           // scan: 1 when the prefix of segment 1 is given (lead plans)
+  int pfold = 0;           // output launch of a three-segment lead plan without a scan launch: segment 2
+                           // folds segment 1's summary onto segment 1's prefix itself
+  float gseg = 1.f;        // decay^(tokens per full segment), for pfold
 };
 // Segment geometry of the AHLA / third-order plans, in chunks of kc tokens.
 __host__ __device__ inline int ahla_seg_chunk0(const AhlaArgs &a, int s) {
