@@ -30,7 +30,13 @@ def test_output_launch_bytes_under_a_lead_plan():
     tokens = 8192 - 34 * 64
     assert bench.output_launch_tokens(w, plan) == tokens
     state = (64 * 64 + 64 * 128 + 64) * 4  # S0, U0, u0 in fp32, read by segments 1 and 2
-    assert bench.output_kernel_bytes(w, 2, plan) == 8 * 16 * tokens * 384 * 2 + 8 * 16 * 2 * state == 604045312
+    # segment 1's summary S, C, U, m, u in fp32, read once by segment 2's workgroups (their prologue fold)
+    summary = (64 * 64 + 2 * 64 * 128 + 2 * 64) * 4
+    assert bench.prologue_folds(w, plan) == 1
+    assert bench.output_kernel_bytes(w, 2, plan) == \
+        8 * 16 * tokens * 384 * 2 + 8 * 16 * 2 * state + 8 * 16 * summary == 614596608
+    # a plan with more segments launches the scan: no fold in the output launch
+    assert bench.prologue_folds(w, (5, 20, 27, True)) == 0
     # a plain plan walks every token in the output launch
     assert bench.output_launch_tokens(w, (4, 32, 32, False)) == 8192
 
