@@ -569,7 +569,12 @@ int hla2_ho3_forward(const void *q, const void *k, const void *v, void *out, int
     // as for AHLA: segment 0's outputs beside the summaries, the scan from its prefix, the rest
     e = hla2::launch_ho3(dt, p.DK, p.DV, norm, hla2::HO3_LEAD, (int)p.BH, a, gseg, stream);
     if (e != hipSuccess) return HLA2_ERR_LAUNCH;
-    if (p.nseg > 2) {
+    if (p.nseg == 3 && !(norm && p.DV > 64)) {
+      // one summary to fold: segment 2's output workgroups fold it in their prologue (the walkers of
+      // the ratio at dv = 128 step by 32-token chunks, whose slots cannot stage the d x d operands)
+      a.pfold = 1;
+      a.gseg = gseg;
+    } else if (p.nseg > 2) {
       a.first = 1;
       e = hla2::launch_ho3(dt, p.DK, p.DV, norm, hla2::HO3_SCAN, (int)p.BH, a, gseg, stream);
       if (e != hipSuccess) return HLA2_ERR_LAUNCH;

@@ -82,7 +82,9 @@ __device__ __forceinline__ void ho3_walk_body(const Ho3Args &a, const int bh, co
   using TS = TileCount<DK, DK>;
   using TU = TileCount<DK, DVP>;
   f32x4 S[TS::PER], P[TU::PER], W[TU::PER];
-  const float *pref = (OUT && seg > 0) ? a.prefix + ((long)bh * a.nseg + seg) * Cfg::PB : nullptr;
+  // with a prologue fold (below) segment 2 starts from segment 1's prefix
+  const bool pfold = OUT && !LEAD && a.pfold && seg == 2;
+  const float *pref = (OUT && seg > 0) ? a.prefix + ((long)bh * a.nseg + (pfold ? 1 : seg)) * Cfg::PB : nullptr;
   for_tiles<DK, DK>(w, [&](int i0, int j0, bool, int it) {
     S[it] = pref ? *(const f32x4 *)(pref + (i0 + nn) * DK + j0 + 4 * gq) : zero4();
   });
@@ -103,6 +105,53 @@ __device__ __forceinline__ void ho3_walk_body(const Ho3Args &a, const int bh, co
   rq.fetch(qh, a.d, tok0, a.n, -1, tid);
   rk.fetch(kh, a.d, tok0, a.n, -1, tid);
   rv.fetch(vh, a.dv, tok0, a.n, NORM ? DV : -1, tid);
+
+  // Prologue fold (a three-segment lead plan has no scan launch): segment 2 folds segment 1's
+  // summary onto segment 1's prefix (S_A, P'_A, W'_A) with the segment combine,
+  //   T = S_A Q2 + X2,  W' <- G^3 W'_A + W'_1 + T P'_A + S_A X1,  S <- G S_A + S_1,  P' <- G P'_A + P'_1,
+  // the products on MFMA from operands staged in the slots that are free until the walk starts (two
+  // bf16 halves under the ratio), while the first chunk's rows are in flight.  The Q, K, Z and Ad slots
+  // take DK rows when the chunk is DK tokens.
+  if constexpr (OUT && !LEAD && BC == DK) {
+    static_assert(Cfg::LDC == Cfg::LDQ, "T's halves share one pitch");
+    if (pfold) {
+      const float G = a.gseg, G3 = G * G * G;
+      const float *sb = a.sums + ((long)bh * (a.nseg - 1) + 1) * Cfg::SB;
+      const float *Q2g = sb + Cfg::PB, *X1g = Q2g + DK * DK, *X2g = X1g + DK * DVP;
+      for_tiles<DK, DK>(w, [&](int i0, int j0, bool ok, int it) {
+        if (ok) st4_split<SPLIT>(Ss, Sls, Cfg::LDQ, i0 + nn, j0 + 4 * gq, S[it]);
+      });
+      for_tiles<DK, DVP>(w, [&](int i0, int j0, bool ok, int it) {
+        if (ok) st4_split<SPLIT>(Ps, Pls, Cfg::LDV, i0 + nn, j0 + 4 * gq, P[it]);
+      });
+      for (int e = 4 * tid; e < DK * DK; e += 4 * BWD_THREADS)
+        st4_split<SPLIT>(Qs, Ks, Cfg::LDQ, e / DK, e % DK, *(const f32x4 *)(Q2g + e));
+      for (int e = 4 * tid; e < DK * DVP; e += 4 * BWD_THREADS)
+        st4_split<SPLIT>(Vs, Ys, Cfg::LDV, e / DVP, e % DVP, *(const f32x4 *)(X1g + e));
+      __syncthreads();
+      // T = S_A Q2 + X2
+      for_tiles<DK, DK>(w, [&](int i0, int j0, bool ok, int) {
+        f32x4 x = pt2x<SPLIT, false, false, DK>(zero4(), Ss, Sls, Cfg::LDQ, Qs, Cfg::LDQ, i0, j0, lane);
+        if constexpr (SPLIT) x = pt<false, false, DK>(x, Ss, Cfg::LDQ, Ks, Cfg::LDQ, i0, j0, lane);
+        x += *(const f32x4 *)(X2g + (i0 + nn) * DK + j0 + 4 * gq);
+        if (ok) st4_split<SPLIT>(Zs, Ads, Cfg::LDQ, i0 + nn, j0 + 4 * gq, x);
+      });
+      __syncthreads();
+      for_tiles<DK, DVP>(w, [&](int i0, int j0, bool, int it) {
+        f32x4 x = pt2x<SPLIT, false, false, DK>(zero4(), Zs, Ads, Cfg::LDQ, Ps, Cfg::LDV, i0, j0, lane);
+        if constexpr (SPLIT) x = pt<false, false, DK>(x, Zs, Cfg::LDQ, Pls, Cfg::LDV, i0, j0, lane);
+        x = pt2x<SPLIT, false, false, DK>(x, Ss, Sls, Cfg::LDQ, Vs, Cfg::LDV, i0, j0, lane);
+        if constexpr (SPLIT) x = pt<false, false, DK>(x, Ss, Cfg::LDQ, Ys, Cfg::LDV, i0, j0, lane);
+        const int o = (i0 + nn) * DVP + j0 + 4 * gq;
+        W[it] = G3 * W[it] + *(const f32x4 *)(sb + DK * DK + DK * DVP + o) + x;
+        P[it] = G * P[it] + *(const f32x4 *)(sb + DK * DK + o);
+      });
+      for_tiles<DK, DK>(w, [&](int i0, int j0, bool, int it) {
+        S[it] = G * S[it] + *(const f32x4 *)(sb + (i0 + nn) * DK + j0 + 4 * gq);
+      });
+      __syncthreads();  // every read of the staged operands done
+    }
+  }
 
   for (int ch = 0; ch < nch; ++ch) {
     const int t0 = tok0 + ch * BC;
