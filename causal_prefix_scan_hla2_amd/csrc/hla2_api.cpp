@@ -698,10 +698,13 @@ int forward_run(const void *q, const void *k, const void *v, void *out, int B, i
   auto mark = [&](int i) { return (events && events[i]) ? hipEventRecord(events[i], stream) : hipSuccess; };
   hipError_t e = mark(0);
   if (e != hipSuccess) return HLA2_ERR_LAUNCH;
+  // with the final state of a sequence shorter than one chunk there is no full chunk to summarise:
+  // the state kernel absorbs every token itself
+  const bool all_tail = state && p.nseg == 1 && n < p.kc;
   if (p.lead) {
     e = hla2::launch_walk_lead(p.DK, p.DV, dim3((unsigned)(p.BH * ns)), a, stream);
     if (e != hipSuccess) return HLA2_ERR_LAUNCH;
-  } else if (ns > 0) {
+  } else if (ns > 0 && !all_tail) {
     e = hla2::launch_walk(dt, p.DK, p.DV, p.CP, false, dim3((unsigned)(p.BH * ns)), a, stream);
     if (e != hipSuccess) return HLA2_ERR_LAUNCH;
   }
@@ -730,7 +733,7 @@ int forward_run(const void *q, const void *k, const void *v, void *out, int B, i
   if (mark(3) != hipSuccess) return HLA2_ERR_LAUNCH;
   if (state) {
     hla2::StateArgs st;
-    st.sums = sums;
+    st.sums = all_tail ? nullptr : sums;
     st.prefix = prefix;
     st.q = q;
     st.k = k;

@@ -39,48 +39,61 @@ __global__ void __launch_bounds__(256) state_kernel(StateArgs a) {
   float *zv = ms + DK;            // z of a tail token (two buffers)
   T *tq = tsh, *tk = tq + TB * DK, *tvv = tk + TB * DK;  // staged tail rows
 
-  const float *sums = a.sums + (long)bh * a.nseg * SB;
+  // a sequence shorter than one chunk is all tail: no summary was written (sums is null)
+  const float *sums = a.sums ? a.sums + (long)bh * a.nseg * SB : nullptr;
   auto gam_tokens = [&](int t) -> float { return a.decay_on ? exp2f((float)t * a.log2g) : 1.f; };
   const int seg_tokens = a.cps * a.kc;
   const int last_tok0 = L * seg_tokens;
   const int last_full = ((min(a.n, last_tok0 + seg_tokens) - last_tok0) / a.kc) * a.kc;  // tokens in L's summary
   const float GL = gam_tokens(last_full);
 
-  // ---- U, u: combine of the prefix of L with the summary of L
-  const float *sL = sums + (long)L * SB;
-  const float *SL = sL, *CL = SL + DK * DK, *UL = CL + DK * DV, *mL = UL + DK * DV, *uL = mL + DK;
-  const float *pref = a.nseg > 1 ? a.prefix + ((long)bh * a.nseg + L) * PB : nullptr;
-  for (int e = tid; e < DK * DK; e += NT) St[e] = pref ? pref[e] : 0.f;  // S0
-  for (int e = tid; e < DK * DV; e += NT) Cs[e] = CL[e];
-  for (int e = tid; e < DK; e += NT) ms[e] = mL[e];
-  __syncthreads();
+  // ---- U, u: combine of the prefix of L with the summary of L (the summary alone when L is the
+  // only segment, whose prefix is zero)
   f32x4 U[NBT][4];  // rows i0 + 0..3 of block (i0, j0), columns j0 .. j0+3
   float u = 0.f;    // u[tid] for tid < DK
+  const float *pref = a.nseg > 1 ? a.prefix + ((long)bh * a.nseg + L) * PB : nullptr;
 #pragma unroll
-  for (int b = 0; b < NBT; ++b) {
-    const int blk = tid + b * NT;
-    if (blk < NB4) {
-      const int i0 = 4 * (blk / BPR), j0 = 4 * (blk % BPR);
-      f32x4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
-      for (int k = 0; k < DK; ++k) {
-        const f32x4 sc = *(const f32x4 *)(St + k * DK + i0);
-        const f32x4 cr = *(const f32x4 *)(Cs + k * DV + j0);
+  for (int b = 0; b < NBT; ++b)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] += sc[r] * cr;
-      }
+    for (int r = 0; r < 4; ++r) U[b][r] = zero4();
+  if (sums) {
+    const float *sL = sums + (long)L * SB;
+    const float *SL = sL, *CL = SL + DK * DK, *UL = CL + DK * DV, *mL = UL + DK * DV, *uL = mL + DK;
+    if (pref) {
+      for (int e = tid; e < DK * DK; e += NT) St[e] = pref[e];  // S0
+      for (int e = tid; e < DK * DV; e += NT) Cs[e] = CL[e];
+      for (int e = tid; e < DK; e += NT) ms[e] = mL[e];
+      __syncthreads();
+    }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const f32x4 u0 = pref ? *(const f32x4 *)(pref + DK * DK + (i0 + r) * DV + j0) : zero4();
-        const f32x4 ul = *(const f32x4 *)(UL + (i0 + r) * DV + j0);
-        U[b][r] = GL * GL * u0 + ul + GL * acc[r];
+    for (int b = 0; b < NBT; ++b) {
+      const int blk = tid + b * NT;
+      if (blk < NB4) {
+        const int i0 = 4 * (blk / BPR), j0 = 4 * (blk % BPR);
+        f32x4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
+        if (pref) {
+          for (int k = 0; k < DK; ++k) {
+            const f32x4 sc = *(const f32x4 *)(St + k * DK + i0);
+            const f32x4 cr = *(const f32x4 *)(Cs + k * DV + j0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] += sc[r] * cr;
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const f32x4 u0 = pref ? *(const f32x4 *)(pref + DK * DK + (i0 + r) * DV + j0) : zero4();
+          const f32x4 ul = *(const f32x4 *)(UL + (i0 + r) * DV + j0);
+          U[b][r] = GL * GL * u0 + ul + GL * acc[r];
+        }
       }
     }
-  }
-  if (tid < DK) {
-    float s = 0.f;
-    for (int k = 0; k < DK; ++k) s += St[k * DK + tid] * ms[k];
-    const float u0 = pref ? pref[DK * DK + DK * DV + tid] : 0.f;
-    u = GL * GL * u0 + uL[tid] + GL * s;
+    if (tid < DK) {
+      float s = 0.f;
+      if (pref)
+        for (int k = 0; k < DK; ++k) s += St[k * DK + tid] * ms[k];
+      const float u0 = pref ? pref[DK * DK + DK * DV + tid] : 0.f;
+      u = GL * GL * u0 + uL[tid] + GL * s;
+    }
   }
   __syncthreads();
 
@@ -93,7 +106,7 @@ __global__ void __launch_bounds__(256) state_kernel(StateArgs a) {
     for (int i = 0; i < NS; ++i) xs[i] = 0.f;
 #pragma unroll
     for (int i = 0; i < NC; ++i) xc[i] = 0.f;
-    for (int r = 0; r <= L; ++r) {
+    for (int r = 0; sums && r <= L; ++r) {
       const float G = r < L ? Gf : GL;
       const float *sr = sums + (long)r * SB;
 #pragma unroll
