@@ -24,12 +24,13 @@ struct Plan {
 constexpr long kComputeUnits = 256;
 constexpr int kMaxSegments = 64;
 constexpr long kMinChunksPerSegment = 4;
-// Lead plans at d = 64 with at most this many summaries to fold fold them in the output walk's
-// prologue instead of launching the scan.  A fold step there is latency-bound (about 2 us: the
-// summary's loads, then two barriers), so the launch is worth saving for one step only (decay
-// workload: 0.2472 -> 0.2443 ms); at six steps (normalised 2k workload) the fold took 13 us of
-// the output walk against 9.7 us for the scan launch.
+// Lead plans at d = 64 with this many summaries to fold (three segments) fold it in the output
+// walk's prologue instead of launching the scan; the walker folds exactly one.  A fold step there
+// is latency-bound (about 2 us: the summary's loads, then two barriers), so the launch is worth
+// saving for one step only (decay workload: 0.2472 -> 0.2443 ms); at six steps (normalised 2k
+// workload) a fold loop took 13 us of the output walk against 9.7 us for the scan launch.
 constexpr int kMaxPrologueFolds = 1;
+static_assert(kMaxPrologueFolds == 1, "the output walker folds exactly one summary in its prologue");
 // Lead plans: segment 0 holds about lead_ratio(DK) times the chunks of the others, so that
 // its output walk (the slower walk per chunk) ends with the summary walks it shares the launch
 // with.  Measured per chunk, one workgroup per CU: d = 64, dv = 128: output 3.3 us, summary
@@ -709,8 +710,8 @@ int forward_run(const void *q, const void *k, const void *v, void *out, int B, i
     if (e != hipSuccess) return HLA2_ERR_LAUNCH;
   }
   if (mark(1) != hipSuccess) return HLA2_ERR_LAUNCH;
-  // a lead plan at d <= 64 with few segments folds the summaries in the output walk's prologue
-  // (segment s folds s - 1 of them) instead of launching the scan
+  // a three-segment lead plan at d = 64 folds segment 1's summary in the prologue of segment 2's
+  // output walk instead of launching the scan
   const float gseg = decay < 1.0f ? (float)pow((double)decay, (double)p.cps * p.kc) : 1.0f;
   const bool pfold = p.lead && dt == 1 && p.DK == 64 && p.nseg > 2 && p.nseg - 2 <= kMaxPrologueFolds;
   if (p.nseg > (p.lead ? 2 : 1) && !pfold) {

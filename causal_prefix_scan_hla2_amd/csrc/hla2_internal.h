@@ -24,8 +24,8 @@ struct WalkArgs {
   int nbh = 0;            // heads B*H (lead launch: its first nbh workgroups walk segment 0)
   float *prefix_out = nullptr;  // lead launch: the prefix blocks (the buffer `prefix` names), where
                                 // segment 0's walk writes the prefix of segment 1
-  int pfold = 0;          // output launch of a lead plan without a scan launch: segment s >= 2 folds
-                          // the summaries of segments 1 .. s-1 onto segment 1's prefix itself
+  int pfold = 0;          // output launch of a three-segment lead plan without a scan launch:
+                          // segment 2 folds segment 1's summary onto segment 1's prefix itself
   float gamma_seg = 1.f;  // decay^(tokens per full segment), for pfold
 };
 // summary blocks per (b, h) in the workspace

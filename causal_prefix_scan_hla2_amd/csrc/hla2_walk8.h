@@ -284,6 +284,78 @@ __device__ __forceinline__ void walk8_body(const WalkArgs &a, const int bh, cons
     }
   };
 
+  // ---------------- prologue: the first chunk's loads, then the prologue fold ----------------
+  load_chunk(0);
+
+  // A three-segment lead plan has no scan launch: the workgroups of segment 2 fold segment 1's
+  // summary onto segment 1's prefix with the scan's combine
+  //   S <- G S + S_1,   U <- G^2 U + U_1 + G S C_1,   u <- G^2 u + u_1 + G S m_1
+  // (G = decay^(tokens per segment); the cross products on bf16 MFMA from a bf16 copy of S, as
+  // in the scan) while the first chunk's rows are in flight.  It runs before the loop-invariant
+  // factors are formed, so its operands never share the register file with them.
+  if constexpr (OUT && !LEAD && DK == 64) {
+    if (a.pfold && seg == 2) {
+      const float G1 = a.gamma_seg, G2 = G1 * G1;
+      const float *sS = a.sums + (long)bh * walk_nsum(a) * sum_block_floats(DK, DV) + sum_block_floats(DK, DV);
+      const float *sC = sS + DK * DK, *sU = sC + DK * DV, *sm = sU + DK * DV, *su = sm + DK;
+      // C_1 in the contiguous k-order of the S rows (lane (g, n): rows 32 s + 8 g + e, column n of the tile)
+      bf16x8 cb[KD][UCT], mb[KD];
+#pragma unroll
+      for (int s2 = 0; s2 < KD; ++s2)
+#pragma unroll
+        for (int j = 0; j < UCT; ++j)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) cb[s2][j][e] = (bf16)sC[(32 * s2 + 8 * g + e) * DV + 16 * vtile(j) + n];
+      f32x4 fu[RT][UCT], fuu = zero4();
+#pragma unroll
+      for (int i = 0; i < RT; ++i)
+#pragma unroll
+        for (int j = 0; j < UCT; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) fu[i][j][q] = sU[(16 * i + 4 * g + q) * DV + 16 * vtile(j) + n];
+      if constexpr (DEN) {
+#pragma unroll
+        for (int s2 = 0; s2 < KD; ++s2)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) mb[s2][e] = (bf16)(n == 0 ? sm[32 * s2 + 8 * g + e] : 0.f);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float x = su[16 * urow + 4 * g + q];
+          fuu[q] = n == 0 ? x : 0.f;  // u lives in column 0 of its tile
+        }
+      }
+      write_S0();
+      __syncthreads();  // the bf16 rows of S
+#pragma unroll
+      for (int i = 0; i < RT; ++i) {
+        bf16x8 sa[KD];
+#pragma unroll
+        for (int s2 = 0; s2 < KD; ++s2) sa[s2] = w8_rows(Sb, LDS0, 16 * i, 32 * s2, lane);
+#pragma unroll
+        for (int j = 0; j < UCT; ++j) {
+          f32x4 mm = zero4();
+#pragma unroll
+          for (int s2 = 0; s2 < KD; ++s2) mm = mma(sa[s2], cb[s2][j], mm);
+          Uacc[i][j] = G2 * Uacc[i][j] + fu[i][j] + G1 * mm;
+        }
+      }
+      if constexpr (DEN) {
+        f32x4 mu = zero4();
+#pragma unroll
+        for (int s2 = 0; s2 < KD; ++s2) mu = mma(w8_rows(Sb, LDS0, 16 * urow, 32 * s2, lane), mb[s2], mu);
+        uacc = G2 * uacc + fuu + G1 * mu;
+      }
+      __syncthreads();  // every read of the bf16 rows of S done
+#pragma unroll
+      for (int i = 0; i < SRT; ++i)
+#pragma unroll
+        for (int j = 0; j < SCT; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            Sacc[i][j][q] = G1 * Sacc[i][j][q] + sS[(16 * (srow0 + i) + 4 * g + q) * DK + 16 * (scol0 + j) + n];
+    }
+  }
+
   // ---------------- loop-invariant factors ----------------
   __syncthreads();  // pw
   const int tau_w = 16 * tb + n;  // this lane's row in the wave's token block
@@ -362,104 +434,6 @@ __device__ __forceinline__ void walk8_body(const WalkArgs &a, const int bh, cons
       }
     }
   };
-
-  // ---------------- prologue ----------------
-  load_chunk(0);
-
-  // ---------------- prologue fold (pfold, d = 64) ----------------
-  // A lead plan with few segments has no scan launch: the workgroup of segment seg >= 2 folds
-  // the summaries of segments 1 .. seg-1 onto segment 1's prefix with the scan's combine
-  //   S <- G S + S_r,   U <- G^2 U + U_r + G S C_r,   u <- G^2 u + u_r + G S m_r
-  // (G = decay^(tokens per segment); the cross products on bf16 MFMA from a bf16 copy of S, as
-  // in the scan).  The next summary's values are loaded while the current one is folded, and the
-  // first chunk's rows are already in flight.
-  if constexpr (OUT && !LEAD && DK == 64) {
-    if (a.pfold && seg > 1) {
-      const float G1 = a.gamma_seg, G2 = G1 * G1;
-      const long sbf = sum_block_floats(DK, DV);
-      const float *const sums_h = a.sums + (long)bh * walk_nsum(a) * sbf;
-      struct FoldIn {
-        f32x4 s[SRT][SCT], u[RT][UCT], uu;
-        float c[KD][UCT][8], m[KD][8];
-      };
-      auto load_fold = [&](int r, FoldIn &f) __attribute__((always_inline)) {
-        const float *sS = sums_h + (long)r * sbf, *sC = sS + DK * DK, *sU = sC + DK * DV;
-        const float *sm = sU + DK * DV, *su = sm + DK;
-#pragma unroll
-        for (int i = 0; i < SRT; ++i)
-#pragma unroll
-          for (int j = 0; j < SCT; ++j)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) f.s[i][j][q] = sS[(16 * (srow0 + i) + 4 * g + q) * DK + 16 * (scol0 + j) + n];
-#pragma unroll
-        for (int i = 0; i < RT; ++i)
-#pragma unroll
-          for (int j = 0; j < UCT; ++j)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) f.u[i][j][q] = sU[(16 * i + 4 * g + q) * DV + 16 * vtile(j) + n];
-        // C_r in the contiguous k-order of the S rows (lane (g, n): rows 32 s + 8 g + e, column n of the tile)
-#pragma unroll
-        for (int s2 = 0; s2 < KD; ++s2)
-#pragma unroll
-          for (int j = 0; j < UCT; ++j)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) f.c[s2][j][e] = sC[(32 * s2 + 8 * g + e) * DV + 16 * vtile(j) + n];
-        if constexpr (DEN) {
-#pragma unroll
-          for (int s2 = 0; s2 < KD; ++s2)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) f.m[s2][e] = sm[32 * s2 + 8 * g + e];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float x = su[16 * urow + 4 * g + q];
-            f.uu[q] = n == 0 ? x : 0.f;  // u lives in column 0 of its tile
-          }
-        }
-      };
-      FoldIn cur, nxt;
-      load_fold(1, cur);
-      for (int r = 1; r < seg; ++r) {
-        if (r + 1 < seg) load_fold(r + 1, nxt);
-        write_S0();
-        __syncthreads();  // the bf16 rows of S
-#pragma unroll
-        for (int i = 0; i < RT; ++i) {
-          bf16x8 sa[KD];
-#pragma unroll
-          for (int s2 = 0; s2 < KD; ++s2) sa[s2] = w8_rows(Sb, LDS0, 16 * i, 32 * s2, lane);
-#pragma unroll
-          for (int j = 0; j < UCT; ++j) {
-            f32x4 mm = zero4();
-#pragma unroll
-            for (int s2 = 0; s2 < KD; ++s2) {
-              bf16x8 cb;
-#pragma unroll
-              for (int e = 0; e < 8; ++e) cb[e] = (bf16)cur.c[s2][j][e];
-              mm = mma(sa[s2], cb, mm);
-            }
-            Uacc[i][j] = G2 * Uacc[i][j] + cur.u[i][j] + G1 * mm;
-          }
-        }
-        if constexpr (DEN) {
-          f32x4 mu = zero4();
-#pragma unroll
-          for (int s2 = 0; s2 < KD; ++s2) {
-            bf16x8 mb;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) mb[e] = (bf16)(n == 0 ? cur.m[s2][e] : 0.f);
-            mu = mma(w8_rows(Sb, LDS0, 16 * urow, 32 * s2, lane), mb, mu);
-          }
-          uacc = G2 * uacc + cur.uu + G1 * mu;
-        }
-        __syncthreads();  // every read of the bf16 rows of S done
-#pragma unroll
-        for (int i = 0; i < SRT; ++i)
-#pragma unroll
-          for (int j = 0; j < SCT; ++j) Sacc[i][j] = G1 * Sacc[i][j] + cur.s[i][j];
-        cur = nxt;
-      }
-    }
-  }
 
   write_S0();
   write_u0(0);
