@@ -58,6 +58,33 @@ __device__ __forceinline__ bf16x8 w8_rows(const bf16 *X, int ld, int row0, int k
   return *(const bf16x8 *)(X + (row0 + (lane & 15)) * ld + k0 + 8 * (lane >> 4));
 }
 
+// Swizzled rows.  The buffers that take 8-byte row writes from accumulator tiles (lane (g, n)
+// writes row n) keep the 16-byte piece j of row r at piece j ^ ((r >> 2) & 1).  Measured on the
+// device at a 160-byte pitch (cycles of LDS time per wave-wide access): 8-byte accumulator-row
+// writes 16 -> 8, while 16-byte row reads stay at 4 and transpose reads of 8 rows at 2 (a swizzle
+// on row bit 3 instead also halves the writes but doubles the 16-byte reads).  In elements: column
+// c of row r sits at c ^ (((r >> 2) & 1) << 3).
+
+// The swizzle of a lane's row in an accumulator-row access (row 16 x + n): bit 2 of n.  Column
+// bases that are multiples of 16 keep bit 3 clear, so the swizzled column is base + (lane part ^
+// sw) and the base stays a constant offset of the access.
+__device__ __forceinline__ int w8_swl(int lane) { return ((lane >> 2) & 1) << 3; }
+
+// w8_rows on a swizzled buffer (row0 and k0 multiples of 16)
+__device__ __forceinline__ bf16x8 w8_rows_sw(const bf16 *X, int ld, int row0, int k0, int lane) {
+  return *(const bf16x8 *)(X + (row0 + (lane & 15)) * ld + k0 + ((8 * (lane >> 4)) ^ w8_swl(lane)));
+}
+
+// ld_cols on a swizzled buffer (k0 a multiple of 32, col0 of 16): lane (g, n) gets
+// X[k-order of group g][col0 + n]; its rows k0 + 4 g + 0..3 (and 16 further) have bit 2 = g & 1
+__device__ __forceinline__ bf16x8 w8_cols_sw(const bf16 *X, int ld, int k0, int col0, int lane) {
+  const int g = lane >> 4, src = lane & 15;
+  const bf16 *p = X + (k0 + 4 * g + (src >> 2)) * ld + col0 + ((4 * (src & 3)) ^ ((g & 1) << 3));
+  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
+  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p + 16 * ld));
+  return cat8(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi));
+}
+
 // LDS byte address of an element, passed through an empty asm: reads made from different
 // laundered addresses are never paired by the compiler into one (slower) paired read.
 __device__ __forceinline__ unsigned w8_lds_addr(const bf16 *p) {
@@ -67,6 +94,13 @@ __device__ __forceinline__ unsigned w8_lds_addr(const bf16 *p) {
 }
 __device__ __forceinline__ bf16x4 w8_ld4(unsigned a) {
   return *(__attribute__((address_space(3))) const bf16x4 *)(size_t)a;
+}
+
+// Row fragment in the accumulator k-order: lane (g, n) gets X[row0 + n][k0 + 4g + 0..3,
+// k0 + 16 + 4g + 0..3] with two 8-byte reads, each from its own opaque base.
+__device__ __forceinline__ bf16x8 w8_rows_acc(const bf16 *X, int ld, int row0, int k0, int lane) {
+  const bf16 *p = X + (row0 + (lane & 15)) * ld + k0 + 4 * (lane >> 4);
+  return cat8(w8_ld4(w8_lds_addr(p)), w8_ld4(w8_lds_addr(p + 16)));
 }
 
 // Column position of logical token j in a W row: within every 32 columns, the four 4-element
@@ -99,7 +133,8 @@ struct W8Cfg {
   // Row pitches (elements) in LDS, chosen for how each buffer is read (gfx950 LDS: 64 banks of
   // 4 bytes).  Measured on the device: 16-byte reads of 16 rows at one column and transpose
   // reads of 8 rows x 32 bytes are conflict-free when rows start 160 (or 288) bytes apart;
-  // 8-byte reads of 16 rows at one column are conflict-free 144 bytes apart.
+  // 8-byte reads of 16 rows at one column are conflict-free 144 bytes apart.  Z~, S0, Z and W,
+  // which also take 8-byte row writes, are swizzled (w8_sw).
   static constexpr int LDK = DK + 16;      // K: 16-byte row reads and transpose reads
   static constexpr int LDQ = OUT ? DK + 8 : DK + 16;  // Q: 8-byte row reads (summary mode: transpose)
   static constexpr int LDT = DK + 16;      // Z~: transpose reads
@@ -276,7 +311,8 @@ __device__ __forceinline__ void walk8_body(const WalkArgs &a, const int bh, cons
 #pragma unroll
     for (int i = 0; i < SRT; ++i)
 #pragma unroll
-      for (int j = 0; j < SCT; ++j) st4(Sb + (16 * (scol0 + j) + n) * LDS0 + 16 * (srow0 + i) + 4 * g, Sacc[i][j]);
+      for (int j = 0; j < SCT; ++j)
+        st4(Sb + (16 * (scol0 + j) + n) * LDS0 + 16 * (srow0 + i) + ((4 * g) ^ w8_swl(lane)), Sacc[i][j]);
   };
   auto write_u0 = [&](int buf) __attribute__((always_inline)) {
     if constexpr (DEN) {
@@ -330,7 +366,7 @@ __device__ __forceinline__ void walk8_body(const WalkArgs &a, const int bh, cons
       for (int i = 0; i < RT; ++i) {
         bf16x8 sa[KD];
 #pragma unroll
-        for (int s2 = 0; s2 < KD; ++s2) sa[s2] = w8_rows(Sb, LDS0, 16 * i, 32 * s2, lane);
+        for (int s2 = 0; s2 < KD; ++s2) sa[s2] = w8_rows_sw(Sb, LDS0, 16 * i, 32 * s2, lane);
 #pragma unroll
         for (int j = 0; j < UCT; ++j) {
           f32x4 mm = zero4();
@@ -342,7 +378,7 @@ __device__ __forceinline__ void walk8_body(const WalkArgs &a, const int bh, cons
       if constexpr (DEN) {
         f32x4 mu = zero4();
 #pragma unroll
-        for (int s2 = 0; s2 < KD; ++s2) mu = mma(w8_rows(Sb, LDS0, 16 * urow, 32 * s2, lane), mb[s2], mu);
+        for (int s2 = 0; s2 < KD; ++s2) mu = mma(w8_rows_sw(Sb, LDS0, 16 * urow, 32 * s2, lane), mb[s2], mu);
         uacc = G2 * uacc + fuu + G1 * mu;
       }
       __syncthreads();  // every read of the bf16 rows of S done
@@ -428,7 +464,11 @@ __device__ __forceinline__ void walk8_body(const WalkArgs &a, const int bh, cons
     if constexpr (OST) {
 #pragma unroll
       for (int i = 0; i < NPO; ++i) {
-        const int id = tid + i * NT, row = id / (DV / 8), cg = 8 * (id % (DV / 8));
+        // rows of 16 pieces: lanes 0-7 and 16-23 (read together) take one whole row, so the
+        // read covers the 64 banks once
+        const int id = tid + i * NT, l = id & 31;
+        const int row = DV / 8 == 16 ? 2 * (id >> 5) + ((l >> 3) & 1) : id / (DV / 8);
+        const int cg = DV / 8 == 16 ? 8 * ((l & 7) | ((l >> 4) << 3)) : 8 * (id % (DV / 8));
         const u32x4 x = *(const u32x4 *)(Os + row * LDO + cg);
         __builtin_amdgcn_raw_buffer_store_b128(x, ro, cg < dv ? ((trow + row) * dv + cg) * 2 : 0x7fffffff, 0, 0);
       }
@@ -498,13 +538,13 @@ __device__ __forceinline__ void walk8_body(const WalkArgs &a, const int bh, cons
       for (int s = 0; s < KC; ++s) kt[s] = ld_cols(Ks, LDK, 32 * s, 16 * ti, lane);
       f32x4 z = zero4();
 #pragma unroll
-      for (int s = 0; s < KD; ++s) z = mma(w8_rows(Sb, LDS0, 16 * ti, 32 * s, lane), qw[s], z);
+      for (int s = 0; s < KD; ++s) z = mma(w8_rows_sw(Sb, LDS0, 16 * ti, 32 * s, lane), qw[s], z);
       if (DEC) z *= zf;
 #pragma unroll
       for (int s = 0; s < KC; ++s) z = mma(kt[s], adf[s], z);
       // Z[tau][16 ti + 4 g + r] and its decayed copy, as rows
-      if constexpr (OUT) st4(Zs + tau_w * LDZ + 16 * ti + 4 * g, z);
-      st4(Zts + tau_w * LDT + 16 * ti + 4 * g, DEC ? z * ztf : z);
+      if constexpr (OUT) st4(Zs + tau_w * LDZ + 16 * ti + ((4 * g) ^ w8_swl(lane)), z);
+      st4(Zts + tau_w * LDT + 16 * ti + ((4 * g) ^ w8_swl(lane)), DEC ? z * ztf : z);
 #pragma unroll
       for (int j = 0; j < SCT; ++j) {
         f32x4 acc = DEC ? Sacc[i][j] * g64 : Sacc[i][j];
@@ -577,17 +617,22 @@ __device__ __forceinline__ void walk8_body(const WalkArgs &a, const int bh, cons
       // W^T tiles J = 2h, 2h+1 of the block (rows j, column tau) -> masked, decayed -> W rows
       // in LDS; the half's part of den
       float rs = 0.f;
+      f32x4 wt[2];
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
         const int J = 2 * hh + jj;
-        f32x4 wt = zero4();
+        wt[jj] = zero4();
 #pragma unroll
-        for (int s = 0; s < KD; ++s) wt = mma(w8_rows(Zs, LDZ, 16 * J, 32 * s, lane), qw[s], wt);
+        for (int s = 0; s < KD; ++s)
+          wt[jj] = mma(w8_rows_sw(Zs, LDZ, 16 * J, 32 * s, lane), qw[s], wt[jj]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) wt[r] *= fw[jj][r];
-        if constexpr (DEN) rs += (wt[0] + wt[1]) + (wt[2] + wt[3]);
-        st4(Ws + tau_w * LDW + w8_wpos(16 * J + 4 * g), wt);
+        for (int r = 0; r < 4; ++r) wt[jj][r] *= fw[jj][r];
+        if constexpr (DEN) rs += (wt[jj][0] + wt[jj][1]) + (wt[jj][2] + wt[jj][3]);
       }
+      // tiles J = 2h and 2h + 1 of a W row sit side by side (w8_wpos): one 16-byte piece
+      *(bf16x8 *)(Ws + tau_w * LDW + ((32 * hh + 8 * g) ^ w8_swl(lane))) =
+          bf16x8{(bf16)wt[0][0], (bf16)wt[0][1], (bf16)wt[0][2], (bf16)wt[0][3],
+                 (bf16)wt[1][0], (bf16)wt[1][1], (bf16)wt[1][2], (bf16)wt[1][3]};
       if constexpr (DEN) {
         // den_tau = g^{2(tau+1)} q_tau . u0 + sum_j W[tau][j]: the first half adds the carried term
         float qu = 0.f;
@@ -612,7 +657,7 @@ __device__ __forceinline__ void walk8_body(const WalkArgs &a, const int bh, cons
 #pragma unroll
       for (int i = 0; i < RT; ++i)
 #pragma unroll
-        for (int s = 0; s < KC; ++s) zt[i][s] = ld_cols(Zts, LDT, 32 * s, 16 * i, lane);
+        for (int s = 0; s < KC; ++s) zt[i][s] = w8_cols_sw(Zts, LDT, 32 * s, 16 * i, lane);
 #pragma unroll
       for (int i = 0; i < RT; ++i)
 #pragma unroll
@@ -625,7 +670,7 @@ __device__ __forceinline__ void walk8_body(const WalkArgs &a, const int bh, cons
       if constexpr (DEN) {
         f32x4 acc = DEC ? uacc * g128 : uacc;
 #pragma unroll
-        for (int s = 0; s < KC; ++s) acc = mma(ld_cols(Zts, LDT, 32 * s, 16 * urow, lane), ones, acc);
+        for (int s = 0; s < KC; ++s) acc = mma(w8_cols_sw(Zts, LDT, 32 * s, 16 * urow, lane), ones, acc);
         uacc = acc;
         if constexpr (OUT) write_u0((c + 1) & 1);
       }
@@ -654,15 +699,11 @@ __device__ __forceinline__ void walk8_body(const WalkArgs &a, const int bh, cons
         // fragment, each from its own opaque base
         bf16x8 qf[KD];
 #pragma unroll
-        for (int s = 0; s < KD; ++s) {
-          const unsigned a0 = w8_lds_addr(Qc + (16 * r + n) * LDQ + 32 * s + 4 * g);
-          const unsigned a1 = w8_lds_addr(Qc + (16 * r + n) * LDQ + 32 * s + 16 + 4 * g);
-          qf[s] = cat8(w8_ld4(a0), w8_ld4(a1));
-        }
+        for (int s = 0; s < KD; ++s) qf[s] = w8_rows_acc(Qc, LDQ, 16 * r, 32 * s, lane);
         bf16x8 wb[KC];
 #pragma unroll
         for (int s = 0; s < KC; ++s)
-          if (VSPLIT ? 32 * s <= 16 * rr + 15 : true) wb[s] = w8_rows(Ws, LDW, 16 * r, 32 * s, lane);
+          if (VSPLIT ? 32 * s <= 16 * rr + 15 : true) wb[s] = w8_rows_sw(Ws, LDW, 16 * r, 32 * s, lane);
 #pragma unroll
         for (int j = 0; j < UCT; ++j) {
           f32x4 o = zero4();

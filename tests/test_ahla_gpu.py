@@ -71,10 +71,14 @@ SMALL = [
     (1, 2, 2048, 64, 64, "bf16", 1.0, True, 0),
     (1, 1, 37, 128, 128, "bf16", 0.9, False, 0),
     # three segments at d = 64: segment 2 folds segment 1's summary in its prologue (ragged tail,
-    # decay, with and without the ratio)
+    # decay, with and without the ratio); without decay, or with a weak one, the folded prefix
+    # keeps its weight (a strong decay all but removes it over a segment)
     (1, 2, 900, 64, 64, "bf16", 0.97, True, 3),
     (1, 2, 900, 64, 128, "bf16", 0.95, False, 3),
     (2, 1, 1000, 48, 80, "bf16", 0.9, True, 3),
+    (1, 2, 900, 64, 64, "bf16", 1.0, True, 3),
+    (1, 2, 900, 64, 128, "bf16", 0.999, False, 3),
+    (2, 1, 1000, 48, 80, "bf16", 1.0, False, 3),
 ]
 
 

@@ -116,6 +116,34 @@ def test_lead_plan_cases(case):
     check_case(q, k, v, decay, norm, 64, "bf16", heads=heads)
 
 
+# Three-segment lead plans at d <= 64 launch no scan: segment 2's output walk folds segment 1's
+# summary onto segment 1's prefix in its prologue.  Without decay (or with a weak one) the folded
+# cross term S0 C_1 keeps its full weight (a strong decay all but removes it over a segment), so
+# these cases see a wrong fold; segment 2's tokens are also checked on their own.
+FOLD = [
+    # B, H, n, d, dv, decay, normalize, segments (0: automatic)
+    (2, 2, 777, 64, 64, 1.0, True, 0),
+    (1, 3, 1000, 64, 128, 1.0, False, 3),
+    (2, 2, 900, 48, 80, 0.999, True, 3),
+    (1, 2, 1500, 32, 128, 1.0, True, 3),
+]
+
+
+@pytest.mark.parametrize("case", FOLD, ids=lambda c: "-".join(str(x) for x in c))
+def test_prologue_fold_cases(case):
+    B, H_, n, d, dv, decay, norm, segs = case
+    nseg, c0, cs, lead = H.hla2_forward_plan(B, H_, n, d, dv, 64, segs)
+    assert lead and nseg == 3, (nseg, lead)
+    q, k, v = draw(B, H_, n, d, dv, "bf16", seed=n + d + 5)
+    check_case(q, k, v, decay, norm, 64, "bf16", segments=segs)
+    t2 = (c0 + cs) * 64  # first token of segment 2
+    num_gpu, _ = gpu_forward(q, k, v, decay, False, 64, segs, want_den=False)
+    num, _, _, _ = O.serial_unorm(q.double().numpy(), k.double().numpy(), v.double().numpy(), decay)
+    r2 = rel_l2(num_gpu[..., t2:, :], num[..., t2:, :])
+    print("segment 2 from token %d: num %.3g" % (t2, r2))
+    assert r2 <= tol_for("bf16"), r2
+
+
 # Degenerate lengths: a single token, one short of a chunk, one past a chunk, exactly one chunk
 # (both element types, ratio and decay on).
 SHORT = [

@@ -75,6 +75,10 @@ SMALL = [
     # decay, with and without the ratio)
     (1, 2, 900, 64, 128, "bf16", 0.95, False, 3),
     (2, 1, 1000, 48, 48, "bf16", 0.9, True, 3),
+    # the same without decay, or with a weak one: the folded prefix keeps its weight
+    (1, 2, 900, 64, 128, "bf16", 1.0, False, 3),
+    (1, 2, 900, 64, 64, "bf16", 1.0, True, 3),
+    (2, 1, 1000, 48, 48, "bf16", 0.999, False, 3),
 ]
 
 
