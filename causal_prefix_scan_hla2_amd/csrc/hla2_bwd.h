@@ -127,16 +127,17 @@ __device__ __forceinline__ void bwd_state_body(const BwdArgs &a, T *smem, const 
   rv.fetch(vh, a.dv, tok0, a.n, NORM ? DV : -1, tid);
 
   for (int ch = 0; ch < nch; ++ch) {
-    // state at the chunk start: a copy of S into LDS, and both into the chunk store
+    // state at the chunk start: a copy of S into LDS, and both into the chunk store (in the LDS
+    // row layout, swizzle included, so the gradient walk reads its fragments with ld_rows_l)
     T *blk = cst + (long)ch * L::BLOCK;
     for_tiles<DK, DK, NW>(w, [&](int i0, int j0, bool ok, int it) {
       if (ok) {
         st4l(Ss, L::LDQ, i0 + nn, j0 + 4 * gq, S[it]);
-        st4g(blk + (i0 + nn) * DK + pcol<T>(j0 + 4 * gq), S[it]);
+        st4g(blk + (i0 + nn) * DK + (pcol<T>(j0 + 4 * gq) ^ tsw<T>(i0 + nn, DK)), S[it]);
       }
     });
     for_tiles<DK, DVP, NW>(w, [&](int i0, int j0, bool ok, int it) {
-      if (ok) st4g(blk + DK * DK + (i0 + nn) * DVP + pcol<T>(j0 + 4 * gq), U[it]);
+      if (ok) st4g(blk + DK * DK + (i0 + nn) * DVP + (pcol<T>(j0 + 4 * gq) ^ tsw<T>(i0 + nn, DVP)), U[it]);
     });
     rq.put(Qs, L::LDQ, tid);
     rk.put(Ks, L::LDQ, tid);

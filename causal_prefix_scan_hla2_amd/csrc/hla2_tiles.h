@@ -21,6 +21,25 @@ template <> __device__ __forceinline__ int pcol<bf16>(int c) {
 }
 template <> __device__ __forceinline__ int pcol<float>(int c) { return c; }
 
+// bf16 rows are also swizzled: the 16-byte piece j of row r sits at piece j ^ s(r), with s chosen
+// by the row pitch.  LDS cycles per wave-wide access, measured on the device for this layout
+// (transpose read / 8-byte accumulator-row write / 16-byte row read / staging write of a row's
+// two 4-column groups):
+//   pitch = 32 mod 64 bytes (96, 160, 224, 288, 352): no swizzle 4 / 16 / 4 / 16;
+//                                                     s = bit 2 of r: 4 / 8 / 4 / 8;
+//   pitch = 16 mod 64 bytes (80, 144, 208, 272, 336): no swizzle 6 / 8 / 8 / 8 (8 / 8 / 8 / 8 at 272);
+//                                                     s = bit 2 ^ bit 3 of r: 6 / 8 / 4 / 4.
+// Only the first kind is swizzled: at the second (the backward's adjoint-summary role, whose 16-byte
+// padding lets two workgroups share a CU) s = bit 2 ^ bit 3 measured no faster, and the chunk states
+// in global memory keep their plain layout.  tsw is the swizzle's element
+// offset; the rows of one access differ in bits 2 and 3 only through the lane, so with the pitch a
+// compile-time constant it is a per-lane constant.
+template <typename T> __device__ __forceinline__ int tsw(int row, int ld);
+template <> __device__ __forceinline__ int tsw<bf16>(int row, int ld) {
+  return ((2 * ld) & 63) == 32 ? ((row >> 2) & 1) << 3 : 0;
+}
+template <> __device__ __forceinline__ int tsw<float>(int, int) { return 0; }
+
 // Row padding in bytes.  bf16 rows 160 or 288 bytes apart (32 bytes of padding on 128- and
 // 256-byte rows) serve 16-byte row reads and LDS transpose reads without bank conflicts
 // (measured on gfx950); fp32 rows keep 16 bytes.
@@ -28,14 +47,16 @@ template <typename T> constexpr int lds_pad_bytes() { return sizeof(T) == 2 ? 32
 
 // fragments of LDS rows / columns in that layout (k0, col0 multiples of the k-tile / 16)
 __device__ __forceinline__ bf16x8 ld_rows_l(const bf16 *X, int ld, int row0, int k0, int lane) {
-  return *(const bf16x8 *)(X + (row0 + (lane & 15)) * ld + k0 + 8 * (lane >> 4));
+  const int r = row0 + (lane & 15);
+  return *(const bf16x8 *)(X + r * ld + k0 + ((8 * (lane >> 4)) ^ tsw<bf16>(r, ld)));
 }
 __device__ __forceinline__ f32x4 ld_rows_l(const float *X, int ld, int row0, int k0, int lane) {
   return ld_rows(X, ld, row0, k0, lane);
 }
 __device__ __forceinline__ bf16x8 ld_cols_l(const bf16 *X, int ld, int k0, int col0, int lane) {
   const int g = lane >> 4, src = lane & 15;
-  const bf16 *p = X + (k0 + 4 * g + (src >> 2)) * ld + pcol<bf16>(col0 + 4 * (src & 3));
+  const int r = k0 + 4 * g + (src >> 2);  // and r + 16: the same swizzle
+  const bf16 *p = X + r * ld + (pcol<bf16>(col0 + 4 * (src & 3)) ^ tsw<bf16>(r, ld));
   s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
   s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p + 16 * ld));
   return cat8(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi));
@@ -46,7 +67,7 @@ __device__ __forceinline__ f32x4 ld_cols_l(const float *X, int ld, int k0, int c
 // four consecutive values of an LDS row at logical column c (a multiple of 4)
 template <typename T>
 __device__ __forceinline__ void st4l(T *X, int ld, int row, int c, f32x4 x) {
-  st4(X + row * ld + pcol<T>(c), x);
+  st4(X + row * ld + (pcol<T>(c) ^ tsw<T>(row, ld)), x);
 }
 
 // ---------------------------------------------------------------------------
@@ -196,10 +217,10 @@ struct RowTile {
       const int i = tid + j * NTH;
       if (EVEN || i < TOT) {
         T *row = dst + (i / PERROW) * ld;
-        const int c = (i % PERROW) * VN;
+        const int c = (i % PERROW) * VN, sw = tsw<T>(i / PERROW, ld);
         if constexpr (VN == 8) {
-          *(bf16x4 *)(row + pcol<T>(c)) = bf16x4{x[j][0], x[j][1], x[j][2], x[j][3]};
-          *(bf16x4 *)(row + pcol<T>(c + 4)) = bf16x4{x[j][4], x[j][5], x[j][6], x[j][7]};
+          *(bf16x4 *)(row + (pcol<T>(c) ^ sw)) = bf16x4{x[j][0], x[j][1], x[j][2], x[j][3]};
+          *(bf16x4 *)(row + (pcol<T>(c + 4) ^ sw)) = bf16x4{x[j][4], x[j][5], x[j][6], x[j][7]};
         } else {
           *(V *)(row + c) = x[j];
         }
