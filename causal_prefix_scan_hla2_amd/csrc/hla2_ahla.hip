@@ -350,6 +350,9 @@ hipError_t launch_ahla(int dtype, int DK, int DV, bool norm, int phase, int BH, 
     return hipErrorInvalidValue;
   }
   if (DK == 64 && DV == 64) return launch_ahla_n<bf16, 64, 64>(norm, phase, BH, a, gseg, s);
+  // without den the walks at d <= 64, dv > 64 run on the register-resident walker; the scan
+  // between them is the same
+  if (DK == 64 && DV == 128 && !norm && phase != AHLA_SCAN) return launch_ahla8(phase, BH, a, s);
   if (DK == 64 && DV == 128) return launch_ahla_n<bf16, 64, 128>(norm, phase, BH, a, gseg, s);
   if (DK == 128 && DV == 64) return launch_ahla_n<bf16, 128, 64>(norm, phase, BH, a, gseg, s);
   if (DK == 128 && DV == 128) return launch_ahla_n<bf16, 128, 128>(norm, phase, BH, a, gseg, s);

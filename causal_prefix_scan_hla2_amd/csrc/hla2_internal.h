@@ -217,6 +217,9 @@ enum { AHLA_SUMMARY = 0, AHLA_SCAN = 1, AHLA_OUTPUT = 2, AHLA_LEAD = 3 };
 // one phase of the AHLA forward; gseg = decay^(tokens per full segment) (scan)
 hipError_t launch_ahla(int dtype, int DK, int DV, bool norm, int phase, int BH, const AhlaArgs &a, float gseg,
                        hipStream_t s);
+// The register-resident walker (hla2_ahla8.hip): bf16, DK = 64, DV = 128, no den; the walk
+// phases (AHLA_SUMMARY, AHLA_OUTPUT, AHLA_LEAD) of launch_ahla for that case.
+hipError_t launch_ahla8(int phase, int BH, const AhlaArgs &a, hipStream_t s);
 
 
 // The third-order kernels (hla2_ho3.hip) take the same argument block; their
