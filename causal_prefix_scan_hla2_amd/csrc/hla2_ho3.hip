@@ -449,6 +449,9 @@ hipError_t launch_ho3(int dtype, int DK, int DV, bool norm, int phase, int BH, c
     return hipErrorInvalidValue;
   }
   if (DK == 64 && DV == 64) return launch_ho3_n<bf16, 64, 64>(norm, phase, BH, a, gseg, s);
+  // without den the walks at d <= 64, dv > 64 run on the register-resident walker; the scan
+  // between them is the same
+  if (DK == 64 && DV == 128 && !norm && phase != HO3_SCAN) return launch_ho38(phase, BH, a, s);
   if (DK == 64 && DV == 128) return launch_ho3_n<bf16, 64, 128>(norm, phase, BH, a, gseg, s);
   return hipErrorInvalidValue;
 }

@@ -228,6 +228,9 @@ using Ho3Args = AhlaArgs;
 enum { HO3_SUMMARY = 0, HO3_SCAN = 1, HO3_OUTPUT = 2, HO3_LEAD = 3 };
 hipError_t launch_ho3(int dtype, int DK, int DV, bool norm, int phase, int BH, const Ho3Args &a, float gseg,
                       hipStream_t s);
+// The register-resident walker (hla2_ho38.hip): bf16, DK = 64, DV = 128, no den; the walk phases
+// (HO3_SUMMARY, HO3_OUTPUT, HO3_LEAD) of launch_ho3 for that case.
+hipError_t launch_ho38(int phase, int BH, const Ho3Args &a, hipStream_t s);
 
 // The forward pass behind every forward entry point (hla2_api.cpp).  forward_check validates a
 // call on the host (everything but the workspace) and reports the workspace bytes it needs;

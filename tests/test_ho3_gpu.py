@@ -152,12 +152,26 @@ def test_ho3_norm_workload_all_heads():
 
 # Without a den buffer and without the ratio the walkers carry no den column (the instantiations the
 # benchmark times): the outputs are compared with the oracle's num.
+# At d <= 64 and dv > 64 these run on the register-resident walker: one segment, the plain scan
+# (five and seven segments), three-segment lead plans whose segment 2 folds segment 1's summary in its
+# prologue (with and without decay), an automatic lead plan, padded head sizes, a sequence of one
+# partial chunk, one chunk exactly and one token past it.
 NODEN = [
     # B, H, n, d, dv, decay, segments, oracle heads (None: all)
     (2, 3, 300, 64, 128, 0.99, 0, None),
     (1, 2, 777, 64, 64, 0.97, 3, None),
     (1, 1, 1000, 64, 128, 1.0, 2, None),
     (1, 1, 200, 48, 80, 0.9, 0, None),
+    (1, 2, 900, 64, 128, 0.95, 3, None),
+    (1, 2, 900, 64, 128, 0.999, 3, None),
+    (1, 2, 900, 64, 128, 1.0, 3, None),
+    (2, 1, 1000, 48, 80, 1.0, 3, None),
+    (1, 2, 4100, 64, 128, 1.0, 5, None),
+    (1, 1, 1000, 32, 112, 0.99, 7, None),
+    (4, 16, 1700, 64, 128, 0.97, 0, [(0, 3), (2, 9), (3, 14)]),
+    (1, 1, 37, 64, 128, 0.9, 0, None),
+    (2, 1, 64, 64, 128, 1.0, 0, None),
+    (2, 1, 65, 16, 96, 0.95, 0, None),
 ]
 
 
@@ -176,8 +190,13 @@ def test_ho3_without_den_matches_oracle(case):
     print("case", case, flush=True)
     q, k, v = draw(B, H_, n, d, dv, "bf16", seed=950 + n + d)
     o = gpu_ho3_noden(q, k, v, decay, segments)
+    if heads is not None:
+        idx = tuple(np.array(heads).T)
+        tidx = tuple(torch.as_tensor(x) for x in idx)
+        q, k, v, o = q[tidx], k[tidx], v[tidx], o[idx]
     num, _, _ = O.ho3_serial(q.double().numpy(), k.double().numpy(), v.double().numpy(), decay)
     r = rel_l2(o, num)
+    print("num %.3g" % r)
     assert r <= tol_for("bf16"), r
 
 
