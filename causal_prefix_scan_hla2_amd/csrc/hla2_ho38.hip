@@ -25,7 +25,7 @@
 // Per chunk there are two workgroup barriers, as in the second-order walker:
 //   [Ad, Z, Z~ -> LDS; S and P updates; operand fragments]
 //   B1
-//   [S0, next chunk's rows -> LDS; Y; Wm -> LDS; W update; maps (summary mode)]
+//   [S0, next chunk's rows -> LDS; Wm -> LDS; Y; W update; maps (summary mode)]
 //   B2
 //   [outputs]
 // Buffer loads past the end of the sequence return zero, so a ragged last chunk needs no special
@@ -426,6 +426,22 @@ __device__ __forceinline__ void ho38_body(const Ho3Args &a, const int bh, const 
     write_S0();
     store_chunk((c + 1) & 1);
 
+    if constexpr (OUT) {
+      // Wm^T tiles J = 2h, 2h+1 of the block (rows l, column tau) -> masked, decayed -> Wm rows
+      f32x4 wt[2];
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int J = 2 * hh + jj;
+        wt[jj] = zero4();
+#pragma unroll
+        for (int s = 0; s < KD; ++s) wt[jj] = mma(w8_rows_sw(Zs, LDZ, 16 * J, 32 * s, lane), qw[s], wt[jj]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) wt[jj][r] *= fw[jj][r];
+      }
+      *(bf16x8 *)(Wms + tau_w * LDW + ((32 * hh + 8 * g) ^ w8_swl(lane))) =
+          bf16x8{(bf16)wt[0][0], (bf16)wt[0][1], (bf16)wt[0][2], (bf16)wt[0][3],
+                 (bf16)wt[1][0], (bf16)wt[1][1], (bf16)wt[1][2], (bf16)wt[1][3]};
+    }
     // Y tiles (rows tau, the wave's columns) = diag(g^{tau+1}) Q P0 + Ad V: the carried-state terms
     // of all four token blocks first (independent chains), then the chunk-local ones
     f32x4 Y[NB];
@@ -454,22 +470,7 @@ __device__ __forceinline__ void ho38_body(const Ho3Args &a, const int bh, const 
 #pragma unroll
     for (int s = 0; s < KC; ++s) yb[s] = frag_from_acc(Y[2 * s], Y[2 * s + 1]);
 
-    if constexpr (OUT) {
-      // Wm^T tiles J = 2h, 2h+1 of the block (rows l, column tau) -> masked, decayed -> Wm rows
-      f32x4 wt[2];
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int J = 2 * hh + jj;
-        wt[jj] = zero4();
-#pragma unroll
-        for (int s = 0; s < KD; ++s) wt[jj] = mma(w8_rows_sw(Zs, LDZ, 16 * J, 32 * s, lane), qw[s], wt[jj]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) wt[jj][r] *= fw[jj][r];
-      }
-      *(bf16x8 *)(Wms + tau_w * LDW + ((32 * hh + 8 * g) ^ w8_swl(lane))) =
-          bf16x8{(bf16)wt[0][0], (bf16)wt[0][1], (bf16)wt[0][2], (bf16)wt[0][3],
-                 (bf16)wt[1][0], (bf16)wt[1][1], (bf16)wt[1][2], (bf16)wt[1][3]};
-    } else {
+    if constexpr (!OUT) {
       // segment maps, weights relative to the segment's end: token u = u0 + t of the chunk carries
       // g^{3L-1-u} = bq g^{63-t} (Q2) and g^{3L-2-2u} = bx g^{2(63-t)} (X1, X2)
       const int u0 = c * CP;

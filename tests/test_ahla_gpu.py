@@ -211,3 +211,17 @@ def test_ahla_without_den_decay_workload_sampled():
     num, _, _ = O.ahla_serial(q[tidx].double().numpy(), k[tidx].double().numpy(), v[tidx].double().numpy(), w.decay)
     r = rel_l2(o[idx], num)
     assert r <= tol_for(w.dtype), r
+
+def test_ahla_without_den_causal_bitwise():
+    """Causality of the no-den walker (d <= 64, dv > 64): outputs before t* are bitwise unchanged by any
+    change of the tokens from t* on, with a plain plan and with three segments (prologue fold)."""
+    q, k, v = draw(1, 2, 700, 64, 128, "bf16", seed=5)
+    for segments in (0, 3):
+        a = gpu_ahla_noden(q, k, v, 0.97, segments)
+        for tstar in (0, 63, 64, 300, 699):
+            q2, k2, v2 = q.clone(), k.clone(), v.clone()
+            q2[:, :, tstar:] *= -1
+            k2[:, :, tstar:] += 0.25
+            v2[:, :, tstar:] *= 2
+            b = gpu_ahla_noden(q2, k2, v2, 0.97, segments)
+            assert np.array_equal(a[:, :, :tstar], b[:, :, :tstar]), (segments, tstar)
