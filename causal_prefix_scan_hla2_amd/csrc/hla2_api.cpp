@@ -426,13 +426,20 @@ static size_t ahla_workspace(const Plan &p, int dtype) {
 }
 
 // AHLA and third order: one workgroup per CU; bf16 runs a lead plan.  Segment 0's share is
-// the ratio of a summary chunk to an output chunk of that walker (measured, d = 64, dv = 128,
-// one workgroup per CU: AHLA 2.75 against 3.8 us, third order 4.5 against 5.1 us).
-static Plan ahla_plan(int B, int H, int n, int d, int dv, int dtype, int segments, double rho = 0.72) {
+// about the ratio of a summary chunk to an output chunk of the walker (tile walkers, d = 64,
+// dv = 128, one workgroup per CU: AHLA 2.75 against 3.8 us, third order 4.5 against 5.1 us).
+// At d <= 64, dv > 64 the calls without den run on the register-resident walkers, for which
+// the share was measured directly at the decay workload's shape (AHLA: 0.72, 0.84, 0.95 gave
+// 218-228, 215-222, 214-217 us; third order: 0.75, 0.88, 1.0 gave 334-344, 327-338, 325-329 us).
+// The share depends only on the shape, so that the workspace query, which does not know
+// whether den is carried, sizes the same plan.
+static bool variant_register_walker(int d, int dv, int dtype) { return dtype == HLA2_BF16 && d <= 64 && dv > 64; }
+static Plan ahla_plan(int B, int H, int n, int d, int dv, int dtype, int segments, double rho = 0.0) {
+  if (rho <= 0.0) rho = variant_register_walker(d, dv, dtype) ? 0.95 : 0.72;
   return make_plan(B, H, n, d, dv, dtype == HLA2_BF16 ? 64 : 32, dtype, segments, 1, true, rho);
 }
 static Plan ho3_plan(int B, int H, int n, int d, int dv, int dtype, int segments) {
-  return ahla_plan(B, H, n, d, dv, dtype, segments, 0.88);
+  return ahla_plan(B, H, n, d, dv, dtype, segments, variant_register_walker(d, dv, dtype) ? 1.0 : 0.88);
 }
 
 size_t hla2_ahla_forward_workspace_bytes(int B, int H, int n, int d, int dv, hla2_dtype_t dtype, int segments) {
