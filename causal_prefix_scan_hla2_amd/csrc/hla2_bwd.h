@@ -70,7 +70,10 @@ struct BwdCfg : BwdPitch<T, DK, DVP, BC> {
                        G_OFF = V_OFF + BC * P::LDV, U_OFF = G_OFF + BC * P::LDV, S_OFF = U_OFF + DK * P::LDV,
                        AD_OFF = S_OFF + DK * P::LDQ, BM_OFF = AD_OFF + BC * P::LDC, W_OFF = BM_OFF + BC * P::LDC,
                        EK_OFF = W_OFF + BC * P::LDC, Z_OFF = EK_OFF + BC * P::LDC, ZB_OFF = Z_OFF + BC * P::LDQ,
-                       ELEMS = ZB_OFF + BC * P::LDQ;
+                       QT_OFF = ZB_OFF + BC * P::LDQ;
+  // at d <= 64 the rows of Q~ = diag(g^tau) Q follow (the Shat update's weighted operand)
+  static constexpr bool QT = DK <= 64;
+  static constexpr int ELEMS = QT_OFF + (QT ? BC * P::LDQ : 0);
 };
 // forward-state walk: Q, K, V', the S copy, Ad, Z
 template <typename T, int DK, int DVP, int BC>
@@ -216,8 +219,9 @@ __device__ __forceinline__ void bwd_bm_zb(T *smem, const float *pw, int w, int l
 }
 
 // Adjoint state update (registers): Ubar <- g^(2BC) Ubar + Q^T diag(g^(2tau)) G';
-// Shat <- g^BC Shat + Zb^T diag(g^tau) Q + Q^T diag(g^tau) Zb.
-template <typename T, int DK, int DVP, int BC, int NW, typename Lay>
+// Shat <- g^BC Shat + Zb^T diag(g^tau) Q + Q^T diag(g^tau) Zb.  With QT the layout holds
+// Q~ = diag(g^tau) Q as well, and the Shat update reads it instead of weighting fragments.
+template <typename T, int DK, int DVP, int BC, int NW, typename Lay, bool QT = false>
 __device__ __forceinline__ void bwd_adjoint_update(T *smem, const float *pw, int w, int lane, f32x4 *Ub, f32x4 *Sh) {
   T *const Qs = smem + Lay::Q_OFF, *const Gs = smem + Lay::G_OFF, *const Zbs = smem + Lay::ZB_OFF;
   const float gB = pw[BC], gB2 = pw[2 * BC];
@@ -225,11 +229,19 @@ __device__ __forceinline__ void bwd_adjoint_update(T *smem, const float *pw, int
     Ub[it] = ptw<true, false, BC>(gB2 * Ub[it], Qs, Lay::LDQ, Gs, Lay::LDV, i0, j0, lane,
                                   [&](int s) { return pw[2 * s]; });
   });
-  for_tiles<DK, DK, NW>(w, [&](int i0, int j0, bool, int it) {
-    f32x4 x = ptw<true, false, BC>(gB * Sh[it], Zbs, Lay::LDQ, Qs, Lay::LDQ, i0, j0, lane,
-                                   [&](int s) { return pw[s]; });
-    Sh[it] = ptw<true, false, BC>(x, Qs, Lay::LDQ, Zbs, Lay::LDQ, i0, j0, lane, [&](int s) { return pw[s]; });
-  });
+  if constexpr (QT) {
+    T *const Qts = smem + Lay::QT_OFF;
+    for_tiles<DK, DK, NW>(w, [&](int i0, int j0, bool, int it) {
+      f32x4 x = pt<true, false, BC>(gB * Sh[it], Zbs, Lay::LDQ, Qts, Lay::LDQ, i0, j0, lane);
+      Sh[it] = pt<true, false, BC>(x, Qts, Lay::LDQ, Zbs, Lay::LDQ, i0, j0, lane);
+    });
+  } else {
+    for_tiles<DK, DK, NW>(w, [&](int i0, int j0, bool, int it) {
+      f32x4 x = ptw<true, false, BC>(gB * Sh[it], Zbs, Lay::LDQ, Qs, Lay::LDQ, i0, j0, lane,
+                                     [&](int s) { return pw[s]; });
+      Sh[it] = ptw<true, false, BC>(x, Qs, Lay::LDQ, Zbs, Lay::LDQ, i0, j0, lane, [&](int s) { return pw[s]; });
+    });
+  }
 }
 
 // copies of the adjoint state for the next chunk's products (Shat only where read)
@@ -387,6 +399,7 @@ __global__ void __launch_bounds__(BWD_THREADS) bwd_walk_kernel(BwdArgs a) {
       for (int k = 0; k < DVP / KT; ++k) u0f[k] = ld_rows_l(U0, DVP, jw, k * KT, lane);
     }
     rq.put(Qs, Cfg::LDQ, tid);
+    if constexpr (Cfg::QT) rq.put_scaled(smem + Cfg::QT_OFF, Cfg::LDQ, tid, a.log2g);  // Q~ = diag(g^tau) Q
     rk.put(Ks, Cfg::LDQ, tid);
     rv.put(Vs, Cfg::LDV, tid);
     rg.put(Gs, Cfg::LDV, tid);
@@ -473,7 +486,7 @@ __global__ void __launch_bounds__(BWD_THREADS) bwd_walk_kernel(BwdArgs a) {
       x = pt<true, false, BC>(x, Eks, Cfg::LDC, Qs, Cfg::LDQ, i0, j0, lane);
       if (ok) st_out(dkh, a.d, t0 + i0 + nn, j0 + 4 * gq, a.n, x);
     });
-    bwd_adjoint_update<T, DK, DVP, BC, NW, Cfg>(smem, pw, w, lane, Ub, Sh);
+    bwd_adjoint_update<T, DK, DVP, BC, NW, Cfg, Cfg::QT>(smem, pw, w, lane, Ub, Sh);
     __syncthreads();  // every read of this chunk's LDS done
     bwd_adjoint_copy<T, DK, DVP, NW, true, Cfg>(smem, w, lane, Ub, Sh);
   }

@@ -227,6 +227,28 @@ struct RowTile {
       }
     }
   }
+  // put with row r scaled by exp2(r * log2w) (a token weight g^r); the weight is formed from the
+  // row index, so it needs no table in LDS
+  __device__ __forceinline__ void put_scaled(T *dst, int ld, int tid, float log2w) const {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int i = tid + j * NTH;
+      if (EVEN || i < TOT) {
+        const int r = i / PERROW, c = (i % PERROW) * VN, sw = tsw<T>(r, ld);
+        T *row = dst + r * ld;
+        const float wr = exp2f((float)r * log2w);
+        V y;
+#pragma unroll
+        for (int e = 0; e < VN; ++e) y[e] = (T)((float)x[j][e] * wr);
+        if constexpr (VN == 8) {
+          *(bf16x4 *)(row + (pcol<T>(c) ^ sw)) = bf16x4{y[0], y[1], y[2], y[3]};
+          *(bf16x4 *)(row + (pcol<T>(c + 4) ^ sw)) = bf16x4{y[4], y[5], y[6], y[7]};
+        } else {
+          *(V *)(row + c) = y;
+        }
+      }
+    }
+  }
 };
 
 // Tile of P = X Y where Y is symmetric or given as its transposed rows: the
