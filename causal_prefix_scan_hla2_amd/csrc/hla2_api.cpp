@@ -409,6 +409,12 @@ int hla2_backward(const void *q, const void *k, const void *v, const void *out, 
   ba.nbc = b.nbc;
   ba.nbh = (int)p.BH;
   ba.log2g = log2g;
+  // With 64-token backward chunks at d <= 64, segment 0's forward-state walk runs in two halves, the
+  // second from the first's summary: the pre-walk then has four workgroups per head, two per CU, and
+  // every CU gets one long walk and one short one instead of half the CUs getting both long ones
+  // (decay workload: 0.967 -> 0.889 ms per backward call; with the ratio at dv = 128, whose chunks
+  // are 32 tokens, it measured 0.6% slower and is not split).
+  ba.half0 = (b.split && p.DK <= 64 && b.BC == 64) ? b.half0 : 0;
   const float gL = decay < 1.0f ? (float)pow((double)decay, (double)p.cps * p.kc) : 1.0f;
   const int phases[] = {hla2::BWD_PRE, hla2::BWD_RSCAN, hla2::BWD_WALK};
   for (int ph : phases) {

@@ -94,23 +94,39 @@ constexpr int BWD_PRE_WAVES = 4, BWD_PRE_THREADS = 64 * BWD_PRE_WAVES;
 // ---------------------------------------------------------------------------
 // Forward state of every chunk of one segment: S0 and U0' at the chunk start,
 // in the element type (the precision the gradient kernel's products consume).
+// part: -1 the whole segment; with a split segment 0 (half0 > 0), 0 its first half (from the zero
+// state) and 1 its second half, which starts from the forward summary of the first (fsum block 0:
+// S | C | U | m | u; the state of a segment that starts from zero is its summary).
 template <typename T, int DK, int DV, int DVP, int BC, bool NORM, int NW>
-__device__ __forceinline__ void bwd_state_body(const BwdArgs &a, T *smem, const float *pw, int bh, int seg) {
+__device__ __forceinline__ void bwd_state_body(const BwdArgs &a, T *smem, const float *pw, int bh, int seg,
+                                               int part = -1) {
   using L = StateLay<T, DK, DVP, BC>;
   constexpr int NTH = 64 * NW;
   T *const Qs = smem + L::Q_OFF, *const Ks = smem + L::K_OFF, *const Vs = smem + L::V_OFF;
   T *const Ss = smem + L::S_OFF, *const Ads = smem + L::AD_OFF, *const Zs = smem + L::Z_OFF;
   const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 4, nn = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tok0 = seg * a.cps * a.kc, tokE = min(a.n, tok0 + a.cps * a.kc);
+  int tok0 = seg * a.cps * a.kc, tokE = min(a.n, tok0 + a.cps * a.kc);
+  if (part == 0) tokE = a.half0 * a.kc;
+  if (part == 1) tok0 = a.half0 * a.kc;
   const int nch = (tokE - tok0 + BC - 1) / BC, c0 = tok0 / BC;
   const T *qh = (const T *)a.q + (long)bh * a.n * a.d, *kh = (const T *)a.k + (long)bh * a.n * a.d;
   const T *vh = (const T *)a.v + (long)bh * a.n * a.dv;
   T *cst = (T *)a.cstate + ((long)bh * a.nbc + c0) * L::BLOCK;
 
   f32x4 S[TileCount<DK, DK, NW>::PER], U[TileCount<DK, DVP, NW>::PER];
-  // incoming state from the scanned prefix (zero for the first segment)
-  const float *pref = (a.prefix && seg > 0) ? a.prefix + ((long)bh * a.nseg + seg) * prefix_block_floats(DK, DV) : nullptr;
+  // incoming state: the scanned prefix (S | U | u), the first half's summary (S | C | U | m | u) for
+  // a second half, or zero for the first segment
+  const float *pref = nullptr, *pU = nullptr, *pu = nullptr;
+  if (part == 1) {
+    pref = a.fsum + (long)bh * 2 * sum_block_floats(DK, DV);
+    pU = pref + DK * DK + DK * DV;
+    pu = pU + DK * DV + DK;
+  } else if (a.prefix && seg > 0) {
+    pref = a.prefix + ((long)bh * a.nseg + seg) * prefix_block_floats(DK, DV);
+    pU = pref + DK * DK;
+    pu = pU + DK * DV;
+  }
   for_tiles<DK, DK, NW>(w, [&](int i0, int j0, bool, int it) {
     S[it] = pref ? *(const f32x4 *)(pref + (i0 + nn) * DK + j0 + 4 * gq) : zero4();
   });
@@ -118,8 +134,8 @@ __device__ __forceinline__ void bwd_state_body(const BwdArgs &a, T *smem, const 
     f32x4 x = zero4();
     if (pref) {
       const int r = i0 + nn, c = j0 + 4 * gq;
-      if (c < DV) x = *(const f32x4 *)(pref + DK * DK + r * DV + c);
-      else if (NORM && c == DV) x[0] = pref[DK * DK + DK * DV + r];
+      if (c < DV) x = *(const f32x4 *)(pU + r * DV + c);
+      else if (NORM && c == DV) x[0] = pu[r];
     }
     U[it] = x;
   });
@@ -328,8 +344,24 @@ __global__ void __launch_bounds__(BWD_PRE_THREADS, MINW) bwd_pre_kernel(BwdArgs 
   __shared__ float pw[2 * BC + 3];
   for (int e = threadIdx.x; e < 2 * BC + 3; e += BWD_PRE_THREADS) pw[e] = exp2f((float)e * a.log2g);
   __syncthreads();
-  const int nstate = (int)(gridDim.x - (unsigned)(a.nbh * (a.nseg - 1)));
   const int b = blockIdx.x;
+  // (d <= 64 only: at d = 128 the extra role copies would push the register allocation into spills)
+  if (DK <= 64 && a.half0 > 0) {
+    // two segments, segment 0's forward-state walk split in halves: the adjoint summaries and the
+    // state walks of segment 1 first, then the halves of segment 0 (four workgroups per head, two
+    // per CU, so that every CU gets a long walk and a short one)
+    const int nb = a.nbh;
+    if (b < nb) {
+      bwd_rsum_body<T, DK, DV, DVP, BC, NORM, BWD_PRE_WAVES>(a, smem, pw, b, 1);
+    } else if (b < 2 * nb) {
+      bwd_state_body<T, DK, DV, DVP, BC, NORM, BWD_PRE_WAVES>(a, smem, pw, b - nb, 1);
+    } else {
+      const int i = b - 2 * nb;
+      bwd_state_body<T, DK, DV, DVP, BC, NORM, BWD_PRE_WAVES>(a, smem, pw, i / 2, 0, i % 2);
+    }
+    return;
+  }
+  const int nstate = (int)(gridDim.x - (unsigned)(a.nbh * (a.nseg - 1)));
   if (b < nstate) {
     bwd_state_body<T, DK, DV, DVP, BC, NORM, BWD_PRE_WAVES>(a, smem, pw, b / a.nseg, b % a.nseg);
   } else {

@@ -138,7 +138,9 @@ static hipError_t launch_bwd_t(int phase, int BH, const BwdArgs &a, const BwdPre
         return hipErrorInvalidValue;
       }
     case BWD_PRE:
-      hipLaunchKernelGGL((bwd_pre_kernel<T, DK, DV, DVP, BC, NORM, DK <= 64 ? 2 : 1>), dim3(BH * a.nseg + BH * (a.nseg - 1)),
+      if (a.half0 > 0 && (DK > 64 || a.nseg != 2 || (a.half0 * a.kc) % BC != 0)) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((bwd_pre_kernel<T, DK, DV, DVP, BC, NORM, DK <= 64 ? 2 : 1>),
+                         dim3(BH * a.nseg + BH * (a.nseg - 1) + (a.half0 > 0 ? BH : 0)),
                          dim3(BWD_PRE_THREADS), 0, s, a);
       return hipGetLastError();
     case BWD_RSCAN:

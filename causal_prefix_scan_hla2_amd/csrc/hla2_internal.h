@@ -155,6 +155,8 @@ struct BwdArgs {
   int nbc;                 // backward chunks per head
   int nbh;                 // B * H
   float log2g;             // log2(decay)
+  int half0 = 0;           // > 0 (two segments): segment 0's forward-state walk in two halves, the
+                           // second from fsum block 0 (the first half's summary); chunks of kc tokens
 };
 // Arguments of the ratio's upstream-gradient preparation.
 struct BwdPrepArgs {

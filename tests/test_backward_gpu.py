@@ -71,6 +71,13 @@ SMALL = [
     (1, 1, 200, 48, 80, "bf16", 0.9, True, 2),
     (1, 1, 37, 128, 128, "bf16", 0.9, False, 0),
     (1, 2, 777, 64, 128, "bf16", 0.97, True, 3),  # ratio at dv = 128: 32-token chunks
+    # two segments with 64-token chunks: segment 0's forward-state walk runs in two halves, the
+    # second starting from the first half's summary (with and without decay, with the den column,
+    # ragged tails)
+    (1, 2, 900, 64, 64, "bf16", 0.99, False, 2),
+    (1, 1, 1000, 64, 128, "bf16", 1.0, False, 2),
+    (2, 1, 777, 48, 48, "bf16", 0.95, True, 2),
+    (1, 1, 1300, 32, 96, "bf16", 0.999, False, 2),
 ]
 
 
