@@ -37,7 +37,8 @@
 // Per chunk there are two workgroup barriers:
 //   [A, Z, Z~ -> LDS; S update; C, m updates; operand fragments to registers]
 //   B1
-//   [S0 -> LDS; next chunk's K, Q, V -> LDS; W -> LDS; den parts; U, u updates]
+//   [S0 -> LDS; W -> LDS; den parts; next chunk's K, Q, V -> LDS; U, u updates]
+//   (the next chunk's rows go in before W except at d = 64, dv = 128)
 //   B2
 //   [outputs]
 // The next chunk's global loads are issued at the top of a chunk and land in LDS after B1, so
@@ -611,7 +612,11 @@ __device__ __forceinline__ void walk8_body(const WalkArgs &a, const int bh, cons
     // the previous chunk's staged outputs (none before the first chunk: row base n)
     flush_out(__builtin_amdgcn_readfirstlane(c > 0 ? tok0 + (c - 1) * CP : a.n));
     write_S0();
-    store_chunk(OUT ? ((c + 1) & 1) : 0);
+    // the next chunk's rows into LDS: this waits for their loads, so at d = 64, dv = 128 it comes
+    // after the W tiles, whose products then overlap the wait (measured: decay workload 0.2313-0.2320
+    // -> 0.2282-0.2295 ms; at dv = 64 and at d = 128 that order was 1% and 4% slower)
+    constexpr bool LATE_STAGE = DK <= 64 && DV > 64;
+    if constexpr (!LATE_STAGE) store_chunk(OUT ? ((c + 1) & 1) : 0);
 
     if constexpr (OUT) {
       // W^T tiles J = 2h, 2h+1 of the block (rows j, column tau) -> masked, decayed -> W rows
@@ -650,6 +655,8 @@ __device__ __forceinline__ void walk8_body(const WalkArgs &a, const int bh, cons
         if (g == 0) dens[hh][tau_w] = part;
       }
     }
+
+    if constexpr (LATE_STAGE) store_chunk(OUT ? ((c + 1) & 1) : 0);
 
     // U <- g^128 U + Z~^T V (the wave's columns); u likewise with the ones column
     {
