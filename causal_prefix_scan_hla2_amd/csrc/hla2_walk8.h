@@ -205,12 +205,16 @@ __device__ __forceinline__ void walk8_body(const WalkArgs &a, const int bh, cons
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tb = w & 3, hh = w >> 2;  // token block, half
+  // half and token block; at d <= 64 the second wave of SIMD w % 4 takes block 3 - (w % 4), so
+  // that every SIMD holds one block near the chunk's start (few unmasked key blocks) and one near
+  // its end, and the products over key blocks that the causal mask zeroes whole are skipped
+  constexpr bool CSKIP = DK <= 64;
+  const int hh = w >> 2, tb = (CSKIP && hh) ? 3 - (w & 3) : (w & 3);
   const int srow0 = hh * SRT;         // first d-row tile of the wave's S and Z^T tiles
   const int scol0 = tb * SCT;         // first column tile of the wave's S tiles
   const int urow = w % RT;            // u (and m) row tile; at d = 64 the second half repeats the first
   const bool u_owner = w < RT;        // writes u, m
-  const bool v_owner = VSPLIT || hh == 0;  // writes its U, C tiles (at dv = 64 both halves hold tile tb)
+  const bool v_owner = VSPLIT || hh == 0;  // writes its U, C tiles (at dv = 64 each half holds every tile once, as tile tb)
   const int rblk0 = VSPLIT ? 0 : 2 * hh;   // first output token block
   // value column tile j of the wave (of U, C, V and the outputs)
   auto vtile = [&](int j) __attribute__((always_inline)) -> int { return VSPLIT ? w * UCT + j : tb; };
@@ -497,19 +501,21 @@ __device__ __forceinline__ void walk8_body(const WalkArgs &a, const int bh, cons
 #pragma unroll
     for (int s = 0; s < KD; ++s) qw[s] = w8_rows(Qc, LDQ, 16 * tb, 32 * s, lane);
 
-    // A^T tiles (rows i, column tau of the block) -> masked, decayed -> Ad^T fragments.  Every
-    // wave computes all four tiles and zeroes those above its block (factor 0), so no
-    // product sits under a branch.
+    // A^T tiles (rows i, column tau of the block) -> masked, decayed -> Ad^T fragments.  Tiles
+    // above the wave's block are zero (at d <= 64 skipped under a wave-uniform branch, else
+    // computed and scaled by a zero factor).
     bf16x8 adf[KC];
     {
       f32x4 at[NB];
 #pragma unroll
       for (int I = 0; I < NB; ++I) {
         at[I] = zero4();
+        if (!CSKIP || I <= tb) {  // key blocks after the wave's block are masked whole
 #pragma unroll
-        for (int s = 0; s < KD; ++s) at[I] = mma(w8_rows(Ks, LDK, 16 * I, 32 * s, lane), qw[s], at[I]);
+          for (int s = 0; s < KD; ++s) at[I] = mma(w8_rows(Ks, LDK, 16 * I, 32 * s, lane), qw[s], at[I]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) at[I][r] *= fa[I][r];
+          for (int r = 0; r < 4; ++r) at[I][r] *= fa[I][r];
+        }
       }
 #pragma unroll
       for (int s = 0; s < KC; ++s) adf[s] = frag_from_acc(at[2 * s], at[2 * s + 1]);
@@ -542,7 +548,8 @@ __device__ __forceinline__ void walk8_body(const WalkArgs &a, const int bh, cons
       for (int s = 0; s < KD; ++s) z = mma(w8_rows_sw(Sb, LDS0, 16 * ti, 32 * s, lane), qw[s], z);
       if (DEC) z *= zf;
 #pragma unroll
-      for (int s = 0; s < KC; ++s) z = mma(kt[s], adf[s], z);
+      for (int s = 0; s < KC; ++s)
+        if (!CSKIP || 32 * s <= 16 * tb + 15) z = mma(kt[s], adf[s], z);
       // Z[tau][16 ti + 4 g + r] and its decayed copy, as rows
       if constexpr (OUT) st4(Zs + tau_w * LDZ + 16 * ti + ((4 * g) ^ w8_swl(lane)), z);
       st4(Zts + tau_w * LDT + 16 * ti + ((4 * g) ^ w8_swl(lane)), DEC ? z * ztf : z);
@@ -627,11 +634,13 @@ __device__ __forceinline__ void walk8_body(const WalkArgs &a, const int bh, cons
       for (int jj = 0; jj < 2; ++jj) {
         const int J = 2 * hh + jj;
         wt[jj] = zero4();
+        if (!CSKIP || J <= tb) {
 #pragma unroll
-        for (int s = 0; s < KD; ++s)
-          wt[jj] = mma(w8_rows_sw(Zs, LDZ, 16 * J, 32 * s, lane), qw[s], wt[jj]);
+          for (int s = 0; s < KD; ++s)
+            wt[jj] = mma(w8_rows_sw(Zs, LDZ, 16 * J, 32 * s, lane), qw[s], wt[jj]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) wt[jj][r] *= fw[jj][r];
+          for (int r = 0; r < 4; ++r) wt[jj][r] *= fw[jj][r];
+        }
         if constexpr (DEN) rs += (wt[jj][0] + wt[jj][1]) + (wt[jj][2] + wt[jj][3]);
       }
       // tiles J = 2h and 2h + 1 of a W row sit side by side (w8_wpos): one 16-byte piece
