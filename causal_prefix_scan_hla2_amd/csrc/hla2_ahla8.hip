@@ -87,7 +87,10 @@ __device__ __forceinline__ void ahla8_body(const AhlaArgs &a, const int bh, cons
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tb = w & 3, hh = w >> 2;  // token block and key-block pair of the wave's Ad tiles
+  // key-block pair and token block of the wave's Ad tiles: the second wave of SIMD w % 4 takes block
+  // 3 - (w % 4), so that the tiles the causal mask zeroes whole (skipped under a wave-uniform branch)
+  // are spread over the SIMDs
+  const int hh = w >> 2, tb = hh ? 3 - (w & 3) : (w & 3);
   const int vc0 = 16 * w;             // first value column of the wave
 
   const int d = a.d, dv = a.dv;
@@ -266,10 +269,12 @@ __device__ __forceinline__ void ahla8_body(const AhlaArgs &a, const int bh, cons
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
         at[jj] = zero4();
+        if (2 * hh + jj <= tb) {
 #pragma unroll
-        for (int s = 0; s < KD; ++s) at[jj] = mma(w8_rows(Kc, LDK, 16 * (2 * hh + jj), 32 * s, lane), qw[s], at[jj]);
+          for (int s = 0; s < KD; ++s) at[jj] = mma(w8_rows(Kc, LDK, 16 * (2 * hh + jj), 32 * s, lane), qw[s], at[jj]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) at[jj][r] *= fa[jj][r];
+          for (int r = 0; r < 4; ++r) at[jj][r] *= fa[jj][r];
+        }
       }
       *(bf16x8 *)(Ads + tau_w * LDA + ((32 * hh + 8 * g) ^ w8_swl(lane))) =
           bf16x8{(bf16)at[0][0], (bf16)at[0][1], (bf16)at[0][2], (bf16)at[0][3],

@@ -108,7 +108,10 @@ __device__ __forceinline__ void ho38_body(const Ho3Args &a, const int bh, const 
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tb = w & 3, hh = w >> 2;  // token block, half
+  // half and token block: the second wave of SIMD w % 4 takes block 3 - (w % 4), so every SIMD holds
+  // one block near the chunk's start and one near its end, and the products over key blocks that the
+  // causal mask zeroes whole (A, Z, Wm) are skipped under wave-uniform branches
+  const int hh = w >> 2, tb = hh ? 3 - (w & 3) : (w & 3);
   const int srow0 = hh * SRT;         // first d-row tile of the wave's S and Z^T tiles
   const int scol0 = tb * SCT;         // column tile of the wave's S tile
   const int vc0 = 16 * w;             // first value column of the wave
@@ -364,10 +367,12 @@ __device__ __forceinline__ void ho38_body(const Ho3Args &a, const int bh, const 
 #pragma unroll
       for (int I = 0; I < NB; ++I) {
         at[I] = zero4();
+        if (I <= tb) {  // key blocks after the wave's block are masked whole
 #pragma unroll
-        for (int s = 0; s < KD; ++s) at[I] = mma(w8_rows(Ks, LDK, 16 * I, 32 * s, lane), qw[s], at[I]);
+          for (int s = 0; s < KD; ++s) at[I] = mma(w8_rows(Ks, LDK, 16 * I, 32 * s, lane), qw[s], at[I]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) at[I][r] *= fa[I][r];
+          for (int r = 0; r < 4; ++r) at[I][r] *= fa[I][r];
+        }
       }
 #pragma unroll
       for (int s = 0; s < KC; ++s) adf[s] = frag_from_acc(at[2 * s], at[2 * s + 1]);
@@ -387,7 +392,8 @@ __device__ __forceinline__ void ho38_body(const Ho3Args &a, const int bh, const 
       for (int s = 0; s < KD; ++s) z = mma(w8_rows_sw(Sb, LDS0, 16 * ti, 32 * s, lane), qw[s], z);
       z *= zf;
 #pragma unroll
-      for (int s = 0; s < KC; ++s) z = mma(kt[s], adf[s], z);
+      for (int s = 0; s < KC; ++s)
+        if (32 * s <= 16 * tb + 15) z = mma(kt[s], adf[s], z);
       st4(Zs + tau_w * LDZ + 16 * ti + ((4 * g) ^ w8_swl(lane)), z);
       st4(Zts + tau_w * LDT + 16 * ti + ((4 * g) ^ w8_swl(lane)), z * ztf);
 #pragma unroll
@@ -433,10 +439,12 @@ __device__ __forceinline__ void ho38_body(const Ho3Args &a, const int bh, const 
       for (int jj = 0; jj < 2; ++jj) {
         const int J = 2 * hh + jj;
         wt[jj] = zero4();
+        if (J <= tb) {
 #pragma unroll
-        for (int s = 0; s < KD; ++s) wt[jj] = mma(w8_rows_sw(Zs, LDZ, 16 * J, 32 * s, lane), qw[s], wt[jj]);
+          for (int s = 0; s < KD; ++s) wt[jj] = mma(w8_rows_sw(Zs, LDZ, 16 * J, 32 * s, lane), qw[s], wt[jj]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) wt[jj][r] *= fw[jj][r];
+          for (int r = 0; r < 4; ++r) wt[jj][r] *= fw[jj][r];
+        }
       }
       *(bf16x8 *)(Wms + tau_w * LDW + ((32 * hh + 8 * g) ^ w8_swl(lane))) =
           bf16x8{(bf16)wt[0][0], (bf16)wt[0][1], (bf16)wt[0][2], (bf16)wt[0][3],
