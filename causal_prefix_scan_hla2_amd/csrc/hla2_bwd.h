@@ -183,10 +183,11 @@ __device__ __forceinline__ void bwd_state_body(const BwdArgs &a, T *smem, const 
     });
     __syncthreads();
     // Z = diag(g^(tau+1)) Q S0 + Ad K
-    for_tiles<BC, DK, NW>(w, [&](int i0, int j0, bool ok, int) {
+    for_tiles<BC, DK, NW>(w, [&](int i0, int j0, bool ok, int it) {
       f32x4 x = pt<false, true, DK>(zero4(), Qs, L::LDQ, Ss, L::LDQ, i0, j0, lane);
       x *= pw[i0 + nn + 1];
-      x = pt<false, false, BC>(x, Ads, L::LDC, Ks, L::LDQ, i0, j0, lane);
+      x = pt_tri<false, false, BC>(x, Ads, L::LDC, Ks, L::LDQ, i0, j0, lane, tile_rows_lo<BC, DK, NW>(it),
+                                   tile_rows_hi<BC, DK, NW>(it));
       if (ok) st4l(Zs, L::LDQ, i0 + nn, j0 + 4 * gq, x);
     });
     __syncthreads();
@@ -226,10 +227,11 @@ __device__ __forceinline__ void bwd_bm_zb(T *smem, const float *pw, int w, int l
   });
   __syncthreads();
   // Zb = Bm^T Q + diag(g^(2(BC-tau))) V' Ubar^T
-  for_tiles<BC, DK, NW>(w, [&](int i0, int j0, bool ok, int) {
+  for_tiles<BC, DK, NW>(w, [&](int i0, int j0, bool ok, int it) {
     f32x4 x = pt<false, true, DVP>(zero4(), Vs, Lay::LDV, Ubs, Lay::LDV, i0, j0, lane);
     x *= pw[2 * (BC - (i0 + nn))];
-    x = pt<true, false, BC>(x, Bms, Lay::LDC, Qs, Lay::LDQ, i0, j0, lane);
+    x = pt_tri<true, false, BC>(x, Bms, Lay::LDC, Qs, Lay::LDQ, i0, j0, lane, tile_rows_lo<BC, DK, NW>(it),
+                                tile_rows_hi<BC, DK, NW>(it));
     if (ok) st4l(Zbs, Lay::LDQ, i0 + nn, j0 + 4 * gq, x);
   });
 }
@@ -459,10 +461,11 @@ __global__ void __launch_bounds__(BWD_THREADS) bwd_walk_kernel(BwdArgs a) {
     // Bm, then Zb (one barrier inside)
     bwd_bm_zb<T, DK, DVP, BC, NW, Cfg>(smem, pw, w, lane);
     // Z = diag(g^(tau+1)) Q S0 + Ad K   (Ad is complete: the barrier inside bwd_bm_zb)
-    for_tiles<BC, DK>(w, [&](int i0, int j0, bool ok, int) {
+    for_tiles<BC, DK>(w, [&](int i0, int j0, bool ok, int it) {
       f32x4 x = pt_frags<DK>(zero4(), s0f, Qs, Cfg::LDQ, i0, lane);
       x *= pw[i0 + nn + 1];
-      x = pt<false, false, BC>(x, Ads, Cfg::LDC, Ks, Cfg::LDQ, i0, j0, lane);
+      x = pt_tri<false, false, BC>(x, Ads, Cfg::LDC, Ks, Cfg::LDQ, i0, j0, lane, tile_rows_lo<BC, DK>(it),
+                                   tile_rows_hi<BC, DK>(it));
       if (ok) st4l(Zs, Cfg::LDQ, i0 + nn, j0 + 4 * gq, x);
     });
     __syncthreads();
@@ -493,29 +496,32 @@ __global__ void __launch_bounds__(BWD_THREADS) bwd_walk_kernel(BwdArgs a) {
     });
     __syncthreads();
     // dV' = W^T G' + diag(g^(2(BC-tau))) Z Ubar
-    for_tiles<BC, DVP>(w, [&](int i0, int j0, bool ok, int) {
+    for_tiles<BC, DVP>(w, [&](int i0, int j0, bool ok, int it) {
       f32x4 x = pt<false, false, DK>(zero4(), Zs, Cfg::LDQ, Ubs, Cfg::LDV, i0, j0, lane);
       x *= pw[2 * (BC - (i0 + nn))];
-      x = pt<true, false, BC>(x, Ws, Cfg::LDC, Gs, Cfg::LDV, i0, j0, lane);
+      x = pt_tri<true, false, BC>(x, Ws, Cfg::LDC, Gs, Cfg::LDV, i0, j0, lane, tile_rows_lo<BC, DVP>(it),
+                                  tile_rows_hi<BC, DVP>(it));
       if (ok) st_out(dvh, a.dv, t0 + i0 + nn, j0 + 4 * gq, a.n, x);
     });
     // dQ = diag(g^(tau+1)) [diag(g^(tau+1)) G' U0'^T + Zb S0] + Bm Z + Ek K
-    for_tiles<BC, DK>(w, [&](int i0, int j0, bool ok, int) {
+    for_tiles<BC, DK>(w, [&](int i0, int j0, bool ok, int it) {
+      const int rlo = tile_rows_lo<BC, DK>(it), rhi = tile_rows_hi<BC, DK>(it);
       const float gt = pw[i0 + nn + 1];
       f32x4 x = pt_frags<DVP>(zero4(), u0f, Gs, Cfg::LDV, i0, lane);
       x *= gt;
       x = pt_frags<DK>(x, s0f, Zbs, Cfg::LDQ, i0, lane);
       x *= gt;
-      x = pt<false, false, BC>(x, Bms, Cfg::LDC, Zs, Cfg::LDQ, i0, j0, lane);
-      x = pt<false, false, BC>(x, Eks, Cfg::LDC, Ks, Cfg::LDQ, i0, j0, lane);
+      x = pt_tri<false, false, BC>(x, Bms, Cfg::LDC, Zs, Cfg::LDQ, i0, j0, lane, rlo, rhi);
+      x = pt_tri<false, false, BC>(x, Eks, Cfg::LDC, Ks, Cfg::LDQ, i0, j0, lane, rlo, rhi);
       if (ok) st_out(dqh, a.d, t0 + i0 + nn, j0 + 4 * gq, a.n, x);
     });
     // dK = Ad^T Zb + Ek^T Q + diag(g^(BC-tau)) K Shat
-    for_tiles<BC, DK>(w, [&](int i0, int j0, bool ok, int) {
+    for_tiles<BC, DK>(w, [&](int i0, int j0, bool ok, int it) {
+      const int rlo = tile_rows_lo<BC, DK>(it), rhi = tile_rows_hi<BC, DK>(it);
       f32x4 x = pt<false, true, DK>(zero4(), Ks, Cfg::LDQ, Shs, Cfg::LDQ, i0, j0, lane);
       x *= pw[BC - (i0 + nn)];
-      x = pt<true, false, BC>(x, Ads, Cfg::LDC, Zbs, Cfg::LDQ, i0, j0, lane);
-      x = pt<true, false, BC>(x, Eks, Cfg::LDC, Qs, Cfg::LDQ, i0, j0, lane);
+      x = pt_tri<true, false, BC>(x, Ads, Cfg::LDC, Zbs, Cfg::LDQ, i0, j0, lane, rlo, rhi);
+      x = pt_tri<true, false, BC>(x, Eks, Cfg::LDC, Qs, Cfg::LDQ, i0, j0, lane, rlo, rhi);
       if (ok) st_out(dkh, a.d, t0 + i0 + nn, j0 + 4 * gq, a.n, x);
     });
     bwd_adjoint_update<T, DK, DVP, BC, NW, Cfg, Cfg::QT>(smem, pw, w, lane, Ub, Sh);

@@ -110,6 +110,26 @@ template <bool XT, bool YT, int K, typename T>
 __device__ __forceinline__ f32x4 pt(f32x4 acc, const T *X, int ldx, const T *Y, int ldy, int i0, int j0, int lane) {
   return mm<!YT, !XT, K>(acc, Y, ldy, X, ldx, j0, i0, lane);
 }
+// pt with a causally masked X over the contraction: X(i, k) = 0 for k > i, or with XT (X held as the
+// rows of a lower triangle, X(i, k) = L(k, i)) X(i, k) = 0 for k < i.  The tile's rows lie in
+// [rlo, rhi + 16); a k-tile that misses the triangle for all of them adds only zeros and is skipped.
+// Callers pass bounds that are constants once the tile loop is unrolled (tile_rows_lo / hi), so no
+// branch remains.
+template <bool XT, bool YT, int K, typename T>
+__device__ __forceinline__ f32x4 pt_tri(f32x4 acc, const T *X, int ldx, const T *Y, int ldy, int i0, int j0,
+                                        int lane, int rlo, int rhi) {
+  constexpr int KT = Ktile<T>::ROWS;
+  static_assert(K % KT == 0, "contraction length must be a whole number of k-tiles");
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += KT) {
+    if (XT ? k0 + KT <= rlo : k0 >= rhi + 16) continue;
+    // as pt: the product is formed transposed, Y's fragment as the A operand
+    auto a = YT ? ld_rows_l(Y, ldy, j0, k0, lane) : ld_cols_l(Y, ldy, k0, j0, lane);
+    auto b = XT ? ld_cols_l(X, ldx, k0, i0, lane) : ld_rows_l(X, ldx, i0, k0, lane);
+    acc = mma(a, b, acc);
+  }
+  return acc;
+}
 // the same with weights w(k) on the contraction index: P = X diag(w) Y
 template <bool XT, bool YT, int K, typename T, typename WF>
 __device__ __forceinline__ f32x4 ptw(f32x4 acc, const T *X, int ldx, const T *Y, int ldy, int i0, int j0, int lane,
@@ -173,6 +193,14 @@ __device__ __forceinline__ void for_tiles(int w, F &&f) {
 template <int I, int J, int NW = BWD_WAVES> struct TileCount {
   static constexpr int NT = (I / 16) * (J / 16), PER = (NT + NW - 1) / NW;
 };
+// First rows of the lowest and highest tile any wave holds at step `it` of for_tiles<I, J, NW>.
+template <int I, int J, int NW = BWD_WAVES>
+__device__ __forceinline__ constexpr int tile_rows_lo(int it) { return 16 * ((NW * it) / (J / 16)); }
+template <int I, int J, int NW = BWD_WAVES>
+__device__ __forceinline__ constexpr int tile_rows_hi(int it) {
+  constexpr int NT = (I / 16) * (J / 16);
+  return 16 * ((NW * it + NW - 1 < NT ? NW * it + NW - 1 : NT - 1) / (J / 16));
+}
 
 // 16-byte vector of the element type
 template <typename T> struct Vec16;
