@@ -42,9 +42,11 @@
 //                      states (fetched a chunk phase ahead) and writes dq, dk, dv.
 // Every product is a set of 16x16 MFMA tiles computed transposed, so that a
 // lane holds four consecutive columns of one row of the result; the waves of
-// a workgroup take the tiles in turn.  MFMAs never sit under a runtime branch: tile
-// loops have compile-time trip counts, and a wave with no tile left repeats
-// the last one without storing it.
+// a workgroup take the tiles in turn.  Tile loops have compile-time trip counts,
+// and a wave with no tile left repeats the last one without storing it.  The
+// only MFMAs under a (wave-uniform) branch are those of the C x C tiles that the
+// causal mask zeroes whole, which are skipped (for_causal_tiles); products that
+// contract over such a matrix skip the k-tiles outside its triangle (pt_tri).
 #pragma once
 #include "hla2_internal.h"
 #include "hla2_tiles.h"
@@ -213,8 +215,9 @@ __device__ __forceinline__ void bwd_bm_zb(T *smem, const float *pw, int w, int l
   T *const Ubs = smem + Lay::U_OFF, *const Bms = smem + Lay::BM_OFF, *const Zbs = smem + Lay::ZB_OFF;
   const int gq = lane >> 4, nn = lane & 15;
   // Bm = L o D2 o (G' V'^T)   (rows s, columns tau <= s)
-  for_tiles<BC, BC, NW>(w, [&](int i0, int j0, bool ok, int) {
-    f32x4 x = pt<false, true, DVP>(zero4(), Gs, Lay::LDV, Vs, Lay::LDV, i0, j0, lane);
+  for_causal_tiles<BC, NW>(w, [&](int i0, int j0, bool ok, bool live) {
+    f32x4 x = zero4();
+    if (live) x = pt<false, true, DVP>(x, Gs, Lay::LDV, Vs, Lay::LDV, i0, j0, lane);
     const int s = i0 + nn;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -446,8 +449,9 @@ __global__ void __launch_bounds__(BWD_THREADS) bwd_walk_kernel(BwdArgs a) {
       rg.fetch(gh, a.gld, tn, a.n, -1, tid);
     }
     // Ad = L o D1 o (Q K^T)
-    for_tiles<BC, BC>(w, [&](int i0, int j0, bool ok, int) {
-      f32x4 x = pt<false, true, DK>(zero4(), Qs, Cfg::LDQ, Ks, Cfg::LDQ, i0, j0, lane);
+    for_causal_tiles<BC>(w, [&](int i0, int j0, bool ok, bool live) {
+      f32x4 x = zero4();
+      if (live) x = pt<false, true, DK>(x, Qs, Cfg::LDQ, Ks, Cfg::LDQ, i0, j0, lane);
       const int tr = i0 + nn;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -470,8 +474,9 @@ __global__ void __launch_bounds__(BWD_THREADS) bwd_walk_kernel(BwdArgs a) {
     });
     __syncthreads();
     // W = L o D2 o (Q Z^T) (rows s, columns tau <= s);  Ek = L o D1 o (Zb K^T)
-    for_tiles<BC, BC>(w, [&](int i0, int j0, bool ok, int) {
-      f32x4 x = pt<false, true, DK>(zero4(), Qs, Cfg::LDQ, Zs, Cfg::LDQ, i0, j0, lane);
+    for_causal_tiles<BC>(w, [&](int i0, int j0, bool ok, bool live) {
+      f32x4 x = zero4();
+      if (live) x = pt<false, true, DK>(x, Qs, Cfg::LDQ, Zs, Cfg::LDQ, i0, j0, lane);
       const int s = i0 + nn;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -482,8 +487,9 @@ __global__ void __launch_bounds__(BWD_THREADS) bwd_walk_kernel(BwdArgs a) {
       }
       if (ok) st4l(Ws, Cfg::LDC, s, j0 + 4 * gq, x);
     });
-    for_tiles<BC, BC>(w, [&](int i0, int j0, bool ok, int) {
-      f32x4 x = pt<false, true, DK>(zero4(), Zbs, Cfg::LDQ, Ks, Cfg::LDQ, i0, j0, lane);
+    for_causal_tiles<BC>(w, [&](int i0, int j0, bool ok, bool live) {
+      f32x4 x = zero4();
+      if (live) x = pt<false, true, DK>(x, Zbs, Cfg::LDQ, Ks, Cfg::LDQ, i0, j0, lane);
       const int tr = i0 + nn;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {

@@ -190,6 +190,21 @@ __device__ __forceinline__ void for_tiles(int w, F &&f) {
     f(16 * (tt / NJ), 16 * (tt % NJ), EVEN || t < NT, it);
   }
 }
+// The tiles of a BC x BC causally masked product: f(i0, j0, store_ok, live), live false for a tile
+// above the diagonal (zero under the mask; the caller skips its products under a wave-uniform branch
+// and still stores its zeros).  With 64-token chunks on 8 waves, wave w takes tile w and then tile
+// 8 + ((w + 3) & 7), so that the six zero tiles fall 1, 1, 2, 2 on the four SIMDs (waves w and w + 4
+// share SIMD w % 4); otherwise the order of for_tiles.
+template <int BC, int NW = BWD_WAVES, typename F>
+__device__ __forceinline__ void for_causal_tiles(int w, F &&f) {
+  if constexpr (BC == 64 && NW == 8) {
+    const int t0 = w, t1 = 8 + ((w + 3) & 7);
+    f(16 * (t0 >> 2), 16 * (t0 & 3), true, (t0 & 3) <= (t0 >> 2));
+    f(16 * (t1 >> 2), 16 * (t1 & 3), true, (t1 & 3) <= (t1 >> 2));
+  } else {
+    for_tiles<BC, BC, NW>(w, [&](int i0, int j0, bool ok, int) { f(i0, j0, ok, true); });
+  }
+}
 template <int I, int J, int NW = BWD_WAVES> struct TileCount {
   static constexpr int NT = (I / 16) * (J / 16), PER = (NT + NW - 1) / NW;
 };
