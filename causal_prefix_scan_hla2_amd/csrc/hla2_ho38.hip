@@ -108,10 +108,12 @@ __device__ __forceinline__ void ho38_body(const Ho3Args &a, const int bh, const 
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // half and token block: the second wave of SIMD w % 4 takes block 3 - (w % 4), so every SIMD holds
-  // one block near the chunk's start and one near its end, and the products over key blocks that the
-  // causal mask zeroes whole (A, Z, Wm) are skipped under wave-uniform branches
-  const int hh = w >> 2, tb = hh ? 3 - (w & 3) : (w & 3);
+  // half and token block.  In output mode the second wave of SIMD w % 4 takes block 3 - (w % 4), so
+  // every SIMD holds one block near the chunk's start and one near its end, and the products over key
+  // blocks that the causal mask zeroes whole (A, Z, Wm) are skipped under wave-uniform branches.  The
+  // summary walk keeps block w % 4 and computes them (the skip measured slower there).
+  constexpr bool CS = OUT;
+  const int hh = w >> 2, tb = (CS && hh) ? 3 - (w & 3) : (w & 3);
   const int srow0 = hh * SRT;         // first d-row tile of the wave's S and Z^T tiles
   const int scol0 = tb * SCT;         // column tile of the wave's S tile
   const int vc0 = 16 * w;             // first value column of the wave
@@ -367,7 +369,7 @@ __device__ __forceinline__ void ho38_body(const Ho3Args &a, const int bh, const 
 #pragma unroll
       for (int I = 0; I < NB; ++I) {
         at[I] = zero4();
-        if (I <= tb) {  // key blocks after the wave's block are masked whole
+        if (!CS || I <= tb) {  // key blocks after the wave's block are masked whole
 #pragma unroll
           for (int s = 0; s < KD; ++s) at[I] = mma(w8_rows(Ks, LDK, 16 * I, 32 * s, lane), qw[s], at[I]);
 #pragma unroll
@@ -393,7 +395,7 @@ __device__ __forceinline__ void ho38_body(const Ho3Args &a, const int bh, const 
       z *= zf;
 #pragma unroll
       for (int s = 0; s < KC; ++s)
-        if (32 * s <= 16 * tb + 15) z = mma(kt[s], adf[s], z);
+        if (!CS || 32 * s <= 16 * tb + 15) z = mma(kt[s], adf[s], z);
       st4(Zs + tau_w * LDZ + 16 * ti + ((4 * g) ^ w8_swl(lane)), z);
       st4(Zts + tau_w * LDT + 16 * ti + ((4 * g) ^ w8_swl(lane)), z * ztf);
 #pragma unroll
@@ -439,7 +441,7 @@ __device__ __forceinline__ void ho38_body(const Ho3Args &a, const int bh, const 
       for (int jj = 0; jj < 2; ++jj) {
         const int J = 2 * hh + jj;
         wt[jj] = zero4();
-        if (J <= tb) {
+        if (!CS || J <= tb) {
 #pragma unroll
           for (int s = 0; s < KD; ++s) wt[jj] = mma(w8_rows_sw(Zs, LDZ, 16 * J, 32 * s, lane), qw[s], wt[jj]);
 #pragma unroll
