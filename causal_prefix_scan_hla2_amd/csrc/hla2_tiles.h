@@ -194,7 +194,8 @@ __device__ __forceinline__ void for_tiles(int w, F &&f) {
 // above the diagonal (zero under the mask; the caller skips its products under a wave-uniform branch
 // and still stores its zeros).  With 64-token chunks on 8 waves, wave w takes tile w and then tile
 // 8 + ((w + 3) & 7), so that the six zero tiles fall 1, 1, 2, 2 on the four SIMDs (waves w and w + 4
-// share SIMD w % 4); otherwise the order of for_tiles.
+// share SIMD w % 4); otherwise the order of for_tiles, where a wave's repeat of the last tile (not
+// stored) is not live either.
 template <int BC, int NW = BWD_WAVES, typename F>
 __device__ __forceinline__ void for_causal_tiles(int w, F &&f) {
   if constexpr (BC == 64 && NW == 8) {
@@ -202,7 +203,7 @@ __device__ __forceinline__ void for_causal_tiles(int w, F &&f) {
     f(16 * (t0 >> 2), 16 * (t0 & 3), true, (t0 & 3) <= (t0 >> 2));
     f(16 * (t1 >> 2), 16 * (t1 & 3), true, (t1 & 3) <= (t1 >> 2));
   } else {
-    for_tiles<BC, BC, NW>(w, [&](int i0, int j0, bool ok, int) { f(i0, j0, ok, true); });
+    for_tiles<BC, BC, NW>(w, [&](int i0, int j0, bool ok, int) { f(i0, j0, ok, ok && j0 <= i0); });
   }
 }
 template <int I, int J, int NW = BWD_WAVES> struct TileCount {
