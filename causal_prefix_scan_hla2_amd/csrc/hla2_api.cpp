@@ -99,7 +99,10 @@ Plan make_plan(int B, int H, int n, int d, int dv, int chunk, int dtype, int seg
     long cps0 = nc - (r - 1) * cps;
     const long lo = (long)ceil(rho * (double)cps);
     if (cps0 < lo) cps0 = lo;
-    if (cps0 > cps) cps0 = cps;
+    // a share above 1 makes segment 0 the longer one (for walkers whose summary walk costs more per
+    // chunk than their output walk); otherwise segment 0 is never the longest
+    if (cps0 > cps && rho <= 1.0) cps0 = cps;
+    if (cps0 > nc - 1) cps0 = nc - 1;
     // spread the chunks after segment 0 evenly (never below segment 0's length), so that the
     // last segment is not the only short one
     const long even = (nc - cps0 + r - 2) / (r - 1);
@@ -436,7 +439,9 @@ static size_t ahla_workspace(const Plan &p, int dtype) {
 // dv = 128, one workgroup per CU: AHLA 2.75 against 3.8 us, third order 4.5 against 5.1 us).
 // At d <= 64, dv > 64 the calls without den run on the register-resident walkers, for which
 // the share was measured directly at the decay workload's shape (AHLA: 0.72, 0.84, 0.95 gave
-// 218-228, 215-222, 214-217 us; third order: 0.75, 0.88, 1.0 gave 334-344, 327-338, 325-329 us).
+// 218-228, 215-222, 214-217 us; third order: 0.75, 0.88, 1.0 gave 334-344, 327-338, 325-329 us,
+// and once its output walk skipped the masked tiles, 1.05 against 1.0 gave 304-323 against 316-330
+// us: its summary walk then costs more per chunk than its output walk, so segment 0 is the longest).
 // The share depends only on the shape, so that the workspace query, which does not know
 // whether den is carried, sizes the same plan.
 static bool variant_register_walker(int d, int dv, int dtype) { return dtype == HLA2_BF16 && d <= 64 && dv > 64; }
@@ -445,7 +450,7 @@ static Plan ahla_plan(int B, int H, int n, int d, int dv, int dtype, int segment
   return make_plan(B, H, n, d, dv, dtype == HLA2_BF16 ? 64 : 32, dtype, segments, 1, true, rho);
 }
 static Plan ho3_plan(int B, int H, int n, int d, int dv, int dtype, int segments) {
-  return ahla_plan(B, H, n, d, dv, dtype, segments, variant_register_walker(d, dv, dtype) ? 1.0 : 0.88);
+  return ahla_plan(B, H, n, d, dv, dtype, segments, variant_register_walker(d, dv, dtype) ? 1.05 : 0.88);
 }
 
 size_t hla2_ahla_forward_workspace_bytes(int B, int H, int n, int d, int dv, hla2_dtype_t dtype, int segments) {
